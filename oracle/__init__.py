@@ -1,0 +1,16 @@
+"""CPU oracle for the dropless MoE expert-MLP layer (test infrastructure only).
+
+Only the test-suite, the smoke check and the benchmark's CPU-baseline leg may import this
+package.  The product path (the HIP library and its binding) never touches it.
+"""
+from .oracle import (  # noqa: F401
+    build,
+    layer_bwd,
+    layer_fwd,
+    lib_path,
+    pairs_from_plan,
+    pairs_from_topk,
+    permute,
+    route_topk,
+    token_round,
+)

@@ -1,0 +1,475 @@
+/*
+ * moe_oracle.c -- plain, slow, CPU reference for the dropless MoE expert-MLP layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or call this
+ * file; only the test-suite, the smoke check and the benchmark's CPU-baseline leg do.
+ * It shares no code, header, table or helper with the HIP library.
+ *
+ * Every function computes the plain definition of one step, in the order the pages
+ * state it, with explicit loops and no blocking, fusion or reordering.  Arithmetic is
+ * carried in `real`, which is double unless the file is compiled with
+ * -DORACLE_REAL=float (the fp32 variant is only used as a timing baseline).
+ *
+ * Pages cited (by title, then section):
+ *   [GG]  "DeepSeek 계열 MoE 학습 가속: Python expert loop → grouped GEMM"
+ *   [EP]  "EP: Expert를 나누고 토큰 보내기"
+ *   [SM]  "SonicMoE: IO·타일 인식 최적화로 MoE 학습 가속하기"
+ *   [DEP] "Deep EP"
+ *
+ * Conventions (all arrays row-major, all indices int32):
+ *   x [N,H], w_gate/w_up [E,I,H], w_down [E,H,I]  (nn.Linear (out,in) stacked per expert,
+ *   [GG] "적용 — fused MoE training forward", step (5)).
+ *   A routing assignment ("pair") is (token t, expert e, combine weight w).
+ *
+ * Return value of every entry point: 0 on success, -1 on a bad argument, -2 on an
+ * allocation failure.  No function keeps state between calls.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifndef ORACLE_REAL
+#define ORACLE_REAL double
+#endif
+typedef ORACLE_REAL real;
+
+#define ORACLE_EXPORT __attribute__((visibility("default")))
+
+ORACLE_EXPORT int oracle_real_bytes(void) { return (int)sizeof(real); }
+
+/* ------------------------------------------------------------------------------------
+ * Router: top-k selection and combine weights.
+ * [DEP] "1) Router": each token's k experts with the largest gate score, returned as an
+ * index array and a score array, both [N,k].  The score is softmax(z); the combine
+ * weights are the chosen scores renormalised to sum to one (the two weights of [EP]
+ * "여러 Expert의 결과도 같은 토큰으로 돌아오기" sum to one).
+ *
+ *   z[t,e]   = logits[t,e] + bias[e]           (one fp32 add; bias may be NULL)
+ *   order    : z descending, then expert id ascending (ties go to the lower id)
+ *   P[t,e]   = exp(z[t,e]) / sum_e' exp(z[t,e'])        (full softmax, in real)
+ *   w[t,j]   = P[t,idx[t,j]] / sum_j' P[t,idx[t,j']]
+ *   probs    : P rounded to fp32 (may be NULL)
+ * ---------------------------------------------------------------------------------- */
+ORACLE_EXPORT int oracle_route_topk(const float* logits, const float* bias, int N, int E, int k,
+                                    int32_t* idx, float* w, float* probs) {
+  if (N < 0 || E < 1 || k < 1 || k > E || !logits || !idx || !w) return -1;
+  float* z = (float*)malloc(sizeof(float) * (size_t)E);
+  real* p = (real*)malloc(sizeof(real) * (size_t)E);
+  char* taken = (char*)malloc((size_t)E);
+  if (!z || !p || !taken) { free(z); free(p); free(taken); return -2; }
+  for (int t = 0; t < N; ++t) {
+    for (int e = 0; e < E; ++e) z[e] = bias ? logits[(size_t)t * E + e] + bias[e] : logits[(size_t)t * E + e];
+    /* selection: k passes, each taking the best remaining expert under the total order */
+    memset(taken, 0, (size_t)E);
+    for (int j = 0; j < k; ++j) {
+      int best = -1;
+      for (int e = 0; e < E; ++e) {
+        if (taken[e]) continue;
+        if (best < 0 || z[e] > z[best]) best = e; /* strict '>' keeps the lower id on ties */
+      }
+      taken[best] = 1;
+      idx[(size_t)t * k + j] = best;
+    }
+    /* full softmax over all E experts */
+    real zmax = (real)z[0];
+    for (int e = 1; e < E; ++e)
+      if ((real)z[e] > zmax) zmax = (real)z[e];
+    real s = 0;
+    for (int e = 0; e < E; ++e) { p[e] = exp((real)z[e] - zmax); s += p[e]; }
+    for (int e = 0; e < E; ++e) p[e] /= s;
+    if (probs)
+      for (int e = 0; e < E; ++e) probs[(size_t)t * E + e] = (float)p[e];
+    /* renormalise over the chosen k */
+    real sk = 0;
+    for (int j = 0; j < k; ++j) sk += p[idx[(size_t)t * k + j]];
+    for (int j = 0; j < k; ++j) w[(size_t)t * k + j] = (float)(p[idx[(size_t)t * k + j]] / sk);
+  }
+  free(z); free(p); free(taken);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------------------
+ * Permute (routing plan).
+ * [GG] "적용 — fused MoE training forward", steps (1)-(3): flatten the top-k ids, sort them
+ * by expert so each expert's rows form one contiguous slice, and count rows per expert
+ * (bincount).  [DEP] "2) Dispatch" (ragged vs padding table, row "추가 정보"): the ragged
+ * layout carries offset and index metadata.  The sort is stable by token index.
+ *
+ *   rows are appended for e = 0..E-1, then t = 0..N-1, then j = 0..k-1 with idx[t,j] == e:
+ *   row_token[r] = t, row_w[r] = w[t,j], row_pair[r] = t*k + j
+ *   counts[e] = rows of expert e, offsets = exclusive prefix sum (offsets[E] = N*k)
+ *   tok_ptr[t] = t*k; tok_rows[tok_ptr[t] ..] = rows of token t in ascending row order
+ * ---------------------------------------------------------------------------------- */
+ORACLE_EXPORT int oracle_permute(const int32_t* idx, const float* w, int N, int E, int k,
+                                 int32_t* counts, int32_t* offsets, int32_t* row_token, float* row_w,
+                                 int32_t* row_pair, int32_t* tok_ptr, int32_t* tok_rows) {
+  if (N < 0 || E < 1 || k < 1 || k > E || !idx || !w || !counts || !offsets || !row_token ||
+      !row_w || !row_pair || !tok_ptr || !tok_rows)
+    return -1;
+  int32_t r = 0;
+  for (int e = 0; e < E; ++e) {
+    offsets[e] = r;
+    for (int t = 0; t < N; ++t)
+      for (int j = 0; j < k; ++j)
+        if (idx[(size_t)t * k + j] == e) {
+          row_token[r] = t;
+          row_w[r] = w[(size_t)t * k + j];
+          row_pair[r] = t * k + j;
+          ++r;
+        }
+    counts[e] = r - offsets[e];
+  }
+  offsets[E] = r;
+  for (int t = 0; t <= N; ++t) tok_ptr[t] = t * k;
+  int32_t* fill = (int32_t*)calloc((size_t)N + 1, sizeof(int32_t));
+  if (!fill) return -2;
+  for (int32_t q = 0; q < r; ++q) {
+    int t = row_token[q];
+    tok_rows[tok_ptr[t] + fill[t]++] = q;
+  }
+  free(fill);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------------------
+ * Token rounding.
+ * [SM] "5 기여 ③ Token Rounding 라우팅": first the ordinary top-K token-choice routing; then,
+ * per expert, order tokens by score and round the expert's count to the nearest multiple
+ * of Mtile, padding with the best-scoring tokens when short and dropping the worst when
+ * over.  Readings where the page is silent:
+ *   score        = P[t,e], the full softmax probability (the router's score)
+ *   target       r_e = Mtile * floor((c_e + Mtile/2) / Mtile)   (a half rounds up),
+ *                clamped to the largest multiple of Mtile that is <= N
+ *   keep/pad     order all N tokens by (routed to e first, P[t,e] descending, t ascending)
+ *                and take the first r_e: this keeps the r_e best routed tokens when
+ *                r_e <= c_e, and adds the best unrouted ones when r_e > c_e
+ *   weight       P[t,e] / S_t with S_t = sum_j P[t,idx[t,j]] (the token's top-k
+ *                normaliser); no renormalisation after rounding
+ *   rows         ascending token index within an expert; row_pair = t*k+j for routed
+ *                pairs and -1 for padded ones; tok_ptr/tok_rows as in the top-k plan
+ * `probs` are the fp32 probabilities that the ordering uses (given, not recomputed), so the
+ * plan is a pure function of (probs, idx).  Returns the row count M (>= 0) or < 0 on error.
+ * ---------------------------------------------------------------------------------- */
+typedef struct { int t; int routed; float p; } tr_cand;
+
+static int tr_cmp(const void* a, const void* b) {
+  const tr_cand* x = (const tr_cand*)a;
+  const tr_cand* y = (const tr_cand*)b;
+  if (x->routed != y->routed) return x->routed ? -1 : 1;
+  if (x->p != y->p) return x->p > y->p ? -1 : 1;
+  return x->t < y->t ? -1 : (x->t > y->t ? 1 : 0);
+}
+
+ORACLE_EXPORT int oracle_token_round(const float* probs, const int32_t* idx, int N, int E, int k, int mtile,
+                                     int M_cap, int32_t* counts, int32_t* offsets, int32_t* row_token,
+                                     float* row_w, int32_t* row_pair, int32_t* tok_ptr, int32_t* tok_rows) {
+  if (N < 0 || E < 1 || k < 1 || k > E || mtile < 1 || !probs || !idx || !counts || !offsets ||
+      !row_token || !row_w || !row_pair || !tok_ptr || !tok_rows)
+    return -1;
+  int32_t* c = (int32_t*)calloc((size_t)E, sizeof(int32_t));
+  tr_cand* cand = (tr_cand*)malloc(sizeof(tr_cand) * ((size_t)N + 1));
+  char* sel = (char*)malloc((size_t)N + 1);
+  int32_t* tcount = (int32_t*)calloc((size_t)N + 1, sizeof(int32_t));
+  if (!c || !cand || !sel || !tcount) { free(c); free(cand); free(sel); free(tcount); return -2; }
+  for (size_t q = 0; q < (size_t)N * k; ++q) c[idx[q]]++;
+  const int rmax = mtile * (N / mtile);
+  int32_t r = 0;
+  for (int e = 0; e < E; ++e) {
+    int re = mtile * ((c[e] + mtile / 2) / mtile);
+    if (re > rmax) re = rmax;
+    offsets[e] = r;
+    if (r + re > M_cap) { free(c); free(cand); free(sel); free(tcount); return -1; }
+    for (int t = 0; t < N; ++t) {
+      int routed = 0;
+      for (int j = 0; j < k; ++j) routed |= (idx[(size_t)t * k + j] == e);
+      cand[t].t = t;
+      cand[t].routed = routed;
+      cand[t].p = probs[(size_t)t * E + e];
+    }
+    qsort(cand, (size_t)N, sizeof(tr_cand), tr_cmp);
+    memset(sel, 0, (size_t)N);
+    for (int q = 0; q < re; ++q) sel[cand[q].t] = 1;
+    for (int t = 0; t < N; ++t) {
+      if (!sel[t]) continue;
+      real st = 0;
+      int slot = -1;
+      for (int j = 0; j < k; ++j) {
+        st += (real)probs[(size_t)t * E + idx[(size_t)t * k + j]];
+        if (idx[(size_t)t * k + j] == e) slot = j;
+      }
+      row_token[r] = t;
+      row_w[r] = (float)((real)probs[(size_t)t * E + e] / st);
+      row_pair[r] = slot >= 0 ? t * k + slot : -1;
+      tcount[t]++;
+      ++r;
+    }
+    counts[e] = r - offsets[e];
+  }
+  offsets[E] = r;
+  tok_ptr[0] = 0;
+  for (int t = 0; t < N; ++t) tok_ptr[t + 1] = tok_ptr[t] + tcount[t];
+  memset(tcount, 0, sizeof(int32_t) * ((size_t)N + 1));
+  for (int32_t q = 0; q < r; ++q) {
+    int t = row_token[q];
+    tok_rows[tok_ptr[t] + tcount[t]++] = q;
+  }
+  free(c); free(cand); free(sel); free(tcount);
+  return (int)r;
+}
+
+/* ------------------------------------------------------------------------------------
+ * Expert MLP pieces shared by forward and backward (plain definitions).
+ * The expert is the SwiGLU MLP named by [GG] "적용" step (6) (gate -> up -> down) and
+ * [SM] "4.2 Epilogue 융합" (SwiGLU): a_i = silu(g_i) * u_i with silu(g) = g * sigmoid(g).
+ * ---------------------------------------------------------------------------------- */
+static real sigmoid_r(real g) { return (real)1 / ((real)1 + exp(-g)); }
+
+/* g = W_gate[e] x, u = W_up[e] x, a = silu(g) * u   (vectors of length I) */
+static void expert_hidden(const float* xt, const float* wg, const float* wu, int H, int I, int e,
+                          real* g, real* u, real* a) {
+  for (int i = 0; i < I; ++i) {
+    const float* rg = wg + ((size_t)e * I + i) * H;
+    const float* ru = wu + ((size_t)e * I + i) * H;
+    real sg = 0, su = 0;
+    for (int h = 0; h < H; ++h) {
+      sg += (real)rg[h] * (real)xt[h];
+      su += (real)ru[h] * (real)xt[h];
+    }
+    g[i] = sg;
+    u[i] = su;
+    a[i] = sg * sigmoid_r(sg) * su;
+  }
+}
+
+/* y = W_down[e] a   (vector of length H) */
+static void expert_out(const real* a, const float* wd, int H, int I, int e, real* y) {
+  for (int h = 0; h < H; ++h) {
+    const float* rd = wd + ((size_t)e * H + h) * I;
+    real s = 0;
+    for (int i = 0; i < I; ++i) s += (real)rd[i] * a[i];
+    y[h] = s;
+  }
+}
+
+/* CSR grouping of pairs by a key (token or expert); plain counting. */
+static int group_pairs(int P, const int32_t* key, int nkeys, int32_t** ptr_out, int32_t** list_out) {
+  int32_t* ptr = (int32_t*)calloc((size_t)nkeys + 1, sizeof(int32_t));
+  int32_t* list = (int32_t*)malloc(sizeof(int32_t) * ((size_t)P + 1));
+  int32_t* fill = (int32_t*)calloc((size_t)nkeys + 1, sizeof(int32_t));
+  if (!ptr || !list || !fill) { free(ptr); free(list); free(fill); return -2; }
+  for (int p = 0; p < P; ++p) ptr[key[p] + 1]++;
+  for (int q = 0; q < nkeys; ++q) ptr[q + 1] += ptr[q];
+  for (int p = 0; p < P; ++p) list[ptr[key[p]] + fill[key[p]]++] = p;
+  free(fill);
+  *ptr_out = ptr;
+  *list_out = list;
+  return 0;
+}
+
+static int check_pairs(int N, int E, int P, const int32_t* pt, const int32_t* pe) {
+  for (int p = 0; p < P; ++p)
+    if (pt[p] < 0 || pt[p] >= N || pe[p] < 0 || pe[p] >= E) return -1;
+  return 0;
+}
+
+/* ------------------------------------------------------------------------------------
+ * Layer forward.
+ * For every token t and each of its pairs (e, w):
+ *   y = W_down[e] (silu(W_gate[e] x_t) * (W_up[e] x_t));   out[t] += w * y
+ * [EP] "여러 Expert의 결과도 같은 토큰으로 돌아오기" (weighted sum of the experts' outputs back
+ * at the token), [DEP] "3) Combine".  A token with no pairs gets out[t] = 0.
+ * out is [N,H] in double.  Pairs need not cover every token (sampled checks pass a subset).
+ * ---------------------------------------------------------------------------------- */
+ORACLE_EXPORT int oracle_layer_fwd(const float* x, const float* wg, const float* wu, const float* wd, int N,
+                                   int H, int I, int E, int P, const int32_t* pair_t, const int32_t* pair_e,
+                                   const float* pair_w, double* out) {
+  if (N < 0 || H < 1 || I < 1 || E < 1 || P < 0 || !x || !wg || !wu || !wd || !out) return -1;
+  if (P > 0 && (!pair_t || !pair_e || !pair_w)) return -1;
+  if (check_pairs(N, E, P, pair_t, pair_e)) return -1;
+  memset(out, 0, sizeof(double) * (size_t)N * H);
+  int32_t *tptr, *tlist;
+  if (group_pairs(P, pair_t, N, &tptr, &tlist)) return -2;
+  int fail = 0;
+#pragma omp parallel
+  {
+    real* g = (real*)malloc(sizeof(real) * (size_t)I);
+    real* u = (real*)malloc(sizeof(real) * (size_t)I);
+    real* a = (real*)malloc(sizeof(real) * (size_t)I);
+    real* y = (real*)malloc(sizeof(real) * (size_t)H);
+    if (!g || !u || !a || !y) {
+#pragma omp atomic write
+      fail = 1;
+    } else {
+#pragma omp for schedule(dynamic, 4)
+      for (int t = 0; t < N; ++t) {
+        for (int q = tptr[t]; q < tptr[t + 1]; ++q) {
+          int p = tlist[q];
+          int e = pair_e[p];
+          expert_hidden(x + (size_t)t * H, wg, wu, H, I, e, g, u, a);
+          expert_out(a, wd, H, I, e, y);
+          for (int h = 0; h < H; ++h) out[(size_t)t * H + h] += (double)((real)pair_w[p] * y[h]);
+        }
+      }
+    }
+    free(g); free(u); free(a); free(y);
+  }
+  free(tptr); free(tlist);
+  return fail ? -2 : 0;
+}
+
+/* ------------------------------------------------------------------------------------
+ * Layer backward, textbook chain rule per pair (it does not use the fused algebra of the
+ * GPU path).  With dy = w * dOut[t]:
+ *   dS[p]     = <dOut[t], y>              gradient w.r.t. the combine weight w of pair p
+ *                                          ([SM] "3 기여 ①": router gradient dS)
+ *   da        = W_down[e]^T dy,            dW_down[e] += dy (x) a
+ *   dg_i      = da_i * u_i * s_i * (1 + g_i (1 - s_i)),  s = sigmoid(g)
+ *   du_i      = da_i * silu(g_i)
+ *   dW_gate[e] += dg (x) x_t,   dW_up[e] += du (x) x_t
+ *   dx[t]     += W_gate[e]^T dg + W_up[e]^T du
+ * Experts without pairs get dW = 0.  dx excludes the router path.  Any output pointer may
+ * be NULL to skip that part.  dx [N,H], dW_gate/dW_up [E,I,H], dW_down [E,H,I], dS [P],
+ * all double.
+ * ---------------------------------------------------------------------------------- */
+ORACLE_EXPORT int oracle_layer_bwd(const float* dout, const float* x, const float* wg, const float* wu,
+                                   const float* wd, int N, int H, int I, int E, int P, const int32_t* pair_t,
+                                   const int32_t* pair_e, const float* pair_w, double* dx, double* dwg,
+                                   double* dwu, double* dwd, double* ds) {
+  if (N < 0 || H < 1 || I < 1 || E < 1 || P < 0 || !dout || !x || !wg || !wu || !wd) return -1;
+  if (P > 0 && (!pair_t || !pair_e || !pair_w)) return -1;
+  if (check_pairs(N, E, P, pair_t, pair_e)) return -1;
+  const size_t PI = (size_t)P * I;
+  real* A = (real*)malloc(sizeof(real) * (PI + 1));
+  real* DG = (real*)malloc(sizeof(real) * (PI + 1));
+  real* DU = (real*)malloc(sizeof(real) * (PI + 1));
+  if (!A || !DG || !DU) { free(A); free(DG); free(DU); return -2; }
+  int fail = 0;
+
+  /* phase 1, per pair: forward recompute, dS, da, dg, du */
+#pragma omp parallel
+  {
+    real* g = (real*)malloc(sizeof(real) * (size_t)I);
+    real* u = (real*)malloc(sizeof(real) * (size_t)I);
+    real* y = (real*)malloc(sizeof(real) * (size_t)H);
+    real* dy = (real*)malloc(sizeof(real) * (size_t)H);
+    real* da = (real*)malloc(sizeof(real) * (size_t)I);
+    if (!g || !u || !y || !dy || !da) {
+#pragma omp atomic write
+      fail = 1;
+    } else {
+#pragma omp for schedule(dynamic, 4)
+      for (int p = 0; p < P; ++p) {
+        const int t = pair_t[p], e = pair_e[p];
+        const real w = (real)pair_w[p];
+        const float* dot = dout + (size_t)t * H;
+        real* a = A + (size_t)p * I;
+        expert_hidden(x + (size_t)t * H, wg, wu, H, I, e, g, u, a);
+        expert_out(a, wd, H, I, e, y);
+        real s = 0;
+        for (int h = 0; h < H; ++h) s += (real)dot[h] * y[h];
+        if (ds) ds[p] = (double)s;
+        for (int h = 0; h < H; ++h) dy[h] = w * (real)dot[h];
+        for (int i = 0; i < I; ++i) da[i] = 0;
+        for (int h = 0; h < H; ++h) {
+          const float* rd = wd + ((size_t)e * H + h) * I;
+          for (int i = 0; i < I; ++i) da[i] += (real)rd[i] * dy[h];
+        }
+        for (int i = 0; i < I; ++i) {
+          const real sg = sigmoid_r(g[i]);
+          DG[(size_t)p * I + i] = da[i] * u[i] * sg * ((real)1 + g[i] * ((real)1 - sg));
+          DU[(size_t)p * I + i] = da[i] * g[i] * sg;
+        }
+      }
+    }
+    free(g); free(u); free(y); free(dy); free(da);
+  }
+  if (fail) { free(A); free(DG); free(DU); return -2; }
+
+  /* phase 2, per token: dx */
+  if (dx) {
+    memset(dx, 0, sizeof(double) * (size_t)N * H);
+    int32_t *tptr, *tlist;
+    if (group_pairs(P, pair_t, N, &tptr, &tlist)) { free(A); free(DG); free(DU); return -2; }
+#pragma omp parallel
+    {
+      real* acc = (real*)malloc(sizeof(real) * (size_t)H);
+      if (!acc) {
+#pragma omp atomic write
+        fail = 1;
+      } else {
+#pragma omp for schedule(dynamic, 4)
+        for (int t = 0; t < N; ++t) {
+          for (int h = 0; h < H; ++h) acc[h] = 0;
+          for (int q = tptr[t]; q < tptr[t + 1]; ++q) {
+            const int p = tlist[q], e = pair_e[p];
+            for (int i = 0; i < I; ++i) {
+              const float* rg = wg + ((size_t)e * I + i) * H;
+              const float* ru = wu + ((size_t)e * I + i) * H;
+              const real dgi = DG[(size_t)p * I + i], dui = DU[(size_t)p * I + i];
+              for (int h = 0; h < H; ++h) acc[h] += (real)rg[h] * dgi + (real)ru[h] * dui;
+            }
+          }
+          for (int h = 0; h < H; ++h) dx[(size_t)t * H + h] = (double)acc[h];
+        }
+      }
+      free(acc);
+    }
+    free(tptr); free(tlist);
+  }
+
+  /* phase 3, per expert: weight gradients */
+  if (dwg || dwu || dwd) {
+    int32_t *eptr, *elist;
+    if (group_pairs(P, pair_e, E, &eptr, &elist)) { free(A); free(DG); free(DU); return -2; }
+#pragma omp parallel
+    {
+      real* acc = (real*)malloc(sizeof(real) * (size_t)(H > I ? H : I));
+      if (!acc) {
+#pragma omp atomic write
+        fail = 1;
+      } else {
+#pragma omp for schedule(dynamic, 1)
+        for (int e = 0; e < E; ++e) {
+          if (dwd)
+            for (int h = 0; h < H; ++h) {
+              for (int i = 0; i < I; ++i) acc[i] = 0;
+              for (int q = eptr[e]; q < eptr[e + 1]; ++q) {
+                const int p = elist[q];
+                const real dyh = (real)pair_w[p] * (real)dout[(size_t)pair_t[p] * H + h];
+                const real* a = A + (size_t)p * I;
+                for (int i = 0; i < I; ++i) acc[i] += dyh * a[i];
+              }
+              for (int i = 0; i < I; ++i) dwd[((size_t)e * H + h) * I + i] = (double)acc[i];
+            }
+          for (int i = 0; i < I; ++i) {
+            if (dwg) {
+              for (int h = 0; h < H; ++h) acc[h] = 0;
+              for (int q = eptr[e]; q < eptr[e + 1]; ++q) {
+                const int p = elist[q];
+                const float* xt = x + (size_t)pair_t[p] * H;
+                const real d = DG[(size_t)p * I + i];
+                for (int h = 0; h < H; ++h) acc[h] += d * (real)xt[h];
+              }
+              for (int h = 0; h < H; ++h) dwg[((size_t)e * I + i) * H + h] = (double)acc[h];
+            }
+            if (dwu) {
+              for (int h = 0; h < H; ++h) acc[h] = 0;
+              for (int q = eptr[e]; q < eptr[e + 1]; ++q) {
+                const int p = elist[q];
+                const float* xt = x + (size_t)pair_t[p] * H;
+                const real d = DU[(size_t)p * I + i];
+                for (int h = 0; h < H; ++h) acc[h] += d * (real)xt[h];
+              }
+              for (int h = 0; h < H; ++h) dwu[((size_t)e * I + i) * H + h] = (double)acc[h];
+            }
+          }
+        }
+      }
+      free(acc);
+    }
+    free(eptr); free(elist);
+  }
+  free(A); free(DG); free(DU);
+  return fail ? -2 : 0;
+}

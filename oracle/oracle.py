@@ -1,0 +1,197 @@
+"""ctypes wrapper over the plain C oracle in ``moe_oracle.c``.
+
+Test infrastructure: importable only by tests, the smoke check and the benchmark's
+CPU-baseline leg.  Arrays go in and out as numpy arrays on the host.  The C file is built
+with gcc into ``liboracle_f64.so`` (fp64 arithmetic, used for parity) and
+``liboracle_f32.so`` (fp32 arithmetic, used only as a timing baseline).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIBS: dict = {}
+
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_f32p = ctypes.POINTER(ctypes.c_float)
+_f64p = ctypes.POINTER(ctypes.c_double)
+
+
+def lib_path(real: str = "f64") -> str:
+    return os.path.join(_HERE, f"liboracle_{real}.so")
+
+
+def build(verbose: bool = False) -> None:
+    """Compile both oracle variants with gcc (always recompiles)."""
+    for real, ctype in (("f64", "double"), ("f32", "float")):
+        out = lib_path(real)
+        tmp = out + ".tmp"
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", f"-DORACLE_REAL={ctype}",
+               "-fvisibility=hidden", _SRC, "-o", tmp, "-lm"]
+        if verbose:
+            print(" ".join(cmd))
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, out)
+    _LIBS.clear()
+
+
+def _lib(real: str = "f64"):
+    if real in _LIBS:
+        return _LIBS[real]
+    path = lib_path(real)
+    if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(path)
+    lib.oracle_route_topk.argtypes = [_f32p, _f32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      _i32p, _f32p, _f32p]
+    lib.oracle_permute.argtypes = [_i32p, _f32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   _i32p, _i32p, _i32p, _f32p, _i32p, _i32p, _i32p]
+    lib.oracle_token_round.argtypes = [_f32p, _i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_int, _i32p, _i32p, _i32p, _f32p,
+                                       _i32p, _i32p, _i32p]
+    lib.oracle_layer_fwd.argtypes = [_f32p, _f32p, _f32p, _f32p, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p, _i32p, _f32p,
+                                     _f64p]
+    lib.oracle_layer_bwd.argtypes = [_f32p, _f32p, _f32p, _f32p, _f32p, ctypes.c_int,
+                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     _i32p, _i32p, _f32p, _f64p, _f64p, _f64p, _f64p, _f64p]
+    for fn in ("oracle_route_topk", "oracle_permute", "oracle_token_round", "oracle_layer_fwd",
+               "oracle_layer_bwd", "oracle_real_bytes"):
+        getattr(lib, fn).restype = ctypes.c_int
+    _LIBS[real] = lib
+    return lib
+
+
+def _p(a, t):
+    if a is None:
+        return None
+    return a.ctypes.data_as(t)
+
+
+def _f32(a):
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def _i32(a):
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def _check(rc, what):
+    if rc < 0:
+        raise RuntimeError(f"{what} failed with code {rc}")
+    return rc
+
+
+def route_topk(logits, bias, k, real="f64", want_probs=False):
+    """Returns (idx [N,k] int32, w [N,k] float32, probs [N,E] float32 or None)."""
+    logits = _f32(logits)
+    N, E = logits.shape
+    bias = None if bias is None else _f32(bias)
+    idx = np.empty((N, k), np.int32)
+    w = np.empty((N, k), np.float32)
+    probs = np.empty((N, E), np.float32) if want_probs else None
+    _check(_lib(real).oracle_route_topk(_p(logits, _f32p), _p(bias, _f32p), N, E, k,
+                                        _p(idx, _i32p), _p(w, _f32p), _p(probs, _f32p)),
+           "oracle_route_topk")
+    return idx, w, probs
+
+
+def _plan_arrays(N, E, mcap):
+    return dict(counts=np.empty(E, np.int32), offsets=np.empty(E + 1, np.int32),
+                row_token=np.empty(mcap, np.int32), row_w=np.empty(mcap, np.float32),
+                row_pair=np.empty(mcap, np.int32), tok_ptr=np.empty(N + 1, np.int32),
+                tok_rows=np.empty(mcap, np.int32))
+
+
+def permute(idx, w, E):
+    """Top-k routing plan: dict of counts, offsets, row_token, row_w, row_pair, tok_ptr,
+    tok_rows (numpy, exactly M = N*k rows)."""
+    idx = _i32(idx)
+    w = _f32(w)
+    N, k = idx.shape
+    pl = _plan_arrays(N, E, N * k)
+    _check(_lib().oracle_permute(_p(idx, _i32p), _p(w, _f32p), N, E, k,
+                                 *[_p(pl[n], _i32p if pl[n].dtype == np.int32 else _f32p)
+                                   for n in ("counts", "offsets", "row_token", "row_w",
+                                             "row_pair", "tok_ptr", "tok_rows")]),
+           "oracle_permute")
+    return pl
+
+
+def token_round(probs, idx, mtile, mcap=None):
+    """Token-rounding plan given fp32 probs [N,E] and the top-k idx [N,k].  Arrays are
+    trimmed to the actual row count M."""
+    probs = _f32(probs)
+    idx = _i32(idx)
+    N, E = probs.shape
+    k = idx.shape[1]
+    if mcap is None:
+        mcap = N * k + E * (mtile // 2)
+    pl = _plan_arrays(N, E, max(mcap, 1))
+    m = _check(_lib().oracle_token_round(_p(probs, _f32p), _p(idx, _i32p), N, E, k, mtile, mcap,
+                                         *[_p(pl[n], _i32p if pl[n].dtype == np.int32 else _f32p)
+                                           for n in ("counts", "offsets", "row_token", "row_w",
+                                                     "row_pair", "tok_ptr", "tok_rows")]),
+               "oracle_token_round")
+    for n in ("row_token", "row_w", "row_pair", "tok_rows"):
+        pl[n] = pl[n][:m].copy()
+    return pl
+
+
+def pairs_from_topk(idx, w):
+    """Flat (token, expert, weight) pair lists in (t, j) order."""
+    idx = _i32(idx)
+    N, k = idx.shape
+    t = np.repeat(np.arange(N, dtype=np.int32), k)
+    return t, idx.reshape(-1).copy(), _f32(w).reshape(-1).copy()
+
+
+def pairs_from_plan(plan, E):
+    """Flat pair lists in row order from a plan (row r -> token row_token[r], the expert
+    whose slice holds r, weight row_w[r])."""
+    counts = np.asarray(plan["counts"])
+    e = np.repeat(np.arange(E, dtype=np.int32), counts)
+    m = int(counts.sum())
+    return _i32(plan["row_token"][:m]), e, _f32(plan["row_w"][:m])
+
+
+def layer_fwd(x, wg, wu, wd, pair_t, pair_e, pair_w, real="f64"):
+    """out [N,H] float64 = sum over pairs of w * expert_e(x_t)."""
+    x, wg, wu, wd = _f32(x), _f32(wg), _f32(wu), _f32(wd)
+    N, H = x.shape
+    E, I, _ = wg.shape
+    pair_t, pair_e, pair_w = _i32(pair_t), _i32(pair_e), _f32(pair_w)
+    out = np.empty((N, H), np.float64)
+    _check(_lib(real).oracle_layer_fwd(_p(x, _f32p), _p(wg, _f32p), _p(wu, _f32p), _p(wd, _f32p),
+                                       N, H, I, E, len(pair_t), _p(pair_t, _i32p),
+                                       _p(pair_e, _i32p), _p(pair_w, _f32p), _p(out, _f64p)),
+           "oracle_layer_fwd")
+    return out
+
+
+def layer_bwd(dout, x, wg, wu, wd, pair_t, pair_e, pair_w, want=("dx", "dwg", "dwu", "dwd", "ds"),
+              real="f64"):
+    """Returns a dict with the requested float64 gradients: dx [N,H], dwg/dwu [E,I,H],
+    dwd [E,H,I], ds [P] (per pair)."""
+    dout, x, wg, wu, wd = _f32(dout), _f32(x), _f32(wg), _f32(wu), _f32(wd)
+    N, H = x.shape
+    E, I, _ = wg.shape
+    pair_t, pair_e, pair_w = _i32(pair_t), _i32(pair_e), _f32(pair_w)
+    P = len(pair_t)
+    res = {}
+    res["dx"] = np.empty((N, H), np.float64) if "dx" in want else None
+    res["dwg"] = np.empty((E, I, H), np.float64) if "dwg" in want else None
+    res["dwu"] = np.empty((E, I, H), np.float64) if "dwu" in want else None
+    res["dwd"] = np.empty((E, H, I), np.float64) if "dwd" in want else None
+    res["ds"] = np.empty((P,), np.float64) if "ds" in want else None
+    _check(_lib(real).oracle_layer_bwd(_p(dout, _f32p), _p(x, _f32p), _p(wg, _f32p), _p(wu, _f32p),
+                                       _p(wd, _f32p), N, H, I, E, P, _p(pair_t, _i32p),
+                                       _p(pair_e, _i32p), _p(pair_w, _f32p),
+                                       *[_p(res[n], _f64p) for n in ("dx", "dwg", "dwu", "dwd", "ds")]),
+           "oracle_layer_bwd")
+    return {n: v for n, v in res.items() if v is not None}
