@@ -1,0 +1,267 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE expert-MLP layer hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input, through the C ABI:
+router top-k -> permute (counts, offsets, row lists) -> grouped GEMM forward (gate/up +
+SwiGLU, down) -> weighted combine -> layer backward (dH/dS/A', dW_down, dX + combine,
+dW_gate/dW_up).  Inputs are resident in HBM before the timed region.
+
+Prints ONE JSON line.  `value` is the layer throughput in TFLOPS (18*M*H*I algorithmic
+FLOPs per fwd+bwd step over the wall time of the timed steps).  Per-kernel durations come
+from HIP events recorded by the library around each launch on its launch stream.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer fwd+bwd ms & TFLOPS (% bf16 MFMA peak), E=128 H=2048 I=512 k=8 N=4096"
+PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 2.4 GHz x 4096 FLOP/clk (dense)
+PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+GEMMS = ("gateup", "down", "dh", "dx", "dwd", "dw1")
+ALL_KERNELS = ("route", "permute", "route_tr_plan", "gateup", "down", "combine", "dh", "ds_reduce", "dwd", "dx",
+               "dx_combine", "dw1")
+
+
+def kernel_work(name, wl, M, e_act, es):
+    """Algorithmic (flops, bytes) of one launch: each tensor touched once, gathered rows
+    counted once (served from cache), weights of the active experts read once, dW written
+    for every expert."""
+    N, H, I, E = wl.N, wl.H, wl.I, wl.E
+    if name == "gateup":
+        return 4.0 * M * H * I, es * (2.0 * e_act * I * H + N * H + 3.0 * M * I)
+    if name == "down":
+        return 2.0 * M * H * I, es * (1.0 * e_act * H * I + M * I + M * H)
+    if name == "dh":
+        return 2.0 * M * H * I, es * (1.0 * e_act * H * I + N * H + 5.0 * M * I) + 4.0 * M * ((I + 127) // 128)
+    if name == "dx":
+        return 4.0 * M * H * I, es * (2.0 * e_act * I * H + 2.0 * M * I + M * H)
+    if name == "dwd":
+        return 2.0 * M * H * I, es * (1.0 * E * H * I + N * H + M * I)
+    if name == "dw1":
+        return 4.0 * M * H * I, es * (2.0 * E * I * H + N * H + 2.0 * M * I)
+    if name in ("combine", "dx_combine"):
+        return 2.0 * M * H, es * (1.0 * M * H + N * H) + 8.0 * M
+    return 0.0, 0.0
+
+
+def load_traffic(name, workload):
+    """HBM traffic per launch measured with rocprofv3 counters (FETCH_SIZE, WRITE_SIZE),
+    committed under profiles/.  Returned only while the kernel sources are unchanged."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    src = os.path.join(ROOT, "grouped_gemm_top_amd", "csrc", kv.get("source", "gemm.hip"))
+    if not os.path.exists(src):
+        return None
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if kv.get("source_sha") != sha:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(T, idx, w, n_tokens):
+    """The fp64 oracle as it stands, on the pairs of the first n_tokens tokens, fwd + bwd."""
+    import oracle
+    wl = T.wl
+    pt, pe, pw = oracle.pairs_from_topk(idx[:n_tokens], w[:n_tokens])
+    t0 = time.perf_counter()
+    oracle.layer_fwd(T.x, T.wg, T.wu, T.wd, pt, pe, pw)
+    oracle.layer_bwd(T.dout, T.x, T.wg, T.wu, T.wd, pt, pe, pw)
+    dt = time.perf_counter() - t0
+    flops = 18.0 * len(pt) * wl.H * wl.I
+    return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"fp64 oracle fwd+bwd (out, dx, dW_gate, dW_up, dW_down, dS) on the {len(pt)} "
+                      f"(token, expert) pairs of the first {n_tokens} of {wl.N} tokens; "
+                      f"{dt:.1f} s; scaled by algorithmic FLOPs (18*pairs*H*I)",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, help="workload number (1-5); 2 is the headline")
+    ap.add_argument("--cpu-tokens", type=int, default=1536,
+                    help="tokens in the CPU-oracle baseline sample (0 disables it)")
+    ap.add_argument("--kernel-events", type=int, default=1, help="record per-kernel HIP events (1/0)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "this layer has no multi-GPU path to time", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import grouped_gemm_top_amd as G
+    from grouped_gemm_top_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    G.lib()
+    wl = W.CONFIGS[args.config]
+    print(f"# generating {wl.name}", file=sys.stderr, flush=True)
+    T = W.generate(wl)
+    dev = "cuda"
+    if wl.dtype == "bf16":
+        up = lambda n: torch.from_numpy(T.bits[n].view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        up = lambda n: torch.from_numpy(getattr(T, n)).to(dev)
+    x, wg, wu, wd, dout = (up(n) for n in ("x", "wg", "wu", "wd", "dout"))
+    logits = torch.from_numpy(T.logits).to(dev)
+    bias = None if T.bias is None else torch.from_numpy(T.bias).to(dev)
+    N, H, I, E, k = wl.N, wl.H, wl.I, wl.E, wl.k
+    tr = wl.routing == "tr"
+    dt_code = G.MOE_BF16 if wl.dtype == "bf16" else G.MOE_F32
+    es = 2 if wl.dtype == "bf16" else 4
+
+    # every buffer allocated once, outside the timed region
+    plan = G.Plan(N, E, k, kind=G.PLAN_TR if tr else G.PLAN_TOPK, mtile=wl.mtile if tr else 0)
+    idx = torch.empty((N, k), dtype=torch.int32, device=dev)
+    wts = torch.empty((N, k), dtype=torch.float32, device=dev)
+    probs = torch.empty((N, E), dtype=torch.float32, device=dev) if tr else None
+    mc = max(plan.M_cap, 1)
+    hcache = torch.empty((mc, 2 * I), dtype=x.dtype, device=dev)
+    y = torch.empty((mc, H), dtype=x.dtype, device=dev)
+    out = torch.empty((N, H), dtype=x.dtype, device=dev)
+    dx = torch.empty_like(x)
+    dwg, dwu, dwd = torch.empty_like(wg), torch.empty_like(wu), torch.empty_like(wd)
+    ds = torch.empty((mc,) if tr else (N, k), dtype=torch.float32, device=dev)
+    ws_route = torch.empty(G.workspace_bytes(G.OP_ROUTE_TR if tr else G.OP_PERMUTE, dt_code, N, E, k),
+                           dtype=torch.uint8, device=dev)
+    ws_fwd = torch.empty(G.workspace_bytes(G.OP_GEMM_FWD, dt_code, N, E, k, H, I, plan.M_cap), dtype=torch.uint8,
+                         device=dev)
+    ws_bwd = torch.empty(G.workspace_bytes(G.OP_LAYER_BWD, dt_code, N, E, k, H, I, plan.M_cap),
+                         dtype=torch.uint8, device=dev)
+
+    def step():
+        if tr:
+            G.route_token_rounding(logits, k, wl.mtile, bias=bias, plan=plan, ws=ws_route, idx=idx, w=wts,
+                                   probs=probs)
+        else:
+            G.route_topk(logits, k, bias=bias, idx=idx, w=wts)
+            G.permute(idx, wts, E, plan=plan, ws=ws_route)
+        G.grouped_gemm_fwd(x, wg, wu, wd, plan, hcache=hcache, y=y, ws=ws_fwd)
+        G.unpermute_combine(y, plan, out=out)
+        G.layer_bwd(dout, x, wg, wu, wd, plan, hcache, dx=dx, dw_gate=dwg, dw_up=dwu, dw_down=dwd, ds=ds,
+                    ws=ws_bwd)
+
+    print(f"# warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    names = [n for n in ALL_KERNELS if not (tr and n == "permute") and not (not tr and n == "route_tr_plan")]
+    evs = {}
+    if args.kernel_events:
+        evs = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.steps)] for n in names}
+    print(f"# timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        for n in evs:
+            G.set_kernel_events(n, *evs[n][i])
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for n in evs:
+        G.set_kernel_events(n, None, None)
+    ms = (t1 - t0) * 1e3 / args.steps
+
+    kern_ms = {n: float(np.mean([a.elapsed_time(b) for a, b in evs[n]])) for n in evs}
+    counts = plan.counts.cpu().numpy()
+    M = int(plan.offsets[-1].item())
+    e_act = int((counts > 0).sum())
+    flops = 18.0 * M * H * I
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
+
+    res = {
+        "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic (seeded gaussian inputs, see workloads.py)",
+        "config": {"workload": wl.name, "N": N, "H": H, "I": I, "E": E, "k": k, "routing": wl.routing,
+                   "rows": M, "active_experts": e_act, "parallelism": "single GPU"},
+        "pct_peak": round(100.0 * tflops / peak, 2),
+    }
+    if kern_ms:
+        gemm_ms = sum(kern_ms[n] for n in GEMMS)
+        res["gemm_ms"] = round(gemm_ms, 4)
+        res["gemm_tflops"] = round(flops / (gemm_ms * 1e-3) / 1e12, 2)
+        res["gemm_pct_peak"] = round(100.0 * res["gemm_tflops"] / peak, 2)
+        res["fwd_ms"] = round(sum(kern_ms.get(n, 0.0) for n in ("route", "permute", "route_tr_plan", "gateup",
+                                                                  "down", "combine")), 4)
+        res["bwd_ms"] = round(sum(kern_ms.get(n, 0.0) for n in ("dh", "ds_reduce", "dwd", "dx", "dx_combine",
+                                                                  "dw1")), 4)
+        kinfo = {}
+        for n in names:
+            f, b = kernel_work(n, wl, M, e_act, es)
+            kinfo[n] = {"us": round(kern_ms[n] * 1e3, 2)}
+            if f:
+                kinfo[n]["tflops"] = round(f / (kern_ms[n] * 1e-3) / 1e12, 2)
+                kinfo[n]["gbs"] = round(b / (kern_ms[n] * 1e-3) / 1e9, 1)
+        res["kernels"] = kinfo
+        dom = max(GEMMS, key=lambda n: kern_ms[n])
+        f, b = kernel_work(dom, wl, M, e_act, es)
+        t_s = kern_ms[dom] * 1e-3
+        hbm_bound = b / (PEAK_HBM_GBS * 1e9) >= f / (peak * 1e12)
+        traffic = load_traffic(dom, wl.name)
+        if hbm_bound:
+            ach = b / t_s / 1e9
+            res["roofline"] = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                               "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic,
+                               "algorithmic_bytes": b, "us": round(kern_ms[dom] * 1e3, 2)}
+        else:
+            ach = f / t_s / 1e12
+            res["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2), "peak": peak,
+                               "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": traffic,
+                               "algorithmic_flops": f, "us": round(kern_ms[dom] * 1e3, 2)}
+    pad = float(sum(((c + 127) // 128) * 128 for c in counts)) / max(M, 1) - 1.0
+    res["padded_row_fraction_tile128"] = round(pad, 4)
+
+    if args.cpu_tokens > 0 and not tr:
+        print(f"# cpu baseline on {args.cpu_tokens} tokens", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(T, idx.cpu().numpy(), wts.cpu().numpy(),
+                                           min(args.cpu_tokens, N))
+    elif args.cpu_tokens > 0:
+        print("# cpu baseline on token-rounding plan", file=sys.stderr, flush=True)
+        import oracle
+        hp = plan.host()
+        pt, pe, pw = oracle.pairs_from_plan(hp, E)
+        keep = pt < args.cpu_tokens
+        t0 = time.perf_counter()
+        oracle.layer_fwd(T.x, T.wg, T.wu, T.wd, pt[keep], pe[keep], pw[keep])
+        oracle.layer_bwd(T.dout, T.x, T.wg, T.wu, T.wd, pt[keep], pe[keep], pw[keep])
+        dtc = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": 18.0 * int(keep.sum()) * H * I / dtc / 1e12, "unit": "TFLOPS",
+                               "cores": oracle.threads(), "kind": "oracle",
+                               "sample": f"fp64 oracle fwd+bwd on the {int(keep.sum())} rows of the first "
+                                         f"{args.cpu_tokens} tokens; {dtc:.1f} s"}
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

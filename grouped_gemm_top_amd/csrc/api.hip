@@ -1,0 +1,256 @@
+// api.hip -- the extern "C" entry points of libmoe.so: argument validation, workspace
+// carving and launch sequencing on the caller's stream.  The operations themselves are
+// documented in moe.h.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "common.h"
+
+namespace {
+
+thread_local char g_err[512];
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+moe_status hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return MOE_OK;
+  return fail(MOE_EHIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+#define REQUIRE(cond, st, ...) \
+  do {                         \
+    if (!(cond)) return fail(st, __VA_ARGS__); \
+  } while (0)
+
+moe_status check_dims(int32_t N, int32_t E, int32_t k) {
+  REQUIRE(N >= 0, MOE_EINVAL, "N must be >= 0 (got %d)", N);
+  REQUIRE(E >= 1 && E <= 1024, MOE_EINVAL, "E must be in [1, 1024] (got %d)", E);
+  REQUIRE(k >= 1 && k <= E, MOE_EINVAL, "k must be in [1, E] (got k=%d, E=%d)", k, E);
+  REQUIRE((int64_t)N * k <= INT32_MAX / 2, MOE_EINVAL, "N*k too large");
+  return MOE_OK;
+}
+
+moe_status check_hi(int32_t H, int32_t I) {
+  REQUIRE(H >= 8 && I >= 8, MOE_EINVAL, "H and I must be >= 8 (got H=%d, I=%d)", H, I);
+  REQUIRE(H % 8 == 0 && I % 8 == 0, MOE_EUNSUPPORTED, "H and I must be multiples of 8 (got H=%d, I=%d)", H, I);
+  return MOE_OK;
+}
+
+moe_status check_dtype(moe_dtype dt) {
+  REQUIRE(dt == MOE_F32 || dt == MOE_BF16, MOE_EUNSUPPORTED, "unknown dtype %d", (int)dt);
+  return MOE_OK;
+}
+
+moe_status check_plan(const moe_plan* p) {
+  REQUIRE(p != nullptr, MOE_EINVAL, "plan is NULL");
+  moe_status st = check_dims(p->N, p->E, p->k);
+  if (st != MOE_OK) return st;
+  REQUIRE(p->kind == MOE_PLAN_TOPK || p->kind == MOE_PLAN_TR, MOE_EINVAL, "unknown plan kind %d", p->kind);
+  const int64_t need = moe_plan_rows_cap(p->kind, p->N, p->E, p->k, p->kind == MOE_PLAN_TR ? p->mtile : 0);
+  REQUIRE(need >= 0, MOE_EINVAL, "invalid plan dimensions");
+  REQUIRE(p->M_cap >= need, MOE_EINVAL, "plan M_cap %d < required %lld", p->M_cap, (long long)need);
+  REQUIRE(p->counts && p->offsets && p->tok_ptr, MOE_EINVAL, "plan has a NULL counts/offsets/tok_ptr array");
+  REQUIRE(p->M_cap == 0 || (p->row_token && p->row_w && p->row_pair && p->tok_rows), MOE_EINVAL,
+          "plan has a NULL row array");
+  return MOE_OK;
+}
+
+int64_t mcap_of(const moe_plan* p) { return p->M_cap; }
+
+}  // namespace
+
+namespace moe {
+DevInfo dev_info() {
+  static DevInfo cache[64];
+  static bool have[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return DevInfo{256, 8};
+  if (!have[dev]) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    cache[dev] = DevInfo{cus, 8};
+    have[dev] = true;
+  }
+  return cache[dev];
+}
+}  // namespace moe
+
+namespace {
+hipEvent_t g_events[MOE_K_COUNT][2];
+}
+
+namespace moe {
+void kernel_event(int kid, int which, hipStream_t s) {
+  hipEvent_t ev = g_events[kid][which];
+  if (ev) (void)hipEventRecord(ev, s);
+}
+}  // namespace moe
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_err; }
+
+moe_status moe_set_kernel_events(int32_t kernel_id, void* start_event, void* stop_event) {
+  g_err[0] = 0;
+  REQUIRE(kernel_id >= 0 && kernel_id < MOE_K_COUNT, MOE_EINVAL, "unknown kernel id %d", kernel_id);
+  g_events[kernel_id][0] = (hipEvent_t)start_event;
+  g_events[kernel_id][1] = (hipEvent_t)stop_event;
+  return MOE_OK;
+}
+
+int64_t moe_plan_rows_cap(int32_t kind, int32_t N, int32_t E, int32_t k, int32_t mtile) {
+  if (N < 0 || E < 1 || E > 1024 || k < 1 || k > E) return -1;
+  if (kind == MOE_PLAN_TOPK) return (int64_t)N * k;
+  if (kind == MOE_PLAN_TR) {
+    if (mtile < 1) return -1;
+    return (int64_t)N * k + (int64_t)E * (mtile / 2);
+  }
+  return -1;
+}
+
+size_t moe_workspace_bytes(moe_op op, moe_dtype dt, int32_t N, int32_t E, int32_t k, int32_t H, int32_t I,
+                           int32_t M_cap) {
+  if (check_dims(N, E, k) != MOE_OK) return 0;
+  switch (op) {
+    case MOE_OP_PERMUTE: return moe::permute_ws_bytes(N, E);
+    case MOE_OP_ROUTE_TR: return moe::tr_ws_bytes(N, E);
+    case MOE_OP_GEMM_FWD:
+      if (check_dtype(dt) != MOE_OK || check_hi(H, I) != MOE_OK || M_cap < 0) return 0;
+      return moe::gemm_fwd_ws_bytes(dt, M_cap, I);
+    case MOE_OP_LAYER_BWD:
+      if (check_dtype(dt) != MOE_OK || check_hi(H, I) != MOE_OK || M_cap < 0) return 0;
+      return moe::layer_bwd_ws_bytes(dt, N, M_cap, H, I);
+  }
+  return 0;
+}
+
+moe_status moe_route_topk(const float* logits, const float* bias, int32_t N, int32_t E, int32_t k,
+                          int32_t* topk_idx, float* topk_w, float* probs, void* stream) {
+  g_err[0] = 0;
+  moe_status st = check_dims(N, E, k);
+  if (st != MOE_OK) return st;
+  REQUIRE(N == 0 || (logits && topk_idx && topk_w), MOE_EINVAL, "NULL logits/topk_idx/topk_w");
+  moe::kernel_event(MOE_K_ROUTE, 0, (hipStream_t)stream);
+  hipError_t e = moe::launch_route_topk(logits, bias, N, E, k, topk_idx, topk_w, probs, nullptr, (hipStream_t)stream);
+  moe::kernel_event(MOE_K_ROUTE, 1, (hipStream_t)stream);
+  return hip_status(e, "moe_route_topk");
+}
+
+moe_status moe_permute(const int32_t* topk_idx, const float* topk_w, int32_t N, int32_t E, int32_t k,
+                       const moe_plan* plan, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  moe_status st = check_dims(N, E, k);
+  if (st != MOE_OK) return st;
+  if ((st = check_plan(plan)) != MOE_OK) return st;
+  REQUIRE(plan->kind == MOE_PLAN_TOPK, MOE_EINVAL, "moe_permute needs a top-k plan");
+  REQUIRE(plan->N == N && plan->E == E && plan->k == k, MOE_EINVAL, "plan dimensions differ from the call");
+  REQUIRE(N == 0 || (topk_idx && topk_w), MOE_EINVAL, "NULL topk_idx/topk_w");
+  const size_t need = moe::permute_ws_bytes(N, E);
+  REQUIRE(ws_bytes >= need, MOE_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  REQUIRE(ws != nullptr, MOE_EINVAL, "NULL workspace");
+  moe::kernel_event(MOE_K_PERMUTE, 0, (hipStream_t)stream);
+  hipError_t e = moe::launch_permute(topk_idx, topk_w, N, E, k, *plan, ws, (hipStream_t)stream);
+  moe::kernel_event(MOE_K_PERMUTE, 1, (hipStream_t)stream);
+  return hip_status(e, "moe_permute");
+}
+
+moe_status moe_route_token_rounding(const float* logits, const float* bias, int32_t N, int32_t E, int32_t k,
+                                    int32_t mtile, int32_t* topk_idx, float* topk_w, float* probs,
+                                    const moe_plan* plan, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  moe_status st = check_dims(N, E, k);
+  if (st != MOE_OK) return st;
+  REQUIRE(mtile >= 1 && mtile <= 65536, MOE_EINVAL, "mtile must be in [1, 65536] (got %d)", mtile);
+  if ((st = check_plan(plan)) != MOE_OK) return st;
+  REQUIRE(plan->kind == MOE_PLAN_TR && plan->mtile == mtile, MOE_EINVAL,
+          "token rounding needs a plan of kind MOE_PLAN_TR with the same mtile");
+  REQUIRE(plan->N == N && plan->E == E && plan->k == k, MOE_EINVAL, "plan dimensions differ from the call");
+  REQUIRE(N == 0 || (logits && topk_idx && topk_w && probs), MOE_EINVAL, "NULL logits/topk_idx/topk_w/probs");
+  const size_t need = moe::tr_ws_bytes(N, E);
+  REQUIRE(ws_bytes >= need, MOE_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  REQUIRE(ws != nullptr, MOE_EINVAL, "NULL workspace");
+  // the token normaliser sits right after the block histogram in the workspace
+  const size_t nb = ((size_t)N + 255) / 256;
+  float* tok_norm = (float*)((char*)ws + (((nb * E * 4) + 255) & ~(size_t)255));
+  hipStream_t s = (hipStream_t)stream;
+  moe::kernel_event(MOE_K_ROUTE, 0, s);
+  hipError_t e = moe::launch_route_topk(logits, bias, N, E, k, topk_idx, topk_w, probs, tok_norm, s);
+  moe::kernel_event(MOE_K_ROUTE, 1, s);
+  if (e != hipSuccess) return hip_status(e, "moe_route_token_rounding/route");
+  moe::kernel_event(MOE_K_ROUTE_TR_PLAN, 0, s);
+  e = moe::launch_token_round(topk_idx, probs, tok_norm, N, E, k, mtile, *plan, ws, s);
+  moe::kernel_event(MOE_K_ROUTE_TR_PLAN, 1, s);
+  return hip_status(e, "moe_route_token_rounding");
+}
+
+moe_status moe_grouped_gemm_fwd(moe_dtype dt, const void* x, const void* w_gate, const void* w_up,
+                                const void* w_down, int32_t H, int32_t I, const moe_plan* plan, void* hcache,
+                                void* y, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  moe_status st;
+  if ((st = check_dtype(dt)) != MOE_OK) return st;
+  if ((st = check_hi(H, I)) != MOE_OK) return st;
+  if ((st = check_plan(plan)) != MOE_OK) return st;
+  REQUIRE(w_gate && w_up && w_down, MOE_EINVAL, "NULL weight argument");
+  REQUIRE(plan->M_cap == 0 || (x && hcache && y), MOE_EINVAL, "NULL tensor argument");
+  REQUIRE(aligned16(x) && aligned16(w_gate) && aligned16(w_up) && aligned16(w_down) && aligned16(hcache) &&
+              aligned16(y) && aligned16(ws),
+          MOE_EUNSUPPORTED, "tensors and workspace must be 16-byte aligned");
+  const size_t need = moe::gemm_fwd_ws_bytes(dt, (int)mcap_of(plan), I);
+  REQUIRE(ws_bytes >= need, MOE_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  REQUIRE(ws != nullptr, MOE_EINVAL, "NULL workspace");
+  return hip_status(moe::launch_gemm_fwd(dt, x, w_gate, w_up, w_down, H, I, *plan, hcache, y, ws,
+                                         (hipStream_t)stream),
+                    "moe_grouped_gemm_fwd");
+}
+
+moe_status moe_unpermute_combine(moe_dtype dt, const void* y, int32_t H, const moe_plan* plan, const float* row_w,
+                                 void* out, void* stream) {
+  g_err[0] = 0;
+  moe_status st;
+  if ((st = check_dtype(dt)) != MOE_OK) return st;
+  REQUIRE(H >= 8, MOE_EINVAL, "H must be >= 8 (got %d)", H);
+  REQUIRE(H % 8 == 0, MOE_EUNSUPPORTED, "H must be a multiple of 8 (got %d)", H);
+  if ((st = check_plan(plan)) != MOE_OK) return st;
+  REQUIRE(plan->N == 0 || (out && (plan->M_cap == 0 || y)), MOE_EINVAL, "NULL tensor argument");
+  REQUIRE(aligned16(y) && aligned16(out), MOE_EUNSUPPORTED, "tensors must be 16-byte aligned");
+  moe::kernel_event(MOE_K_COMBINE, 0, (hipStream_t)stream);
+  hipError_t e = moe::launch_combine(dt, y, H, *plan, row_w, out, (hipStream_t)stream);
+  moe::kernel_event(MOE_K_COMBINE, 1, (hipStream_t)stream);
+  return hip_status(e, "moe_unpermute_combine");
+}
+
+moe_status moe_layer_bwd(moe_dtype dt, const void* dout, const void* x, const void* w_gate, const void* w_up,
+                         const void* w_down, int32_t H, int32_t I, const moe_plan* plan, const void* hcache,
+                         void* dx, void* dw_gate, void* dw_up, void* dw_down, float* ds, void* ws, size_t ws_bytes,
+                         void* stream) {
+  g_err[0] = 0;
+  moe_status st;
+  if ((st = check_dtype(dt)) != MOE_OK) return st;
+  if ((st = check_hi(H, I)) != MOE_OK) return st;
+  if ((st = check_plan(plan)) != MOE_OK) return st;
+  REQUIRE(w_gate && w_up && w_down && dw_gate && dw_up && dw_down, MOE_EINVAL, "NULL weight/gradient argument");
+  REQUIRE(plan->N == 0 || (dout && x && dx), MOE_EINVAL, "NULL activation argument");
+  REQUIRE(plan->M_cap == 0 || (hcache && ds), MOE_EINVAL, "NULL hcache/ds argument");
+  REQUIRE(aligned16(dout) && aligned16(x) && aligned16(w_gate) && aligned16(w_up) && aligned16(w_down) &&
+              aligned16(hcache) && aligned16(dx) && aligned16(dw_gate) && aligned16(dw_up) && aligned16(dw_down) &&
+              aligned16(ws),
+          MOE_EUNSUPPORTED, "tensors and workspace must be 16-byte aligned");
+  const size_t need = moe::layer_bwd_ws_bytes(dt, plan->N, (int)mcap_of(plan), H, I);
+  REQUIRE(ws_bytes >= need, MOE_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  REQUIRE(ws != nullptr, MOE_EINVAL, "NULL workspace");
+  return hip_status(moe::launch_layer_bwd(dt, dout, x, w_gate, w_up, w_down, H, I, *plan, hcache, dx, dw_gate,
+                                          dw_up, dw_down, ds, ws, (hipStream_t)stream),
+                    "moe_layer_bwd");
+}
+
+}  // extern "C"

@@ -1,0 +1,55 @@
+// combine.hip -- weighted combine of expert rows back to token order.
+//
+// Pages cited (by title, then section):
+//   [EP]  "EP: Expert를 나누고 토큰 보내기", section "여러 Expert의 결과도 같은 토큰으로 돌아오기"
+//         (each token's expert outputs are summed with the combine weights, back at the token)
+//   [DEP] "Deep EP", section "3) Combine" (weighted sum of the k expert outputs per token)
+//
+//   out[t] = sum over r in tok_rows[tok_ptr[t] .. tok_ptr[t+1]) of row_w[r] * y[r]
+// One workgroup per token, 16-byte vectors along H, fp32 accumulation in ascending row
+// order (deterministic, no atomics).  Pure HBM streaming: each y row is read once.
+#include "common.h"
+
+namespace moe {
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_combine(const T* __restrict__ y, int H, const int32_t* __restrict__ tok_ptr,
+                                                 const int32_t* __restrict__ tok_rows,
+                                                 const float* __restrict__ row_w, T* __restrict__ out) {
+  constexpr int VEC = 16 / sizeof(T);
+  const int t = blockIdx.x;
+  const int q0 = tok_ptr[t], q1 = tok_ptr[t + 1];
+  const int nv = H / VEC;
+  for (int v = threadIdx.x; v < nv; v += 256) {
+    float acc[VEC];
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) acc[c] = 0.f;
+    for (int q = q0; q < q1; ++q) {
+      const int r = tok_rows[q];
+      const float wr = row_w ? row_w[r] : 1.0f;
+      const uint4 raw = *reinterpret_cast<const uint4*>(y + (size_t)r * H + (size_t)v * VEC);
+      const T* vals = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+      for (int c = 0; c < VEC; ++c) acc[c] += wr * to_f32<T>(vals[c]);
+    }
+    uint4 o;
+    T* ov = reinterpret_cast<T*>(&o);
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) ov[c] = from_f32<T>(acc[c]);
+    *reinterpret_cast<uint4*>(out + (size_t)t * H + (size_t)v * VEC) = o;
+  }
+}
+
+hipError_t launch_combine(moe_dtype dt, const void* y, int H, const moe_plan& p, const float* row_w, void* out,
+                          hipStream_t s) {
+  if (p.N == 0) return hipSuccess;
+  if (dt == MOE_BF16)
+    hipLaunchKernelGGL(k_combine<bf16_t>, dim3(p.N), dim3(256), 0, s, (const bf16_t*)y, H, p.tok_ptr, p.tok_rows,
+                       row_w, (bf16_t*)out);
+  else
+    hipLaunchKernelGGL(k_combine<float>, dim3(p.N), dim3(256), 0, s, (const float*)y, H, p.tok_ptr, p.tok_rows,
+                       row_w, (float*)out);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,85 @@
+// common.h -- internal helpers shared by the HIP sources of libmoe.so (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+typedef uint16_t bf16_t;  // storage type of bf16 values (bit pattern)
+
+// Round-to-nearest-even fp32 -> bf16 (inputs are finite; a NaN stays a quiet NaN).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (bf16_t)((u >> 16) | 0x40);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+template <typename T> __device__ __forceinline__ float to_f32(T v);
+template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f32<bf16_t>(bf16_t v) { return bf16_to_f32(v); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return f32_to_bf16(v); }
+
+// Store 4 consecutive values (the 4 accumulator lanes of one MFMA output row segment).
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
+__device__ __forceinline__ void store4(bf16_t* p, float a, float b, float c, float d) {
+  uint2 v;
+  v.x = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+  v.y = (uint32_t)f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16);
+  *reinterpret_cast<uint2*>(p) = v;
+}
+__device__ __forceinline__ void load4(const float* p, float& a, float& b, float& c, float& d) {
+  float4 v = *reinterpret_cast<const float4*>(p);
+  a = v.x; b = v.y; c = v.z; d = v.w;
+}
+__device__ __forceinline__ void load4(const bf16_t* p, float& a, float& b, float& c, float& d) {
+  uint2 v = *reinterpret_cast<const uint2*>(p);
+  a = __uint_as_float(v.x << 16); b = __uint_as_float(v.x & 0xFFFF0000u);
+  c = __uint_as_float(v.y << 16); d = __uint_as_float(v.y & 0xFFFF0000u);
+}
+
+__device__ __forceinline__ float sigmoidf_(float g) { return 1.0f / (1.0f + expf(-g)); }
+
+// Device facts the launch shapes need (cached per device by the host side).
+struct DevInfo {
+  int cus;   // compute units
+  int xcds;  // accelerator complex dies sharing the dispatcher's round-robin
+};
+DevInfo dev_info();
+
+}  // namespace moe
+
+// Measurement hook: records the registered start/stop event around a launch (no-op when unset).
+namespace moe {
+void kernel_event(int kid, int which, hipStream_t s);
+}
+
+// ---- launchers implemented in the .hip files and sequenced by api.hip ----
+namespace moe {
+hipError_t launch_route_topk(const float* logits, const float* bias, int N, int E, int k, int32_t* idx,
+                             float* w, float* probs, float* tok_norm, hipStream_t s);
+size_t permute_ws_bytes(int N, int E);
+hipError_t launch_permute(const int32_t* idx, const float* w, int N, int E, int k, const moe_plan& p,
+                          void* ws, hipStream_t s);
+size_t tr_ws_bytes(int N, int E);
+hipError_t launch_token_round(const int32_t* idx, const float* probs, const float* tok_norm, int N, int E,
+                              int k, int mtile, const moe_plan& p, void* ws, hipStream_t s);
+hipError_t launch_combine(moe_dtype dt, const void* y, int H, const moe_plan& p, const float* row_w,
+                          void* out, hipStream_t s);
+size_t gemm_fwd_ws_bytes(moe_dtype dt, int M_cap, int I);
+hipError_t launch_gemm_fwd(moe_dtype dt, const void* x, const void* wg, const void* wu, const void* wd, int H,
+                           int I, const moe_plan& p, void* hcache, void* y, void* ws, hipStream_t s);
+size_t layer_bwd_ws_bytes(moe_dtype dt, int N, int M_cap, int H, int I);
+hipError_t launch_layer_bwd(moe_dtype dt, const void* dout, const void* x, const void* wg, const void* wu,
+                            const void* wd, int H, int I, const moe_plan& p, const void* hcache, void* dx,
+                            void* dwg, void* dwu, void* dwd, float* ds, void* ws, hipStream_t s);
+}  // namespace moe

@@ -1,0 +1,349 @@
+// route.hip -- router top-k and token-rounding plan kernels.
+//
+// Pages cited (by title, then section):
+//   [DEP] "Deep EP", section "1) Router"
+//   [SM]  "SonicMoE: IO·타일 인식 최적화로 MoE 학습 가속하기", section "5 기여 ③ Token Rounding 라우팅"
+#include <limits.h>
+
+#include "common.h"
+
+namespace moe {
+
+constexpr int kMaxE = 1024;
+constexpr int kPerLane = kMaxE / 64;
+
+// ---------------------------------------------------------------------------------------
+// Top-k router ([DEP] "1) Router").  One 64-lane wavefront per token; lane l holds experts
+// l, l+64, ...  Selection takes k rounds of a wave-wide arg-max under the total order
+// (z descending, expert id ascending); IEEE compares only, so -0 and +0 tie.  Weights are
+// the softmax over the chosen k (the full-E denominator cancels); probs is the full softmax.
+// tok_norm (optional) is the sum of the chosen probs, the normaliser token rounding uses.
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ logits,
+                                                    const float* __restrict__ bias, int N, int E, int k,
+                                                    int32_t* __restrict__ idx, float* __restrict__ w,
+                                                    float* __restrict__ probs, float* __restrict__ tok_norm) {
+  __shared__ float s_z[4][kMaxE];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= N) return;  // whole wavefronts exit together; no block barrier below
+  const float* lt = logits + (size_t)t * E;
+  float z[kPerLane];
+  uint32_t avail = 0;
+#pragma unroll
+  for (int q = 0; q < kPerLane; ++q) {
+    const int e = lane + 64 * q;
+    z[q] = 0.f;
+    if (e < E) {
+      z[q] = bias ? lt[e] + bias[e] : lt[e];
+      avail |= 1u << q;
+    }
+  }
+  float zmax = 0.f;
+  for (int j = 0; j < k; ++j) {
+    float bz = 0.f;
+    int be = INT_MAX;
+#pragma unroll
+    for (int q = 0; q < kPerLane; ++q) {
+      if ((avail >> q) & 1u) {
+        if (be == INT_MAX || z[q] > bz) {  // ascending q = ascending id: strict '>' keeps the lower id
+          bz = z[q];
+          be = lane + 64 * q;
+        }
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float oz = __shfl_xor(bz, off);
+      const int oe = __shfl_xor(be, off);
+      const bool take = oe != INT_MAX && (be == INT_MAX || oz > bz || (oz == bz && oe < be));
+      if (take) { bz = oz; be = oe; }
+    }
+    if ((be & 63) == lane) avail &= ~(1u << (be >> 6));
+    if (lane == 0) idx[(size_t)t * k + j] = be;
+    if (j == 0) zmax = bz;
+    if (lane == 0) s_z[wave][j] = bz;
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  // renormalised weights: softmax over the chosen k
+  float sk = 0.f;
+  for (int j = lane; j < k; j += 64) sk += expf(s_z[wave][j] - zmax);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) sk += __shfl_xor(sk, off);
+  for (int j = lane; j < k; j += 64) w[(size_t)t * k + j] = expf(s_z[wave][j] - zmax) / sk;
+  if (probs || tok_norm) {
+    float sa = 0.f;
+#pragma unroll
+    for (int q = 0; q < kPerLane; ++q)
+      if (lane + 64 * q < E) sa += expf(z[q] - zmax);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) sa += __shfl_xor(sa, off);
+    if (probs) {
+#pragma unroll
+      for (int q = 0; q < kPerLane; ++q)
+        if (lane + 64 * q < E) probs[(size_t)t * E + lane + 64 * q] = expf(z[q] - zmax) / sa;
+    }
+    if (tok_norm) {
+      // sum of the chosen probabilities, in slot order, from the same fp32 values as probs
+      if (lane == 0) {
+        float s = 0.f;
+        for (int j = 0; j < k; ++j) s += expf(s_z[wave][j] - zmax) / sa;
+        tok_norm[t] = s;
+      }
+    }
+  }
+}
+
+hipError_t launch_route_topk(const float* logits, const float* bias, int N, int E, int k, int32_t* idx,
+                             float* w, float* probs, float* tok_norm, hipStream_t s) {
+  if (N == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_route_topk, dim3((N + 3) / 4), dim3(256), 0, s, logits, bias, N, E, k, idx, w, probs,
+                     tok_norm);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
+// Token rounding ([SM] "5 기여 ③ Token Rounding 라우팅").  After the top-k route and the
+// per-block histogram of the permute step:
+//   k_tr_sizes   c_e -> r_e = mtile*floor((c_e + mtile/2)/mtile) (<= largest multiple of
+//                mtile <= N); plan counts = r_e, offsets = exclusive scan
+//   k_tr_keys    key[e][t] = routed(t,e) << 63 | bits(P[t,e]) << 32 | ~t, so that the key
+//                order is (routed first, score descending, token ascending)
+//   k_tr_select  one block per expert: radix-select the r_e-th largest key, keep every key
+//                >= it, compact in token order -> rows of expert e
+//   k_tr_tokcount / scan / k_tr_tokfill   token-major row lists
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ int block_excl_scan_1024(int v, int* s_wave, int* total) {
+  // 1024 threads = 16 wavefronts; returns the exclusive prefix of v in thread order
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) s_wave[wv] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int q = 0; q < 16; ++q) {
+      const int c = s_wave[q];
+      s_wave[q] = run;
+      run += c;
+    }
+    s_wave[16] = run;
+  }
+  __syncthreads();
+  const int res = s_wave[wv] + x - v;
+  *total = s_wave[16];
+  __syncthreads();
+  return res;
+}
+
+__global__ __launch_bounds__(1024) void k_tr_sizes(const int32_t* __restrict__ bcnt, int nb, int N, int E,
+                                                   int mtile, int32_t* __restrict__ counts,
+                                                   int32_t* __restrict__ offsets) {
+  __shared__ int s_wave[17];
+  const int e = threadIdx.x;
+  int r = 0;
+  if (e < E) {
+    int c = 0;
+    for (int b = 0; b < nb; ++b) c += bcnt[(size_t)b * E + e];
+    const int rmax = mtile * (N / mtile);
+    r = mtile * ((c + mtile / 2) / mtile);
+    if (r > rmax) r = rmax;
+    counts[e] = r;
+  }
+  int total;
+  const int ex = block_excl_scan_1024(r, s_wave, &total);
+  if (e < E) offsets[e] = ex;
+  if (e == 0) offsets[E] = total;
+}
+
+__global__ __launch_bounds__(256) void k_tr_keys(const float* __restrict__ probs, const int32_t* __restrict__ idx,
+                                                 int N, int E, int k, uint64_t* __restrict__ keys) {
+  __shared__ uint32_t s_p[64][65];
+  __shared__ uint8_t s_r[64][64];
+  const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+  for (int q = threadIdx.x; q < 64 * 64; q += 256) {
+    const int tl = q >> 6, el = q & 63;
+    const int t = t0 + tl, e = e0 + el;
+    s_p[tl][el] = (t < N && e < E) ? (__float_as_uint(probs[(size_t)t * E + e]) & 0x7FFFFFFFu) : 0u;
+    s_r[tl][el] = 0;
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int t = t0 + threadIdx.x;
+    if (t < N)
+      for (int j = 0; j < k; ++j) {
+        const int e = idx[(size_t)t * k + j];
+        if (e >= e0 && e < e0 + 64) s_r[threadIdx.x][e - e0] = 1;
+      }
+  }
+  __syncthreads();
+  for (int q = threadIdx.x; q < 64 * 64; q += 256) {
+    const int el = q >> 6, tl = q & 63;
+    const int t = t0 + tl, e = e0 + el;
+    if (t < N && e < E)
+      keys[(size_t)e * N + t] = ((uint64_t)s_r[tl][el] << 63) | ((uint64_t)s_p[tl][el] << 32) |
+                                (uint64_t)(0xFFFFFFFFu - (uint32_t)t);
+  }
+}
+
+__global__ __launch_bounds__(1024) void k_tr_select(const uint64_t* __restrict__ keys, const float* __restrict__ probs,
+                                                    const float* __restrict__ tok_norm,
+                                                    const int32_t* __restrict__ idx, int N, int E, int k,
+                                                    const int32_t* __restrict__ counts,
+                                                    const int32_t* __restrict__ offsets,
+                                                    int32_t* __restrict__ row_of, int32_t* __restrict__ row_token,
+                                                    float* __restrict__ row_w, int32_t* __restrict__ row_pair) {
+  __shared__ int s_hist[256];
+  __shared__ int s_wave[17];
+  __shared__ unsigned long long s_prefix;
+  __shared__ int s_remaining;
+  const int e = blockIdx.x;
+  const int r = counts[e];
+  const int off = offsets[e];
+  const uint64_t* ke = keys + (size_t)e * N;
+  uint64_t thr = ~0ull;  // select nothing unless r > 0
+  if (r > 0) {
+    if (threadIdx.x == 0) { s_prefix = 0ull; s_remaining = r; }
+    uint64_t mask = 0ull;
+    for (int pass = 0; pass < 8; ++pass) {
+      const int shift = 56 - 8 * pass;
+      if (threadIdx.x < 256) s_hist[threadIdx.x] = 0;
+      __syncthreads();
+      const uint64_t prefix = s_prefix;
+      for (int t = threadIdx.x; t < N; t += 1024) {
+        const uint64_t key = ke[t];
+        if ((key & mask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], 1);
+      }
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        int cum = 0;
+        const int rem = s_remaining;
+        for (int b = 255; b >= 0; --b) {
+          const int c = s_hist[b];
+          if (cum + c >= rem) {
+            s_prefix = prefix | ((uint64_t)b << shift);
+            s_remaining = rem - cum;
+            break;
+          }
+          cum += c;
+        }
+      }
+      mask |= 0xFFull << shift;
+      __syncthreads();
+    }
+    thr = s_prefix;
+  }
+  int run = 0;
+  for (int base = 0; base < N; base += 1024) {
+    const int t = base + threadIdx.x;
+    const bool sel = (t < N) && (r > 0) && (ke[t] >= thr);
+    int total;
+    const int pos = block_excl_scan_1024(sel ? 1 : 0, s_wave, &total);
+    if (t < N) {
+      if (sel) {
+        const int row = off + run + pos;
+        row_of[(size_t)e * N + t] = row;
+        row_token[row] = t;
+        row_w[row] = probs[(size_t)t * E + e] / tok_norm[t];
+        int pair = -1;
+        for (int j = 0; j < k; ++j)
+          if (idx[(size_t)t * k + j] == e) { pair = t * k + j; break; }
+        row_pair[row] = pair;
+      } else {
+        row_of[(size_t)e * N + t] = -1;
+      }
+    }
+    run += total;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_tr_tokcount(const int32_t* __restrict__ row_of, int N, int E,
+                                                     int32_t* __restrict__ tcount) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= N) return;
+  int c = 0;
+  for (int e = 0; e < E; ++e) c += row_of[(size_t)e * N + t] >= 0;
+  tcount[t] = c;
+}
+
+// exclusive scan of tcount[0..N) into tok_ptr[0..N]; one block of 1024 threads
+__global__ __launch_bounds__(1024) void k_scan_tokens(const int32_t* __restrict__ tcount, int N,
+                                                      int32_t* __restrict__ tok_ptr) {
+  __shared__ int s_wave[17];
+  int run = 0;
+  for (int base = 0; base < N; base += 1024) {
+    const int t = base + threadIdx.x;
+    const int v = t < N ? tcount[t] : 0;
+    int total;
+    const int ex = block_excl_scan_1024(v, s_wave, &total);
+    if (t < N) tok_ptr[t] = run + ex;
+    run += total;
+  }
+  if (threadIdx.x == 0) tok_ptr[N] = run;
+}
+
+__global__ __launch_bounds__(256) void k_tr_tokfill(const int32_t* __restrict__ row_of, int N, int E,
+                                                    const int32_t* __restrict__ tok_ptr,
+                                                    int32_t* __restrict__ tok_rows) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= N) return;
+  int p = tok_ptr[t];
+  for (int e = 0; e < E; ++e) {
+    const int r = row_of[(size_t)e * N + t];
+    if (r >= 0) tok_rows[p++] = r;
+  }
+}
+
+// defined in permute.hip
+hipError_t launch_perm_hist(const int32_t* idx, int N, int E, int k, int32_t* bcnt, hipStream_t s);
+
+static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+size_t tr_ws_bytes(int N, int E) {
+  const size_t nb = ((size_t)N + 255) / 256;
+  return align256(nb * E * 4) + align256((size_t)N * 4) + align256((size_t)E * N * 8) +
+         align256((size_t)E * N * 4) + align256((size_t)N * 4) + 256;
+}
+
+hipError_t launch_token_round(const int32_t* idx, const float* probs, const float* tok_norm, int N, int E,
+                              int k, int mtile, const moe_plan& p, void* ws, hipStream_t s) {
+  const int nb = (N + 255) / 256;
+  char* w = (char*)ws;
+  int32_t* bcnt = (int32_t*)w;
+  w += align256((size_t)nb * E * 4);
+  w += align256((size_t)N * 4);  // tok_norm lives here (written by the route kernel)
+  uint64_t* keys = (uint64_t*)w;
+  w += align256((size_t)E * N * 8);
+  int32_t* row_of = (int32_t*)w;
+  w += align256((size_t)E * N * 4);
+  int32_t* tcount = (int32_t*)w;
+  hipError_t err;
+  if (N > 0) {
+    if ((err = launch_perm_hist(idx, N, E, k, bcnt, s)) != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(k_tr_sizes, dim3(1), dim3(1024), 0, s, bcnt, nb, N, E, mtile, p.counts, p.offsets);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (N > 0) {
+    hipLaunchKernelGGL(k_tr_keys, dim3((N + 63) / 64, (E + 63) / 64), dim3(256), 0, s, probs, idx, N, E, k, keys);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(k_tr_select, dim3(E), dim3(1024), 0, s, keys, probs, tok_norm, idx, N, E, k, p.counts,
+                       p.offsets, row_of, p.row_token, p.row_w, p.row_pair);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(k_tr_tokcount, dim3((N + 255) / 256), dim3(256), 0, s, row_of, N, E, tcount);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(k_scan_tokens, dim3(1), dim3(1024), 0, s, tcount, N, p.tok_ptr);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (N > 0) {
+    hipLaunchKernelGGL(k_tr_tokfill, dim3((N + 255) / 256), dim3(256), 0, s, row_of, N, E, p.tok_ptr, p.tok_rows);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+}  // namespace moe

@@ -1,0 +1,244 @@
+/*
+ * moe.h -- C ABI of libmoe.so: the dropless Mixture-of-Experts expert-MLP layer on one
+ * MI355X (gfx950), forward and backward.
+ *
+ * Pages cited (by title, then section):
+ *   [GG]  "DeepSeek 계열 MoE 학습 가속: Python expert loop → grouped GEMM"
+ *   [EP]  "EP: Expert를 나누고 토큰 보내기"
+ *   [SM]  "SonicMoE: IO·타일 인식 최적화로 MoE 학습 가속하기"
+ *   [DEP] "Deep EP"
+ *
+ * General contract (applies to every entry point):
+ *  - Array arguments are DEVICE pointers unless stated otherwise.  The caller allocates and
+ *    owns every buffer, including the workspace, and keeps them alive until the work queued
+ *    on `stream` has finished.  The library never allocates, frees or synchronises on these
+ *    paths, and keeps no state between calls except a per-thread error string, a
+ *    per-device cache of device properties and the optional kernel-event registry of
+ *    moe_set_kernel_events().
+ *  - `stream` is a hipStream_t passed as void*; NULL means the default stream.  All work is
+ *    queued on that stream in order; nothing is copied back to the host.
+ *  - Layouts are row-major.  Expert weights are stacked nn.Linear (out, in) matrices,
+ *    [GG] "적용 — fused MoE training forward" step (5):
+ *        w_gate, w_up : [E, I, H]      w_down : [E, H, I]
+ *  - Element type: x, weights, dout, hcache, y, out, dx and dW share one moe_dtype
+ *    (MOE_F32 or MOE_BF16, bf16 values rounded to nearest even on every store).  Logits,
+ *    bias, combine weights, probabilities and dS are always fp32; indices are int32.
+ *    Contractions accumulate in fp32.
+ *  - H and I must be multiples of 8 and every data pointer 16-byte aligned, else
+ *    MOE_EUNSUPPORTED.  1 <= k <= E <= 1024; N >= 0 (N == 0 is a valid empty call).
+ *  - Outputs are always overwritten, never accumulated into.
+ *  - Errors: arguments are validated before anything is queued; on failure nothing is
+ *    queued and moe_last_error() describes the problem.  MOE_EHIP reports a launch error
+ *    seen right after a launch.  Faults inside kernels surface at the caller's next
+ *    synchronisation, as with any stream-ordered HIP library.
+ *  - Integer outputs (routing indices, counts, offsets, row lists) are deterministic; the
+ *    floating-point outputs are deterministic too (no atomics; every reduction has a fixed
+ *    order), so two identical calls give bitwise identical results.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,        /* null pointer, size out of range, inconsistent plan */
+  MOE_EUNSUPPORTED = 2,  /* alignment, H/I not multiples of 8, unknown dtype */
+  MOE_EWORKSPACE = 3,    /* workspace smaller than moe_workspace_bytes() */
+  MOE_EHIP = 4           /* HIP runtime error while queueing work */
+} moe_status;
+
+typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+typedef enum moe_plan_kind {
+  MOE_PLAN_TOPK = 0,     /* plain top-k: exactly N*k rows */
+  MOE_PLAN_TR = 1        /* token rounding: per-expert rows rounded to multiples of mtile */
+} moe_plan_kind;
+
+typedef enum moe_op {
+  MOE_OP_PERMUTE = 0,
+  MOE_OP_ROUTE_TR = 1,
+  MOE_OP_GEMM_FWD = 2,
+  MOE_OP_LAYER_BWD = 3
+} moe_op;
+
+/*
+ * Routing plan: the ragged, expert-sorted layout with its offset and index metadata
+ * ([DEP] "2) Dispatch", ragged-vs-padding table, row "추가 정보"; [GG] "적용" steps (1)-(3)).
+ * A host struct of caller-owned device pointers.  Rows are grouped by expert (expert e
+ * owns rows offsets[e] .. offsets[e+1]-1) and, inside an expert, ascend by token index.
+ *
+ *   counts    int32 [E]       rows per expert
+ *   offsets   int32 [E+1]     exclusive prefix sum of counts; offsets[E] = M (rows in use)
+ *   row_token int32 [M_cap]   token of each row
+ *   row_w     fp32  [M_cap]   combine weight of each row
+ *   row_pair  int32 [M_cap]   t*k + j for the row made from topk slot j of token t;
+ *                             -1 for a row added by token rounding (padding)
+ *   tok_ptr   int32 [N+1]     token t owns tok_rows[tok_ptr[t] .. tok_ptr[t+1]-1]
+ *   tok_rows  int32 [M_cap]   rows of each token, ascending
+ *
+ * M_cap is the row capacity of the row arrays, of hcache/y and of the bwd row buffers;
+ * use moe_plan_rows_cap().  For MOE_PLAN_TOPK M = N*k exactly and tok_ptr[t] = t*k.
+ */
+typedef struct moe_plan {
+  int32_t kind;      /* moe_plan_kind */
+  int32_t N, E, k;
+  int32_t M_cap;
+  int32_t mtile;     /* MOE_PLAN_TR only (rounding granule); 0 for top-k */
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* row_token;
+  float* row_w;
+  int32_t* row_pair;
+  int32_t* tok_ptr;
+  int32_t* tok_rows;
+} moe_plan;
+
+/* Row capacity a plan of this kind needs: N*k for top-k; N*k + E*(mtile/2) for token
+ * rounding (rounding to the nearest multiple adds at most mtile/2 rows per expert).
+ * Returns -1 for invalid arguments.  Host-only, no GPU needed. */
+int64_t moe_plan_rows_cap(int32_t kind, int32_t N, int32_t E, int32_t k, int32_t mtile);
+
+/* Bytes of workspace an operation needs (host-only, no GPU needed).  M_cap is the plan's
+ * row capacity (ignored for MOE_OP_PERMUTE).  Returns 0 if the arguments are invalid;
+ * a valid operation may also need 0 bytes only if it has no workspace (none do). */
+size_t moe_workspace_bytes(moe_op op, moe_dtype dt, int32_t N, int32_t E, int32_t k, int32_t H,
+                           int32_t I, int32_t M_cap);
+
+/* Human-readable description of the last error on the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+/*
+ * Router top-k.  [DEP] "1) Router": for each of N tokens, the k experts with the largest
+ * score, returned as index and weight arrays [N,k].
+ *   z[t,e] = logits[t,e] + bias[e]              (bias may be NULL; one fp32 add)
+ *   slot j of token t = the j-th expert in the order (z descending, expert id ascending);
+ *                       -0 and +0 compare equal and tie; inputs must be finite
+ *   topk_w[t,j] = exp(z_j - z_max) / sum over the chosen k of exp(z - z_max)
+ *                       (softmax over all E renormalised over the chosen k; the full
+ *                        denominator cancels)
+ *   probs[t,e]  = softmax over all E of z[t,:]  (optional: NULL skips it)
+ * logits fp32 [N,E], bias fp32 [E] or NULL, topk_idx int32 [N,k], topk_w fp32 [N,k],
+ * probs fp32 [N,E] or NULL.
+ */
+moe_status moe_route_topk(const float* logits, const float* bias, int32_t N, int32_t E, int32_t k,
+                          int32_t* topk_idx, float* topk_w, float* probs, void* stream);
+
+/*
+ * Permute: build the top-k routing plan from topk_idx/topk_w without moving activations
+ * ([GG] "적용" steps (1)-(3): flatten, sort by expert, bincount).  A stable counting sort:
+ * rows of expert e appear in ascending token order.  Requires plan->kind == MOE_PLAN_TOPK,
+ * plan->N/E/k equal to the arguments, plan->M_cap >= N*k, every topk_idx value in [0,E)
+ * and the k experts of a token distinct (as moe_route_topk produces); other inputs give
+ * an unspecified but memory-safe plan.  Workspace: moe_workspace_bytes(MOE_OP_PERMUTE, ...).
+ */
+moe_status moe_permute(const int32_t* topk_idx, const float* topk_w, int32_t N, int32_t E, int32_t k,
+                       const moe_plan* plan, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Token-rounding route ([SM] "5 기여 ③ Token Rounding 라우팅"): ordinary top-k first (as
+ * moe_route_topk, writing topk_idx, topk_w and probs, all required), then per expert the
+ * row count c_e is rounded to r_e = mtile * floor((c_e + mtile/2) / mtile), clamped to the
+ * largest multiple of mtile <= N; the r_e rows are the first r_e tokens in the order
+ * (routed to e first, probs[t,e] descending, token ascending): surplus routed tokens with
+ * the lowest scores are dropped, missing rows are padded with the best unrouted tokens.
+ * Row weight = probs[t,e] / sum_j probs[t, topk_idx[t,j]] (kept pairs keep their top-k
+ * weight up to rounding).  A token left with no rows contributes nothing.  The result is
+ * written to `plan` (kind MOE_PLAN_TR, mtile as given, M_cap >= moe_plan_rows_cap()).
+ * The number of rows M lives on the device in plan->offsets[E].
+ */
+moe_status moe_route_token_rounding(const float* logits, const float* bias, int32_t N, int32_t E,
+                                    int32_t k, int32_t mtile, int32_t* topk_idx, float* topk_w,
+                                    float* probs, const moe_plan* plan, void* ws, size_t ws_bytes,
+                                    void* stream);
+
+/*
+ * Grouped expert MLP forward: for every row r of expert e (token t = row_token[r]),
+ *   G = x[t] W_gate[e]^T,  U = x[t] W_up[e]^T        (variable-M grouped GEMM, gate and up
+ *                                                      share the group sizes, [GG] "적용" (6))
+ *   hcache[r] = [G | U]                              (cached for the backward instead of
+ *                                                      the O(TKd) activations, [SM] "3 기여 ①")
+ *   A = silu(G) * U                                   (SwiGLU fused in the epilogue,
+ *                                                      [SM] "4.2 Epilogue 융합")
+ *   y[r] = A W_down[e]^T                              (variable-M grouped GEMM)
+ * x rows are gathered inside the GEMM's global->LDS load ([SM] "4.1 Gather 융합"); the
+ * permuted activations are never materialised.
+ *   x [N,H], hcache [M_cap, 2I], y [M_cap, H]; rows >= M are not written.
+ * Workspace: moe_workspace_bytes(MOE_OP_GEMM_FWD, ...) (holds A [M_cap, I]).
+ */
+moe_status moe_grouped_gemm_fwd(moe_dtype dt, const void* x, const void* w_gate, const void* w_up,
+                                const void* w_down, int32_t H, int32_t I, const moe_plan* plan,
+                                void* hcache, void* y, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Weighted combine back to token order ([EP] "여러 Expert의 결과도 같은 토큰으로
+ * 돌아오기"; [DEP] "3) Combine"):
+ *   out[t] = sum over r in tok_rows(t) of row_w[r] * y[r]     (row_w NULL: weights 1)
+ * Rows are summed in ascending row order in fp32.  A token without rows gets 0.
+ *   y [M_cap, H], row_w fp32 [M_cap] or NULL, out [N, H].
+ */
+moe_status moe_unpermute_combine(moe_dtype dt, const void* y, int32_t H, const moe_plan* plan,
+                                 const float* row_w, void* out, void* stream);
+
+/*
+ * Layer backward given dOut (gradient of the combined output) and the forward's hcache.
+ * For row r (expert e, token t, weight w) with G, U from hcache and A = silu(G) * U:
+ *   dA'  = dOut[t] W_down[e]                  (varlen-M grouped GEMM, dOut gathered)
+ *   dS_r = <dA', A>                           (= <dOut[t], y_r>: router-score gradient
+ *                                              without loading Y, [SM] "3 기여 ①")
+ *   dA   = w dA';  dG = dA U s (1 + G (1 - s)), s = sigmoid(G);  dU = dA silu(G)
+ *   A'   = w A                                (dH, dS and A' from one epilogue,
+ *                                              [SM] "4.2 Epilogue 융합")
+ *   dW_down[e] = sum_r dOut[t]^T A'           (varlen-K grouped GEMM, dOut gathered)
+ *   dW_gate[e] = sum_r dG^T x[t],  dW_up[e] = sum_r dU^T x[t]   (varlen-K, x gathered)
+ *   dx[t] = sum over rows of t of (dG W_gate[e] + dU W_up[e])  (varlen-M GEMM + combine)
+ * ([SM] "4 기여 ②": varlen-M / varlen-K grouped GEMMs, gathers fused in the backward too.)
+ *   dout, x [N,H]; hcache [M_cap,2I]; dx [N,H]; dw_gate, dw_up [E,I,H]; dw_down [E,H,I]
+ *   (experts without rows get zeros); ds fp32: [N,k] in (t,j) order for top-k plans,
+ *   [M_cap] in row order for token-rounding plans.  dx excludes the router's own path.
+ * Workspace: moe_workspace_bytes(MOE_OP_LAYER_BWD, ...).
+ */
+moe_status moe_layer_bwd(moe_dtype dt, const void* dout, const void* x, const void* w_gate,
+                         const void* w_up, const void* w_down, int32_t H, int32_t I,
+                         const moe_plan* plan, const void* hcache, void* dx, void* dw_gate,
+                         void* dw_up, void* dw_down, float* ds, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/*
+ * Measurement hook (for benchmarks and profilers, not needed for computing): kernels of
+ * the library, identified by moe_kernel_id.  After moe_set_kernel_events(id, start, stop)
+ * with two hipEvent_t handles (passed as void*), every later launch of that kernel records
+ * `start` on the launch stream right before the launch and `stop` right after it; NULL
+ * handles switch recording off.  The registry is process-global and not synchronised:
+ * set it from one thread while no other thread calls the library.  Returns MOE_EINVAL for
+ * an unknown id.  Ids that name a sequence (ROUTE_TR_PLAN, PERMUTE) bracket all of its
+ * kernels.
+ */
+typedef enum moe_kernel_id {
+  MOE_K_GATEUP = 0,      /* forward gate/up grouped GEMM + SwiGLU epilogue */
+  MOE_K_DOWN = 1,        /* forward down grouped GEMM */
+  MOE_K_DH = 2,          /* backward dH kernel (dSwiGLU, dS partials, A') */
+  MOE_K_DX = 3,          /* backward dX grouped GEMM (expert rows) */
+  MOE_K_DWD = 4,         /* backward dW_down varlen-K GEMM */
+  MOE_K_DW1 = 5,         /* backward dW_gate / dW_up varlen-K GEMM */
+  MOE_K_COMBINE = 6,     /* weighted combine (moe_unpermute_combine) */
+  MOE_K_DX_COMBINE = 7,  /* unweighted combine of dX rows inside moe_layer_bwd */
+  MOE_K_ROUTE = 8,       /* top-k router kernel */
+  MOE_K_PERMUTE = 9,     /* histogram + scan + scatter of moe_permute */
+  MOE_K_ROUTE_TR_PLAN = 10, /* the token-rounding plan kernels after the router */
+  MOE_K_DS_REDUCE = 11,  /* ordered reduction of the dS partials */
+  MOE_K_COUNT = 12
+} moe_kernel_id;
+
+moe_status moe_set_kernel_events(int32_t kernel_id, void* start_event, void* stop_event);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -12,5 +12,6 @@ from .oracle import (  # noqa: F401
     pairs_from_topk,
     permute,
     route_topk,
+    threads,
     token_round,
 )

@@ -25,6 +25,7 @@
  * allocation failure.  No function keeps state between calls.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -37,6 +38,17 @@ typedef ORACLE_REAL real;
 #define ORACLE_EXPORT __attribute__((visibility("default")))
 
 ORACLE_EXPORT int oracle_real_bytes(void) { return (int)sizeof(real); }
+
+/* Number of OpenMP threads a parallel region of this library uses. */
+ORACLE_EXPORT int oracle_threads(void) {
+  int n = 1;
+#pragma omp parallel
+  {
+#pragma omp single
+    n = omp_get_num_threads();
+  }
+  return n;
+}
 
 /* ------------------------------------------------------------------------------------
  * Router: top-k selection and combine weights.

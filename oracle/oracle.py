@@ -61,10 +61,15 @@ def _lib(real: str = "f64"):
                                      ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                      _i32p, _i32p, _f32p, _f64p, _f64p, _f64p, _f64p, _f64p]
     for fn in ("oracle_route_topk", "oracle_permute", "oracle_token_round", "oracle_layer_fwd",
-               "oracle_layer_bwd", "oracle_real_bytes"):
+               "oracle_layer_bwd", "oracle_real_bytes", "oracle_threads"):
         getattr(lib, fn).restype = ctypes.c_int
     _LIBS[real] = lib
     return lib
+
+
+def threads(real: str = "f64") -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_lib(real).oracle_threads())
 
 
 def _p(a, t):

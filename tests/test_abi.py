@@ -1,0 +1,147 @@
+"""C-ABI contract of libmoe.so, checked on the host: the library loads, exports every entry
+point that include/moe.h declares, and rejects bad arguments with the documented status
+before anything is queued.  No test here launches a kernel (every call fails validation),
+so the suite runs without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import grouped_gemm_top_amd as G
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+FAKE = 0x10000  # a non-NULL, 16-byte aligned address; never dereferenced by these calls
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(G.lib_path()):
+        import grouped_gemm_top_amd.build as B
+        B.build()
+    return G.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert set(names) == set(G.EXPORTED_SYMBOLS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_plan_struct_layout():
+    assert ctypes.sizeof(G.CPlan) == 6 * 4 + 7 * 8
+
+
+def test_rows_cap(L):
+    assert L.moe_plan_rows_cap(G.PLAN_TOPK, 4096, 128, 8, 0) == 4096 * 8
+    assert L.moe_plan_rows_cap(G.PLAN_TR, 16384, 256, 8, 128) == 16384 * 8 + 256 * 64
+    assert L.moe_plan_rows_cap(G.PLAN_TOPK, 10, 4, 5, 0) == -1      # k > E
+    assert L.moe_plan_rows_cap(G.PLAN_TR, 10, 4, 2, 0) == -1         # mtile < 1
+    assert L.moe_plan_rows_cap(7, 10, 4, 2, 0) == -1                 # unknown kind
+    assert L.moe_plan_rows_cap(G.PLAN_TOPK, 0, 4, 2, 0) == 0         # empty input is valid
+
+
+def test_workspace_bytes(L):
+    for op in (G.OP_PERMUTE, G.OP_ROUTE_TR, G.OP_GEMM_FWD, G.OP_LAYER_BWD):
+        assert L.moe_workspace_bytes(op, G.MOE_BF16, 4096, 128, 8, 2048, 512, 32768) > 0
+        assert L.moe_workspace_bytes(op, G.MOE_BF16, 4096, 128, 0, 2048, 512, 32768) == 0  # k = 0
+    assert L.moe_workspace_bytes(G.OP_GEMM_FWD, G.MOE_BF16, 64, 8, 2, 60, 32, 128) == 0     # H % 8
+    assert L.moe_workspace_bytes(G.OP_LAYER_BWD, 9, 64, 8, 2, 64, 32, 128) == 0            # dtype
+    # forward workspace holds the activation A [M_cap, I]
+    assert L.moe_workspace_bytes(G.OP_GEMM_FWD, G.MOE_BF16, 4096, 128, 8, 2048, 512, 32768) >= 32768 * 512 * 2
+
+
+def _plan(N=64, E=8, k=2, kind=G.PLAN_TOPK, mtile=0, M_cap=None):
+    mc = M_cap if M_cap is not None else (N * k if kind == G.PLAN_TOPK else N * k + E * (mtile // 2))
+    return G.CPlan(kind, N, E, k, mc, mtile, *([FAKE] * 7))
+
+
+def _err(L):
+    return L.moe_last_error().decode()
+
+
+def test_route_topk_errors(L):
+    f = ctypes.c_void_p(FAKE)
+    assert L.moe_route_topk(f, None, 64, 8, 9, f, f, None, None) == G.MOE_EINVAL     # k > E
+    assert "k must be" in _err(L)
+    assert L.moe_route_topk(f, None, 64, 2000, 2, f, f, None, None) == G.MOE_EINVAL  # E > 1024
+    assert L.moe_route_topk(f, None, -1, 8, 2, f, f, None, None) == G.MOE_EINVAL     # N < 0
+    assert L.moe_route_topk(None, None, 64, 8, 2, f, f, None, None) == G.MOE_EINVAL  # NULL logits
+
+
+def test_permute_errors(L):
+    f = ctypes.c_void_p(FAKE)
+    p = _plan()
+    need = L.moe_workspace_bytes(G.OP_PERMUTE, G.MOE_BF16, 64, 8, 2, 8, 8, 0)
+    assert L.moe_permute(f, f, 64, 8, 2, ctypes.byref(p), f, need - 1, None) == G.MOE_EWORKSPACE
+    assert L.moe_permute(f, f, 64, 8, 2, None, f, need, None) == G.MOE_EINVAL
+    small = _plan(M_cap=100)
+    assert L.moe_permute(f, f, 64, 8, 2, ctypes.byref(small), f, need, None) == G.MOE_EINVAL
+    other = _plan(N=32)
+    assert L.moe_permute(f, f, 64, 8, 2, ctypes.byref(other), f, need, None) == G.MOE_EINVAL
+    tr = _plan(kind=G.PLAN_TR, mtile=16)
+    assert L.moe_permute(f, f, 64, 8, 2, ctypes.byref(tr), f, need, None) == G.MOE_EINVAL
+    nullrows = _plan()
+    nullrows.row_token = None
+    assert L.moe_permute(f, f, 64, 8, 2, ctypes.byref(nullrows), f, need, None) == G.MOE_EINVAL
+    assert L.moe_permute(None, f, 64, 8, 2, ctypes.byref(p), f, need, None) == G.MOE_EINVAL
+
+
+def test_token_rounding_errors(L):
+    f = ctypes.c_void_p(FAKE)
+    p = _plan(kind=G.PLAN_TR, mtile=16)
+    need = L.moe_workspace_bytes(G.OP_ROUTE_TR, G.MOE_BF16, 64, 8, 2, 8, 8, 0)
+    args = lambda plan, mt, ws, probs=f: L.moe_route_token_rounding(f, None, 64, 8, 2, mt, f, f, probs,
+                                                                    ctypes.byref(plan), f, ws, None)
+    assert args(p, 16, need - 1) == G.MOE_EWORKSPACE
+    assert args(p, 0, need) == G.MOE_EINVAL
+    assert args(p, 32, need) == G.MOE_EINVAL           # mtile differs from the plan's
+    assert args(_plan(), 16, need) == G.MOE_EINVAL     # top-k plan
+    assert args(p, 16, need, probs=None) == G.MOE_EINVAL
+
+
+def test_gemm_fwd_errors(L):
+    f = ctypes.c_void_p(FAKE)
+    p = _plan()
+    need = L.moe_workspace_bytes(G.OP_GEMM_FWD, G.MOE_BF16, 64, 8, 2, 64, 32, p.M_cap)
+    call = lambda dt, x, H, I, ws: L.moe_grouped_gemm_fwd(dt, x, f, f, f, H, I, ctypes.byref(p), f, f, f, ws, None)
+    assert call(G.MOE_BF16, f, 60, 32, need) == G.MOE_EUNSUPPORTED      # H % 8
+    assert call(G.MOE_BF16, f, 64, 36, need) == G.MOE_EUNSUPPORTED      # I % 8
+    assert call(G.MOE_BF16, f, 0, 32, need) == G.MOE_EINVAL
+    assert call(5, f, 64, 32, need) == G.MOE_EUNSUPPORTED               # dtype
+    assert call(G.MOE_BF16, ctypes.c_void_p(FAKE + 2), 64, 32, need) == G.MOE_EUNSUPPORTED  # misaligned
+    assert call(G.MOE_BF16, None, 64, 32, need) == G.MOE_EINVAL         # NULL x
+    assert call(G.MOE_BF16, f, 64, 32, need - 1) == G.MOE_EWORKSPACE
+
+
+def test_combine_errors(L):
+    f = ctypes.c_void_p(FAKE)
+    p = _plan()
+    assert L.moe_unpermute_combine(G.MOE_BF16, f, 60, ctypes.byref(p), None, f, None) == G.MOE_EUNSUPPORTED
+    assert L.moe_unpermute_combine(G.MOE_BF16, f, 64, ctypes.byref(p), None, None, None) == G.MOE_EINVAL
+    assert L.moe_unpermute_combine(G.MOE_BF16, ctypes.c_void_p(FAKE + 8), 64, ctypes.byref(p), None, f,
+                                   None) == G.MOE_EUNSUPPORTED
+    assert L.moe_unpermute_combine(3, f, 64, ctypes.byref(p), None, f, None) == G.MOE_EUNSUPPORTED
+
+
+def test_layer_bwd_errors(L):
+    f = ctypes.c_void_p(FAKE)
+    p = _plan()
+    need = L.moe_workspace_bytes(G.OP_LAYER_BWD, G.MOE_BF16, 64, 8, 2, 64, 32, p.M_cap)
+
+    def call(ws=need, dx=f, H=64, ds=f, plan=p):
+        return L.moe_layer_bwd(G.MOE_BF16, f, f, f, f, f, H, 32, ctypes.byref(plan), f, dx, f, f, f, ds, f, ws,
+                               None)
+    assert call(ws=need - 1) == G.MOE_EWORKSPACE
+    assert call(dx=None) == G.MOE_EINVAL
+    assert call(ds=None) == G.MOE_EINVAL
+    assert call(H=12) == G.MOE_EUNSUPPORTED
+    assert call(plan=_plan(M_cap=3)) == G.MOE_EINVAL
