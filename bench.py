@@ -105,6 +105,9 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=1536,
                     help="tokens in the CPU-oracle baseline sample (0 disables it)")
     ap.add_argument("--kernel-events", type=int, default=1, help="record per-kernel HIP events (1/0)")
+    ap.add_argument("--mode", choices=("layer", "copy"), default="layer",
+                    help="copy: time a plain 1 GiB device-to-device copy (the calibration run for the "
+                         "FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -120,6 +123,21 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.mode == "copy":
+        nbytes = 1 << 30
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / args.steps
+        print(json.dumps({"mode": "copy", "bytes_read": nbytes, "bytes_written": nbytes, "launches": args.steps,
+                          "ms": round(dt * 1e3, 4), "gbs": round(2 * nbytes / dt / 1e9, 1)}), flush=True)
+        return
     G.lib()
     wl = W.CONFIGS[args.config]
     print(f"# generating {wl.name}", file=sys.stderr, flush=True)
@@ -178,6 +196,10 @@ def main():
     if args.kernel_events:
         evs = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                    for _ in range(args.steps)] for n in names}
+        for pairs in evs.values():  # torch creates the HIP event lazily, at its first record
+            for a, b in pairs:
+                a.record()
+                b.record()
     print(f"# timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()

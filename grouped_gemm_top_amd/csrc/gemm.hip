@@ -34,6 +34,8 @@
 //    the same XCD and share its L2.
 //  * No atomics anywhere; the dS row-dot is reduced across lanes and wavefronts in a fixed
 //    order and across N-tiles by a separate ordered pass.
+#include <type_traits>
+
 #include "common.h"
 
 namespace moe {
@@ -94,210 +96,579 @@ struct Args {
   const int32_t* row_token;
   const float* row_w;
   int E, H, I;
+  int N, M_cap;
 };
 
-struct Tile {
-  int e;      // expert
-  int roff;   // first plan row of the expert
-  int m0;     // varlen-M: row offset inside the expert; varlen-K: first output row
-  int n0;     // first output column (GATEUP: first i)
-  int nt;     // n-tile index
-  int mlen;   // varlen-M: valid rows in this tile
-  int K;      // reduction length
+// ------------------------------------------------------------------ buffer loads
+// Raw buffer loads: an offset at or beyond the descriptor's byte range returns zeros and
+// touches no memory, so masked rows, K tails and steps past the last tile cost nothing and
+// need no branch.  Every pipeline step therefore issues the same instructions, which keeps
+// the compiler's memory-counter waits static.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t OOB = 0x80000000u;  // larger than every descriptor range (< 2^31 bytes)
+
+__device__ __forceinline__ rsrc_t mkr(const void* p, long long bytes) {
+  const int n = bytes > 0x7FFFFFFFLL ? 0x7FFFFFFF : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, n, 0x00020000);
+}
+__device__ __forceinline__ uint4 bld16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ int bld4(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ int ufl(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// ------------------------------------------------------------------ tile schedule
+// A cursor is a position (tile, k-step) in this workgroup's sequence of tiles.
+struct Cur {
+  int it;     // persistent iteration that produced the tile
+  int valid;  // 0 once past the last tile
+  int e, roff, m0, n0, nt, mlen, K, nk, kt;
 };
 
 template <typename T, int KIND>
-struct Problem {
+struct Sched {
+  using TR = KindTraits<KIND>;
+  static constexpr int BK = ElemCfg<T>::BK;
+  const int* s_sched;  // LDS: varlen-M tile prefix [E+1]; varlen-K expert order [E]
+  int total, G, per, xcd, slot, E, nN, nM;
+
+  // K (reduction length) and the number of k-steps of a tile of expert e with `cnt` rows
+  __device__ __forceinline__ void klen(const Args& a, int cnt, int& K, int& nk) const {
+    switch (KIND) {
+      case GATEUP: K = a.H; break;
+      case DOWN: K = a.I; break;
+      case DH: K = a.H; break;
+      case DX: K = a.I; break;  // two segments (gate rows, then up rows) of ceil(I/BK) steps
+      default: K = cnt; break;
+    }
+    nk = (K + BK - 1) / BK;
+    if (KIND == DX) nk *= 2;
+  }
+
+  __device__ __forceinline__ void decode(const Args& a, Cur& c, int it) const {
+    c.it = it;
+    c.kt = 0;
+    const long long tile_ll = (long long)it * G + (long long)xcd * per + slot;
+    c.valid = tile_ll < (long long)total;
+    if (!c.valid) {
+      c.e = 0; c.roff = 0; c.m0 = 0; c.n0 = 0; c.nt = 0; c.mlen = 0; c.K = 0; c.nk = 0;
+      return;
+    }
+    const int tile = (int)tile_ll;
+    if constexpr (!TR::VK) {
+      int lo = 0, hi = E;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_sched[mid] <= tile) lo = mid; else hi = mid;
+      }
+      const int e = ufl(lo);
+      const int cnt = a.counts[e];
+      const int mtiles = (cnt + BM - 1) / BM;
+      const int local = tile - ufl(s_sched[e]);
+      const int mt = local % mtiles, nt = local / mtiles;
+      c.e = e;
+      c.roff = a.offsets[e];
+      c.m0 = mt * BM;
+      c.nt = nt;
+      c.n0 = (KIND == GATEUP) ? nt * 64 : nt * BN;
+      c.mlen = min(BM, cnt - c.m0);
+      klen(a, cnt, c.K, c.nk);
+    } else {
+      const int per_e = nM * nN;
+      const int rank = tile / per_e;
+      const int local = tile - rank * per_e;
+      const int e = ufl(s_sched[rank]);
+      c.e = e;
+      c.roff = a.offsets[e];
+      c.m0 = (local / nN) * BM;
+      c.nt = local % nN;
+      c.n0 = c.nt * BN;
+      c.mlen = BM;
+      klen(a, a.counts[e], c.K, c.nk);
+    }
+  }
+  // the next tile after c's tile (tiles without k-steps are skipped when skip_empty)
+  __device__ __forceinline__ void next_tile(const Args& a, Cur& c, bool skip_empty) const {
+    int it = c.it + 1;
+    for (;;) {
+      decode(a, c, it);
+      if (!c.valid || !skip_empty || c.nk > 0) return;
+      ++it;
+    }
+  }
+};
+
+// ------------------------------------------------------------------ operand addressing
+// K-contiguous operands (LDS rows = operand rows): thread t loads 16-byte chunk t % 8 of rows
+// t/8 + 32v (v = 0..3), so 8 consecutive lanes read one full 128-byte row segment.
+__device__ __forceinline__ int kc_row(int v, int w, int lane) { return 8 * w + (lane >> 3) + 32 * v; }
+__device__ __forceinline__ int kc_chunk(int v, int w, int lane) { return lane & 7; }
+
+// MN-contiguous operands (k-rows x columns in memory): thread -> k-group kg = tid % KG
+// (k-rows 4kg .. 4kg+3 of the step) and column chunk ch = tid / KG.
+
+template <typename T, int KIND>
+struct Ops {
+  using TR = KindTraits<KIND>;
   using C = ElemCfg<T>;
-  static constexpr int VEC = C::VEC, BK = C::BK;
+  static constexpr int VEC = C::VEC, BK = C::BK, LDSW = C::LDSW, KG = BK / 4;
+  static constexpr uint32_t ES = sizeof(T);
 
-  __device__ static int n_tiles(const Args& a) {
-    switch (KIND) {
-      case GATEUP: return (a.I + 63) / 64;
-      case DOWN: return (a.H + BN - 1) / BN;
-      case DH: return (a.I + BN - 1) / BN;
-      case DX: return (a.H + BN - 1) / BN;
-      case DWD: return (a.I + BN - 1) / BN;
-      default: return (a.H + BN - 1) / BN;  // DW1
-    }
-  }
-  __device__ static int m_tiles_k(const Args& a) {  // varlen-K: output rows
-    return KIND == DWD ? (a.H + BM - 1) / BM : (2 * a.I + BM - 1) / BM;
-  }
-  __device__ static int k_len(const Args& a, int cnt) {
-    switch (KIND) {
-      case GATEUP: return a.H;
-      case DOWN: return a.I;
-      case DH: return a.H;
-      case DX: return 2 * a.I;
-      default: return cnt;
-    }
-  }
+  // per-tile state of the load cursor
+  rsrc_t ra, rb0, rb1, rrt;
+  uint32_t rowA[4];  // K-contiguous A: byte offset of each thread row (OOB if masked)
+  uint32_t rowB[4];  // K-contiguous B
+  int segB[4];       // GATEUP: 0 = gate rows, 1 = up rows (uniform per wavefront and load)
 
-  // ---- K-contiguous operand: row `row` of the tile (tile-local), pointer to element k=0 ----
-  __device__ static const T* a_row(const Args& a, const Tile& tl, int row) {
-    if (row >= tl.mlen) return nullptr;
-    const int r = tl.roff + tl.m0 + row;
+  __device__ __forceinline__ void setup_tile(const Args& a, const Cur& L, const int (&tok)[4], int w, int lane) {
+    const int H = a.H, I = a.I;
+    rrt = mkr(a.row_token, 4LL * (long long)a.M_cap);
     switch (KIND) {
-      case GATEUP: return (const T*)a.x + (size_t)a.row_token[r] * a.H;
-      case DOWN: return (const T*)a.act + (size_t)r * a.I;
-      case DH: return (const T*)a.dout + (size_t)a.row_token[r] * a.H;
-      default: return (const T*)a.dh + (size_t)r * (2 * a.I);  // DX
-    }
-  }
-  __device__ static const T* b_row(const Args& a, const Tile& tl, int n) {  // GATEUP, DOWN
-    if (KIND == GATEUP) {
-      const int seg = (n >> 5) & 1;
-      const int i = tl.n0 + (n >> 6) * 32 + (n & 31);
-      if (i >= a.I) return nullptr;
-      return (const T*)(seg ? a.wu : a.wg) + ((size_t)tl.e * a.I + i) * a.H;
-    } else {
-      const int h = tl.n0 + n;
-      if (h >= a.H) return nullptr;
-      return (const T*)a.wd + ((size_t)tl.e * a.H + h) * a.I;
-    }
-  }
-  // ---- MN-contiguous operand: k-row `kk` (global k index), pointer to output column 0 of
-  //      the tile's range, and the number of valid columns from there ----
-  __device__ static const T* a_krow(const Args& a, const Tile& tl, int kk, int& lim) {  // DWD, DW1
-    if (kk >= tl.K) return nullptr;
-    const int r = tl.roff + kk;
-    if (KIND == DWD) {
-      lim = a.H - tl.m0;
-      return (const T*)a.dout + (size_t)a.row_token[r] * a.H + tl.m0;
-    } else {
-      lim = 2 * a.I - tl.m0;
-      return (const T*)a.dh + (size_t)r * (2 * a.I) + tl.m0;
-    }
-  }
-  __device__ static const T* b_krow(const Args& a, const Tile& tl, int kk, int& lim) {  // DH, DX, DWD, DW1
-    if (kk >= tl.K) return nullptr;
-    switch (KIND) {
+      case GATEUP:
+        ra = mkr(a.x, (long long)a.N * H * ES);
+        rb0 = mkr((const T*)a.wg + (size_t)L.e * I * H, (long long)I * H * ES);
+        rb1 = mkr((const T*)a.wu + (size_t)L.e * I * H, (long long)I * H * ES);
+        break;
+      case DOWN:
+        ra = mkr(a.act, (long long)a.M_cap * I * ES);
+        rb0 = rb1 = mkr((const T*)a.wd + (size_t)L.e * H * I, (long long)H * I * ES);
+        break;
       case DH:
-        lim = a.I - tl.n0;
-        return (const T*)a.wd + ((size_t)tl.e * a.H + kk) * a.I + tl.n0;
+        ra = mkr(a.dout, (long long)a.N * H * ES);
+        rb0 = rb1 = mkr((const T*)a.wd + (size_t)L.e * H * I, (long long)H * I * ES);
+        break;
       case DX:
-        lim = a.H - tl.n0;
-        return (kk < a.I ? (const T*)a.wg + ((size_t)tl.e * a.I + kk) * a.H
-                         : (const T*)a.wu + ((size_t)tl.e * a.I + (kk - a.I)) * a.H) +
-               tl.n0;
+        ra = mkr(a.dh, (long long)a.M_cap * 2 * I * ES);
+        rb0 = mkr((const T*)a.wg + (size_t)L.e * I * H, (long long)I * H * ES);
+        rb1 = mkr((const T*)a.wu + (size_t)L.e * I * H, (long long)I * H * ES);
+        break;
       case DWD:
-        lim = a.I - tl.n0;
-        return (const T*)a.act + (size_t)(tl.roff + kk) * a.I + tl.n0;
+        ra = mkr(a.dout, (long long)a.N * H * ES);
+        rb0 = rb1 = mkr(a.act, (long long)a.M_cap * I * ES);
+        break;
       default:  // DW1
-        lim = a.H - tl.n0;
-        return (const T*)a.x + (size_t)a.row_token[tl.roff + kk] * a.H + tl.n0;
+        ra = mkr(a.dh, (long long)a.M_cap * 2 * I * ES);
+        rb0 = rb1 = mkr(a.x, (long long)a.N * H * ES);
+        break;
+    }
+    if constexpr (TR::A_KC) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = kc_row(v, w, lane);
+        const bool ok = L.valid && row < L.mlen;
+        const int r = L.roff + L.m0 + row;
+        uint32_t off = OOB;
+        if (ok) {
+          switch (KIND) {
+            case GATEUP:
+            case DH: off = (uint32_t)tok[v] * (uint32_t)(H * ES); break;
+            case DOWN: off = (uint32_t)r * (uint32_t)(I * ES); break;
+            default: off = (uint32_t)r * (uint32_t)(2 * I * ES); break;  // DX
+          }
+        }
+        rowA[v] = off;
+      }
+    }
+    if constexpr (TR::B_KC) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int n = kc_row(v, w, lane);
+        uint32_t off = OOB;
+        if (KIND == GATEUP) {
+          segB[v] = v & 1;  // = (n >> 5) & 1: rows 32v .. 32v+31 of the tile
+          const int i = L.n0 + (n >> 6) * 32 + (n & 31);
+          if (L.valid && i < I) off = (uint32_t)i * (uint32_t)(H * ES);
+        } else {  // DOWN
+          segB[v] = 0;
+          const int h = L.n0 + n;
+          if (L.valid && h < H) off = (uint32_t)h * (uint32_t)(I * ES);
+        }
+        rowB[v] = off;
+      }
+    }
+  }
+
+  // row tokens of the K-contiguous gathered rows of tile c (GATEUP, DH)
+  __device__ __forceinline__ static void tile_tokens(const Args& a, rsrc_t rrt, const Cur& c, int (&tok)[4], int w, int lane) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int row = kc_row(v, w, lane);
+      const bool ok = c.valid && row < c.mlen;
+      tok[v] = bld4(rrt, ok ? (uint32_t)(c.roff + c.m0 + row) * 4u : OOB);
+    }
+  }
+  // row tokens of the k-rows of step (c, kt) for varlen-K gathered operands (DWD, DW1)
+  __device__ __forceinline__ static void step_tokens(rsrc_t rrt, const Cur& c, int kt, int (&tok)[4], int tid) {
+    const int kg = tid % KG;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int kk = kt * BK + 4 * kg + q;
+      const bool ok = c.valid && kt < c.nk && kk < c.K;
+      tok[q] = bld4(rrt, ok ? (uint32_t)(c.roff + kk) * 4u : OOB);
+    }
+  }
+
+  // issue the 8 loads of step (L, L.kt): R[0..3] A, R[4..7] B
+  __device__ __forceinline__ void issue(const Args& a, const Cur& L, uint4 (&R)[8], const int (&tok)[4], int w, int lane,
+                        int tid) const {
+    const int H = a.H, I = a.I;
+    const bool live = L.valid && L.kt < L.nk;
+    if constexpr (TR::A_KC) {
+      int kofs, klim;
+      if (KIND == DX) {
+        const int half = L.nk / 2;
+        const int seg = L.kt >= half;
+        kofs = seg * I + (L.kt - seg * half) * BK;
+        klim = seg * I + I;
+      } else {
+        kofs = L.kt * BK;
+        klim = L.K;
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int k = kofs + kc_chunk(v, w, lane) * VEC;
+        const uint32_t off = (live && rowA[v] != OOB && k < klim) ? rowA[v] + (uint32_t)k * ES : OOB;
+        R[v] = bld16(ra, off);
+      }
+    } else {  // MN-contiguous A (DWD: gathered dout rows, DW1: dH rows)
+      const int kg = tid % KG, ch = tid / KG;
+      const int col = L.m0 + ch * VEC;
+      const int lim = (KIND == DWD) ? H : 2 * I;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int kk = L.kt * BK + 4 * kg + q;
+        const bool ok = live && kk < L.K && col < lim;
+        uint32_t off = OOB;
+        if (ok) {
+          if (KIND == DWD) off = ((uint32_t)tok[q] * (uint32_t)H + (uint32_t)col) * ES;
+          else off = ((uint32_t)(L.roff + kk) * (uint32_t)(2 * I) + (uint32_t)col) * ES;
+        }
+        R[q] = bld16(ra, off);
+      }
+    }
+    if constexpr (TR::B_KC) {
+      const int k = L.kt * BK;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int kk = k + kc_chunk(v, w, lane) * VEC;
+        const uint32_t off = (live && rowB[v] != OOB && kk < L.K) ? rowB[v] + (uint32_t)kk * ES : OOB;
+        R[4 + v] = bld16(segB[v] ? rb1 : rb0, off);
+      }
+    } else {  // MN-contiguous B
+      const int kg = tid % KG, ch = tid / KG;
+      const int col = L.n0 + ch * VEC;
+      int seg = 0, kbase = L.kt * BK, klim = L.K;
+      if (KIND == DX) {
+        const int half = L.nk / 2;
+        seg = L.kt >= half;
+        kbase = (L.kt - seg * half) * BK;
+        klim = I;
+      }
+      const int lim = (KIND == DH || KIND == DWD) ? I : H;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int kk = kbase + 4 * kg + q;
+        const bool ok = live && kk < klim && col < lim;
+        uint32_t off = OOB;
+        if (ok) {
+          switch (KIND) {
+            case DH: off = ((uint32_t)kk * (uint32_t)I + (uint32_t)col) * ES; break;
+            case DX: off = ((uint32_t)kk * (uint32_t)H + (uint32_t)col) * ES; break;
+            case DWD: off = ((uint32_t)(L.roff + kk) * (uint32_t)I + (uint32_t)col) * ES; break;
+            default: off = ((uint32_t)tok[q] * (uint32_t)H + (uint32_t)col) * ES; break;  // DW1
+          }
+        }
+        R[4 + q] = bld16(seg ? rb1 : rb0, off);
+      }
     }
   }
 };
 
-// ------------------------------------------------------------------ operand staging
-template <typename T>
-struct Stage {
-  using C = ElemCfg<T>;
-  static constexpr int VEC = C::VEC, BK = C::BK, LDSW = C::LDSW;
-  static constexpr int KG = BK / 4;          // k-groups of 4 for the transposing path
-};
+// ------------------------------------------------------------------ LDS staging
+// A stage holds 256 rows (A rows 0..127, B rows 128..255) of 128 bytes, K-contiguous: eight
+// 16-byte chunks per row.  Chunk c of row r sits at position c ^ swz(r): full-row writes
+// (two rows per 16 lanes), 16-row fragment reads at one chunk and the transposing writes all
+// hit distinct banks, with 32 or 64 four-byte banks alike.
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int lds_byte(int row, int chunk) { return row * 128 + ((chunk ^ swz(row)) << 4); }
 
-__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
-
-// K-contiguous: thread -> chunk c = tid % 8 (VEC elements), rows tid/8 + 32v
-template <typename T, class Src>
-__device__ __forceinline__ void gload_kc(uint4 (&r)[4], const Src& src, int k0, int K) {
-  constexpr int VEC = ElemCfg<T>::VEC;
-  const int c = threadIdx.x & 7;
-  const int kk = k0 + c * VEC;
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const T* p = src.rows[v];
-    r[v] = (p != nullptr && kk < K) ? ld16(p + kk) : make_uint4(0, 0, 0, 0);
-  }
-}
 template <typename T>
-__device__ __forceinline__ void sstore_kc(T* lds, const uint4 (&r)[4]) {
-  constexpr int VEC = ElemCfg<T>::VEC, LDSW = ElemCfg<T>::LDSW;
-  const int c = threadIdx.x & 7;
+__device__ __forceinline__ void sstore_kc(char* lds, const uint4* r, int w, int lane) {
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int row = (threadIdx.x >> 3) + 32 * v;
-    *reinterpret_cast<uint4*>(lds + row * LDSW + c * VEC) = r[v];
-  }
+  for (int v = 0; v < 4; ++v)
+    *reinterpret_cast<uint4*>(lds + lds_byte(kc_row(v, w, lane), kc_chunk(v, w, lane))) = r[v];
 }
-// MN-contiguous: thread -> k-group kg = tid % KG (k-rows 4kg..4kg+3), chunk ch = tid / KG
+// 4 k-rows x VEC columns in registers -> VEC LDS rows of 4 consecutive k values.  Threads of
+// odd column chunks visit their rows in the order j ^ 1, so the two chunks written by one
+// instruction land on rows of different parity (different bank halves).
 template <typename T>
-__device__ __forceinline__ void sstore_mn(T* lds, const uint4 (&r)[4]);
+__device__ __forceinline__ void sstore_mn(char* lds, const uint4* r, int tid);
 template <>
-__device__ __forceinline__ void sstore_mn<bf16_t>(bf16_t* lds, const uint4 (&r)[4]) {
-  constexpr int KG = 16, LDSW = ElemCfg<bf16_t>::LDSW;
-  const int kg = threadIdx.x % KG, ch = threadIdx.x / KG;
+__device__ __forceinline__ void sstore_mn<bf16_t>(char* lds, const uint4* r, int tid) {
+  const int kg = tid & 15, ch = tid >> 4;
   const uint32_t* q0 = reinterpret_cast<const uint32_t*>(&r[0]);
   const uint32_t* q1 = reinterpret_cast<const uint32_t*>(&r[1]);
   const uint32_t* q2 = reinterpret_cast<const uint32_t*>(&r[2]);
   const uint32_t* q3 = reinterpret_cast<const uint32_t*>(&r[3]);
+  const int flip = ch & 1;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int h = j >> 1;
+    const int jj = j ^ flip;
+    const int h = jj >> 1;
     uint2 o;
-    if (j & 1) {
+    if (jj & 1) {
       o.x = (q0[h] >> 16) | (q1[h] & 0xFFFF0000u);
       o.y = (q2[h] >> 16) | (q3[h] & 0xFFFF0000u);
     } else {
       o.x = (q0[h] & 0xFFFFu) | (q1[h] << 16);
       o.y = (q2[h] & 0xFFFFu) | (q3[h] << 16);
     }
-    *reinterpret_cast<uint2*>(lds + (ch * 8 + j) * LDSW + 4 * kg) = o;
+    *reinterpret_cast<uint2*>(lds + lds_byte(ch * 8 + jj, kg >> 1) + ((kg & 1) << 3)) = o;
   }
 }
 template <>
-__device__ __forceinline__ void sstore_mn<float>(float* lds, const uint4 (&r)[4]) {
-  constexpr int KG = 8, LDSW = ElemCfg<float>::LDSW;
-  const int kg = threadIdx.x % KG, ch = threadIdx.x / KG;
+__device__ __forceinline__ void sstore_mn<float>(char* lds, const uint4* r, int tid) {
+  const int kg = tid & 7, ch = tid >> 3;
+  const int flip = ch & 1;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
+    const int jj = j ^ flip;
     uint4 o;
-    o.x = reinterpret_cast<const uint32_t*>(&r[0])[j];
-    o.y = reinterpret_cast<const uint32_t*>(&r[1])[j];
-    o.z = reinterpret_cast<const uint32_t*>(&r[2])[j];
-    o.w = reinterpret_cast<const uint32_t*>(&r[3])[j];
-    *reinterpret_cast<uint4*>(lds + (ch * 4 + j) * LDSW + 4 * kg) = o;
+    o.x = reinterpret_cast<const uint32_t*>(&r[0])[jj];
+    o.y = reinterpret_cast<const uint32_t*>(&r[1])[jj];
+    o.z = reinterpret_cast<const uint32_t*>(&r[2])[jj];
+    o.w = reinterpret_cast<const uint32_t*>(&r[3])[jj];
+    *reinterpret_cast<uint4*>(lds + lds_byte(ch * 4 + jj, kg)) = o;
   }
 }
 
-template <typename T>
-struct RowSrc {
-  const T* rows[4];
-};
+// ------------------------------------------------------------------ epilogues
+template <typename T, int KIND>
+__device__ __forceinline__ void epilogue(const Args& a, const Cur& c, f32x4 (&acc)[4][4], float* s_red, int wm, int wn,
+                                         int lane) {
+  const int mrow = wm * 64 + (lane & 15);
+  const int ncol = wn * 64 + 4 * (lane >> 4);
+  if constexpr (KIND == GATEUP) {
+    T* hc = (T*)a.out0;
+    T* ac = (T*)a.out1;
+    const int I = a.I;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = mrow + i * 16;
+      if (m >= c.mlen) continue;
+      const size_t r = (size_t)(c.roff + c.m0 + m);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int ii = c.n0 + wn * 32 + j * 16 + 4 * (lane >> 4);
+        if (ii >= I) continue;
+        const f32x4 g = acc[i][j], u = acc[i][j + 2];
+        store4(hc + r * (2 * I) + ii, g[0], g[1], g[2], g[3]);
+        store4(hc + r * (2 * I) + I + ii, u[0], u[1], u[2], u[3]);
+        float av[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) av[v] = g[v] * sigmoidf_(g[v]) * u[v];
+        store4(ac + r * I + ii, av[0], av[1], av[2], av[3]);
+      }
+    }
+  } else if constexpr (KIND == DOWN || KIND == DX) {
+    T* out = (T*)a.out0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = mrow + i * 16;
+      if (m >= c.mlen) continue;
+      const size_t r = (size_t)(c.roff + c.m0 + m);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int h = c.n0 + ncol + j * 16;
+        if (h >= a.H) continue;
+        store4(out + r * a.H + h, acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+      }
+    }
+  } else if constexpr (KIND == DH) {
+    T* dh = (T*)a.out0;
+    T* ap = (T*)a.out1;
+    const int I = a.I;
+    constexpr uint32_t ES = sizeof(T);
+    const rsrc_t rh = mkr(a.hcache, (long long)a.M_cap * 2 * I * ES);
+    const rsrc_t rw = mkr(a.row_w, 4LL * a.M_cap);
+    float dsum[4] = {0.f, 0.f, 0.f, 0.f};
+    // two halves of the wavefront's rows: all loads of a half are issued before any use,
+    // masked rows and columns read zeros (out-of-range buffer offsets)
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      uint4 graw[2][4], uraw[2][4];
+      float wrow[2];
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii) {
+        const int i = half * 2 + ii;
+        const int m = mrow + i * 16;
+        const bool okr = m < c.mlen;
+        const uint32_t r = (uint32_t)(c.roff + c.m0 + m);
+        wrow[ii] = __int_as_float(bld4(rw, okr ? r * 4u : OOB));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int col = c.n0 + ncol + j * 16;
+          const bool ok = okr && col < I;
+          const uint32_t og = ok ? (r * (uint32_t)(2 * I) + (uint32_t)col) * ES : OOB;
+          const uint32_t ou = ok ? og + (uint32_t)I * ES : OOB;
+          if constexpr (sizeof(T) == 2) {
+            graw[ii][j] = make_uint4(0, 0, 0, 0);
+            uraw[ii][j] = make_uint4(0, 0, 0, 0);
+            const auto g2 = __builtin_amdgcn_raw_buffer_load_b64(rh, og, 0, 0);
+            const auto u2 = __builtin_amdgcn_raw_buffer_load_b64(rh, ou, 0, 0);
+            graw[ii][j].x = g2[0]; graw[ii][j].y = g2[1];
+            uraw[ii][j].x = u2[0]; uraw[ii][j].y = u2[1];
+          } else {
+            graw[ii][j] = bld16(rh, og);
+            uraw[ii][j] = bld16(rh, ou);
+          }
+        }
+      }
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii) {
+        const int i = half * 2 + ii;
+        const int m = mrow + i * 16;
+        const bool okr = m < c.mlen;
+        const size_t r = (size_t)(c.roff + c.m0 + m);
+        const float w = wrow[ii];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int col = c.n0 + ncol + j * 16;
+          float g[4], u[4], dg[4], du[4], av[4];
+          if constexpr (sizeof(T) == 2) {
+            g[0] = __uint_as_float(graw[ii][j].x << 16); g[1] = __uint_as_float(graw[ii][j].x & 0xFFFF0000u);
+            g[2] = __uint_as_float(graw[ii][j].y << 16); g[3] = __uint_as_float(graw[ii][j].y & 0xFFFF0000u);
+            u[0] = __uint_as_float(uraw[ii][j].x << 16); u[1] = __uint_as_float(uraw[ii][j].x & 0xFFFF0000u);
+            u[2] = __uint_as_float(uraw[ii][j].y << 16); u[3] = __uint_as_float(uraw[ii][j].y & 0xFFFF0000u);
+          } else {
+            g[0] = __uint_as_float(graw[ii][j].x); g[1] = __uint_as_float(graw[ii][j].y);
+            g[2] = __uint_as_float(graw[ii][j].z); g[3] = __uint_as_float(graw[ii][j].w);
+            u[0] = __uint_as_float(uraw[ii][j].x); u[1] = __uint_as_float(uraw[ii][j].y);
+            u[2] = __uint_as_float(uraw[ii][j].z); u[3] = __uint_as_float(uraw[ii][j].w);
+          }
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float sg = sigmoidf_(g[v]);
+            const float silu = g[v] * sg;
+            const float A = silu * u[v];
+            const float dap = acc[i][j][v];
+            dsum[i] += dap * A;  // masked rows/columns hold zeros in both factors
+            const float da = w * dap;
+            dg[v] = da * u[v] * sg * (1.0f + g[v] * (1.0f - sg));
+            du[v] = da * silu;
+            av[v] = w * A;
+          }
+          if (okr && col < I) {
+            store4(dh + r * (2 * I) + col, dg[0], dg[1], dg[2], dg[3]);
+            store4(dh + r * (2 * I) + I + col, du[0], du[1], du[2], du[3]);
+            store4(ap + r * I + col, av[0], av[1], av[2], av[3]);
+          }
+        }
+      }
+    }
+    // row-dot partials: lanes l, l^16, l^32, l^48 hold the same row; then the two
+    // wavefronts of a row block (wn = 0, 1), always in the same order
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      dsum[i] += __shfl_xor(dsum[i], 16);
+      dsum[i] += __shfl_xor(dsum[i], 32);
+    }
+    if (wn == 1 && lane < 16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_red[wm * 64 + i * 16 + lane] = dsum[i];
+    }
+    __syncthreads();
+    if (wn == 0 && lane < 16) {
+      const int nTN = (I + BN - 1) / BN;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = mrow + i * 16;
+        if (m < c.mlen) a.dspart[(size_t)(c.roff + c.m0 + m) * nTN + c.nt] = dsum[i] + s_red[m];
+      }
+    }
+    __syncthreads();
+  } else if constexpr (KIND == DWD) {
+    T* dw = (T*)a.out0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = c.m0 + mrow + i * 16;
+      if (h >= a.H) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int ii = c.n0 + ncol + j * 16;
+        if (ii >= a.I) continue;
+        store4(dw + ((size_t)c.e * a.H + h) * a.I + ii, acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+      }
+    }
+  } else {  // DW1
+    T* dwg = (T*)a.out0;
+    T* dwu = (T*)a.out1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ip = c.m0 + mrow + i * 16;
+      if (ip >= 2 * a.I) continue;
+      T* base = ip < a.I ? dwg + ((size_t)c.e * a.I + ip) * a.H : dwu + ((size_t)c.e * a.I + (ip - a.I)) * a.H;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int h = c.n0 + ncol + j * 16;
+        if (h >= a.H) continue;
+        store4(base + h, acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+      }
+    }
+  }
+}
 
 // ------------------------------------------------------------------ the kernel
 template <typename T, int KIND>
-__global__ __launch_bounds__(NTHR, 2) void k_grouped_gemm(Args a) {
+__global__ __launch_bounds__(NTHR, 2) void k_grouped_gemm(Args a, const int32_t* __restrict__ counts,
+                                                          const int32_t* __restrict__ offsets) {
+  // The expert counts and offsets are read-only here; passing them as restrict kernel
+  // arguments lets the compiler fetch them with scalar loads, which do not wait behind the
+  // vector-memory prefetch queue.
+  a.counts = counts;
+  a.offsets = offsets;
   using C = ElemCfg<T>;
-  using P = Problem<T, KIND>;
   using TR = KindTraits<KIND>;
-  constexpr int BK = C::BK, LDSW = C::LDSW, VEC = C::VEC, KPL = C::KPL;
+  using O = Ops<T, KIND>;
+  constexpr int BK = C::BK, LDSW = C::LDSW, KPL = C::KPL;
   constexpr int KSTEP = 4 * KPL;
-  constexpr int KG = BK / 4;
-  constexpr int STAGE = (BM + BN) * LDSW;
+  constexpr int STAGE = (BM + BN) * 128;  // bytes
+  constexpr bool GATHER_KC = (KIND == GATEUP || KIND == DH);   // per-tile row tokens
+  constexpr bool GATHER_MN = (KIND == DWD || KIND == DW1);     // per-step row tokens
 
-  __shared__ __attribute__((aligned(16))) T s_tile[2 * STAGE];
+  __shared__ __attribute__((aligned(16))) char s_tile[2 * STAGE];
   __shared__ int s_sched[1025];
   __shared__ int s_wave[5];
   __shared__ float s_red[BM];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = ufl(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int E = a.E;
-  const int nN = P::n_tiles(a);
+
+  Sched<T, KIND> S;
+  S.s_sched = s_sched;
+  S.E = E;
+  S.G = gridDim.x;
+  S.per = S.G >> 3;
+  S.xcd = blockIdx.x & 7;
+  S.slot = blockIdx.x >> 3;
+  switch (KIND) {
+    case GATEUP: S.nN = (a.I + 63) / 64; break;
+    case DOWN: case DX: case DW1: S.nN = (a.H + BN - 1) / BN; break;
+    default: S.nN = (a.I + BN - 1) / BN; break;  // DH, DWD
+  }
+  S.nM = KIND == DWD ? (a.H + BM - 1) / BM : (2 * a.I + BM - 1) / BM;
 
   // ---- tile space from the device-resident counts ----
-  int total;
   if constexpr (!TR::VK) {
-    // per-expert tile count ceil(c/BM)*nN, exclusive prefix over experts (4 per thread)
     int loc[4], sum = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = tid * 4 + q;
-      loc[q] = e < E ? ((a.counts[e] + BM - 1) / BM) * nN : 0;
+      loc[q] = e < E ? ((a.counts[e] + BM - 1) / BM) * S.nN : 0;
       sum += loc[q];
     }
     int x = sum;
@@ -322,11 +693,11 @@ __global__ __launch_bounds__(NTHR, 2) void k_grouped_gemm(Args a) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = tid * 4 + q;
-      if (e <= E) s_sched[e] = run;
+      if (e < E) s_sched[e] = run;
       run += loc[q];
     }
-    total = s_wave[4];
-    if (tid == 0) s_sched[E] = total;
+    if (tid == 0) s_sched[E] = s_wave[4];
+    S.total = ufl(s_wave[4]);
     __syncthreads();
   } else {
     // heaviest expert first: rank_e = #{e' : c_e' > c_e or (c_e' == c_e and e' < e)}
@@ -343,257 +714,160 @@ __global__ __launch_bounds__(NTHR, 2) void k_grouped_gemm(Args a) {
       s_sched[rank] = e;
     }
     __syncthreads();
-    total = E * P::m_tiles_k(a) * nN;
+    S.total = E * S.nM * S.nN;
   }
 
-  const int G = gridDim.x;
-  const int per = G >> 3;
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  // ---- cursors: L = next step to load, Lx = the tile after L's, C = step being computed ----
+  Cur L, Lx, Cc;
+  S.decode(a, L, 0);
+  if (L.valid && L.nk == 0) S.next_tile(a, L, true);
+  Lx = L;
+  S.next_tile(a, Lx, true);
+  S.decode(a, Cc, 0);
 
-  for (int it = 0;; ++it) {
-    const long long tile_ll = (long long)it * G + (long long)xcd * per + slot;
-    if (tile_ll >= total) break;
-    const int tile = (int)tile_ll;
+  O ops;
+  int tokA[4] = {0, 0, 0, 0}, tokN[4] = {0, 0, 0, 0};  // per-tile gathered rows (current / next tile)
+  int rtE[4] = {0, 0, 0, 0}, rtO[4] = {0, 0, 0, 0};    // per-step gathered rows (even / odd steps)
+  const rsrc_t rrt = mkr(a.row_token, 4LL * (long long)a.M_cap);
+  if constexpr (GATHER_KC) {
+    O::tile_tokens(a, rrt, L, tokA, wave, lane);
+    O::tile_tokens(a, rrt, Lx, tokN, wave, lane);
+  }
+  ops.setup_tile(a, L, tokA, wave, lane);
 
-    // ---- decode ----
-    Tile tl;
-    if constexpr (!TR::VK) {
-      int lo = 0, hi = E;
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (s_sched[mid] <= tile) lo = mid; else hi = mid;
-      }
-      const int e = lo;
-      const int cnt = a.counts[e];
-      const int mtiles = (cnt + BM - 1) / BM;
-      const int local = tile - s_sched[e];
-      const int mt = local % mtiles, nt = local / mtiles;
-      tl.e = e;
-      tl.roff = a.offsets[e];
-      tl.m0 = mt * BM;
-      tl.nt = nt;
-      tl.n0 = (KIND == GATEUP) ? nt * 64 : nt * BN;
-      tl.mlen = min(BM, cnt - tl.m0);
-      tl.K = P::k_len(a, cnt);
+  // advance L by one step; at a tile change the next tile's state becomes current
+  auto advance_L = [&]() __attribute__((always_inline)) {
+    if (L.valid && L.kt + 1 < L.nk) {
+      ++L.kt;
+      return;
+    }
+    L = Lx;
+    Lx = L;
+    S.next_tile(a, Lx, true);
+    if constexpr (GATHER_KC) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) tokA[v] = tokN[v];
+      O::tile_tokens(a, rrt, Lx, tokN, wave, lane);
+    }
+    ops.setup_tile(a, L, tokA, wave, lane);
+  };
+  // position one step after L (for the per-step token prefetch)
+  auto peek_next = [&](Cur& p, int& kt) __attribute__((always_inline)) {
+    if (L.valid && L.kt + 1 < L.nk) {
+      p = L;
+      kt = L.kt + 1;
     } else {
-      const int per_e = P::m_tiles_k(a) * nN;
-      const int rank = tile / per_e;
-      const int local = tile - rank * per_e;
-      const int e = s_sched[rank];
-      tl.e = e;
-      tl.roff = a.offsets[e];
-      tl.m0 = (local / nN) * BM;
-      tl.nt = local % nN;
-      tl.n0 = tl.nt * BN;
-      tl.mlen = BM;
-      tl.K = a.counts[e];
+      p = Lx;
+      kt = 0;
     }
+  };
 
-    // ---- per-thread operand row pointers (K-contiguous operands) ----
-    RowSrc<T> asrc, bsrc;
-    if constexpr (TR::A_KC) {
+  f32x4 acc[4][4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) asrc.rows[v] = P::a_row(a, tl, (tid >> 3) + 32 * v);
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // tiles without k-steps at the start of the sequence (empty experts, varlen-K only)
+  while (Cc.valid && Cc.nk == 0) {
+    epilogue<T, KIND>(a, Cc, acc, s_red, wm, wn, lane);
+    S.next_tile(a, Cc, false);
+  }
+  if (!Cc.valid) return;
+
+  // ---- prologue: steps 0 and 1 in flight, step 0 in LDS ----
+  uint4 R0[8], R1[8];
+  if constexpr (GATHER_MN) {
+    O::step_tokens(rrt, L, L.kt, rtE, tid);
+    Cur p;
+    int pk;
+    peek_next(p, pk);
+    O::step_tokens(rrt, p, pk, rtO, tid);
+  }
+  ops.issue(a, L, R0, rtE, wave, lane, tid);
+  advance_L();
+  if constexpr (GATHER_MN) {
+    Cur p;
+    int pk;
+    peek_next(p, pk);
+    O::step_tokens(rrt, p, pk, rtE, tid);
+  }
+  ops.issue(a, L, R1, rtO, wave, lane, tid);
+  advance_L();
+  {
+    char* la = s_tile;
+    if constexpr (TR::A_KC) sstore_kc<T>(la, R0, wave, lane); else sstore_mn<T>(la, R0, tid);
+    if constexpr (TR::B_KC) sstore_kc<T>(la + BM * 128, R0 + 4, wave, lane); else sstore_mn<T>(la + BM * 128, R0 + 4, tid);
+  }
+  __syncthreads();
+
+  // one pipeline step: prefetch step s+2 into Rp, compute stage P, store Rq (step s+1) into stage 1-P
+  auto step = [&](auto PP, uint4 (&Rp)[8], uint4 (&Rq)[8], int (&rt_use)[4], int (&rt_fill)[4])
+                  __attribute__((always_inline)) {
+    constexpr int P = decltype(PP)::value;
+    if constexpr (GATHER_MN) {
+      Cur p;
+      int pk;
+      peek_next(p, pk);
+      O::step_tokens(rrt, p, pk, rt_fill, tid);  // tokens of step s+3, issued before the data of s+2
     }
-    if constexpr (TR::B_KC) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) bsrc.rows[v] = P::b_row(a, tl, (tid >> 3) + 32 * v);
-    }
+    ops.issue(a, L, Rp, rt_use, wave, lane, tid);
+    advance_L();
 
-    auto gload = [&](uint4 (&ra)[4], uint4 (&rb)[4], int k0) {
-      if constexpr (TR::A_KC) {
-        gload_kc<T>(ra, asrc, k0, tl.K);
-      } else {
-        const int kg = tid % KG, ch = tid / KG;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          int lim = 0;
-          const T* p = P::a_krow(a, tl, k0 + 4 * kg + q, lim);
-          ra[q] = (p != nullptr && ch * VEC < lim) ? ld16(p + ch * VEC) : make_uint4(0, 0, 0, 0);
-        }
-      }
-      if constexpr (TR::B_KC) {
-        gload_kc<T>(rb, bsrc, k0, tl.K);
-      } else {
-        const int kg = tid % KG, ch = tid / KG;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          int lim = 0;
-          const T* p = P::b_krow(a, tl, k0 + 4 * kg + q, lim);
-          rb[q] = (p != nullptr && ch * VEC < lim) ? ld16(p + ch * VEC) : make_uint4(0, 0, 0, 0);
-        }
-      }
-    };
-    auto sstore = [&](int s, const uint4 (&ra)[4], const uint4 (&rb)[4]) {
-      T* la = s_tile + s * STAGE;
-      T* lb = la + BM * LDSW;
-      if constexpr (TR::A_KC) sstore_kc<T>(la, ra); else sstore_mn<T>(la, ra);
-      if constexpr (TR::B_KC) sstore_kc<T>(lb, rb); else sstore_mn<T>(lb, rb);
-    };
-
-    f32x4 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const int nk = (tl.K + BK - 1) / BK;
-    uint4 ra[4], rb[4];
-    if (nk > 0) {
-      gload(ra, rb, 0);
-      sstore(0, ra, rb);
-    }
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int s = kt & 1;
-      if (kt + 1 < nk) gload(ra, rb, (kt + 1) * BK);
-      const T* la = s_tile + s * STAGE + (wm * 64 + (lane & 15)) * LDSW + (lane >> 4) * KPL;
-      const T* lb = s_tile + s * STAGE + (BM + wn * 64 + (lane & 15)) * LDSW + (lane >> 4) * KPL;
+    // fragment rows: A rows wm*64 + i*16 + (lane & 15), B rows 128 + wn*64 + j*16 + (lane & 15);
+    // the swizzle depends on row & 15 = lane & 15 only
+    const char* sa = s_tile + P * STAGE + (wm * 64 + (lane & 15)) * 128;
+    const char* sb = s_tile + P * STAGE + (BM + wn * 64 + (lane & 15)) * 128;
+    const int fsw = swz(lane & 15);
+    // a wavefront whose 64 rows all lie past the tile's valid rows has no work this step
+    if (Cc.mlen > wm * 64) {
 #pragma unroll
       for (int ks = 0; ks < BK / KSTEP; ++ks) {
+        // byte offset of this lane's k values inside its row for k-step ks
+        const int kbyte = (ks * KSTEP + (lane >> 4) * KPL) * (int)sizeof(T);
+        const int off = (((kbyte >> 4) ^ fsw) << 4) + (kbyte & 15);
         typename C::frag_t fa[4], fb[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          fa[i] = *reinterpret_cast<const typename C::frag_t*>(la + i * 16 * LDSW + ks * KSTEP);
-#pragma unroll
         for (int j = 0; j < 4; ++j)
-          fb[j] = *reinterpret_cast<const typename C::frag_t*>(lb + j * 16 * LDSW + ks * KSTEP);
+          fb[j] = *reinterpret_cast<const typename C::frag_t*>(sb + j * 16 * 128 + off);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          fa[i] = *reinterpret_cast<const typename C::frag_t*>(sa + i * 16 * 128 + off);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j) acc[i][j] = mma(fb[j], fa[i], acc[i][j]);
       }
-      if (kt + 1 < nk) sstore(s ^ 1, ra, rb);
-      __syncthreads();
     }
+    {
+      char* la = s_tile + (1 - P) * STAGE;
+      if constexpr (TR::A_KC) sstore_kc<T>(la, Rq, wave, lane); else sstore_mn<T>(la, Rq, tid);
+      if constexpr (TR::B_KC) sstore_kc<T>(la + BM * 128, Rq + 4, wave, lane);
+      else sstore_mn<T>(la + BM * 128, Rq + 4, tid);
+    }
+    __syncthreads();
+    // advance the compute cursor; finish the tile after its last step
+    if (Cc.kt + 1 < Cc.nk) {
+      ++Cc.kt;
+    } else {
+      epilogue<T, KIND>(a, Cc, acc, s_red, wm, wn, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      S.next_tile(a, Cc, false);
+      while (Cc.valid && Cc.nk == 0) {
+        epilogue<T, KIND>(a, Cc, acc, s_red, wm, wn, lane);
+        S.next_tile(a, Cc, false);
+      }
+    }
+  };
 
-    // ---- epilogue: acc[i][j][v] = C[m = wm*64 + i*16 + (lane&15)][n = wn*64 + j*16 + 4*(lane>>4) + v] ----
-    const int mrow = wm * 64 + (lane & 15);
-    const int ncol = wn * 64 + 4 * (lane >> 4);
-    if constexpr (KIND == GATEUP) {
-      T* hc = (T*)a.out0;
-      T* ac = (T*)a.out1;
-      const int I = a.I;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = mrow + i * 16;
-        if (m >= tl.mlen) continue;
-        const size_t r = (size_t)(tl.roff + tl.m0 + m);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int ii = tl.n0 + wn * 32 + j * 16 + 4 * (lane >> 4);
-          if (ii >= I) continue;
-          const f32x4 g = acc[i][j], u = acc[i][j + 2];
-          store4(hc + r * (2 * I) + ii, g[0], g[1], g[2], g[3]);
-          store4(hc + r * (2 * I) + I + ii, u[0], u[1], u[2], u[3]);
-          float av[4];
-#pragma unroll
-          for (int v = 0; v < 4; ++v) av[v] = g[v] * sigmoidf_(g[v]) * u[v];
-          store4(ac + r * I + ii, av[0], av[1], av[2], av[3]);
-        }
-      }
-    } else if constexpr (KIND == DOWN || KIND == DX) {
-      T* out = (T*)a.out0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = mrow + i * 16;
-        if (m >= tl.mlen) continue;
-        const size_t r = (size_t)(tl.roff + tl.m0 + m);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int h = tl.n0 + ncol + j * 16;
-          if (h >= a.H) continue;
-          store4(out + r * a.H + h, acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-        }
-      }
-    } else if constexpr (KIND == DH) {
-      T* dh = (T*)a.out0;
-      T* ap = (T*)a.out1;
-      const T* hc = (const T*)a.hcache;
-      const int I = a.I;
-      float dsum[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        dsum[i] = 0.f;
-        const int m = mrow + i * 16;
-        if (m >= tl.mlen) continue;
-        const size_t r = (size_t)(tl.roff + tl.m0 + m);
-        const float w = a.row_w[r];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int ii = tl.n0 + ncol + j * 16;
-          if (ii >= I) continue;
-          float g[4], u[4], dg[4], du[4], av[4];
-          load4(hc + r * (2 * I) + ii, g[0], g[1], g[2], g[3]);
-          load4(hc + r * (2 * I) + I + ii, u[0], u[1], u[2], u[3]);
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const float sg = sigmoidf_(g[v]);
-            const float silu = g[v] * sg;
-            const float A = silu * u[v];
-            const float dap = acc[i][j][v];
-            dsum[i] += dap * A;
-            const float da = w * dap;
-            dg[v] = da * u[v] * sg * (1.0f + g[v] * (1.0f - sg));
-            du[v] = da * silu;
-            av[v] = w * A;
-          }
-          store4(dh + r * (2 * I) + ii, dg[0], dg[1], dg[2], dg[3]);
-          store4(dh + r * (2 * I) + I + ii, du[0], du[1], du[2], du[3]);
-          store4(ap + r * I + ii, av[0], av[1], av[2], av[3]);
-        }
-      }
-      // row-dot partials: lanes l, l^16, l^32, l^48 hold the same row; then the two
-      // wavefronts of a row block (wn = 0, 1), always in the same order
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        dsum[i] += __shfl_xor(dsum[i], 16);
-        dsum[i] += __shfl_xor(dsum[i], 32);
-      }
-      if (wn == 1 && lane < 16) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s_red[wm * 64 + i * 16 + lane] = dsum[i];
-      }
-      __syncthreads();
-      if (wn == 0 && lane < 16) {
-        const int nTN = (I + BN - 1) / BN;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = mrow + i * 16;
-          if (m < tl.mlen)
-            a.dspart[(size_t)(tl.roff + tl.m0 + m) * nTN + tl.nt] = dsum[i] + s_red[m];
-        }
-      }
-      __syncthreads();
-    } else if constexpr (KIND == DWD) {
-      T* dw = (T*)a.out0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int h = tl.m0 + mrow + i * 16;
-        if (h >= a.H) continue;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int ii = tl.n0 + ncol + j * 16;
-          if (ii >= a.I) continue;
-          store4(dw + ((size_t)tl.e * a.H + h) * a.I + ii, acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-        }
-      }
-    } else {  // DW1
-      T* dwg = (T*)a.out0;
-      T* dwu = (T*)a.out1;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ip = tl.m0 + mrow + i * 16;
-        if (ip >= 2 * a.I) continue;
-        T* base = ip < a.I ? dwg + ((size_t)tl.e * a.I + ip) * a.H : dwu + ((size_t)tl.e * a.I + (ip - a.I)) * a.H;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int h = tl.n0 + ncol + j * 16;
-          if (h >= a.H) continue;
-          store4(base + h, acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-        }
-      }
-    }
+  for (;;) {
+    step(std::integral_constant<int, 0>{}, R0, R1, rtE, rtO);
+    if (!Cc.valid) break;
+    step(std::integral_constant<int, 1>{}, R1, R0, rtO, rtE);
+    if (!Cc.valid) break;
   }
 }
 
@@ -636,7 +910,8 @@ template <typename T, int KIND>
 static hipError_t run(const gg::Args& a, long long max_tiles, hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
   kernel_event(KIND, 0, s);  // gg::Kind values equal the moe_kernel_id of each GEMM
-  hipLaunchKernelGGL((gg::k_grouped_gemm<T, KIND>), dim3(persistent_grid(max_tiles)), dim3(gg::NTHR), 0, s, a);
+  hipLaunchKernelGGL((gg::k_grouped_gemm<T, KIND>), dim3(persistent_grid(max_tiles)), dim3(gg::NTHR), 0, s, a,
+                     a.counts, a.offsets);
   kernel_event(KIND, 1, s);
   return hipGetLastError();
 }
@@ -652,7 +927,7 @@ static hipError_t gemm_fwd_t(const void* x, const void* wg, const void* wu, cons
   gg::Args a{};
   a.x = x; a.wg = wg; a.wu = wu; a.wd = wd;
   a.counts = p.counts; a.offsets = p.offsets; a.row_token = p.row_token; a.row_w = p.row_w;
-  a.E = p.E; a.H = H; a.I = I;
+  a.E = p.E; a.H = H; a.I = I; a.N = p.N; a.M_cap = p.M_cap;
   void* act = ws;
   const long long mt = (long long)(p.M_cap + gg::BM - 1) / gg::BM + p.E;
   a.out0 = hcache; a.out1 = act;
@@ -694,7 +969,7 @@ static hipError_t layer_bwd_t(const void* dout, const void* x, const void* wg, c
   gg::Args a{};
   a.x = x; a.wg = wg; a.wu = wu; a.wd = wd; a.dout = dout; a.hcache = hcache;
   a.counts = p.counts; a.offsets = p.offsets; a.row_token = p.row_token; a.row_w = p.row_w;
-  a.E = p.E; a.H = H; a.I = I;
+  a.E = p.E; a.H = H; a.I = I; a.N = p.N; a.M_cap = p.M_cap;
   const long long mt = (long long)(p.M_cap + gg::BM - 1) / gg::BM + p.E;
   hipError_t err;
 
