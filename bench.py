@@ -56,10 +56,11 @@ def kernel_work(name, wl, M, e_act, es):
 
 
 def load_traffic(name, workload):
-    """HBM traffic per launch measured with rocprofv3 counters (FETCH_SIZE, WRITE_SIZE),
-    committed under profiles/.  Returned only while the kernel sources are unchanged."""
+    """HBM bytes per launch of kernel `name`, from the rocprofv3 FETCH_SIZE / WRITE_SIZE passes
+    summarised in profiles/traffic_<workload>.txt.  Returned only while the kernel's source file
+    still hashes to the value recorded beside the counters; otherwise None."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"traffic_{name}_{workload}.txt")
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -67,14 +68,14 @@ def load_traffic(name, workload):
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    src = os.path.join(ROOT, "grouped_gemm_top_amd", "csrc", kv.get("source", "gemm.hip"))
+    src = os.path.join(ROOT, "grouped_gemm_top_amd", "csrc", kv.get(f"{name}.source", "gemm.hip"))
     if not os.path.exists(src):
         return None
     sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    if kv.get("source_sha") != sha:
+    if kv.get(f"{name}.source_sha") != sha:
         return None
     try:
-        return float(kv["hbm_bytes_per_launch"])
+        return float(kv[f"{name}.hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
 
@@ -102,7 +103,7 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, help="workload number (1-5); 2 is the headline")
-    ap.add_argument("--cpu-tokens", type=int, default=1536,
+    ap.add_argument("--cpu-tokens", type=int, default=4096,
                     help="tokens in the CPU-oracle baseline sample (0 disables it)")
     ap.add_argument("--kernel-events", type=int, default=1, help="record per-kernel HIP events (1/0)")
     ap.add_argument("--mode", choices=("layer", "copy"), default="layer",

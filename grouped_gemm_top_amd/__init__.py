@@ -38,7 +38,9 @@ _LIB = None
 
 
 def lib_path() -> str:
-    return os.path.join(_HERE, "libmoe.so")
+    """The in-tree libmoe.so; MOE_LIBRARY may name another build of the same sources (used
+    only to compare kernel variants side by side)."""
+    return os.environ.get("MOE_LIBRARY") or os.path.join(_HERE, "libmoe.so")
 
 
 class MoEError(RuntimeError):
