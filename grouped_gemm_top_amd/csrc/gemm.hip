@@ -36,14 +36,13 @@
 //    order and across N-tiles by a separate ordered pass.
 #include <type_traits>
 
-#include "common.h"
+#include "gemm_common.h"
 
 namespace moe {
 namespace gg {
 
 constexpr int BM = 128, BN = 128, NTHR = 256;
 
-enum Kind { GATEUP = MOE_K_GATEUP, DOWN = MOE_K_DOWN, DH = MOE_K_DH, DX = MOE_K_DX, DWD = MOE_K_DWD, DW1 = MOE_K_DW1 };
 
 template <int K> struct KindTraits;
 template <> struct KindTraits<GATEUP> { static constexpr bool A_KC = true, B_KC = true, VK = false; };
@@ -78,46 +77,6 @@ __device__ __forceinline__ f32x4 mma(const bf16x8& a, const bf16x8& b, f32x4 c) 
 __device__ __forceinline__ f32x4 mma(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
-
-struct Args {
-  const void* x;      // [N,H] activations (gathered)
-  const void* wg;     // [E,I,H]
-  const void* wu;     // [E,I,H]
-  const void* wd;     // [E,H,I]
-  const void* dout;   // [N,H]
-  const void* hcache; // [M_cap, 2I]
-  const void* act;    // [M_cap, I]   (DOWN: A;  DWD: A')
-  const void* dh;     // [M_cap, 2I]  (DX, DW1)
-  void* out0;         // GATEUP: hcache; DOWN: y; DH: dH; DX: dXe; DWD: dW_down; DW1: dW_gate
-  void* out1;         // GATEUP: act;  DH: A';  DW1: dW_up
-  float* dspart;      // DH: [M_cap, nTN] partial row-dots
-  const int32_t* counts;
-  const int32_t* offsets;
-  const int32_t* row_token;
-  const float* row_w;
-  int E, H, I;
-  int N, M_cap;
-};
-
-// ------------------------------------------------------------------ buffer loads
-// Raw buffer loads: an offset at or beyond the descriptor's byte range returns zeros and
-// touches no memory, so masked rows, K tails and steps past the last tile cost nothing and
-// need no branch.  Every pipeline step therefore issues the same instructions, which keeps
-// the compiler's memory-counter waits static.
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-constexpr uint32_t OOB = 0x80000000u;  // larger than every descriptor range (< 2^31 bytes)
-
-__device__ __forceinline__ rsrc_t mkr(const void* p, long long bytes) {
-  const int n = bytes > 0x7FFFFFFFLL ? 0x7FFFFFFF : (int)bytes;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, n, 0x00020000);
-}
-__device__ __forceinline__ uint4 bld16(rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-__device__ __forceinline__ int bld4(rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-}
-__device__ __forceinline__ int ufl(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // ------------------------------------------------------------------ tile schedule
 // A cursor is a position (tile, k-step) in this workgroup's sequence of tiles.
@@ -934,12 +893,19 @@ static hipError_t gemm_fwd_t(const void* x, const void* wg, const void* wu, cons
   a.counts = p.counts; a.offsets = p.offsets; a.row_token = p.row_token; a.row_w = p.row_w;
   a.E = p.E; a.H = H; a.I = I; a.N = p.N; a.M_cap = p.M_cap;
   void* act = ws;
-  const long long mt = (long long)(p.M_cap + gg::BM - 1) / gg::BM + p.E;
   a.out0 = hcache; a.out1 = act;
-  hipError_t err = run<T, gg::GATEUP>(a, mt * ((I + 63) / 64), s);
-  if (err != hipSuccess) return err;
-  a.act = act; a.out0 = y; a.out1 = nullptr;
-  return run<T, gg::DOWN>(a, mt * ((H + gg::BN - 1) / gg::BN), s);
+  hipError_t err;
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    const long long mt = (long long)(p.M_cap + 255) / 256 + p.E;
+    if ((err = run_gemm_bf16<gg::GATEUP>(a, mt * ((I + 127) / 128), s)) != hipSuccess) return err;
+    a.act = act; a.out0 = y; a.out1 = nullptr;
+    return run_gemm_bf16<gg::DOWN>(a, mt * ((H + 255) / 256), s);
+  } else {
+    const long long mt = (long long)(p.M_cap + gg::BM - 1) / gg::BM + p.E;
+    if ((err = run<T, gg::GATEUP>(a, mt * ((I + 63) / 64), s)) != hipSuccess) return err;
+    a.act = act; a.out0 = y; a.out1 = nullptr;
+    return run<T, gg::DOWN>(a, mt * ((H + gg::BN - 1) / gg::BN), s);
+  }
 }
 
 hipError_t launch_gemm_fwd(moe_dtype dt, const void* x, const void* wg, const void* wu, const void* wd, int H,
@@ -961,7 +927,9 @@ static hipError_t layer_bwd_t(const void* dout, const void* x, const void* wg, c
                               int H, int I, const moe_plan& p, const void* hcache, void* dx, void* dwg,
                               void* dwu, void* dwd, float* ds, void* ws, hipStream_t s) {
   const size_t es = sizeof(T);
-  const int nTN = (I + gg::BN - 1) / gg::BN;
+  constexpr bool BF = std::is_same<T, bf16_t>::value;
+  const int tn = BF ? 256 : gg::BN;  // N-tile width of the dH kernel (one dS partial per N-tile)
+  const int nTN = (I + tn - 1) / tn;
   char* w = (char*)ws;
   void* dh = w;
   w += align256((size_t)p.M_cap * 2 * I * es);
@@ -975,12 +943,23 @@ static hipError_t layer_bwd_t(const void* dout, const void* x, const void* wg, c
   a.x = x; a.wg = wg; a.wu = wu; a.wd = wd; a.dout = dout; a.hcache = hcache;
   a.counts = p.counts; a.offsets = p.offsets; a.row_token = p.row_token; a.row_w = p.row_w;
   a.E = p.E; a.H = H; a.I = I; a.N = p.N; a.M_cap = p.M_cap;
-  const long long mt = (long long)(p.M_cap + gg::BM - 1) / gg::BM + p.E;
+  const int tm = BF ? 256 : gg::BM;
+  const long long mt = (long long)(p.M_cap + tm - 1) / tm + p.E;
+  // the launch of one grouped GEMM: the bf16 kernel or the fp32 one
+  auto launch = [&](auto kind, long long tiles) -> hipError_t {
+    constexpr int K = decltype(kind)::value;
+    if constexpr (BF) return run_gemm_bf16<K>(a, tiles, s);
+    else return run<T, K>(a, tiles, s);
+  };
+  using KDH = std::integral_constant<int, gg::DH>;
+  using KDWD = std::integral_constant<int, gg::DWD>;
+  using KDX = std::integral_constant<int, gg::DX>;
+  using KDW1 = std::integral_constant<int, gg::DW1>;
   hipError_t err;
 
   // dH epilogue kernel: dH = [dG | dU], A' = w A, dS partials
   a.out0 = dh; a.out1 = aprime; a.dspart = dspart;
-  if ((err = run<T, gg::DH>(a, mt * nTN, s)) != hipSuccess) return err;
+  if ((err = launch(KDH{}, mt * nTN)) != hipSuccess) return err;
   if (p.M_cap > 0) {
     kernel_event(MOE_K_DS_REDUCE, 0, s);
     hipLaunchKernelGGL(gg::k_ds_reduce, dim3((p.M_cap + 255) / 256), dim3(256), 0, s, dspart, nTN, p.offsets, p.E,
@@ -990,17 +969,18 @@ static hipError_t layer_bwd_t(const void* dout, const void* x, const void* wg, c
   }
   // dW_down = sum_r dOut[t]^T A'   (varlen-K)
   a.act = aprime; a.out0 = dwd; a.out1 = nullptr;
-  if ((err = run<T, gg::DWD>(a, (long long)p.E * ((H + 127) / 128) * nTN, s)) != hipSuccess) return err;
+  if ((err = launch(KDWD{}, (long long)p.E * ((H + tm - 1) / tm) * nTN)) != hipSuccess) return err;
   // dXe = dH [W_gate; W_up]   (varlen-M), then the unweighted combine to token order
   a.dh = dh; a.out0 = dxe;
-  if ((err = run<T, gg::DX>(a, mt * ((H + gg::BN - 1) / gg::BN), s)) != hipSuccess) return err;
+  if ((err = launch(KDX{}, mt * ((H + tn - 1) / tn))) != hipSuccess) return err;
   kernel_event(MOE_K_DX_COMBINE, 0, s);
   err = launch_combine(sizeof(T) == 2 ? MOE_BF16 : MOE_F32, dxe, H, p, nullptr, dx, s);
   kernel_event(MOE_K_DX_COMBINE, 1, s);
   if (err != hipSuccess) return err;
   // dW_gate, dW_up = sum_r dH^T x[t]   (varlen-K)
   a.out0 = dwg; a.out1 = dwu;
-  return run<T, gg::DW1>(a, (long long)p.E * ((2 * I + 127) / 128) * ((H + 127) / 128), s);
+  const long long mtw = BF ? 2LL * ((I + 255) / 256) : (2LL * I + 127) / 128;
+  return launch(KDW1{}, (long long)p.E * mtw * ((H + tn - 1) / tn));
 }
 
 hipError_t launch_layer_bwd(moe_dtype dt, const void* dout, const void* x, const void* wg, const void* wu,

@@ -1,0 +1,795 @@
+// gemm_bf16.hip -- the bf16 grouped GEMMs of the layer (forward and backward) for gfx950.
+//
+// Pages cited (by title, then section):
+//   [GG] "DeepSeek 계열 MoE 학습 가속: Python expert loop → grouped GEMM",
+//        "무엇이 필요한가 — Variable-M batched matmul" (one launch over ragged expert groups)
+//        and "적용" step (6) (gate, up and down share one set of group sizes)
+//   [SM] "SonicMoE: IO·타일 인식 최적화로 MoE 학습 가속하기": "3 기여 ①" (cache [G|U] only;
+//        dS = <dA', A> without Y), "4 기여 ②" (varlen-M and varlen-K grouped GEMMs),
+//        "4.1 Gather 융합" (the token gather happens inside the operand load, backward
+//        included), "4.2 Epilogue 융합" (SwiGLU, dSwiGLU, dS and A' in the epilogue),
+//        "4.3 MMA ↔ IO 오버랩" (hide the loads and the heavy epilogue behind the MMAs),
+//        "7 한계 & 의의" (no atomic reductions)
+//
+// Design:
+//  * One workgroup of 512 threads (8 wavefronts, 4 along M x 2 along N) per compute unit
+//    owns a 256x256 output tile; each wavefront computes 64x128 with
+//    v_mfma_f32_16x16x32_bf16 (4 x 8 blocks of 16x16).  The grid is persistent: one
+//    workgroup per CU walks its share of the tile list.
+//  * Operands go from HBM straight into LDS with buffer_load ... lds (no VGPR staging).
+//    LDS holds a ring of 4 stages of k = 32 (16 KB per operand and stage); the loads run
+//    three k-steps ahead of the MFMAs, across tile boundaries, so a tile's prologue overlaps
+//    the previous tile's last steps and its epilogue.
+//  * K-contiguous operands are stored as 64-byte rows, chunk c of row r at c ^ ((r >> 2) & 3),
+//    and read as one 16-byte fragment per lane.  K-strided operands (the backward's weights,
+//    both varlen-K operands) are stored in their natural layout, k-rows of 512 bytes with
+//    chunk c at c ^ f(k), and read with ds_read_b64_tr_b16, which transposes 4x16 blocks of
+//    16-bit values across each group of 16 lanes; two such reads make one MFMA fragment.
+//    Both placements spread every read over all LDS banks.
+//  * Gathered rows (x and dOut through row_token) need the token of each row: a small per-
+//    wavefront ring in LDS is filled by 4-byte LDS loads six steps ahead of use.
+//  * Loads never branch: a buffer offset beyond the descriptor range returns zeros, which
+//    masks rows past a group's end, K tails and steps past the last tile.  Every step issues
+//    the same number of loads, so the wait for step s is an immediate vmcnt equal to the
+//    number of memory instructions issued after step s's loads (the later steps' loads plus
+//    the stores of any epilogue in between); a raw s_barrier then publishes the stage.
+//  * Varlen-M tiles are ordered (expert, n-tile, m-tile) so tiles that share a weight slice
+//    run together; varlen-K tiles are ordered heaviest expert first.  Each XCD gets
+//    contiguous runs of the tile list, so neighbouring tiles share its L2.
+//  * No atomics; every reduction has a fixed order, so results are bitwise reproducible.
+#include "gemm_common.h"
+
+namespace moe {
+namespace g4 {
+
+using gg::Args;
+using gg::mkr;
+using gg::OOB;
+using gg::rsrc_t;
+using gg::ufl;
+using gg::GATEUP;
+using gg::DOWN;
+using gg::DH;
+using gg::DX;
+using gg::DWD;
+using gg::DW1;
+
+constexpr int NT = 512;        // threads per workgroup
+constexpr int BM = 256, BN = 256, BK = 32;
+constexpr int NSTG = 4;        // LDS ring depth (stages)
+constexpr int AHEAD = NSTG - 1;
+constexpr int OPB = 16384;     // bytes of one operand per stage
+constexpr int STG = 2 * OPB;   // bytes per stage
+constexpr int TOKB = 256;      // bytes per token slot (64 row indices)
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+
+// A_KC / B_KC: operand is K-contiguous in memory; GA / GB: operand rows are gathered through
+// row_token; VK: the reduction runs over an expert's rows (varlen-K); ST: a lower bound on the
+// memory instructions one epilogue issues (used for the vmcnt immediates).
+template <int K> struct KT;
+template <> struct KT<GATEUP> { static constexpr bool A_KC = true, B_KC = true, VK = false, GA = true, GB = false; static constexpr int ST = 48; };
+template <> struct KT<DOWN> { static constexpr bool A_KC = true, B_KC = true, VK = false, GA = false, GB = false; static constexpr int ST = 32; };
+template <> struct KT<DH> { static constexpr bool A_KC = true, B_KC = false, VK = false, GA = true, GB = false; static constexpr int ST = 96; };
+template <> struct KT<DX> { static constexpr bool A_KC = true, B_KC = false, VK = false, GA = false, GB = false; static constexpr int ST = 32; };
+template <> struct KT<DWD> { static constexpr bool A_KC = false, B_KC = false, VK = true, GA = true, GB = false; static constexpr int ST = 32; };
+template <> struct KT<DW1> { static constexpr bool A_KC = false, B_KC = false, VK = true, GA = false, GB = true; static constexpr int ST = 32; };
+
+// LDS loads.  They are written as inline assembly on purpose: the compiler then does not
+// track them as LDS writes and inserts no vmcnt waits of its own before LDS reads (it cannot
+// tell the ring stages apart and would drain every load in flight).  Completion is ordered
+// explicitly instead: every stage is read only after the vmcnt wait and barrier that follow
+// its loads.  M0 holds the wavefront's LDS destination; lane L writes at M0 + 16 L (4 L for
+// the 4-byte form).
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 dmadesc(const void* p, long long bytes) {
+  const uint64_t a = (uint64_t)p;
+  const int n = bytes > 0x7FFFFFFFLL ? 0x7FFFFFFF : (int)bytes;
+  return i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xFFFFu), n, 0x00020000};
+}
+__device__ __forceinline__ i32x4 dmadesc_off(const void* p, long long off, long long bytes) {
+  return dmadesc(static_cast<const char*>(p) + off, bytes);
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)(p);
+}
+// The descriptor and the LDS address are wavefront-uniform; readfirstlane puts them in SGPRs.
+// The compiler's hazard recognizer does not look inside inline assembly, so the required
+// wait states are spelled out: a vector-memory instruction may read an SGPR only 5 wait
+// states after a VALU instruction (such as readfirstlane) wrote it, and an LDS load needs 1
+// after M0 was written.  s_nop 4 gives 5.
+__device__ __forceinline__ i32x4 sgpr4(const i32x4& r) {
+  return i32x4{ufl(r.x), ufl(r.y), ufl(r.z), ufl(r.w)};
+}
+__device__ __forceinline__ void dma16(const i32x4& r, const char* lds, uint32_t off) {
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(sgpr4(r)),
+               "{m0}"(ufl((int)lds_addr(lds)))
+               : "memory");
+}
+__device__ __forceinline__ void dma4(const i32x4& r, const char* lds, uint32_t off) {
+  asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(off), "s"(sgpr4(r)),
+               "{m0}"(ufl((int)lds_addr(lds)))
+               : "memory");
+}
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// Two fp32 values to two bf16 (v_cvt_pk_bf16_f32: round to nearest even, the same bits as
+// the scalar rounding for every finite value).
+__device__ __forceinline__ uint32_t pk2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+// sigmoid(g) = 1 / (1 + e^-g) with the hardware exponential and reciprocal (about 1 ulp each,
+// far below the bf16 storage precision of every value it feeds)
+__device__ __forceinline__ float sigm(float g) { return __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
+__device__ __forceinline__ void st4(rsrc_t r, uint32_t off, float a, float b, float c, float d) {
+  u32x2 v;
+  v.x = pk2(a, b);
+  v.y = pk2(c, d);
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(const bf16x8& a, const bf16x8& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Wait until at most N vector-memory instructions of this wavefront are outstanding, then
+// meet the other wavefronts.  The memory clobber keeps every LDS access on its side.
+template <int N>
+__device__ __forceinline__ void vm_wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+__device__ __forceinline__ void vm_drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// ------------------------------------------------------------------ tile list
+struct Tile {
+  int valid, it, e, roff, mt, nt, mlen, K, nk, kt;
+};
+
+template <int KIND>
+struct Sched {
+  using T = KT<KIND>;
+  const int* s_sched;  // LDS: varlen-M tile prefix [E+1]; varlen-K expert order [E]
+  int total, G, per, xcd, slot, E, nN, nMg, nM;
+
+  __device__ __forceinline__ void decode(const Args& a, Tile& c, int it) const {
+    c.it = it;
+    c.kt = 0;
+    const long long tl = (long long)it * G + (long long)xcd * per + slot;
+    c.valid = tl < (long long)total;
+    if (!c.valid) {
+      c.e = 0; c.roff = 0; c.mt = 0; c.nt = 0; c.mlen = 0; c.K = 0; c.nk = 0;
+      return;
+    }
+    const int tile = (int)tl;
+    if constexpr (!T::VK) {
+      int lo = 0, hi = E;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_sched[mid] <= tile) lo = mid; else hi = mid;
+      }
+      const int e = ufl(lo);
+      const int cnt = a.counts[e];
+      const int mtiles = (cnt + BM - 1) / BM;
+      const int local = tile - ufl(s_sched[e]);
+      c.e = e;
+      c.roff = a.offsets[e];
+      c.nt = local / mtiles;
+      c.mt = local - c.nt * mtiles;
+      c.mlen = min(BM, cnt - c.mt * BM);
+      switch (KIND) {
+        case GATEUP: case DH: c.K = a.H; break;
+        case DOWN: c.K = a.I; break;
+        default: c.K = 2 * a.I; break;  // DX
+      }
+    } else {
+      const int per_e = nM * nN;
+      const int rank = tile / per_e;
+      const int local = tile - rank * per_e;
+      const int e = ufl(s_sched[rank]);
+      c.e = e;
+      c.roff = a.offsets[e];
+      c.mt = local / nN;
+      c.nt = local - c.mt * nN;
+      if (KIND == DWD) {
+        c.mlen = min(BM, a.H - c.mt * BM);
+      } else {
+        const int seg = c.mt >= nMg;
+        c.mlen = min(BM, a.I - (c.mt - seg * nMg) * BM);
+      }
+      c.K = a.counts[e];
+    }
+    c.nk = (c.K + BK - 1) / BK;
+  }
+  // Step forward; at a tile's end move to the next tile (skipping tiles without k-steps
+  // when skip_empty is set).
+  __device__ __forceinline__ void next(const Args& a, Tile& c, bool skip_empty) const {
+    if (c.valid && c.kt + 1 < c.nk) {
+      ++c.kt;
+      return;
+    }
+    int it = c.it + 1;
+    for (;;) {
+      decode(a, c, it);
+      if (!c.valid || !skip_empty || c.nk > 0) return;
+      ++it;
+    }
+  }
+};
+
+// ------------------------------------------------------------------ operand loads
+// Instruction q (0, 1) of wavefront w fills bytes [(2w+q)*1024, +1024) of an operand's stage
+// area; lane L writes the 16 bytes at offset 16 L of that kilobyte.
+//  K-contiguous: rows (2w+q)*16 + (L >> 2), position L & 3 holds k-chunk (L & 3) ^ ((L >> 4) & 3).
+//  K-strided:    k-row (2w+q)*2 + (L >> 5), position L & 31 holds column chunk (L & 31) ^ f(k).
+__device__ __forceinline__ int mn_f(int k) { return 2 * ((k & 3) | (((k >> 3) & 1) << 2)); }
+// K-contiguous placement: chunk c of 64-byte row r sits at position c ^ kc_swz(r).
+#ifndef MOE_KC_SWZ
+#define MOE_KC_SWZ 2
+#endif
+__device__ __forceinline__ int kc_swz(int r) {
+  if (MOE_KC_SWZ == 1) return (r >> 1) & 3;
+  if (MOE_KC_SWZ == 2) return ((r >> 2) & 3) ^ ((r >> 1) & 2);
+  return (r >> 2) & 3;
+}
+
+template <int KIND>
+struct Loader {
+  using T = KT<KIND>;
+  i32x4 rA0, rA1, rB0, rB1;    // descriptors (the second of each pair: the other segment)
+  uint32_t rowA[2], rowB[2];   // K-contiguous operands: per-lane row byte offset (OOB if masked)
+  uint32_t colA[2], colB[2];   // K-strided operands: per-lane column byte offset (OOB if masked)
+  int kc_c;                    // k-chunk this lane loads (K-contiguous)
+  int mn_k[2], mn_c[2];        // k-row and column chunk this lane loads (K-strided)
+
+  __device__ __forceinline__ void init(int w, int L) {
+    kc_c = (L & 3) ^ kc_swz(L >> 2);  // the row of this lane is (2w+q)*16 + (L >> 2)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      mn_k[q] = (2 * w + q) * 2 + (L >> 5);
+      mn_c[q] = (L & 31) ^ mn_f(mn_k[q]);
+    }
+  }
+
+  // per-tile state; tok points at this wavefront's token slot of the tile's first step
+  __device__ __forceinline__ void setup(const Args& a, const Tile& c, const int* tok, int w, int L, int nMg) {
+    const int H = a.H, I = a.I;
+    const int kr[2] = {(2 * w) * 16 + (L >> 2), (2 * w + 1) * 16 + (L >> 2)};
+    const long long rb = (long long)c.roff + (long long)c.mt * BM;  // first row of an M-tile
+    if constexpr (KIND == GATEUP || KIND == DH) {
+      const void* src = KIND == GATEUP ? a.x : a.dout;
+      rA0 = dmadesc(src, (long long)a.N * H * 2);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int t = tok[(L >> 2) + 16 * q];
+        rowA[q] = (c.valid && kr[q] < c.mlen) ? (uint32_t)t * (uint32_t)H * 2u : OOB;
+      }
+    }
+    if constexpr (KIND == GATEUP) {
+      const long long es = (long long)c.e * I * H * 2;
+      const i32x4 rg = dmadesc_off(a.wg, es, (long long)I * H * 2);
+      const i32x4 ru = dmadesc_off(a.wu, es, (long long)I * H * 2);
+      // rows 64..127 of each 128-row half are up-projection rows
+      rB0 = (((2 * w) & 7) >= 4) ? ru : rg;
+      rB1 = (((2 * w + 1) & 7) >= 4) ? ru : rg;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int n = kr[q];
+        const int i = c.nt * 128 + (n >> 7) * 64 + (n & 63);
+        rowB[q] = c.valid ? (uint32_t)i * (uint32_t)H * 2u : OOB;  // i >= I lies past the range
+      }
+    } else if constexpr (KIND == DOWN) {
+      rA0 = dmadesc_off(a.act, rb * I * 2, (long long)c.mlen * I * 2);
+      rB0 = dmadesc_off(a.wd, (long long)c.e * H * I * 2, (long long)H * I * 2);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        rowA[q] = c.valid ? (uint32_t)kr[q] * (uint32_t)I * 2u : OOB;
+        rowB[q] = c.valid ? (uint32_t)(c.nt * BN + kr[q]) * (uint32_t)I * 2u : OOB;
+      }
+    } else if constexpr (KIND == DH) {
+      rB0 = dmadesc_off(a.wd, (long long)c.e * H * I * 2, (long long)H * I * 2);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int col = c.nt * BN + 8 * mn_c[q];
+        colB[q] = (c.valid && col < I) ? (uint32_t)col * 2u : OOB;
+      }
+    } else if constexpr (KIND == DX) {
+      rA0 = dmadesc_off(a.dh, rb * 2 * I * 2, (long long)c.mlen * 2 * I * 2);
+      const long long es = (long long)c.e * I * H * 2;
+      rB0 = dmadesc_off(a.wg, es, (long long)I * H * 2);
+      rB1 = dmadesc_off(a.wu, es, (long long)I * H * 2);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        rowA[q] = c.valid ? (uint32_t)kr[q] * (uint32_t)(2 * I) * 2u : OOB;
+        const int col = c.nt * BN + 8 * mn_c[q];
+        colB[q] = (c.valid && col < H) ? (uint32_t)col * 2u : OOB;
+      }
+    } else if constexpr (KIND == DWD) {
+      rA0 = dmadesc(a.dout, (long long)a.N * H * 2);
+      rB0 = dmadesc_off(a.act, (long long)c.roff * I * 2, (long long)c.K * I * 2);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int ca = c.mt * BM + 8 * mn_c[q];
+        colA[q] = (c.valid && ca < H) ? (uint32_t)ca * 2u : OOB;
+        const int cb = c.nt * BN + 8 * mn_c[q];
+        colB[q] = (c.valid && cb < I) ? (uint32_t)cb * 2u : OOB;
+      }
+    } else {  // DW1
+      const int seg = c.mt >= nMg;
+      const int m0 = (c.mt - seg * nMg) * BM;
+      rA0 = dmadesc_off(a.dh, (long long)c.roff * 2 * I * 2, (long long)c.K * 2 * I * 2);
+      rB0 = dmadesc(a.x, (long long)a.N * H * 2);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int ma = m0 + 8 * mn_c[q];
+        colA[q] = (c.valid && ma < I) ? (uint32_t)(seg * I + ma) * 2u : OOB;
+        const int cb = c.nt * BN + 8 * mn_c[q];
+        colB[q] = (c.valid && cb < H) ? (uint32_t)cb * 2u : OOB;
+      }
+    }
+  }
+
+  // keep the descriptors in SGPRs: readfirstlane once per tile instead of once per load
+  __device__ __forceinline__ void uniform() {
+    rA0 = sgpr4(rA0);
+    rB0 = sgpr4(rB0);
+    if constexpr (KIND == GATEUP || KIND == DX) rB1 = sgpr4(rB1);
+  }
+
+  // the four operand loads of step c.kt into the stage at `stage`; tok = this step's token
+  // slot (varlen-K gathers)
+  __device__ __forceinline__ void issue(const Args& a, const Tile& c, char* stage, const int* tok, int w, int L) {
+    const int H = a.H, I = a.I;
+    const int k0 = c.kt * BK;
+    char* la = stage + (2 * w) * 1024;
+    char* lb = stage + OPB + (2 * w) * 1024;
+    if constexpr (T::A_KC) {
+      const int kk = k0 + 8 * kc_c;
+      const bool kv = kk < c.K;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) dma16(rA0, la + q * 1024, kv ? rowA[q] + (uint32_t)kk * 2u : OOB);
+      if constexpr (T::B_KC) {
+        dma16(rB0, lb, kv ? rowB[0] + (uint32_t)kk * 2u : OOB);
+        dma16(KIND == GATEUP ? rB1 : rB0, lb + 1024, kv ? rowB[1] + (uint32_t)kk * 2u : OOB);
+      }
+    }
+    if constexpr (KIND == DH) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const uint32_t k = (uint32_t)(k0 + mn_k[q]);
+        dma16(rB0, lb + q * 1024, colB[q] + k * (uint32_t)I * 2u);  // k >= H lies past the range
+      }
+    } else if constexpr (KIND == DX) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int kb = k0 + (2 * w + q) * 2;  // both k-rows of this instruction: same segment
+        const bool up = kb >= I;
+        const uint32_t k = (uint32_t)(k0 + mn_k[q] - (up ? I : 0));
+        dma16(up ? rB1 : rB0, lb + q * 1024, colB[q] + k * (uint32_t)H * 2u);
+      }
+    } else if constexpr (KIND == DWD) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int r = k0 + mn_k[q];
+        const uint32_t t = (uint32_t)tok[2 * q + (L >> 5)];
+        dma16(rA0, la + q * 1024, r < c.K ? t * (uint32_t)H * 2u + colA[q] : OOB);
+        dma16(rB0, lb + q * 1024, colB[q] + (uint32_t)r * (uint32_t)I * 2u);
+      }
+    } else if constexpr (KIND == DW1) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int r = k0 + mn_k[q];
+        const uint32_t t = (uint32_t)tok[2 * q + (L >> 5)];
+        dma16(rA0, la + q * 1024, colA[q] + (uint32_t)r * (uint32_t)(2 * I) * 2u);
+        dma16(rB0, lb + q * 1024, r < c.K ? t * (uint32_t)H * 2u + colB[q] : OOB);
+      }
+    }
+  }
+};
+
+// ------------------------------------------------------------------ epilogues
+// acc[i][j][v] = C[m = wm*64 + 16i + (L & 15)][n = wn*128 + 16j + 4(L >> 4) + v]
+template <int KIND>
+__device__ __forceinline__ void epilogue(const Args& a, const Tile& c, f32x4 (&acc)[4][8], float* s_red, int wm,
+                                         int wn, int L, int nMg, int nTN) {
+  const int H = a.H, I = a.I;
+  const int cl = L & 15, g = L >> 4;
+  const long long rb = (long long)c.roff + (long long)c.mt * BM;
+  if constexpr (KIND == GATEUP) {
+    const rsrc_t rh = gg::mkr_off(a.out0, rb * 2 * I * 2, (long long)c.mlen * 2 * I * 2);
+    const rsrc_t ra = gg::mkr_off(a.out1, rb * I * 2, (long long)c.mlen * I * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t m = (uint32_t)(wm * 64 + 16 * i + cl);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int ii = c.nt * 128 + wn * 64 + 16 * j + 4 * g;
+        const bool iv = ii < I;
+        const f32x4 G = acc[i][j], U = acc[i][j + 4];
+        float av[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) av[v] = G[v] * sigm(G[v]) * U[v];
+        const uint32_t hrow = m * (uint32_t)(2 * I) * 2u;
+        st4(rh, iv ? hrow + (uint32_t)ii * 2u : OOB, G[0], G[1], G[2], G[3]);
+        st4(rh, iv ? hrow + (uint32_t)(I + ii) * 2u : OOB, U[0], U[1], U[2], U[3]);
+        st4(ra, iv ? m * (uint32_t)I * 2u + (uint32_t)ii * 2u : OOB, av[0], av[1], av[2], av[3]);
+      }
+    }
+  } else if constexpr (KIND == DOWN || KIND == DX) {
+    const rsrc_t ro = gg::mkr_off(a.out0, rb * H * 2, (long long)c.mlen * H * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t m = (uint32_t)(wm * 64 + 16 * i + cl);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int n = c.nt * BN + wn * 128 + 16 * j + 4 * g;
+        st4(ro, n < H ? m * (uint32_t)H * 2u + (uint32_t)n * 2u : OOB, acc[i][j][0], acc[i][j][1], acc[i][j][2],
+            acc[i][j][3]);
+      }
+    }
+  } else if constexpr (KIND == DH) {
+    const rsrc_t rhc = gg::mkr_off(a.hcache, rb * 2 * I * 2, (long long)c.mlen * 2 * I * 2);
+    const rsrc_t rdh = gg::mkr_off(a.out0, rb * 2 * I * 2, (long long)c.mlen * 2 * I * 2);
+    const rsrc_t rap = gg::mkr_off(a.out1, rb * I * 2, (long long)c.mlen * I * 2);
+    const rsrc_t rw = gg::mkr_off(a.row_w, rb * 4, (long long)c.mlen * 4);
+    float dsum[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t m = (uint32_t)(wm * 64 + 16 * i + cl);
+      const float wr = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rw, m * 4u, 0, 0));
+      const uint32_t hrow = m * (uint32_t)(2 * I) * 2u;
+      // G and U stay packed (two bf16 per register) until they are used
+      u32x2 Gp[8], Up[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int ii = c.nt * BN + wn * 128 + 16 * j + 4 * g;
+        const bool iv = ii < I;
+        Gp[j] = __builtin_amdgcn_raw_buffer_load_b64(rhc, iv ? hrow + (uint32_t)ii * 2u : OOB, 0, 0);
+        Up[j] = __builtin_amdgcn_raw_buffer_load_b64(rhc, iv ? hrow + (uint32_t)(I + ii) * 2u : OOB, 0, 0);
+      }
+      float ds = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int ii = c.nt * BN + wn * 128 + 16 * j + 4 * g;
+        const bool iv = ii < I;
+        float dg[4], du[4], ap[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const uint32_t gw = Gp[j][v >> 1], uw = Up[j][v >> 1];
+          const float gg_ = __uint_as_float((v & 1) ? (gw & 0xFFFF0000u) : (gw << 16));
+          const float u = __uint_as_float((v & 1) ? (uw & 0xFFFF0000u) : (uw << 16));
+          const float sg = sigm(gg_);
+          const float silu = gg_ * sg;
+          const float act = silu * u;
+          const float dap = acc[i][j][v];
+          ds += dap * act;
+          const float da = wr * dap;
+          dg[v] = da * u * sg * (1.0f + gg_ * (1.0f - sg));
+          du[v] = da * silu;
+          ap[v] = wr * act;
+        }
+        st4(rdh, iv ? hrow + (uint32_t)ii * 2u : OOB, dg[0], dg[1], dg[2], dg[3]);
+        st4(rdh, iv ? hrow + (uint32_t)(I + ii) * 2u : OOB, du[0], du[1], du[2], du[3]);
+        st4(rap, iv ? m * (uint32_t)I * 2u + (uint32_t)ii * 2u : OOB, ap[0], ap[1], ap[2], ap[3]);
+      }
+      ds += __shfl_xor(ds, 16);
+      ds += __shfl_xor(ds, 32);
+      dsum[i] = ds;
+    }
+    // the two wavefronts of a row block hold the two column halves: wn 0 adds wn 1's half
+    if (wn == 1 && L < 16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_red[wm * 64 + 16 * i + L] = dsum[i];
+    }
+    lds_barrier();
+    if (wn == 0 && L < 16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = wm * 64 + 16 * i + L;
+        if (m < c.mlen) a.dspart[(size_t)(rb + m) * nTN + c.nt] = dsum[i] + s_red[m];
+      }
+    }
+  } else if constexpr (KIND == DWD) {
+    const rsrc_t ro = gg::mkr_off(a.out0, (long long)c.e * H * I * 2, (long long)H * I * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = c.mt * BM + wm * 64 + 16 * i + cl;  // h
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int n = c.nt * BN + wn * 128 + 16 * j + 4 * g;  // i
+        st4(ro, (m < H && n < I) ? (uint32_t)m * (uint32_t)I * 2u + (uint32_t)n * 2u : OOB, acc[i][j][0],
+            acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+      }
+    }
+  } else {  // DW1
+    const int seg = c.mt >= nMg;
+    const int m0 = (c.mt - seg * nMg) * BM;
+    const rsrc_t ro = gg::mkr_off(seg ? a.out1 : a.out0, (long long)c.e * I * H * 2, (long long)I * H * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + wm * 64 + 16 * i + cl;  // i of dW_gate / dW_up
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int n = c.nt * BN + wn * 128 + 16 * j + 4 * g;  // h
+        st4(ro, (m < I && n < H) ? (uint32_t)m * (uint32_t)H * 2u + (uint32_t)n * 2u : OOB, acc[i][j][0],
+            acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ fragments
+// K-contiguous fragment of rows r0 .. r0+15: lane reads row r0 + (L & 15), k-chunk L >> 4.
+__device__ __forceinline__ bf16x8 frag_kc(const char* op, int r0, int kc_off) {
+  return *reinterpret_cast<const bf16x8*>(op + r0 * 64 + kc_off);
+}
+// K-strided fragment of columns x0 .. x0+15 (x0 a multiple of 16): two transposing reads of
+// k-rows 8(L>>4) + 0..3 and + 4..7.
+__device__ __forceinline__ bf16x8 frag_mn(const char* op, int x0, int mn_k0, int mn_f_, int mn_b) {
+  const int pos = ((((x0 >> 3) ^ mn_f_) | mn_b) << 4);
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(op + mn_k0 + pos));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(op + mn_k0 + 4 * 512 + pos));
+  struct P { s16x4 a, b; } p{lo, hi};
+  return __builtin_bit_cast(bf16x8, p);
+}
+
+// ------------------------------------------------------------------ the kernel
+template <int KIND>
+__global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __restrict__ counts,
+                                                   const int32_t* __restrict__ offsets) {
+  a.counts = counts;
+  a.offsets = offsets;
+  using T = KT<KIND>;
+  constexpr bool GATHER = T::GA || T::GB;
+  constexpr int NLW = 4 + (GATHER ? 1 : 0);  // memory instructions per step and wavefront
+
+  __shared__ __attribute__((aligned(1024))) char s_ring[NSTG * STG];
+  __shared__ __attribute__((aligned(256))) int s_tok[8 * NSTG * (TOKB / 4)];
+  __shared__ int s_sched[1025];
+  __shared__ int s_wsum[9];
+  __shared__ float s_red[BM];
+
+  const int tid = threadIdx.x, L = tid & 63;
+  const int w = ufl(tid >> 6);
+  const int wm = w & 3, wn = w >> 2;
+  const int E = a.E;
+
+  Sched<KIND> S;
+  S.s_sched = s_sched;
+  S.E = E;
+  S.G = gridDim.x;
+  S.per = S.G >> 3;
+  S.xcd = blockIdx.x & 7;
+  S.slot = blockIdx.x >> 3;
+  switch (KIND) {
+    case GATEUP: S.nN = (a.I + 127) / 128; break;
+    case DOWN: case DX: case DW1: S.nN = (a.H + BN - 1) / BN; break;
+    default: S.nN = (a.I + BN - 1) / BN; break;  // DH, DWD
+  }
+  S.nMg = (a.I + BM - 1) / BM;
+  S.nM = KIND == DWD ? (a.H + BM - 1) / BM : 2 * S.nMg;
+  const int nTN = (a.I + BN - 1) / BN;
+
+  // ---- tile list from the device-resident counts ----
+  if constexpr (!T::VK) {
+    int loc[2], sum = 0;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int e = tid * 2 + q;
+      loc[q] = e < E ? ((a.counts[e] + BM - 1) / BM) * S.nN : 0;
+      sum += loc[q];
+    }
+    int x = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off);
+      if (L >= off) x += y;
+    }
+    if (L == 63) s_wsum[w] = x;
+    __syncthreads();
+    if (tid == 0) {
+      int run = 0;
+      for (int q = 0; q < 8; ++q) {
+        const int v = s_wsum[q];
+        s_wsum[q] = run;
+        run += v;
+      }
+      s_wsum[8] = run;
+    }
+    __syncthreads();
+    int run = s_wsum[w] + x - sum;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int e = tid * 2 + q;
+      if (e < E) s_sched[e] = run;
+      run += loc[q];
+    }
+    if (tid == 0) s_sched[E] = s_wsum[8];
+    S.total = ufl(s_wsum[8]);
+    __syncthreads();
+  } else {
+    // heaviest expert first: rank_e = #{f : c_f > c_e or (c_f == c_e and f < e)}
+    int* s_cnt = reinterpret_cast<int*>(s_ring);  // the ring is free until the first load
+    for (int e = tid; e < E; e += NT) s_cnt[e] = a.counts[e];
+    __syncthreads();
+    for (int e = tid; e < E; e += NT) {
+      const int ce = s_cnt[e];
+      int rank = 0;
+      for (int f = 0; f < E; ++f) {
+        const int cf = s_cnt[f];
+        rank += (cf > ce) || (cf == ce && f < e);
+      }
+      s_sched[rank] = e;
+    }
+    __syncthreads();
+    S.total = E * S.nM * S.nN;
+  }
+
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // ---- compute cursor; tiles without k-steps (empty experts, varlen-K) only write zeros ----
+  Tile Cc;
+  S.decode(a, Cc, 0);
+  if constexpr (T::VK) {
+    while (Cc.valid && Cc.nk == 0) {
+      epilogue<KIND>(a, Cc, acc, s_red, wm, wn, L, S.nMg, nTN);
+      S.decode(a, Cc, Cc.it + 1);
+    }
+  }
+  if (!Cc.valid) return;
+
+  // per-lane fragment addressing
+  const int kc_off = (L & 15) * 64 + ((((L >> 4) ^ kc_swz(L & 15)) & 3) << 4);
+  const int mn_m = L & 15, mn_g = L >> 4;
+  const int mn_k0 = (8 * mn_g + (mn_m >> 2)) * 512 + 8 * (mn_m & 1);
+  const int mn_ff = 2 * ((mn_m >> 2) | ((mn_g & 1) << 2));
+  const int mn_b = (mn_m >> 1) & 1;
+
+  Loader<KIND> ld;
+  ld.init(w, L);
+  const i32x4 rtok = dmadesc(a.row_token, 4LL * (long long)a.M_cap);
+  int* my_tok = s_tok + w * NSTG * (TOKB / 4);  // this wavefront's token ring
+
+  // token load for cursor t (its step index s): per tile (varlen-M) or per step (varlen-K)
+  auto tok_issue = [&](const Tile& t, int s) __attribute__((always_inline)) {
+    uint32_t off = OOB;
+    if constexpr (T::VK) {
+      if (t.valid) off = (uint32_t)(t.roff + t.kt * BK + 4 * w + L) * 4u;
+    } else {
+      if (t.valid && t.kt == 0) off = (uint32_t)(t.roff + t.mt * BM + 32 * w + L) * 4u;
+    }
+    dma4(rtok, reinterpret_cast<char*>(my_tok + (s & (NSTG - 1)) * (TOKB / 4)), off);
+  };
+  Tile Ld = Cc, Tk = Cc;
+  auto load_issue = [&](int s) __attribute__((always_inline)) {
+    const int* tk = my_tok + (s & (NSTG - 1)) * (TOKB / 4);
+    if (Ld.kt == 0) {
+      ld.setup(a, Ld, tk, w, L, S.nMg);
+      ld.uniform();
+    }
+    ld.issue(a, Ld, s_ring + (s & (NSTG - 1)) * STG, tk, w, L);
+    S.next(a, Ld, true);
+  };
+
+  // ---- prologue: tokens of steps 0..2 resident, loads of steps 0..2 in flight ----
+  if constexpr (GATHER) {
+#pragma unroll 1
+    for (int s = 0; s < AHEAD; ++s) {
+      tok_issue(Tk, s);
+      S.next(a, Tk, true);
+    }
+    vm_drain();
+  }
+#pragma unroll 1
+  for (int s = 0; s < AHEAD; ++s) {
+    if constexpr (GATHER) {
+      tok_issue(Tk, s + AHEAD);
+      S.next(a, Tk, true);
+    }
+    load_issue(s);
+  }
+
+  // epilogues issued after the loads of the last three steps (their stores are younger)
+  int h0 = 0, h1 = 0, h2 = 0;
+  constexpr int X0 = 2 * NLW;
+  constexpr int X1 = (X0 + T::ST) < 63 ? (X0 + T::ST) : 63;
+  constexpr int X2 = (X0 + 2 * T::ST) < 63 ? (X0 + 2 * T::ST) : 63;
+  constexpr int X3 = (X0 + 3 * T::ST) < 63 ? (X0 + 3 * T::ST) : 63;
+
+#pragma unroll 1
+  for (int s = 0;; ++s) {
+    // step s's loads (issued three steps ago) have landed for every wavefront, and every
+    // wavefront is done with the stage that the loads below overwrite
+    const int ne = h0 + h1 + h2;
+    if (ne == 0) vm_wait_barrier<X0>();
+    else if (ne == 1) vm_wait_barrier<X1>();
+    else if (ne == 2) vm_wait_barrier<X2>();
+    else vm_wait_barrier<X3>();
+    h2 = h1;
+    h1 = h0;
+    h0 = 0;
+
+    if constexpr (GATHER) {
+      tok_issue(Tk, s + 2 * AHEAD);
+      S.next(a, Tk, true);
+    }
+    load_issue(s + AHEAD);
+
+    // ---- MFMAs of step s ----
+    if (Cc.mlen > wm * 64) {
+      const char* sa = s_ring + (s & (NSTG - 1)) * STG;
+      const char* sb = sa + OPB;
+      bf16x8 fa[4], fb[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if constexpr (T::B_KC) fb[j] = frag_kc(sb, wn * 128 + 16 * j, kc_off);
+        else fb[j] = frag_mn(sb, wn * 128 + 16 * j, mn_k0, mn_ff, mn_b);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (T::A_KC) fa[i] = frag_kc(sa, wm * 64 + 16 * i, kc_off);
+        else fa[i] = frag_mn(sa, wm * 64 + 16 * i, mn_k0, mn_ff, mn_b);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = mma(fb[j], fa[i], acc[i][j]);
+    }
+
+    // ---- advance the compute cursor; finish a tile after its last step ----
+    if (Cc.kt + 1 < Cc.nk) {
+      ++Cc.kt;
+    } else {
+      epilogue<KIND>(a, Cc, acc, s_red, wm, wn, L, S.nMg, nTN);
+      ++h0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      S.decode(a, Cc, Cc.it + 1);
+      if constexpr (T::VK) {
+        while (Cc.valid && Cc.nk == 0) {
+          epilogue<KIND>(a, Cc, acc, s_red, wm, wn, L, S.nMg, nTN);
+          ++h0;
+          S.decode(a, Cc, Cc.it + 1);
+        }
+      }
+      if (!Cc.valid) break;
+    }
+  }
+  // loads past the last tile (all masked) must land before the workgroup's LDS is released
+  vm_drain();
+}
+
+}  // namespace g4
+
+// ------------------------------------------------------------------ host side
+template <int KIND>
+hipError_t run_gemm_bf16(const gg::Args& a, long long max_tiles, hipStream_t s) {
+  if (max_tiles <= 0) return hipSuccess;
+  const DevInfo d = dev_info();
+  long long g = d.cus;
+  if (max_tiles < g) g = max_tiles;
+  g = (g + 7) / 8 * 8;
+  kernel_event(KIND, 0, s);
+  hipLaunchKernelGGL((g4::k_gg_bf16<KIND>), dim3((unsigned)g), dim3(g4::NT), 0, s, a, a.counts, a.offsets);
+  kernel_event(KIND, 1, s);
+  return hipGetLastError();
+}
+
+template hipError_t run_gemm_bf16<gg::GATEUP>(const gg::Args&, long long, hipStream_t);
+template hipError_t run_gemm_bf16<gg::DOWN>(const gg::Args&, long long, hipStream_t);
+template hipError_t run_gemm_bf16<gg::DH>(const gg::Args&, long long, hipStream_t);
+template hipError_t run_gemm_bf16<gg::DX>(const gg::Args&, long long, hipStream_t);
+template hipError_t run_gemm_bf16<gg::DWD>(const gg::Args&, long long, hipStream_t);
+template hipError_t run_gemm_bf16<gg::DW1>(const gg::Args&, long long, hipStream_t);
+
+}  // namespace moe
