@@ -105,14 +105,17 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 __device__ __forceinline__ i32x4 sgpr4(const i32x4& r) {
   return i32x4{ufl(r.x), ufl(r.y), ufl(r.z), ufl(r.w)};
 }
-__device__ __forceinline__ void dma16(const i32x4& r, const char* lds, uint32_t off) {
-  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(sgpr4(r)),
-               "{m0}"(ufl((int)lds_addr(lds)))
+// m0: LDS byte address of the wavefront's destination; voff: per-lane byte offset; soff: a
+// wavefront-uniform byte offset added to every lane's address.  Every use below keeps each
+// valid lane's voff + soff inside its tensor, and gives masked lanes a voff at or beyond the
+// descriptor range, so both operands of a masked access fail the range check.
+__device__ __forceinline__ void dma16(const i32x4& r, uint32_t m0, uint32_t voff, uint32_t soff) {
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(sgpr4(r)),
+               "s"(ufl((int)soff)), "{m0}"(ufl((int)m0))
                : "memory");
 }
-__device__ __forceinline__ void dma4(const i32x4& r, const char* lds, uint32_t off) {
-  asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(off), "s"(sgpr4(r)),
-               "{m0}"(ufl((int)lds_addr(lds)))
+__device__ __forceinline__ void dma4(const i32x4& r, uint32_t m0, uint32_t voff) {
+  asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(sgpr4(r)), "{m0}"(ufl((int)m0))
                : "memory");
 }
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -239,11 +242,12 @@ __device__ __forceinline__ int kc_swz(int r) {
 template <int KIND>
 struct Loader {
   using T = KT<KIND>;
-  i32x4 rA0, rA1, rB0, rB1;    // descriptors (the second of each pair: the other segment)
-  uint32_t rowA[2], rowB[2];   // K-contiguous operands: per-lane row byte offset (OOB if masked)
-  uint32_t colA[2], colB[2];   // K-strided operands: per-lane column byte offset (OOB if masked)
-  int kc_c;                    // k-chunk this lane loads (K-contiguous)
-  int mn_k[2], mn_c[2];        // k-row and column chunk this lane loads (K-strided)
+  i32x4 rA, rB, rB2;          // descriptors; rB2: the up-projection half (GATEUP rows, DX k-rows)
+  uint32_t vA[2], vB[2];      // this lane's byte offsets at k = 0 (OOB when masked)
+  uint32_t rowA[2], rowB[2];  // K-contiguous: row byte offsets (OOB when masked)
+  uint32_t colA[2], colB[2];  // K-strided: column byte offsets (OOB when masked)
+  int kc_c;                   // k-chunk this lane loads (K-contiguous)
+  int mn_k[2], mn_c[2];       // k-row and column chunk this lane loads (K-strided)
 
   __device__ __forceinline__ void init(int w, int L) {
     kc_c = (L & 3) ^ kc_swz(L >> 2);  // the row of this lane is (2w+q)*16 + (L >> 2)
@@ -254,14 +258,13 @@ struct Loader {
     }
   }
 
-  // per-tile state; tok points at this wavefront's token slot of the tile's first step
+  // per-tile state; tok = this wavefront's token slot of the tile's first step
   __device__ __forceinline__ void setup(const Args& a, const Tile& c, const int* tok, int w, int L, int nMg) {
     const int H = a.H, I = a.I;
     const int kr[2] = {(2 * w) * 16 + (L >> 2), (2 * w + 1) * 16 + (L >> 2)};
     const long long rb = (long long)c.roff + (long long)c.mt * BM;  // first row of an M-tile
     if constexpr (KIND == GATEUP || KIND == DH) {
-      const void* src = KIND == GATEUP ? a.x : a.dout;
-      rA0 = dmadesc(src, (long long)a.N * H * 2);
+      rA = dmadesc(KIND == GATEUP ? a.x : a.dout, (long long)a.N * H * 2);
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const int t = tok[(L >> 2) + 16 * q];
@@ -273,8 +276,8 @@ struct Loader {
       const i32x4 rg = dmadesc_off(a.wg, es, (long long)I * H * 2);
       const i32x4 ru = dmadesc_off(a.wu, es, (long long)I * H * 2);
       // rows 64..127 of each 128-row half are up-projection rows
-      rB0 = (((2 * w) & 7) >= 4) ? ru : rg;
-      rB1 = (((2 * w + 1) & 7) >= 4) ? ru : rg;
+      rB = (((2 * w) & 7) >= 4) ? ru : rg;
+      rB2 = (((2 * w + 1) & 7) >= 4) ? ru : rg;
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const int n = kr[q];
@@ -282,34 +285,35 @@ struct Loader {
         rowB[q] = c.valid ? (uint32_t)i * (uint32_t)H * 2u : OOB;  // i >= I lies past the range
       }
     } else if constexpr (KIND == DOWN) {
-      rA0 = dmadesc_off(a.act, rb * I * 2, (long long)c.mlen * I * 2);
-      rB0 = dmadesc_off(a.wd, (long long)c.e * H * I * 2, (long long)H * I * 2);
+      rA = dmadesc_off(a.act, rb * I * 2, (long long)c.mlen * I * 2);
+      rB = dmadesc_off(a.wd, (long long)c.e * H * I * 2, (long long)H * I * 2);
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        rowA[q] = c.valid ? (uint32_t)kr[q] * (uint32_t)I * 2u : OOB;
-        rowB[q] = c.valid ? (uint32_t)(c.nt * BN + kr[q]) * (uint32_t)I * 2u : OOB;
+        rowA[q] = (c.valid && kr[q] < c.mlen) ? (uint32_t)kr[q] * (uint32_t)I * 2u : OOB;
+        const int n = c.nt * BN + kr[q];
+        rowB[q] = (c.valid && n < H) ? (uint32_t)n * (uint32_t)I * 2u : OOB;
       }
     } else if constexpr (KIND == DH) {
-      rB0 = dmadesc_off(a.wd, (long long)c.e * H * I * 2, (long long)H * I * 2);
+      rB = dmadesc_off(a.wd, (long long)c.e * H * I * 2, (long long)H * I * 2);
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const int col = c.nt * BN + 8 * mn_c[q];
         colB[q] = (c.valid && col < I) ? (uint32_t)col * 2u : OOB;
       }
     } else if constexpr (KIND == DX) {
-      rA0 = dmadesc_off(a.dh, rb * 2 * I * 2, (long long)c.mlen * 2 * I * 2);
+      rA = dmadesc_off(a.dh, rb * 2 * I * 2, (long long)c.mlen * 2 * I * 2);
       const long long es = (long long)c.e * I * H * 2;
-      rB0 = dmadesc_off(a.wg, es, (long long)I * H * 2);
-      rB1 = dmadesc_off(a.wu, es, (long long)I * H * 2);
+      rB = dmadesc_off(a.wg, es, (long long)I * H * 2);
+      rB2 = dmadesc_off(a.wu, es, (long long)I * H * 2);
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        rowA[q] = c.valid ? (uint32_t)kr[q] * (uint32_t)(2 * I) * 2u : OOB;
+        rowA[q] = (c.valid && kr[q] < c.mlen) ? (uint32_t)kr[q] * (uint32_t)(2 * I) * 2u : OOB;
         const int col = c.nt * BN + 8 * mn_c[q];
         colB[q] = (c.valid && col < H) ? (uint32_t)col * 2u : OOB;
       }
     } else if constexpr (KIND == DWD) {
-      rA0 = dmadesc(a.dout, (long long)a.N * H * 2);
-      rB0 = dmadesc_off(a.act, (long long)c.roff * I * 2, (long long)c.K * I * 2);
+      rA = dmadesc(a.dout, (long long)a.N * H * 2);
+      rB = dmadesc_off(a.act, (long long)c.roff * I * 2, (long long)c.K * I * 2);
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const int ca = c.mt * BM + 8 * mn_c[q];
@@ -320,8 +324,8 @@ struct Loader {
     } else {  // DW1
       const int seg = c.mt >= nMg;
       const int m0 = (c.mt - seg * nMg) * BM;
-      rA0 = dmadesc_off(a.dh, (long long)c.roff * 2 * I * 2, (long long)c.K * 2 * I * 2);
-      rB0 = dmadesc(a.x, (long long)a.N * H * 2);
+      rA = dmadesc_off(a.dh, (long long)c.roff * 2 * I * 2, (long long)c.K * 2 * I * 2);
+      rB = dmadesc(a.x, (long long)a.N * H * 2);
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const int ma = m0 + 8 * mn_c[q];
@@ -330,61 +334,113 @@ struct Loader {
         colB[q] = (c.valid && cb < H) ? (uint32_t)cb * 2u : OOB;
       }
     }
+    // offsets at k = 0 for the steps without a K tail (OOB stays OOB: no 32-bit wrap)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      if constexpr (T::A_KC) vA[q] = rowA[q] + 16u * (uint32_t)kc_c;
+      if constexpr (T::B_KC) vB[q] = rowB[q] + 16u * (uint32_t)kc_c;
+      if constexpr (KIND == DH) vB[q] = colB[q] + (uint32_t)mn_k[q] * (uint32_t)I * 2u;
+      if constexpr (KIND == DX) vB[q] = colB[q] + (uint32_t)mn_k[q] * (uint32_t)H * 2u;
+      if constexpr (KIND == DWD) vB[q] = colB[q] + (uint32_t)mn_k[q] * (uint32_t)I * 2u;
+      if constexpr (KIND == DW1) vA[q] = colA[q] + (uint32_t)mn_k[q] * (uint32_t)(2 * I) * 2u;
+    }
+    rA = sgpr4(rA);
+    rB = sgpr4(rB);
+    if constexpr (KIND == GATEUP || KIND == DX) rB2 = sgpr4(rB2);
   }
 
-  // keep the descriptors in SGPRs: readfirstlane once per tile instead of once per load
-  __device__ __forceinline__ void uniform() {
-    rA0 = sgpr4(rA0);
-    rB0 = sgpr4(rB0);
-    if constexpr (KIND == GATEUP || KIND == DX) rB1 = sgpr4(rB1);
-  }
-
-  // the four operand loads of step c.kt into the stage at `stage`; tok = this step's token
-  // slot (varlen-K gathers)
-  __device__ __forceinline__ void issue(const Args& a, const Tile& c, char* stage, const int* tok, int w, int L) {
+  // The four operand loads of step c.kt.  mA: LDS address of this wavefront's A kilobyte in
+  // the step's stage (B: + OPB).  tok: the step's token slot (varlen-K gathers).
+  // A step without a K tail adds the k advance as the uniform offset; the last step of a tile
+  // whose K is not a multiple of 32 builds every lane's offset and masks k >= K.
+  __device__ __forceinline__ void issue(const Args& a, const Tile& c, uint32_t mA, const int* tok, int w, int L) {
     const int H = a.H, I = a.I;
     const int k0 = c.kt * BK;
-    char* la = stage + (2 * w) * 1024;
-    char* lb = stage + OPB + (2 * w) * 1024;
+    const uint32_t mB = mA + OPB;
+    // the uniform advance is only used where it is non-negative and keeps every lane inside
+    // its row: no K tail, and (dX) no stage that straddles the gate / up boundary at k = I
+    bool fast = k0 + BK <= c.K;
+    if constexpr (KIND == DX) fast = fast && (k0 + BK <= I || k0 >= I);
+    if (fast) {
+      if constexpr (T::A_KC) {
+        const uint32_t so = (uint32_t)k0 * 2u;
+        dma16(rA, mA, vA[0], so);
+        dma16(rA, mA + 1024, vA[1], so);
+        if constexpr (T::B_KC) {
+          dma16(rB, mB, vB[0], so);
+          dma16(KIND == GATEUP ? rB2 : rB, mB + 1024, vB[1], so);
+        }
+      }
+      if constexpr (KIND == DH) {
+        const uint32_t so = (uint32_t)k0 * (uint32_t)I * 2u;
+        dma16(rB, mB, vB[0], so);
+        dma16(rB, mB + 1024, vB[1], so);
+      } else if constexpr (KIND == DX) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int kb = k0 + (2 * w + q) * 2;  // both k-rows of this instruction: same half
+          const bool up = kb >= I;
+          dma16(up ? rB2 : rB, mB + q * 1024, vB[q], (uint32_t)(k0 - (up ? I : 0)) * (uint32_t)H * 2u);
+        }
+      } else if constexpr (KIND == DWD) {
+        const uint32_t so = (uint32_t)k0 * (uint32_t)I * 2u;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const uint32_t t = (uint32_t)tok[2 * q + (L >> 5)];
+          dma16(rA, mA + q * 1024, t * (uint32_t)H * 2u + colA[q], 0u);
+          dma16(rB, mB + q * 1024, vB[q], so);
+        }
+      } else if constexpr (KIND == DW1) {
+        const uint32_t so = (uint32_t)k0 * (uint32_t)(2 * I) * 2u;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const uint32_t t = (uint32_t)tok[2 * q + (L >> 5)];
+          dma16(rA, mA + q * 1024, vA[q], so);
+          dma16(rB, mB + q * 1024, t * (uint32_t)H * 2u + colB[q], 0u);
+        }
+      }
+      return;
+    }
+    // K tail (or a dX stage across k = I): full per-lane offsets, k >= K masked
     if constexpr (T::A_KC) {
       const int kk = k0 + 8 * kc_c;
       const bool kv = kk < c.K;
 #pragma unroll
-      for (int q = 0; q < 2; ++q) dma16(rA0, la + q * 1024, kv ? rowA[q] + (uint32_t)kk * 2u : OOB);
+      for (int q = 0; q < 2; ++q) dma16(rA, mA + q * 1024, kv ? rowA[q] + (uint32_t)kk * 2u : OOB, 0u);
       if constexpr (T::B_KC) {
-        dma16(rB0, lb, kv ? rowB[0] + (uint32_t)kk * 2u : OOB);
-        dma16(KIND == GATEUP ? rB1 : rB0, lb + 1024, kv ? rowB[1] + (uint32_t)kk * 2u : OOB);
+        dma16(rB, mB, kv ? rowB[0] + (uint32_t)kk * 2u : OOB, 0u);
+        dma16(KIND == GATEUP ? rB2 : rB, mB + 1024, kv ? rowB[1] + (uint32_t)kk * 2u : OOB, 0u);
       }
     }
     if constexpr (KIND == DH) {
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const uint32_t k = (uint32_t)(k0 + mn_k[q]);
-        dma16(rB0, lb + q * 1024, colB[q] + k * (uint32_t)I * 2u);  // k >= H lies past the range
+        dma16(rB, mB + q * 1024, colB[q] + k * (uint32_t)I * 2u, 0u);  // k >= H lies past the range
       }
     } else if constexpr (KIND == DX) {
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        const int kb = k0 + (2 * w + q) * 2;  // both k-rows of this instruction: same segment
+        const int kb = k0 + (2 * w + q) * 2;
         const bool up = kb >= I;
         const uint32_t k = (uint32_t)(k0 + mn_k[q] - (up ? I : 0));
-        dma16(up ? rB1 : rB0, lb + q * 1024, colB[q] + k * (uint32_t)H * 2u);
+        dma16(up ? rB2 : rB, mB + q * 1024, colB[q] + k * (uint32_t)H * 2u, 0u);  // k >= 2I: past the range
       }
     } else if constexpr (KIND == DWD) {
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const int r = k0 + mn_k[q];
         const uint32_t t = (uint32_t)tok[2 * q + (L >> 5)];
-        dma16(rA0, la + q * 1024, r < c.K ? t * (uint32_t)H * 2u + colA[q] : OOB);
-        dma16(rB0, lb + q * 1024, colB[q] + (uint32_t)r * (uint32_t)I * 2u);
+        dma16(rA, mA + q * 1024, r < c.K ? t * (uint32_t)H * 2u + colA[q] : OOB, 0u);
+        dma16(rB, mB + q * 1024, colB[q] + (uint32_t)r * (uint32_t)I * 2u, 0u);
       }
     } else if constexpr (KIND == DW1) {
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const int r = k0 + mn_k[q];
         const uint32_t t = (uint32_t)tok[2 * q + (L >> 5)];
-        dma16(rA0, la + q * 1024, colA[q] + (uint32_t)r * (uint32_t)(2 * I) * 2u);
-        dma16(rB0, lb + q * 1024, r < c.K ? t * (uint32_t)H * 2u + colB[q] : OOB);
+        dma16(rA, mA + q * 1024, colA[q] + (uint32_t)r * (uint32_t)(2 * I) * 2u, 0u);
+        dma16(rB, mB + q * 1024, r < c.K ? t * (uint32_t)H * 2u + colB[q] : OOB, 0u);
       }
     }
   }
@@ -545,7 +601,10 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
   a.offsets = offsets;
   using T = KT<KIND>;
   constexpr bool GATHER = T::GA || T::GB;
-  constexpr int NLW = 4 + (GATHER ? 1 : 0);  // memory instructions per step and wavefront
+  // memory instructions per step and wavefront: 4 operand loads, plus the token load that
+  // varlen-K kinds issue every step (varlen-M kinds issue theirs only at tile starts and count
+  // them separately)
+  constexpr int NLW = 4 + (T::VK && GATHER ? 1 : 0);
 
   __shared__ __attribute__((aligned(1024))) char s_ring[NSTG * STG];
   __shared__ __attribute__((aligned(256))) int s_tok[8 * NSTG * (TOKB / 4)];
@@ -657,29 +716,35 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
   ld.init(w, L);
   const i32x4 rtok = dmadesc(a.row_token, 4LL * (long long)a.M_cap);
   int* my_tok = s_tok + w * NSTG * (TOKB / 4);  // this wavefront's token ring
+  const uint32_t tok_m0 = lds_addr(my_tok);
+  const uint32_t ring_m0 = lds_addr(s_ring) + (uint32_t)(2 * w) * 1024u;  // this wavefront's A kilobyte, stage 0
 
-  // token load for cursor t (its step index s): per tile (varlen-M) or per step (varlen-K)
-  auto tok_issue = [&](const Tile& t, int s) __attribute__((always_inline)) {
-    uint32_t off = OOB;
+  // token load for cursor t at step index s: per step (varlen-K), or at a tile's first step
+  // (varlen-M, which then returns 1: the number of loads it issued)
+  auto tok_issue = [&](const Tile& t, int s) __attribute__((always_inline)) -> int {
+    const uint32_t m0 = tok_m0 + (uint32_t)(s & (NSTG - 1)) * TOKB;
     if constexpr (T::VK) {
-      if (t.valid) off = (uint32_t)(t.roff + t.kt * BK + 4 * w + L) * 4u;
+      dma4(rtok, m0, t.valid ? (uint32_t)(t.roff + t.kt * BK + 4 * w + L) * 4u : OOB);
+      return 1;
     } else {
-      if (t.valid && t.kt == 0) off = (uint32_t)(t.roff + t.mt * BM + 32 * w + L) * 4u;
+      if (t.valid && t.kt == 0) {
+        dma4(rtok, m0, (uint32_t)(t.roff + t.mt * BM + 32 * w + L) * 4u);
+        return 1;
+      }
+      return 0;
     }
-    dma4(rtok, reinterpret_cast<char*>(my_tok + (s & (NSTG - 1)) * (TOKB / 4)), off);
   };
   Tile Ld = Cc, Tk = Cc;
   auto load_issue = [&](int s) __attribute__((always_inline)) {
     const int* tk = my_tok + (s & (NSTG - 1)) * (TOKB / 4);
-    if (Ld.kt == 0) {
-      ld.setup(a, Ld, tk, w, L, S.nMg);
-      ld.uniform();
-    }
-    ld.issue(a, Ld, s_ring + (s & (NSTG - 1)) * STG, tk, w, L);
+    if (Ld.kt == 0) ld.setup(a, Ld, tk, w, L, S.nMg);
+    ld.issue(a, Ld, ring_m0 + (uint32_t)(s & (NSTG - 1)) * STG, tk, w, L);
     S.next(a, Ld, true);
   };
 
   // ---- prologue: tokens of steps 0..2 resident, loads of steps 0..2 in flight ----
+  // t1, t2: token loads issued with the last and the second-to-last step's loads (varlen-M)
+  int t1 = 0, t2 = 0;
   if constexpr (GATHER) {
 #pragma unroll 1
     for (int s = 0; s < AHEAD; ++s) {
@@ -690,16 +755,22 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
   }
 #pragma unroll 1
   for (int s = 0; s < AHEAD; ++s) {
+    int tn = 0;
     if constexpr (GATHER) {
-      tok_issue(Tk, s + AHEAD);
+      tn = tok_issue(Tk, s + AHEAD);
       S.next(a, Tk, true);
     }
     load_issue(s);
+    t2 = t1;
+    t1 = tn;
   }
 
   // epilogues issued after the loads of the last three steps (their stores are younger)
+  // The wait for step s allows the memory instructions issued after step s's loads: the two
+  // later steps' loads (4 each, plus a token load where one was issued) and the stores of any
+  // epilogue since.  Rounding an allowance down only makes the wait stricter.
   int h0 = 0, h1 = 0, h2 = 0;
-  constexpr int X0 = 2 * NLW;
+  constexpr int X0 = 2 * NLW;  // varlen-K: the token loads are part of NLW
   constexpr int X1 = (X0 + T::ST) < 63 ? (X0 + T::ST) : 63;
   constexpr int X2 = (X0 + 2 * T::ST) < 63 ? (X0 + 2 * T::ST) : 63;
   constexpr int X3 = (X0 + 3 * T::ST) < 63 ? (X0 + 3 * T::ST) : 63;
@@ -709,19 +780,34 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
     // step s's loads (issued three steps ago) have landed for every wavefront, and every
     // wavefront is done with the stage that the loads below overwrite
     const int ne = h0 + h1 + h2;
-    if (ne == 0) vm_wait_barrier<X0>();
-    else if (ne == 1) vm_wait_barrier<X1>();
+    if (ne == 0) {
+      if constexpr (T::GA && !T::VK) {
+        const int ts = t1 + t2;
+        if (ts == 0) vm_wait_barrier<8>();
+        else if (ts == 1) vm_wait_barrier<9>();
+        else vm_wait_barrier<10>();
+      } else {
+        vm_wait_barrier<X0>();
+      }
+    } else if (ne == 1) vm_wait_barrier<X1>();
     else if (ne == 2) vm_wait_barrier<X2>();
     else vm_wait_barrier<X3>();
     h2 = h1;
     h1 = h0;
     h0 = 0;
 
-    if constexpr (GATHER) {
-      tok_issue(Tk, s + 2 * AHEAD);
-      S.next(a, Tk, true);
+#ifndef MOE_DMA_LATE
+    {
+      int tn = 0;
+      if constexpr (GATHER) {
+        tn = tok_issue(Tk, s + 2 * AHEAD);
+        S.next(a, Tk, true);
+      }
+      load_issue(s + AHEAD);
+      t2 = t1;
+      t1 = tn;
     }
-    load_issue(s + AHEAD);
+#endif
 
     // ---- MFMAs of step s ----
     if (Cc.mlen > wm * 64) {
@@ -743,6 +829,18 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = mma(fb[j], fa[i], acc[i][j]);
     }
+#ifdef MOE_DMA_LATE
+    {
+      int tn = 0;
+      if constexpr (GATHER) {
+        tn = tok_issue(Tk, s + 2 * AHEAD);
+        S.next(a, Tk, true);
+      }
+      load_issue(s + AHEAD);
+      t2 = t1;
+      t1 = tn;
+    }
+#endif
 
     // ---- advance the compute cursor; finish a tile after its last step ----
     if (Cc.kt + 1 < Cc.nk) {
