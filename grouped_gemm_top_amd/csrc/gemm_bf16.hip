@@ -66,18 +66,19 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 
 // A_KC / B_KC: operand is K-contiguous in memory; GA / GB: operand rows are gathered through
 // row_token; VK: the reduction runs over an expert's rows (varlen-K); ST: a lower bound on the
 // memory instructions one epilogue issues (used for the vmcnt immediates).
 template <int K> struct KT;
-template <> struct KT<GATEUP> { static constexpr bool A_KC = true, B_KC = true, VK = false, GA = true, GB = false; static constexpr int ST = 48; };
-template <> struct KT<DOWN> { static constexpr bool A_KC = true, B_KC = true, VK = false, GA = false, GB = false; static constexpr int ST = 32; };
+template <> struct KT<GATEUP> { static constexpr bool A_KC = true, B_KC = true, VK = false, GA = true, GB = false; static constexpr int ST = 32; };
+template <> struct KT<DOWN> { static constexpr bool A_KC = true, B_KC = true, VK = false, GA = false, GB = false; static constexpr int ST = 16; };
 template <> struct KT<DH> { static constexpr bool A_KC = true, B_KC = false, VK = false, GA = true, GB = false; static constexpr int ST = 96; };
-template <> struct KT<DX> { static constexpr bool A_KC = true, B_KC = false, VK = false, GA = false, GB = false; static constexpr int ST = 32; };
-template <> struct KT<DWD> { static constexpr bool A_KC = false, B_KC = false, VK = true, GA = true, GB = false; static constexpr int ST = 32; };
-template <> struct KT<DW1> { static constexpr bool A_KC = false, B_KC = false, VK = true, GA = false, GB = true; static constexpr int ST = 32; };
+template <> struct KT<DX> { static constexpr bool A_KC = true, B_KC = false, VK = false, GA = false, GB = false; static constexpr int ST = 16; };
+template <> struct KT<DWD> { static constexpr bool A_KC = false, B_KC = false, VK = true, GA = true, GB = false; static constexpr int ST = 16; };
+template <> struct KT<DW1> { static constexpr bool A_KC = false, B_KC = false, VK = true, GA = false, GB = true; static constexpr int ST = 16; };
 
 // LDS loads.  They are written as inline assembly on purpose: the compiler then does not
 // track them as LDS writes and inserts no vmcnt waits of its own before LDS reads (it cannot
@@ -447,43 +448,83 @@ struct Loader {
 };
 
 // ------------------------------------------------------------------ epilogues
+// Stores go through LDS: a lane holds 4 consecutive columns of one row, which as a store would
+// touch 16 rows x 32 bytes per instruction; staged through LDS, 16 lanes instead cover 256
+// contiguous bytes of one row.  `st` is this wavefront's 4 KB of LDS.  A 16-row block of 128
+// columns (blk[0..7], as acc[i][0..7]) is written as rows of 256 bytes, 16-byte chunk q of row
+// r at position q ^ r, then read back 16 bytes per lane.
+__device__ __forceinline__ void stage_write(char* st, const f32x4 (&blk)[8], int L) {
+  const int c = L & 15, g = L >> 4;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int pos = (2 * j + (g >> 1)) ^ c;
+    u32x2 v;
+    v.x = pk2(blk[j][0], blk[j][1]);
+    v.y = pk2(blk[j][2], blk[j][3]);
+    *reinterpret_cast<u32x2*>(st + c * 256 + pos * 16 + (g & 1) * 8) = v;
+  }
+}
+// the 16 bytes (8 columns, chunk L & 15) of row 4p + (L >> 4) of the staged block
+__device__ __forceinline__ uint4 stage_read(const char* st, int p, int L) {
+  const int row = 4 * p + (L >> 4), q = L & 15;
+  return *reinterpret_cast<const uint4*>(st + row * 256 + ((q ^ row) << 4));
+}
+__device__ __forceinline__ void st16(rsrc_t r, uint32_t off, const uint4& v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 0);
+}
+
 // acc[i][j][v] = C[m = wm*64 + 16i + (L & 15)][n = wn*128 + 16j + 4(L >> 4) + v]
+// `st`: this wavefront's 4 KB of LDS staging, free for the duration of the epilogue.
 template <int KIND>
 __device__ __forceinline__ void epilogue(const Args& a, const Tile& c, f32x4 (&acc)[4][8], float* s_red, int wm,
-                                         int wn, int L, int nMg, int nTN) {
+                                         int wn, int L, int nMg, int nTN, char* st) {
   const int H = a.H, I = a.I;
   const int cl = L & 15, g = L >> 4;
   const long long rb = (long long)c.roff + (long long)c.mt * BM;
   if constexpr (KIND == GATEUP) {
     const rsrc_t rh = gg::mkr_off(a.out0, rb * 2 * I * 2, (long long)c.mlen * 2 * I * 2);
     const rsrc_t ra = gg::mkr_off(a.out1, rb * I * 2, (long long)c.mlen * I * 2);
+    const int i0 = c.nt * 128 + wn * 64;  // first i of this wavefront's 64 gate and 64 up columns
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t m = (uint32_t)(wm * 64 + 16 * i + cl);
+      // [G | U] block: staged columns 0..63 gate, 64..127 up, for i0 .. i0 + 63
+      stage_write(st, acc[i], L);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint4 v = stage_read(st, p, L);
+        const uint32_t m = (uint32_t)(wm * 64 + 16 * i + 4 * p + (L >> 4));  // rows >= mlen: past the range
+        const int q = L & 15, ii = i0 + (q & 7) * 8;
+        const uint32_t off = m * (uint32_t)(2 * I) * 2u + (uint32_t)((q >= 8 ? I : 0) + ii) * 2u;
+        st16(rh, ii < I ? off : OOB, v);
+      }
+      // A = silu(G) * U, staged in the first 64 columns
+      f32x4 ab[8];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int ii = c.nt * 128 + wn * 64 + 16 * j + 4 * g;
-        const bool iv = ii < I;
-        const f32x4 G = acc[i][j], U = acc[i][j + 4];
-        float av[4];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) av[v] = G[v] * sigm(G[v]) * U[v];
-        const uint32_t hrow = m * (uint32_t)(2 * I) * 2u;
-        st4(rh, iv ? hrow + (uint32_t)ii * 2u : OOB, G[0], G[1], G[2], G[3]);
-        st4(rh, iv ? hrow + (uint32_t)(I + ii) * 2u : OOB, U[0], U[1], U[2], U[3]);
-        st4(ra, iv ? m * (uint32_t)I * 2u + (uint32_t)ii * 2u : OOB, av[0], av[1], av[2], av[3]);
+        for (int v = 0; v < 4; ++v) ab[j][v] = acc[i][j][v] * sigm(acc[i][j][v]) * acc[i][j + 4][v];
+        ab[j + 4] = ab[j];
+      }
+      stage_write(st, ab, L);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint4 v = stage_read(st, p, L);
+        const uint32_t m = (uint32_t)(wm * 64 + 16 * i + 4 * p + (L >> 4));
+        const int q = L & 15, ii = i0 + q * 8;
+        if (q < 8) st16(ra, ii < I ? m * (uint32_t)I * 2u + (uint32_t)ii * 2u : OOB, v);
       }
     }
   } else if constexpr (KIND == DOWN || KIND == DX) {
     const rsrc_t ro = gg::mkr_off(a.out0, rb * H * 2, (long long)c.mlen * H * 2);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t m = (uint32_t)(wm * 64 + 16 * i + cl);
+      stage_write(st, acc[i], L);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int n = c.nt * BN + wn * 128 + 16 * j + 4 * g;
-        st4(ro, n < H ? m * (uint32_t)H * 2u + (uint32_t)n * 2u : OOB, acc[i][j][0], acc[i][j][1], acc[i][j][2],
-            acc[i][j][3]);
+      for (int p = 0; p < 4; ++p) {
+        const uint4 v = stage_read(st, p, L);
+        const uint32_t m = (uint32_t)(wm * 64 + 16 * i + 4 * p + (L >> 4));  // rows >= mlen: past the range
+        const int n = c.nt * BN + wn * 128 + (L & 15) * 8;
+        st16(ro, n < H ? m * (uint32_t)H * 2u + (uint32_t)n * 2u : OOB, v);
       }
     }
   } else if constexpr (KIND == DH) {
@@ -552,12 +593,13 @@ __device__ __forceinline__ void epilogue(const Args& a, const Tile& c, f32x4 (&a
     const rsrc_t ro = gg::mkr_off(a.out0, (long long)c.e * H * I * 2, (long long)H * I * 2);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int m = c.mt * BM + wm * 64 + 16 * i + cl;  // h
+      stage_write(st, acc[i], L);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int n = c.nt * BN + wn * 128 + 16 * j + 4 * g;  // i
-        st4(ro, (m < H && n < I) ? (uint32_t)m * (uint32_t)I * 2u + (uint32_t)n * 2u : OOB, acc[i][j][0],
-            acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+      for (int p = 0; p < 4; ++p) {
+        const uint4 v = stage_read(st, p, L);
+        const int m = c.mt * BM + wm * 64 + 16 * i + 4 * p + (L >> 4);  // h
+        const int n = c.nt * BN + wn * 128 + (L & 15) * 8;                 // i
+        st16(ro, (m < H && n < I) ? (uint32_t)m * (uint32_t)I * 2u + (uint32_t)n * 2u : OOB, v);
       }
     }
   } else {  // DW1
@@ -566,12 +608,13 @@ __device__ __forceinline__ void epilogue(const Args& a, const Tile& c, f32x4 (&a
     const rsrc_t ro = gg::mkr_off(seg ? a.out1 : a.out0, (long long)c.e * I * H * 2, (long long)I * H * 2);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int m = m0 + wm * 64 + 16 * i + cl;  // i of dW_gate / dW_up
+      stage_write(st, acc[i], L);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int n = c.nt * BN + wn * 128 + 16 * j + 4 * g;  // h
-        st4(ro, (m < I && n < H) ? (uint32_t)m * (uint32_t)H * 2u + (uint32_t)n * 2u : OOB, acc[i][j][0],
-            acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+      for (int p = 0; p < 4; ++p) {
+        const uint4 v = stage_read(st, p, L);
+        const int m = m0 + wm * 64 + 16 * i + 4 * p + (L >> 4);  // i of dW_gate / dW_up
+        const int n = c.nt * BN + wn * 128 + (L & 15) * 8;        // h
+        st16(ro, (m < I && n < H) ? (uint32_t)m * (uint32_t)H * 2u + (uint32_t)n * 2u : OOB, v);
       }
     }
   }
@@ -699,7 +742,7 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
   S.decode(a, Cc, 0);
   if constexpr (T::VK) {
     while (Cc.valid && Cc.nk == 0) {
-      epilogue<KIND>(a, Cc, acc, s_red, wm, wn, L, S.nMg, nTN);
+      epilogue<KIND>(a, Cc, acc, s_red, wm, wn, L, S.nMg, nTN, s_ring + w * 4096);
       S.decode(a, Cc, Cc.it + 1);
     }
   }
@@ -846,7 +889,11 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
     if (Cc.kt + 1 < Cc.nk) {
       ++Cc.kt;
     } else {
-      epilogue<KIND>(a, Cc, acc, s_red, wm, wn, L, S.nMg, nTN);
+      // the stage of step s is free once every wavefront has read its fragments; the loads
+      // that refill it are issued only after the next step's barrier
+      char* st = s_ring + (s & (NSTG - 1)) * STG + w * 4096;
+      if constexpr (KIND != DH) lds_barrier();
+      epilogue<KIND>(a, Cc, acc, s_red, wm, wn, L, S.nMg, nTN, st);
       ++h0;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -855,7 +902,7 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
       S.decode(a, Cc, Cc.it + 1);
       if constexpr (T::VK) {
         while (Cc.valid && Cc.nk == 0) {
-          epilogue<KIND>(a, Cc, acc, s_red, wm, wn, L, S.nMg, nTN);
+          epilogue<KIND>(a, Cc, acc, s_red, wm, wn, L, S.nMg, nTN, st);
           ++h0;
           S.decode(a, Cc, Cc.it + 1);
         }
