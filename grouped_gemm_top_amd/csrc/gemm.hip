@@ -835,6 +835,12 @@ __global__ __launch_bounds__(NTHR, 2) void k_grouped_gemm(Args a, const int32_t*
   }
 }
 
+// Zero the tile counters of the dynamically scheduled grouped GEMMs of one call (a kernel
+// rather than a memset, so the call can be captured into a graph).
+__global__ __launch_bounds__(256) void k_zero_qctr(int* __restrict__ q, int n) {
+  for (int i = threadIdx.x; i < n; i += 256) q[i] = 0;
+}
+
 // dS: ordered sum of the N-tile partials; scattered to (t, j) order through row_pair for
 // top-k plans, kept in row order for token-rounding plans.
 __global__ __launch_bounds__(256) void k_ds_reduce(const float* __restrict__ dspart, int nTN,
@@ -880,9 +886,17 @@ static hipError_t run(const gg::Args& a, long long max_tiles, hipStream_t s) {
   return hipGetLastError();
 }
 
+// tile counters of one call: two dynamically scheduled launches x 8 XCDs, 16 ints apart
+constexpr int QCTR_INTS = 2 * 8 * 16;
+
+static hipError_t zero_qctr(int* q, hipStream_t s) {
+  hipLaunchKernelGGL(gg::k_zero_qctr, dim3(1), dim3(256), 0, s, q, QCTR_INTS);
+  return hipGetLastError();
+}
+
 size_t gemm_fwd_ws_bytes(moe_dtype dt, int M_cap, int I) {
   const size_t es = dt == MOE_BF16 ? 2 : 4;
-  return align256((size_t)M_cap * I * es) + 256;
+  return align256((size_t)M_cap * I * es) + align256(QCTR_INTS * 4) + 256;
 }
 
 template <typename T>
@@ -896,9 +910,12 @@ static hipError_t gemm_fwd_t(const void* x, const void* wg, const void* wu, cons
   a.out0 = hcache; a.out1 = act;
   hipError_t err;
   if constexpr (std::is_same<T, bf16_t>::value) {
+    int* q = (int*)((char*)ws + align256((size_t)p.M_cap * I * sizeof(T)));
+    if ((err = zero_qctr(q, s)) != hipSuccess) return err;
     const long long mt = (long long)(p.M_cap + 255) / 256 + p.E;
+    a.qctr = q;
     if ((err = run_gemm_bf16<gg::GATEUP>(a, mt * ((I + 127) / 128), s)) != hipSuccess) return err;
-    a.act = act; a.out0 = y; a.out1 = nullptr;
+    a.act = act; a.out0 = y; a.out1 = nullptr; a.qctr = q + QCTR_INTS / 2;
     return run_gemm_bf16<gg::DOWN>(a, mt * ((H + 255) / 256), s);
   } else {
     const long long mt = (long long)(p.M_cap + gg::BM - 1) / gg::BM + p.E;
@@ -919,7 +936,7 @@ size_t layer_bwd_ws_bytes(moe_dtype dt, int N, int M_cap, int H, int I) {
   const size_t es = dt == MOE_BF16 ? 2 : 4;
   const size_t nTN = (size_t)(I + gg::BN - 1) / gg::BN;
   return align256((size_t)M_cap * 2 * I * es) + align256((size_t)M_cap * I * es) +
-         align256((size_t)M_cap * H * es) + align256((size_t)M_cap * nTN * 4) + 256;
+         align256((size_t)M_cap * H * es) + align256((size_t)M_cap * nTN * 4) + align256(QCTR_INTS * 4) + 256;
 }
 
 template <typename T>
@@ -938,6 +955,8 @@ static hipError_t layer_bwd_t(const void* dout, const void* x, const void* wg, c
   void* dxe = w;
   w += align256((size_t)p.M_cap * H * es);
   float* dspart = (float*)w;
+  w += align256((size_t)p.M_cap * nTN * 4);
+  int* q = (int*)w;
 
   gg::Args a{};
   a.x = x; a.wg = wg; a.wu = wu; a.wd = wd; a.dout = dout; a.hcache = hcache;
@@ -958,8 +977,13 @@ static hipError_t layer_bwd_t(const void* dout, const void* x, const void* wg, c
   hipError_t err;
 
   // dH epilogue kernel: dH = [dG | dU], A' = w A, dS partials
+  if constexpr (BF) {
+    if ((err = zero_qctr(q, s)) != hipSuccess) return err;
+    a.qctr = q;
+  }
   a.out0 = dh; a.out1 = aprime; a.dspart = dspart;
   if ((err = launch(KDH{}, mt * nTN)) != hipSuccess) return err;
+  a.qctr = nullptr;
   if (p.M_cap > 0) {
     kernel_event(MOE_K_DS_REDUCE, 0, s);
     hipLaunchKernelGGL(gg::k_ds_reduce, dim3((p.M_cap + 255) / 256), dim3(256), 0, s, dspart, nTN, p.offsets, p.E,
@@ -972,7 +996,9 @@ static hipError_t layer_bwd_t(const void* dout, const void* x, const void* wg, c
   if ((err = launch(KDWD{}, (long long)p.E * ((H + tm - 1) / tm) * nTN)) != hipSuccess) return err;
   // dXe = dH [W_gate; W_up]   (varlen-M), then the unweighted combine to token order
   a.dh = dh; a.out0 = dxe;
+  if constexpr (BF) a.qctr = q + QCTR_INTS / 2;
   if ((err = launch(KDX{}, mt * ((H + tn - 1) / tn))) != hipSuccess) return err;
+  a.qctr = nullptr;
   kernel_event(MOE_K_DX_COMBINE, 0, s);
   err = launch_combine(sizeof(T) == 2 ? MOE_BF16 : MOE_F32, dxe, H, p, nullptr, dx, s);
   kernel_event(MOE_K_DX_COMBINE, 1, s);

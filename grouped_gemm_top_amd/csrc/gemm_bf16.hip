@@ -13,9 +13,11 @@
 //
 // Design:
 //  * One workgroup of 512 threads (8 wavefronts, 4 along M x 2 along N) per compute unit
-//    owns a 256x256 output tile; each wavefront computes 64x128 with
-//    v_mfma_f32_16x16x32_bf16 (4 x 8 blocks of 16x16).  The grid is persistent: one
-//    workgroup per CU walks its share of the tile list.
+//    owns a 256x256 output tile; wavefront (wm, wn) computes the 16-row blocks 16(4i + wm),
+//    i = 0..3, times 128 columns with v_mfma_f32_16x16x32_bf16 (4 x 8 blocks of 16x16).
+//    Wavefront w runs on SIMD w % 4 = wm, so interleaving the row blocks spreads a short
+//    tile's work over all four SIMDs; blocks at or past the tile's row count are skipped.
+//    The grid is persistent: one workgroup per CU walks its share of the tile list.
 //  * Operands go from HBM straight into LDS with buffer_load ... lds (no VGPR staging).
 //    LDS holds a ring of 4 stages of k = 32 (16 KB per operand and stage); the loads run
 //    three k-steps ahead of the MFMAs, across tile boundaries, so a tile's prologue overlaps
@@ -36,7 +38,12 @@
 //  * Varlen-M tiles are ordered (expert, n-tile, m-tile) so tiles that share a weight slice
 //    run together; varlen-K tiles are ordered heaviest expert first.  Each XCD gets
 //    contiguous runs of the tile list, so neighbouring tiles share its L2.
-//  * No atomics; every reduction has a fixed order, so results are bitwise reproducible.
+//  * Varlen-M tile costs vary (a group's last m-tile holds its leftover rows), so the
+//    bf16 varlen-M kinds balance dynamically: each XCD owns an eighth of the tile list, its
+//    workgroups take the first rounds in a fixed order and then draw further tiles from an
+//    XCD-local counter (one atomic add per tile).  Every tile is still computed by one
+//    workgroup in a fixed k order, so results stay bitwise reproducible; no reduction uses
+//    atomics.
 #include "gemm_common.h"
 
 namespace moe {
@@ -61,6 +68,7 @@ constexpr int AHEAD = NSTG - 1;
 constexpr int OPB = 16384;     // bytes of one operand per stage
 constexpr int STG = 2 * OPB;   // bytes per stage
 constexpr int TOKB = 256;      // bytes per token slot (64 row indices)
+constexpr int QN = 16;         // ring of dynamically assigned tile indices (a power of two)
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -157,13 +165,23 @@ template <int KIND>
 struct Sched {
   using T = KT<KIND>;
   const int* s_sched;  // LDS: varlen-M tile prefix [E+1]; varlen-K expert order [E]
+  const int* s_q;      // LDS: tile index of the workgroup's j-th tile at [j & (QN - 1)] (dynamic)
   int total, G, per, xcd, slot, E, nN, nMg, nM;
+  // dynamic schedule (varlen-M): this XCD owns tiles [lo, hi); its workgroups take rounds
+  // 0 .. R-1 statically (tile lo + j*per + slot) and the rest from the XCD's counter
+  int dyn, lo, hi, R;
 
   __device__ __forceinline__ void decode(const Args& a, Tile& c, int it) const {
     c.it = it;
     c.kt = 0;
-    const long long tl = (long long)it * G + (long long)xcd * per + slot;
-    c.valid = tl < (long long)total;
+    long long tl;
+    if (dyn) {
+      tl = it < R ? (long long)lo + (long long)it * per + slot : (long long)ufl(s_q[it & (QN - 1)]);
+      c.valid = tl >= 0 && tl < (long long)hi;
+    } else {
+      tl = (long long)it * G + (long long)xcd * per + slot;
+      c.valid = tl < (long long)total;
+    }
     if (!c.valid) {
       c.e = 0; c.roff = 0; c.mt = 0; c.nt = 0; c.mlen = 0; c.K = 0; c.nk = 0;
       return;
@@ -473,11 +491,16 @@ __device__ __forceinline__ void st16(rsrc_t r, uint32_t off, const uint4& v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 0);
 }
 
-// acc[i][j][v] = C[m = wm*64 + 16i + (L & 15)][n = wn*128 + 16j + 4(L >> 4) + v]
+// acc[i][j][v] = C[m = 16(4i + wm) + (L & 15)][n = wn*128 + 16j + 4(L >> 4) + v]
 // `st`: this wavefront's 4 KB of LDS staging, free for the duration of the epilogue.
 template <int KIND>
 __device__ __forceinline__ void epilogue(const Args& a, const Tile& c, f32x4 (&acc)[4][8], float* s_red, int wm,
-                                         int wn, int L, int nMg, int nTN, char* st) {
+                                         int wn, int L_, int nMg, int nTN, char* st) {
+  // The lane's address arithmetic depends only on kernel constants; an opaque copy of the lane
+  // index keeps the compiler from computing it once for the whole kernel and holding the
+  // results in registers across the k-loop (where they would push the MFMA loop into spills).
+  int L = L_;
+  asm volatile("" : "+v"(L));
   const int H = a.H, I = a.I;
   const int cl = L & 15, g = L >> 4;
   const long long rb = (long long)c.roff + (long long)c.mt * BM;
@@ -492,7 +515,7 @@ __device__ __forceinline__ void epilogue(const Args& a, const Tile& c, f32x4 (&a
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         const uint4 v = stage_read(st, p, L);
-        const uint32_t m = (uint32_t)(wm * 64 + 16 * i + 4 * p + (L >> 4));  // rows >= mlen: past the range
+        const uint32_t m = (uint32_t)(16 * (4 * i + wm) + 4 * p + (L >> 4));  // rows >= mlen: past the range
         const int q = L & 15, ii = i0 + (q & 7) * 8;
         const uint32_t off = m * (uint32_t)(2 * I) * 2u + (uint32_t)((q >= 8 ? I : 0) + ii) * 2u;
         st16(rh, ii < I ? off : OOB, v);
@@ -509,7 +532,7 @@ __device__ __forceinline__ void epilogue(const Args& a, const Tile& c, f32x4 (&a
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         const uint4 v = stage_read(st, p, L);
-        const uint32_t m = (uint32_t)(wm * 64 + 16 * i + 4 * p + (L >> 4));
+        const uint32_t m = (uint32_t)(16 * (4 * i + wm) + 4 * p + (L >> 4));
         const int q = L & 15, ii = i0 + q * 8;
         if (q < 8) st16(ra, ii < I ? m * (uint32_t)I * 2u + (uint32_t)ii * 2u : OOB, v);
       }
@@ -522,7 +545,7 @@ __device__ __forceinline__ void epilogue(const Args& a, const Tile& c, f32x4 (&a
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         const uint4 v = stage_read(st, p, L);
-        const uint32_t m = (uint32_t)(wm * 64 + 16 * i + 4 * p + (L >> 4));  // rows >= mlen: past the range
+        const uint32_t m = (uint32_t)(16 * (4 * i + wm) + 4 * p + (L >> 4));  // rows >= mlen: past the range
         const int n = c.nt * BN + wn * 128 + (L & 15) * 8;
         st16(ro, n < H ? m * (uint32_t)H * 2u + (uint32_t)n * 2u : OOB, v);
       }
@@ -535,7 +558,7 @@ __device__ __forceinline__ void epilogue(const Args& a, const Tile& c, f32x4 (&a
     float dsum[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t m = (uint32_t)(wm * 64 + 16 * i + cl);
+      const uint32_t m = (uint32_t)(16 * (4 * i + wm) + cl);
       const float wr = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rw, m * 4u, 0, 0));
       const uint32_t hrow = m * (uint32_t)(2 * I) * 2u;
       // G and U stay packed (two bf16 per register) until they are used
@@ -579,13 +602,13 @@ __device__ __forceinline__ void epilogue(const Args& a, const Tile& c, f32x4 (&a
     // the two wavefronts of a row block hold the two column halves: wn 0 adds wn 1's half
     if (wn == 1 && L < 16) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s_red[wm * 64 + 16 * i + L] = dsum[i];
+      for (int i = 0; i < 4; ++i) s_red[16 * (4 * i + wm) + L] = dsum[i];
     }
     lds_barrier();
     if (wn == 0 && L < 16) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int m = wm * 64 + 16 * i + L;
+        const int m = 16 * (4 * i + wm) + L;
         if (m < c.mlen) a.dspart[(size_t)(rb + m) * nTN + c.nt] = dsum[i] + s_red[m];
       }
     }
@@ -597,7 +620,7 @@ __device__ __forceinline__ void epilogue(const Args& a, const Tile& c, f32x4 (&a
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         const uint4 v = stage_read(st, p, L);
-        const int m = c.mt * BM + wm * 64 + 16 * i + 4 * p + (L >> 4);  // h
+        const int m = c.mt * BM + 16 * (4 * i + wm) + 4 * p + (L >> 4);  // h
         const int n = c.nt * BN + wn * 128 + (L & 15) * 8;                 // i
         st16(ro, (m < H && n < I) ? (uint32_t)m * (uint32_t)I * 2u + (uint32_t)n * 2u : OOB, v);
       }
@@ -612,7 +635,7 @@ __device__ __forceinline__ void epilogue(const Args& a, const Tile& c, f32x4 (&a
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         const uint4 v = stage_read(st, p, L);
-        const int m = m0 + wm * 64 + 16 * i + 4 * p + (L >> 4);  // i of dW_gate / dW_up
+        const int m = m0 + 16 * (4 * i + wm) + 4 * p + (L >> 4);  // i of dW_gate / dW_up
         const int n = c.nt * BN + wn * 128 + (L & 15) * 8;        // h
         st16(ro, (m < I && n < H) ? (uint32_t)m * (uint32_t)H * 2u + (uint32_t)n * 2u : OOB, v);
       }
@@ -652,6 +675,7 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
   __shared__ __attribute__((aligned(1024))) char s_ring[NSTG * STG];
   __shared__ __attribute__((aligned(256))) int s_tok[8 * NSTG * (TOKB / 4)];
   __shared__ int s_sched[1025];
+  __shared__ int s_q[QN];
   __shared__ int s_wsum[9];
   __shared__ float s_red[BM];
 
@@ -662,6 +686,8 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
 
   Sched<KIND> S;
   S.s_sched = s_sched;
+  S.s_q = s_q;
+  S.dyn = 0;
   S.E = E;
   S.G = gridDim.x;
   S.per = S.G >> 3;
@@ -713,6 +739,12 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
     if (tid == 0) s_sched[E] = s_wsum[8];
     S.total = ufl(s_wsum[8]);
     __syncthreads();
+    if (a.qctr != nullptr) {
+      S.dyn = 1;
+      S.lo = (int)((long long)S.total * S.xcd / 8);
+      S.hi = (int)((long long)S.total * (S.xcd + 1) / 8);
+      S.R = max(1, S.total / S.G - 1);
+    }
   } else {
     // heaviest expert first: rank_e = #{f : c_f > c_e or (c_f == c_e and f < e)}
     int* s_cnt = reinterpret_cast<int*>(s_ring);  // the ring is free until the first load
@@ -784,6 +816,31 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
     ld.issue(a, Ld, ring_m0 + (uint32_t)(s & (NSTG - 1)) * STG, tk, w, L);
     S.next(a, Ld, true);
   };
+  // Dynamic schedule: when the leading cursor (Tk for gathered kinds, else Ld) starts the tile
+  // before sequence index f_next, wavefront 0 takes tile f_next from the XCD's counter and
+  // stores its index in s_q.  Waiting for the atomic also waits for wavefront 0's loads in
+  // flight, so it happens once per dynamic tile only.  The index reaches the other
+  // wavefronts through the next barrier (sync: a barrier right here, where several cursor
+  // steps follow without one, as in the prologue).
+  int f_next = S.R;
+  auto lead_moved = [&](const Tile& lead, bool sync) __attribute__((always_inline)) {
+    if constexpr (!T::VK) {
+      if (S.dyn && lead.valid && lead.it + 1 == f_next) {
+        if (w == 0) {
+          if (L == 0) {
+            const int v = __hip_atomic_fetch_add(a.qctr + 16 * S.xcd, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const long long t = (long long)S.lo + (long long)S.R * S.per + v;
+            s_q[f_next & (QN - 1)] = t < (long long)S.hi ? (int)t : -1;
+          }
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        }
+        ++f_next;
+        if (sync) lds_barrier();
+      }
+    }
+  };
+  if constexpr (GATHER) lead_moved(Tk, true);
+  else lead_moved(Ld, true);
 
   // ---- prologue: tokens of steps 0..2 resident, loads of steps 0..2 in flight ----
   // t1, t2: token loads issued with the last and the second-to-last step's loads (varlen-M)
@@ -793,6 +850,7 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
     for (int s = 0; s < AHEAD; ++s) {
       tok_issue(Tk, s);
       S.next(a, Tk, true);
+      lead_moved(Tk, true);
     }
     vm_drain();
   }
@@ -802,8 +860,10 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
     if constexpr (GATHER) {
       tn = tok_issue(Tk, s + AHEAD);
       S.next(a, Tk, true);
+      lead_moved(Tk, true);
     }
     load_issue(s);
+    if constexpr (!GATHER) lead_moved(Ld, true);
     t2 = t1;
     t1 = tn;
   }
@@ -845,32 +905,43 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
       if constexpr (GATHER) {
         tn = tok_issue(Tk, s + 2 * AHEAD);
         S.next(a, Tk, true);
+        lead_moved(Tk, false);
       }
       load_issue(s + AHEAD);
+      if constexpr (!GATHER) lead_moved(Ld, false);
       t2 = t1;
       t1 = tn;
     }
 #endif
 
     // ---- MFMAs of step s ----
-    if (Cc.mlen > wm * 64) {
+    // row block i of this wavefront (rows 16(4i + wm) ..) takes part while it starts below
+    // mlen; a short tile's blocks are spread over all four SIMDs
+    if (Cc.mlen > 16 * wm) {
+      const int nb = Cc.mlen - 16 * wm;
       const char* sa = s_ring + (s & (NSTG - 1)) * STG;
       const char* sb = sa + OPB;
-      bf16x8 fa[4], fb[8];
+      bf16x8 fb[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         if constexpr (T::B_KC) fb[j] = frag_kc(sb, wn * 128 + 16 * j, kc_off);
         else fb[j] = frag_mn(sb, wn * 128 + 16 * j, mn_k0, mn_ff, mn_b);
       }
+      // every fragment read is issued before the MFMAs; a row block at or past mlen skips
+      // its MFMAs (its fragment holds rows of no group, never used)
+      bf16x8 fa[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if constexpr (T::A_KC) fa[i] = frag_kc(sa, wm * 64 + 16 * i, kc_off);
-        else fa[i] = frag_mn(sa, wm * 64 + 16 * i, mn_k0, mn_ff, mn_b);
+        if constexpr (T::A_KC) fa[i] = frag_kc(sa, 16 * (4 * i + wm), kc_off);
+        else fa[i] = frag_mn(sa, 16 * (4 * i + wm), mn_k0, mn_ff, mn_b);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i) {
+        if (i == 0 || nb > 64 * i) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = mma(fb[j], fa[i], acc[i][j]);
+          for (int j = 0; j < 8; ++j) acc[i][j] = mma(fb[j], fa[i], acc[i][j]);
+        }
+      }
     }
 #ifdef MOE_DMA_LATE
     {
@@ -878,8 +949,10 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
       if constexpr (GATHER) {
         tn = tok_issue(Tk, s + 2 * AHEAD);
         S.next(a, Tk, true);
+        lead_moved(Tk, false);
       }
       load_issue(s + AHEAD);
+      if constexpr (!GATHER) lead_moved(Ld, false);
       t2 = t1;
       t1 = tn;
     }
