@@ -7,44 +7,70 @@
 //   [DEP] "Deep EP", section "2) Dispatch" (ragged layout needs offset/index metadata)
 //
 // A stable counting sort over the N*k (token, slot) pairs, never a comparison sort:
-//   k_perm_hist     per block of 256 tokens: expert histogram in LDS -> bcnt[b][e]
+//   k_perm_hist     per block of TB tokens: expert histogram in LDS -> bcnt[b][e]
 //   k_perm_scan     counts[e] = sum_b bcnt[b][e]; offsets = exclusive scan over e;
 //                   bbase[b][e] = offsets[e] + sum_{b'<b} bcnt[b'][e]
 //   k_perm_scatter  rank of a pair inside (block, expert) = number of earlier tokens of the
-//                   block routed to the same expert (LDS bitmask + popcount), so rows of an
-//                   expert ascend by token; also writes the token-major row lists
+//                   block routed to the same expert (an LDS bitmask of the block's 64 tokens
+//                   and one popcount), so rows of an expert ascend by token; also writes the
+//                   token-major row lists
 // Integer counting only: the plan is bit-exact and independent of scheduling.
 #include "common.h"
 
 namespace moe {
 
-constexpr int kPT = 256;  // tokens per block
+constexpr int kPT = 256;  // threads per block
+constexpr int kTB = 64;   // tokens per block of the top-k permute (one 64-bit mask per expert)
 
+// per-block expert histogram; pair p of the block is (token p / k, slot p % k), read in order
+template <int TB>
 __global__ __launch_bounds__(kPT) void k_perm_hist(const int32_t* __restrict__ idx, int N, int E, int k,
                                                    int32_t* __restrict__ bcnt) {
   __shared__ int s_cnt[1024];
   for (int e = threadIdx.x; e < E; e += kPT) s_cnt[e] = 0;
   __syncthreads();
-  const int t = blockIdx.x * kPT + threadIdx.x;
-  if (t < N)
-    for (int j = 0; j < k; ++j) {
-      const int e = idx[(size_t)t * k + j];
-      if (e >= 0 && e < E) atomicAdd(&s_cnt[e], 1);
-    }
+  const long long t0 = (long long)blockIdx.x * TB;
+  const int np = (int)(min((long long)TB, (long long)N - t0) * k);
+  const int32_t* ib = idx + t0 * k;
+  for (int q = threadIdx.x; q < np; q += kPT) {
+    const int e = ib[q];
+    if (e >= 0 && e < E) atomicAdd(&s_cnt[e], 1);
+  }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += kPT) bcnt[(size_t)blockIdx.x * E + e] = s_cnt[e];
 }
 
+// One block of 1024 threads.  Thread (part, e) owns the contiguous run of blocks
+// [part * C, part * C + C) of expert e (P = 1024 / ES parts, ES = E rounded up to a power of
+// two), so the per-expert sums and the block bases need one pass over short runs.
 __global__ __launch_bounds__(1024) void k_perm_scan(const int32_t* __restrict__ bcnt, int nb, int N, int E, int k,
                                                     int32_t* __restrict__ bbase, int32_t* __restrict__ counts,
                                                     int32_t* __restrict__ offsets, int32_t* __restrict__ tok_ptr) {
+  __shared__ int s_part[1024];
   __shared__ int s_wave[17];
-  const int e = threadIdx.x, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int ES = 1;
+  while (ES < E) ES <<= 1;
+  const int P = 1024 / ES;
+  const int e = threadIdx.x % ES, part = threadIdx.x / ES;
+  const int C = (nb + P - 1) / P;
+  const int b0 = part * C, b1 = min(nb, b0 + C);
   int c = 0;
-  if (e < E)
-    for (int b = 0; b < nb; ++b) c += bcnt[(size_t)b * E + e];
-  // block exclusive scan of c over the 1024 threads
-  int x = c;
+  if (e < E) {
+    for (int b = b0; b < b1; ++b) c += bcnt[(size_t)b * E + e];
+  }
+  s_part[threadIdx.x] = c;
+  __syncthreads();
+  // expert totals (thread e of part 0) and this thread's base within its expert
+  int before = 0, total = 0;
+  for (int q = 0; q < P; ++q) {
+    const int v = s_part[q * ES + e];
+    if (q < part) before += v;
+    total += v;
+  }
+  // exclusive scan of the totals over e (threads of part 0 hold e = 0 .. ES-1 in order)
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int x = (part == 0 && e < E) ? total : 0;
+  const int xin = x;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const int y = __shfl_up(x, off);
@@ -62,12 +88,16 @@ __global__ __launch_bounds__(1024) void k_perm_scan(const int32_t* __restrict__ 
     s_wave[16] = run;
   }
   __syncthreads();
-  const int ex = s_wave[wv] + x - c;
-  if (e < E) {
-    counts[e] = c;
+  if (part == 0 && e < E) {
+    const int ex = s_wave[wv] + x - xin;
+    counts[e] = total;
     offsets[e] = ex;
-    int run = ex;
-    for (int b = 0; b < nb; ++b) {
+    s_part[e] = ex;  // every thread of expert e has read its s_part values above
+  }
+  __syncthreads();
+  if (e < E) {
+    int run = s_part[e] + before;
+    for (int b = b0; b < b1; ++b) {
       const int v = bcnt[(size_t)b * E + e];
       bbase[(size_t)b * E + e] = run;
       run += v;
@@ -84,60 +114,61 @@ __global__ __launch_bounds__(kPT) void k_perm_scatter(const int32_t* __restrict_
                                                       int32_t* __restrict__ row_token, float* __restrict__ row_w,
                                                       int32_t* __restrict__ row_pair, int32_t* __restrict__ tok_ptr,
                                                       int32_t* __restrict__ tok_rows) {
-  constexpr int W = kPT / 32;  // bitmask words per expert
-  __shared__ uint32_t s_bits[1024 * W];
-  for (int q = threadIdx.x; q < E * W; q += kPT) s_bits[q] = 0u;
+  __shared__ uint32_t s_bits[1024 * 2];  // expert e: tokens 0-31 and 32-63 of the block
+  for (int q = threadIdx.x; q < 2 * E; q += kPT) s_bits[q] = 0u;
   __syncthreads();
-  const int tl = threadIdx.x;
-  const int t = blockIdx.x * kPT + tl;
-  const int32_t* it = idx + (size_t)t * k;
-  if (t < N)
-    for (int j = 0; j < k; ++j) {
-      const int e = it[j];
-      if (e >= 0 && e < E) atomicOr(&s_bits[e * W + (tl >> 5)], 1u << (tl & 31));
-    }
+  const int t0 = blockIdx.x * kTB;
+  const int nt = min(kTB, N - t0);
+  const int np = nt * k;
+  const int32_t* ib = idx + (size_t)t0 * k;
+  for (int q = threadIdx.x; q < np; q += kPT) {
+    const int e = ib[q], tl = q / k;
+    if (e >= 0 && e < E) atomicOr(&s_bits[2 * e + (tl >> 5)], 1u << (tl & 31));
+  }
+  if (threadIdx.x < nt) tok_ptr[t0 + threadIdx.x] = (t0 + threadIdx.x) * k;
   __syncthreads();
-  if (t >= N) return;
-  tok_ptr[t] = t * k;
   const int32_t* bb = bbase + (size_t)blockIdx.x * E;
-  for (int j = 0; j < k; ++j) {
-    const int e = it[j];
+  for (int q = threadIdx.x; q < np; q += kPT) {
+    const int e = ib[q];
     if (e < 0 || e >= E) continue;
-    int rank = 0;
-    const uint32_t* bits = s_bits + e * W;
-    for (int q = 0; q < (tl >> 5); ++q) rank += __popc(bits[q]);
-    rank += __popc(bits[tl >> 5] & ((1u << (tl & 31)) - 1u));
+    const int tl = q / k, j = q - tl * k;
+    const uint32_t lo = s_bits[2 * e], hi = s_bits[2 * e + 1];
+    const int rank = tl < 32 ? __popc(lo & ((1u << tl) - 1u)) : __popc(lo) + __popc(hi & ((1u << (tl - 32)) - 1u));
     const int row = bb[e] + rank;
+    const int t = t0 + tl;
     row_token[row] = t;
     row_w[row] = w[(size_t)t * k + j];
     row_pair[row] = t * k + j;
     // rows ascend with the expert id, so the token-major position is the number of this
     // token's experts with a smaller id
+    const int32_t* it = ib + (size_t)tl * k;
     int pos = 0;
-    for (int q = 0; q < k; ++q) pos += (it[q] < e);
+    for (int x = 0; x < k; ++x) pos += (it[x] < e);
     tok_rows[(size_t)t * k + pos] = row;
   }
 }
 
 size_t permute_ws_bytes(int N, int E) {
-  const size_t nb = ((size_t)N + kPT - 1) / kPT;
+  const size_t nb = ((size_t)N + kTB - 1) / kTB;
   return 2 * (((nb * E * 4) + 255) & ~(size_t)255) + 256;
 }
 
+// histogram over blocks of 256 tokens (the token-rounding plan's layout: bcnt[ceil(N/256)][E])
 hipError_t launch_perm_hist(const int32_t* idx, int N, int E, int k, int32_t* bcnt, hipStream_t s) {
-  const int nb = (N + kPT - 1) / kPT;
-  hipLaunchKernelGGL(k_perm_hist, dim3(nb), dim3(kPT), 0, s, idx, N, E, k, bcnt);
+  const int nb = (N + 255) / 256;
+  hipLaunchKernelGGL(k_perm_hist<256>, dim3(nb), dim3(kPT), 0, s, idx, N, E, k, bcnt);
   return hipGetLastError();
 }
 
 hipError_t launch_permute(const int32_t* idx, const float* w, int N, int E, int k, const moe_plan& p, void* ws,
                           hipStream_t s) {
-  const int nb = (N + kPT - 1) / kPT;
+  const int nb = (N + kTB - 1) / kTB;
   int32_t* bcnt = (int32_t*)ws;
   int32_t* bbase = (int32_t*)((char*)ws + ((((size_t)nb * E * 4) + 255) & ~(size_t)255));
   hipError_t err;
   if (nb > 0) {
-    if ((err = launch_perm_hist(idx, N, E, k, bcnt, s)) != hipSuccess) return err;
+    hipLaunchKernelGGL(k_perm_hist<kTB>, dim3(nb), dim3(kPT), 0, s, idx, N, E, k, bcnt);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, s, bcnt, nb, N, E, k, bbase, p.counts, p.offsets,
                      p.tok_ptr);

@@ -19,6 +19,7 @@ constexpr int kPerLane = kMaxE / 64;
 // the softmax over the chosen k (the full-E denominator cancels); probs is the full softmax.
 // tok_norm (optional) is the sum of the chosen probs, the normaliser token rounding uses.
 // ---------------------------------------------------------------------------------------
+template <int PL>  // experts per lane: E <= 64 * PL
 __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ logits,
                                                     const float* __restrict__ bias, int N, int E, int k,
                                                     int32_t* __restrict__ idx, float* __restrict__ w,
@@ -28,23 +29,23 @@ __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ lo
   const int t = blockIdx.x * 4 + wave;
   if (t >= N) return;  // whole wavefronts exit together; no block barrier below
   const float* lt = logits + (size_t)t * E;
-  float z[kPerLane];
+  // all loads first (clamped index, masked afterwards), so they are in flight together
+  float z[PL];
   uint32_t avail = 0;
 #pragma unroll
-  for (int q = 0; q < kPerLane; ++q) {
+  for (int q = 0; q < PL; ++q) {
     const int e = lane + 64 * q;
-    z[q] = 0.f;
-    if (e < E) {
-      z[q] = bias ? lt[e] + bias[e] : lt[e];
-      avail |= 1u << q;
-    }
+    const int ec = e < E ? e : 0;
+    z[q] = lt[ec];
+    if (bias) z[q] += bias[ec];
+    if (e < E) avail |= 1u << q;
   }
   float zmax = 0.f;
   for (int j = 0; j < k; ++j) {
     float bz = 0.f;
     int be = INT_MAX;
 #pragma unroll
-    for (int q = 0; q < kPerLane; ++q) {
+    for (int q = 0; q < PL; ++q) {
       if ((avail >> q) & 1u) {
         if (be == INT_MAX || z[q] > bz) {  // ascending q = ascending id: strict '>' keeps the lower id
           bz = z[q];
@@ -73,16 +74,19 @@ __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ lo
   for (int off = 32; off >= 1; off >>= 1) sk += __shfl_xor(sk, off);
   for (int j = lane; j < k; j += 64) w[(size_t)t * k + j] = expf(s_z[wave][j] - zmax) / sk;
   if (probs || tok_norm) {
+    float ez[PL];
     float sa = 0.f;
 #pragma unroll
-    for (int q = 0; q < kPerLane; ++q)
-      if (lane + 64 * q < E) sa += expf(z[q] - zmax);
+    for (int q = 0; q < PL; ++q) {
+      ez[q] = lane + 64 * q < E ? expf(z[q] - zmax) : 0.f;
+      sa += ez[q];
+    }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) sa += __shfl_xor(sa, off);
     if (probs) {
 #pragma unroll
-      for (int q = 0; q < kPerLane; ++q)
-        if (lane + 64 * q < E) probs[(size_t)t * E + lane + 64 * q] = expf(z[q] - zmax) / sa;
+      for (int q = 0; q < PL; ++q)
+        if (lane + 64 * q < E) probs[(size_t)t * E + lane + 64 * q] = ez[q] / sa;
     }
     if (tok_norm) {
       // sum of the chosen probabilities, in slot order, from the same fp32 values as probs
@@ -98,8 +102,12 @@ __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ lo
 hipError_t launch_route_topk(const float* logits, const float* bias, int N, int E, int k, int32_t* idx,
                              float* w, float* probs, float* tok_norm, hipStream_t s) {
   if (N == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_route_topk, dim3((N + 3) / 4), dim3(256), 0, s, logits, bias, N, E, k, idx, w, probs,
-                     tok_norm);
+  const dim3 g((N + 3) / 4), b(256);
+  if (E <= 64) hipLaunchKernelGGL(k_route_topk<1>, g, b, 0, s, logits, bias, N, E, k, idx, w, probs, tok_norm);
+  else if (E <= 128) hipLaunchKernelGGL(k_route_topk<2>, g, b, 0, s, logits, bias, N, E, k, idx, w, probs, tok_norm);
+  else if (E <= 256) hipLaunchKernelGGL(k_route_topk<4>, g, b, 0, s, logits, bias, N, E, k, idx, w, probs, tok_norm);
+  else if (E <= 512) hipLaunchKernelGGL(k_route_topk<8>, g, b, 0, s, logits, bias, N, E, k, idx, w, probs, tok_norm);
+  else hipLaunchKernelGGL(k_route_topk<16>, g, b, 0, s, logits, bias, N, E, k, idx, w, probs, tok_norm);
   return hipGetLastError();
 }
 
