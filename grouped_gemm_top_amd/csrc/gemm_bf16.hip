@@ -482,6 +482,15 @@ __device__ __forceinline__ void stage_write(char* st, const f32x4 (&blk)[8], int
     *reinterpret_cast<u32x2*>(st + c * 256 + pos * 16 + (g & 1) * 8) = v;
   }
 }
+// the same placement for a block already packed to bf16 pairs (blk[j] = columns 16j + 4(L>>4) + 0..3)
+__device__ __forceinline__ void stage_write_pk(char* st, const u32x2 (&blk)[8], int L) {
+  const int c = L & 15, g = L >> 4;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int pos = (2 * j + (g >> 1)) ^ c;
+    *reinterpret_cast<u32x2*>(st + c * 256 + pos * 16 + (g & 1) * 8) = blk[j];
+  }
+}
 // the 16 bytes (8 columns, chunk L & 15) of row 4p + (L >> 4) of the staged block
 __device__ __forceinline__ uint4 stage_read(const char* st, int p, int L) {
   const int row = 4 * p + (L >> 4), q = L & 15;
@@ -555,26 +564,32 @@ __device__ __forceinline__ void epilogue(const Args& a, const Tile& c, f32x4 (&a
     const rsrc_t rdh = gg::mkr_off(a.out0, rb * 2 * I * 2, (long long)c.mlen * 2 * I * 2);
     const rsrc_t rap = gg::mkr_off(a.out1, rb * I * 2, (long long)c.mlen * I * 2);
     const rsrc_t rw = gg::mkr_off(a.row_w, rb * 4, (long long)c.mlen * 4);
-    float dsum[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    const int c0 = c.nt * BN + wn * 128;  // first of this wavefront's 128 columns of I
+    // G and U of row block i, in the accumulator layout, packed two bf16 per register until
+    // used; the next block's loads are issued before this block's stores, so waiting for
+    // them never waits for the stores
+    u32x2 Gp[8], Up[8];
+    float wr;
+    auto load_gu = [&](int i) __attribute__((always_inline)) {
       const uint32_t m = (uint32_t)(16 * (4 * i + wm) + cl);
-      const float wr = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rw, m * 4u, 0, 0));
+      wr = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rw, m * 4u, 0, 0));
       const uint32_t hrow = m * (uint32_t)(2 * I) * 2u;
-      // G and U stay packed (two bf16 per register) until they are used
-      u32x2 Gp[8], Up[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int ii = c.nt * BN + wn * 128 + 16 * j + 4 * g;
+        const int ii = c0 + 16 * j + 4 * g;
         const bool iv = ii < I;
         Gp[j] = __builtin_amdgcn_raw_buffer_load_b64(rhc, iv ? hrow + (uint32_t)ii * 2u : OOB, 0, 0);
         Up[j] = __builtin_amdgcn_raw_buffer_load_b64(rhc, iv ? hrow + (uint32_t)(I + ii) * 2u : OOB, 0, 0);
       }
+    };
+    float dsum[4];
+    load_gu(0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      u32x2 dgp[8], dup[8], app[8];
       float ds = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int ii = c.nt * BN + wn * 128 + 16 * j + 4 * g;
-        const bool iv = ii < I;
         float dg[4], du[4], ap[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
@@ -591,13 +606,29 @@ __device__ __forceinline__ void epilogue(const Args& a, const Tile& c, f32x4 (&a
           du[v] = da * silu;
           ap[v] = wr * act;
         }
-        st4(rdh, iv ? hrow + (uint32_t)ii * 2u : OOB, dg[0], dg[1], dg[2], dg[3]);
-        st4(rdh, iv ? hrow + (uint32_t)(I + ii) * 2u : OOB, du[0], du[1], du[2], du[3]);
-        st4(rap, iv ? m * (uint32_t)I * 2u + (uint32_t)ii * 2u : OOB, ap[0], ap[1], ap[2], ap[3]);
+        dgp[j] = u32x2{pk2(dg[0], dg[1]), pk2(dg[2], dg[3])};
+        dup[j] = u32x2{pk2(du[0], du[1]), pk2(du[2], du[3])};
+        app[j] = u32x2{pk2(ap[0], ap[1]), pk2(ap[2], ap[3])};
       }
       ds += __shfl_xor(ds, 16);
       ds += __shfl_xor(ds, 32);
       dsum[i] = ds;
+      if (i < 3) load_gu(i + 1);
+      // dG, dU and A' of the block through the staging area: 16 lanes store 256 contiguous
+      // bytes of one row; rows >= mlen lie past the descriptors' ranges
+      const int q = L & 15, col = c0 + 8 * q;
+      const bool cv = col < I;
+#pragma unroll
+      for (int o = 0; o < 3; ++o) {
+        stage_write_pk(st, o == 0 ? dgp : (o == 1 ? dup : app), L);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint4 v = stage_read(st, p, L);
+          const uint32_t m = (uint32_t)(16 * (4 * i + wm) + 4 * p + (L >> 4));
+          if (o == 2) st16(rap, cv ? m * (uint32_t)I * 2u + (uint32_t)col * 2u : OOB, v);
+          else st16(rdh, cv ? m * (uint32_t)(2 * I) * 2u + (uint32_t)(o * I + col) * 2u : OOB, v);
+        }
+      }
     }
     // the two wavefronts of a row block hold the two column halves: wn 0 adds wn 1's half
     if (wn == 1 && L < 16) {
@@ -965,7 +996,7 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
       // the stage of step s is free once every wavefront has read its fragments; the loads
       // that refill it are issued only after the next step's barrier
       char* st = s_ring + (s & (NSTG - 1)) * STG + w * 4096;
-      if constexpr (KIND != DH) lds_barrier();
+      lds_barrier();
       epilogue<KIND>(a, Cc, acc, s_red, wm, wn, L, S.nMg, nTN, st);
       ++h0;
 #pragma unroll
