@@ -79,14 +79,23 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // A_KC / B_KC: operand is K-contiguous in memory; GA / GB: operand rows are gathered through
 // row_token; VK: the reduction runs over an expert's rows (varlen-K); ST: a lower bound on the
-// memory instructions one epilogue issues (used for the vmcnt immediates).
+// memory instructions one epilogue issues (used for the vmcnt immediates); MI: row blocks of 16
+// per wavefront, so an M-tile has 64 MI rows (varlen-M: 320, which makes a group of up to 320
+// rows a single M-tile; varlen-K: 256).
 template <int K> struct KT;
-template <> struct KT<GATEUP> { static constexpr bool A_KC = true, B_KC = true, VK = false, GA = true, GB = false; static constexpr int ST = 32; };
-template <> struct KT<DOWN> { static constexpr bool A_KC = true, B_KC = true, VK = false, GA = false, GB = false; static constexpr int ST = 16; };
-template <> struct KT<DH> { static constexpr bool A_KC = true, B_KC = false, VK = false, GA = true, GB = false; static constexpr int ST = 96; };
-template <> struct KT<DX> { static constexpr bool A_KC = true, B_KC = false, VK = false, GA = false, GB = false; static constexpr int ST = 16; };
-template <> struct KT<DWD> { static constexpr bool A_KC = false, B_KC = false, VK = true, GA = true, GB = false; static constexpr int ST = 16; };
-template <> struct KT<DW1> { static constexpr bool A_KC = false, B_KC = false, VK = true, GA = false, GB = true; static constexpr int ST = 16; };
+template <> struct KT<GATEUP> { static constexpr bool A_KC = true, B_KC = true, VK = false, GA = true, GB = false; static constexpr int ST = 32, MI = 5; };
+template <> struct KT<DOWN> { static constexpr bool A_KC = true, B_KC = true, VK = false, GA = false, GB = false; static constexpr int ST = 16, MI = 5; };
+template <> struct KT<DH> { static constexpr bool A_KC = true, B_KC = false, VK = false, GA = true, GB = false; static constexpr int ST = 96, MI = 4; };
+template <> struct KT<DX> { static constexpr bool A_KC = true, B_KC = false, VK = false, GA = false, GB = false; static constexpr int ST = 16, MI = 5; };
+template <> struct KT<DWD> { static constexpr bool A_KC = false, B_KC = false, VK = true, GA = true, GB = false; static constexpr int ST = 16, MI = 4; };
+template <> struct KT<DW1> { static constexpr bool A_KC = false, B_KC = false, VK = true, GA = false, GB = true; static constexpr int ST = 16, MI = 4; };
+
+// Per-kind tile geometry: BMK rows per M-tile; a stage holds OPA bytes of A (BMK rows of 64
+// bytes, or 32 k-rows of 512 bytes when A is K-strided) then OPB bytes of B; NA: A load
+// instructions per stage (16 rows of 64 bytes each).
+template <int KIND> struct Geo {
+  static constexpr int MI = KT<KIND>::MI, BMK = 64 * MI, OPA = BMK * 64, STGK = OPA + OPB, NA = BMK / 16;
+};
 
 // LDS loads.  They are written as inline assembly on purpose: the compiler then does not
 // track them as LDS writes and inserts no vmcnt waits of its own before LDS reads (it cannot
@@ -153,6 +162,24 @@ template <int N>
 __device__ __forceinline__ void vm_wait_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
+// The wait for step s of a wavefront that issues NLW loads per step: the memory instructions it
+// issued after step s's loads are the two later steps' loads, the token loads among them (ts,
+// varlen-M gathers) and the stores of the ne epilogues in between (at least ST each).
+// Rounding an allowance down only makes the wait stricter.
+template <int NLW, int ST>
+__device__ __forceinline__ void step_wait(int ne, int ts) {
+  constexpr int X0 = 2 * NLW;
+  constexpr int X1 = (X0 + ST) < 63 ? (X0 + ST) : 63;
+  constexpr int X2 = (X0 + 2 * ST) < 63 ? (X0 + 2 * ST) : 63;
+  constexpr int X3 = (X0 + 3 * ST) < 63 ? (X0 + 3 * ST) : 63;
+  if (ne == 0) {
+    if (ts == 0) vm_wait_barrier<X0>();
+    else if (ts == 1) vm_wait_barrier<X0 + 1>();
+    else vm_wait_barrier<X0 + 2>();
+  } else if (ne == 1) vm_wait_barrier<X1>();
+  else if (ne == 2) vm_wait_barrier<X2>();
+  else vm_wait_barrier<X3>();
+}
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 __device__ __forceinline__ void vm_drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -164,6 +191,7 @@ struct Tile {
 template <int KIND>
 struct Sched {
   using T = KT<KIND>;
+  static constexpr int BMK = Geo<KIND>::BMK;
   const int* s_sched;  // LDS: varlen-M tile prefix [E+1]; varlen-K expert order [E]
   const int* s_q;      // LDS: tile index of the workgroup's j-th tile at [j & (QN - 1)] (dynamic)
   int total, G, per, xcd, slot, E, nN, nMg, nM;
@@ -195,13 +223,13 @@ struct Sched {
       }
       const int e = ufl(lo);
       const int cnt = a.counts[e];
-      const int mtiles = (cnt + BM - 1) / BM;
+      const int mtiles = (cnt + BMK - 1) / BMK;
       const int local = tile - ufl(s_sched[e]);
       c.e = e;
       c.roff = a.offsets[e];
       c.nt = local / mtiles;
       c.mt = local - c.nt * mtiles;
-      c.mlen = min(BM, cnt - c.mt * BM);
+      c.mlen = min(BMK, cnt - c.mt * BMK);
       switch (KIND) {
         case GATEUP: case DH: c.K = a.H; break;
         case DOWN: c.K = a.I; break;
@@ -261,9 +289,9 @@ __device__ __forceinline__ int kc_swz(int r) {
 template <int KIND>
 struct Loader {
   using T = KT<KIND>;
+  using G = Geo<KIND>;
   i32x4 rA, rB, rB2;          // descriptors; rB2: the up-projection half (GATEUP rows, DX k-rows)
-  uint32_t vA[2], vB[2];      // this lane's byte offsets at k = 0 (OOB when masked)
-  uint32_t rowA[2], rowB[2];  // K-contiguous: row byte offsets (OOB when masked)
+  uint32_t vA[3], vB[2];      // this lane's byte offsets at k = 0 (OOB when masked)
   uint32_t colA[2], colB[2];  // K-strided: column byte offsets (OOB when masked)
   int kc_c;                   // k-chunk this lane loads (K-contiguous)
   int mn_k[2], mn_c[2];       // k-row and column chunk this lane loads (K-strided)
@@ -280,14 +308,19 @@ struct Loader {
   // per-tile state; tok = this wavefront's token slot of the tile's first step
   __device__ __forceinline__ void setup(const Args& a, const Tile& c, const int* tok, int w, int L, int nMg) {
     const int H = a.H, I = a.I;
+    uint32_t rowA[3], rowB[2];  // K-contiguous: row byte offsets (OOB when masked)
     const int kr[2] = {(2 * w) * 16 + (L >> 2), (2 * w + 1) * 16 + (L >> 2)};
-    const long long rb = (long long)c.roff + (long long)c.mt * BM;  // first row of an M-tile
+    const long long rb = (long long)c.roff + (long long)c.mt * G::BMK;  // first row of an M-tile
+    // K-contiguous A: instruction w + 8q (q < 3, while below NA) loads rows 16(w + 8q) + 0..15
+    int ka[3];
+#pragma unroll
+    for (int q = 0; q < 3; ++q) ka[q] = (w + 8 * q < G::NA) ? 16 * (w + 8 * q) + (L >> 2) : 1 << 30;
     if constexpr (KIND == GATEUP || KIND == DH) {
       rA = dmadesc(KIND == GATEUP ? a.x : a.dout, (long long)a.N * H * 2);
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
+      for (int q = 0; q < 3; ++q) {
         const int t = tok[(L >> 2) + 16 * q];
-        rowA[q] = (c.valid && kr[q] < c.mlen) ? (uint32_t)t * (uint32_t)H * 2u : OOB;
+        rowA[q] = (c.valid && ka[q] < c.mlen) ? (uint32_t)t * (uint32_t)H * 2u : OOB;
       }
     }
     if constexpr (KIND == GATEUP) {
@@ -307,8 +340,9 @@ struct Loader {
       rA = dmadesc_off(a.act, rb * I * 2, (long long)c.mlen * I * 2);
       rB = dmadesc_off(a.wd, (long long)c.e * H * I * 2, (long long)H * I * 2);
 #pragma unroll
+      for (int q = 0; q < 3; ++q) rowA[q] = (c.valid && ka[q] < c.mlen) ? (uint32_t)ka[q] * (uint32_t)I * 2u : OOB;
+#pragma unroll
       for (int q = 0; q < 2; ++q) {
-        rowA[q] = (c.valid && kr[q] < c.mlen) ? (uint32_t)kr[q] * (uint32_t)I * 2u : OOB;
         const int n = c.nt * BN + kr[q];
         rowB[q] = (c.valid && n < H) ? (uint32_t)n * (uint32_t)I * 2u : OOB;
       }
@@ -325,8 +359,10 @@ struct Loader {
       rB = dmadesc_off(a.wg, es, (long long)I * H * 2);
       rB2 = dmadesc_off(a.wu, es, (long long)I * H * 2);
 #pragma unroll
+      for (int q = 0; q < 3; ++q)
+        rowA[q] = (c.valid && ka[q] < c.mlen) ? (uint32_t)ka[q] * (uint32_t)(2 * I) * 2u : OOB;
+#pragma unroll
       for (int q = 0; q < 2; ++q) {
-        rowA[q] = (c.valid && kr[q] < c.mlen) ? (uint32_t)kr[q] * (uint32_t)(2 * I) * 2u : OOB;
         const int col = c.nt * BN + 8 * mn_c[q];
         colB[q] = (c.valid && col < H) ? (uint32_t)col * 2u : OOB;
       }
@@ -355,8 +391,10 @@ struct Loader {
     }
     // offsets at k = 0 for the steps without a K tail (OOB stays OOB: no 32-bit wrap)
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < 3; ++q)
       if constexpr (T::A_KC) vA[q] = rowA[q] + 16u * (uint32_t)kc_c;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
       if constexpr (T::B_KC) vB[q] = rowB[q] + 16u * (uint32_t)kc_c;
       if constexpr (KIND == DH) vB[q] = colB[q] + (uint32_t)mn_k[q] * (uint32_t)I * 2u;
       if constexpr (KIND == DX) vB[q] = colB[q] + (uint32_t)mn_k[q] * (uint32_t)H * 2u;
@@ -368,14 +406,16 @@ struct Loader {
     if constexpr (KIND == GATEUP || KIND == DX) rB2 = sgpr4(rB2);
   }
 
-  // The four operand loads of step c.kt.  mA: LDS address of this wavefront's A kilobyte in
-  // the step's stage (B: + OPB).  tok: the step's token slot (varlen-K gathers).
+  // The operand loads of step c.kt.  mS: LDS address of the step's stage; this wavefront's
+  // kilobytes are A: (w + 8q) (K-contiguous) or 2w, 2w+1 (K-strided), B: OPA + 2w, 2w+1.
+  // tok: the step's token slot (varlen-K gathers).
   // A step without a K tail adds the k advance as the uniform offset; the last step of a tile
   // whose K is not a multiple of 32 builds every lane's offset and masks k >= K.
-  __device__ __forceinline__ void issue(const Args& a, const Tile& c, uint32_t mA, const int* tok, int w, int L) {
+  __device__ __forceinline__ void issue(const Args& a, const Tile& c, uint32_t mS, const int* tok, int w, int L) {
     const int H = a.H, I = a.I;
     const int k0 = c.kt * BK;
-    const uint32_t mB = mA + OPB;
+    const uint32_t mA = mS + (uint32_t)(2 * w) * 1024u;
+    const uint32_t mB = mS + (uint32_t)G::OPA + (uint32_t)(2 * w) * 1024u;
     // the uniform advance is only used where it is non-negative and keeps every lane inside
     // its row: no K tail, and (dX) no stage that straddles the gate / up boundary at k = I
     bool fast = k0 + BK <= c.K;
@@ -383,8 +423,9 @@ struct Loader {
     if (fast) {
       if constexpr (T::A_KC) {
         const uint32_t so = (uint32_t)k0 * 2u;
-        dma16(rA, mA, vA[0], so);
-        dma16(rA, mA + 1024, vA[1], so);
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+          if (w + 8 * q < G::NA) dma16(rA, mS + (uint32_t)(w + 8 * q) * 1024u, vA[q], so);
         if constexpr (T::B_KC) {
           dma16(rB, mB, vB[0], so);
           dma16(KIND == GATEUP ? rB2 : rB, mB + 1024, vB[1], so);
@@ -425,10 +466,11 @@ struct Loader {
       const int kk = k0 + 8 * kc_c;
       const bool kv = kk < c.K;
 #pragma unroll
-      for (int q = 0; q < 2; ++q) dma16(rA, mA + q * 1024, kv ? rowA[q] + (uint32_t)kk * 2u : OOB, 0u);
+      for (int q = 0; q < 3; ++q)
+        if (w + 8 * q < G::NA) dma16(rA, mS + (uint32_t)(w + 8 * q) * 1024u, kv ? vA[q] + (uint32_t)k0 * 2u : OOB, 0u);
       if constexpr (T::B_KC) {
-        dma16(rB, mB, kv ? rowB[0] + (uint32_t)kk * 2u : OOB, 0u);
-        dma16(KIND == GATEUP ? rB2 : rB, mB + 1024, kv ? rowB[1] + (uint32_t)kk * 2u : OOB, 0u);
+        dma16(rB, mB, kv ? vB[0] + (uint32_t)k0 * 2u : OOB, 0u);
+        dma16(KIND == GATEUP ? rB2 : rB, mB + 1024, kv ? vB[1] + (uint32_t)k0 * 2u : OOB, 0u);
       }
     }
     if constexpr (KIND == DH) {
@@ -503,7 +545,7 @@ __device__ __forceinline__ void st16(rsrc_t r, uint32_t off, const uint4& v) {
 // acc[i][j][v] = C[m = 16(4i + wm) + (L & 15)][n = wn*128 + 16j + 4(L >> 4) + v]
 // `st`: this wavefront's 4 KB of LDS staging, free for the duration of the epilogue.
 template <int KIND>
-__device__ __forceinline__ void epilogue(const Args& a, const Tile& c, f32x4 (&acc)[4][8], float* s_red, int wm,
+__device__ __forceinline__ void epilogue(const Args& a, const Tile& c, f32x4 (&acc)[KT<KIND>::MI][8], float* s_red, int wm,
                                          int wn, int L_, int nMg, int nTN, char* st) {
   // The lane's address arithmetic depends only on kernel constants; an opaque copy of the lane
   // index keeps the compiler from computing it once for the whole kernel and holding the
@@ -511,14 +553,15 @@ __device__ __forceinline__ void epilogue(const Args& a, const Tile& c, f32x4 (&a
   int L = L_;
   asm volatile("" : "+v"(L));
   const int H = a.H, I = a.I;
+  constexpr int MI = KT<KIND>::MI;
   const int cl = L & 15, g = L >> 4;
-  const long long rb = (long long)c.roff + (long long)c.mt * BM;
+  const long long rb = (long long)c.roff + (long long)c.mt * Geo<KIND>::BMK;
   if constexpr (KIND == GATEUP) {
     const rsrc_t rh = gg::mkr_off(a.out0, rb * 2 * I * 2, (long long)c.mlen * 2 * I * 2);
     const rsrc_t ra = gg::mkr_off(a.out1, rb * I * 2, (long long)c.mlen * I * 2);
     const int i0 = c.nt * 128 + wn * 64;  // first i of this wavefront's 64 gate and 64 up columns
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < MI; ++i) {
       // [G | U] block: staged columns 0..63 gate, 64..127 up, for i0 .. i0 + 63
       stage_write(st, acc[i], L);
 #pragma unroll
@@ -549,7 +592,7 @@ __device__ __forceinline__ void epilogue(const Args& a, const Tile& c, f32x4 (&a
   } else if constexpr (KIND == DOWN || KIND == DX) {
     const rsrc_t ro = gg::mkr_off(a.out0, rb * H * 2, (long long)c.mlen * H * 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < MI; ++i) {
       stage_write(st, acc[i], L);
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
@@ -582,10 +625,10 @@ __device__ __forceinline__ void epilogue(const Args& a, const Tile& c, f32x4 (&a
         Up[j] = __builtin_amdgcn_raw_buffer_load_b64(rhc, iv ? hrow + (uint32_t)(I + ii) * 2u : OOB, 0, 0);
       }
     };
-    float dsum[4];
+    float dsum[MI];
     load_gu(0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < MI; ++i) {
       u32x2 dgp[8], dup[8], app[8];
       float ds = 0.f;
 #pragma unroll
@@ -613,7 +656,7 @@ __device__ __forceinline__ void epilogue(const Args& a, const Tile& c, f32x4 (&a
       ds += __shfl_xor(ds, 16);
       ds += __shfl_xor(ds, 32);
       dsum[i] = ds;
-      if (i < 3) load_gu(i + 1);
+      if (i < MI - 1) load_gu(i + 1);
       // dG, dU and A' of the block through the staging area: 16 lanes store 256 contiguous
       // bytes of one row; rows >= mlen lie past the descriptors' ranges
       const int q = L & 15, col = c0 + 8 * q;
@@ -633,12 +676,12 @@ __device__ __forceinline__ void epilogue(const Args& a, const Tile& c, f32x4 (&a
     // the two wavefronts of a row block hold the two column halves: wn 0 adds wn 1's half
     if (wn == 1 && L < 16) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s_red[16 * (4 * i + wm) + L] = dsum[i];
+      for (int i = 0; i < MI; ++i) s_red[16 * (4 * i + wm) + L] = dsum[i];
     }
     lds_barrier();
     if (wn == 0 && L < 16) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < MI; ++i) {
         const int m = 16 * (4 * i + wm) + L;
         if (m < c.mlen) a.dspart[(size_t)(rb + m) * nTN + c.nt] = dsum[i] + s_red[m];
       }
@@ -646,7 +689,7 @@ __device__ __forceinline__ void epilogue(const Args& a, const Tile& c, f32x4 (&a
   } else if constexpr (KIND == DWD) {
     const rsrc_t ro = gg::mkr_off(a.out0, (long long)c.e * H * I * 2, (long long)H * I * 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < MI; ++i) {
       stage_write(st, acc[i], L);
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
@@ -661,7 +704,7 @@ __device__ __forceinline__ void epilogue(const Args& a, const Tile& c, f32x4 (&a
     const int m0 = (c.mt - seg * nMg) * BM;
     const rsrc_t ro = gg::mkr_off(seg ? a.out1 : a.out0, (long long)c.e * I * H * 2, (long long)I * H * 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < MI; ++i) {
       stage_write(st, acc[i], L);
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
@@ -697,18 +740,19 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
   a.counts = counts;
   a.offsets = offsets;
   using T = KT<KIND>;
+  using G = Geo<KIND>;
   constexpr bool GATHER = T::GA || T::GB;
-  // memory instructions per step and wavefront: 4 operand loads, plus the token load that
-  // varlen-K kinds issue every step (varlen-M kinds issue theirs only at tile starts and count
-  // them separately)
+  // memory instructions per step and wavefront: 4 operand loads (plus one more A load on
+  // wavefronts w < NA - 16), plus the token load that varlen-K kinds issue every step
+  // (varlen-M kinds issue theirs only at tile starts and count them separately)
   constexpr int NLW = 4 + (T::VK && GATHER ? 1 : 0);
 
-  __shared__ __attribute__((aligned(1024))) char s_ring[NSTG * STG];
+  __shared__ __attribute__((aligned(1024))) char s_ring[NSTG * G::STGK];
   __shared__ __attribute__((aligned(256))) int s_tok[8 * NSTG * (TOKB / 4)];
   __shared__ int s_sched[1025];
   __shared__ int s_q[QN];
   __shared__ int s_wsum[9];
-  __shared__ float s_red[BM];
+  __shared__ float s_red[G::BMK];
 
   const int tid = threadIdx.x, L = tid & 63;
   const int w = ufl(tid >> 6);
@@ -739,7 +783,7 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int e = tid * 2 + q;
-      loc[q] = e < E ? ((a.counts[e] + BM - 1) / BM) * S.nN : 0;
+      loc[q] = e < E ? ((a.counts[e] + G::BMK - 1) / G::BMK) * S.nN : 0;
       sum += loc[q];
     }
     int x = sum;
@@ -794,9 +838,9 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
     S.total = E * S.nM * S.nN;
   }
 
-  f32x4 acc[4][8];
+  f32x4 acc[G::MI][8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < G::MI; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -823,7 +867,7 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
   const i32x4 rtok = dmadesc(a.row_token, 4LL * (long long)a.M_cap);
   int* my_tok = s_tok + w * NSTG * (TOKB / 4);  // this wavefront's token ring
   const uint32_t tok_m0 = lds_addr(my_tok);
-  const uint32_t ring_m0 = lds_addr(s_ring) + (uint32_t)(2 * w) * 1024u;  // this wavefront's A kilobyte, stage 0
+  const uint32_t ring_m0 = lds_addr(s_ring);  // stage 0
 
   // token load for cursor t at step index s: per step (varlen-K), or at a tile's first step
   // (varlen-M, which then returns 1: the number of loads it issued)
@@ -834,7 +878,9 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
       return 1;
     } else {
       if (t.valid && t.kt == 0) {
-        dma4(rtok, m0, (uint32_t)(t.roff + t.mt * BM + 32 * w + L) * 4u);
+        // lane L: the token of row 16w + (L & 15) + 128 (L >> 4), i.e. of A instruction
+        // w + 8 (L >> 4) (rows past the tile's instructions are never used)
+        dma4(rtok, m0, (uint32_t)(t.roff + t.mt * G::BMK + 16 * w + (L & 15) + 128 * (L >> 4)) * 4u);
         return 1;
       }
       return 0;
@@ -844,7 +890,7 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
   auto load_issue = [&](int s) __attribute__((always_inline)) {
     const int* tk = my_tok + (s & (NSTG - 1)) * (TOKB / 4);
     if (Ld.kt == 0) ld.setup(a, Ld, tk, w, L, S.nMg);
-    ld.issue(a, Ld, ring_m0 + (uint32_t)(s & (NSTG - 1)) * STG, tk, w, L);
+    ld.issue(a, Ld, ring_m0 + (uint32_t)(s & (NSTG - 1)) * G::STGK, tk, w, L);
     S.next(a, Ld, true);
   };
   // Dynamic schedule: when the leading cursor (Tk for gathered kinds, else Ld) starts the tile
@@ -900,32 +946,20 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
   }
 
   // epilogues issued after the loads of the last three steps (their stores are younger)
-  // The wait for step s allows the memory instructions issued after step s's loads: the two
-  // later steps' loads (4 each, plus a token load where one was issued) and the stores of any
-  // epilogue since.  Rounding an allowance down only makes the wait stricter.
   int h0 = 0, h1 = 0, h2 = 0;
-  constexpr int X0 = 2 * NLW;  // varlen-K: the token loads are part of NLW
-  constexpr int X1 = (X0 + T::ST) < 63 ? (X0 + T::ST) : 63;
-  constexpr int X2 = (X0 + 2 * T::ST) < 63 ? (X0 + 2 * T::ST) : 63;
-  constexpr int X3 = (X0 + 3 * T::ST) < 63 ? (X0 + 3 * T::ST) : 63;
 
 #pragma unroll 1
   for (int s = 0;; ++s) {
     // step s's loads (issued three steps ago) have landed for every wavefront, and every
     // wavefront is done with the stage that the loads below overwrite
     const int ne = h0 + h1 + h2;
-    if (ne == 0) {
-      if constexpr (T::GA && !T::VK) {
-        const int ts = t1 + t2;
-        if (ts == 0) vm_wait_barrier<8>();
-        else if (ts == 1) vm_wait_barrier<9>();
-        else vm_wait_barrier<10>();
-      } else {
-        vm_wait_barrier<X0>();
-      }
-    } else if (ne == 1) vm_wait_barrier<X1>();
-    else if (ne == 2) vm_wait_barrier<X2>();
-    else vm_wait_barrier<X3>();
+    const int ts = (T::GA && !T::VK) ? t1 + t2 : 0;  // varlen-K: the token loads are part of NLW
+    if constexpr (G::NA > 16) {
+      if (w < G::NA - 16) step_wait<NLW + 1, T::ST>(ne, ts);
+      else step_wait<NLW, T::ST>(ne, ts);
+    } else {
+      step_wait<NLW, T::ST>(ne, ts);
+    }
     h2 = h1;
     h1 = h0;
     h0 = 0;
@@ -950,27 +984,50 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
     // mlen; a short tile's blocks are spread over all four SIMDs
     if (Cc.mlen > 16 * wm) {
       const int nb = Cc.mlen - 16 * wm;
-      const char* sa = s_ring + (s & (NSTG - 1)) * STG;
-      const char* sb = sa + OPB;
-      bf16x8 fb[8];
+      // opaque copies: the per-fragment LDS positions derived from these are recomputed each
+      // step rather than held in registers across the loop
+      int kco = kc_off, k0o = mn_k0, ffo = mn_ff, bo = mn_b;
+      asm volatile("" : "+v"(kco), "+v"(k0o), "+v"(ffo), "+v"(bo));
+      const char* sa = s_ring + (s & (NSTG - 1)) * G::STGK;
+      const char* sb = sa + G::OPA;
+      auto frag_a = [&](int i) __attribute__((always_inline)) {
+        if constexpr (T::A_KC) return frag_kc(sa, 16 * (4 * i + wm), kco);
+        else return frag_mn(sa, 16 * (4 * i + wm), k0o, ffo, bo);
+      };
+      auto frag_b = [&](int j) __attribute__((always_inline)) {
+        if constexpr (T::B_KC) return frag_kc(sb, wn * 128 + 16 * j, kco);
+        else return frag_mn(sb, wn * 128 + 16 * j, k0o, ffo, bo);
+      };
+      // a row block at or past mlen skips its MFMAs (its fragment holds rows of no group)
+      if constexpr (G::MI == 4) {
+        // every fragment read first, then the MFMAs
+        bf16x8 fa[4], fb[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if constexpr (T::B_KC) fb[j] = frag_kc(sb, wn * 128 + 16 * j, kc_off);
-        else fb[j] = frag_mn(sb, wn * 128 + 16 * j, mn_k0, mn_ff, mn_b);
-      }
-      // every fragment read is issued before the MFMAs; a row block at or past mlen skips
-      // its MFMAs (its fragment holds rows of no group, never used)
-      bf16x8 fa[4];
+        for (int j = 0; j < 8; ++j) fb[j] = frag_b(j);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if constexpr (T::A_KC) fa[i] = frag_kc(sa, 16 * (4 * i + wm), kc_off);
-        else fa[i] = frag_mn(sa, 16 * (4 * i + wm), mn_k0, mn_ff, mn_b);
-      }
+        for (int i = 0; i < 4; ++i) fa[i] = frag_a(i);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (i == 0 || nb > 64 * i) {
+        for (int i = 0; i < 4; ++i)
+          if (i == 0 || nb > 64 * i) {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) acc[i][j] = mma(fb[j], fa[i], acc[i][j]);
+            for (int j = 0; j < 8; ++j) acc[i][j] = mma(fb[j], fa[i], acc[i][j]);
+          }
+      } else {
+        // all B fragments first, then the A fragments one row block ahead: block i + 1's read
+        // is in flight during block i's MFMAs
+        bf16x8 fb[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) fb[j] = frag_b(j);
+        bf16x8 fa = frag_a(0);
+#pragma unroll
+        for (int i = 0; i < G::MI; ++i) {
+          bf16x8 fn;
+          if (i + 1 < G::MI) fn = frag_a(i + 1);
+          if (i == 0 || nb > 64 * i) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[i][j] = mma(fb[j], fa, acc[i][j]);
+          }
+          if (i + 1 < G::MI) fa = fn;
         }
       }
     }
@@ -995,12 +1052,12 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
     } else {
       // the stage of step s is free once every wavefront has read its fragments; the loads
       // that refill it are issued only after the next step's barrier
-      char* st = s_ring + (s & (NSTG - 1)) * STG + w * 4096;
+      char* st = s_ring + (s & (NSTG - 1)) * G::STGK + w * 4096;
       lds_barrier();
       epilogue<KIND>(a, Cc, acc, s_red, wm, wn, L, S.nMg, nTN, st);
       ++h0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < G::MI; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
       S.decode(a, Cc, Cc.it + 1);
