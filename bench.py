@@ -29,7 +29,7 @@ PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 2.4 GHz x 4096 FLOP/clk (dense)
 PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 GEMMS = ("gateup", "down", "dh", "dx", "dwd", "dw1")
-ALL_KERNELS = ("route", "permute", "route_tr_plan", "gateup", "down", "combine", "dh", "ds_reduce", "dwd", "dx",
+ALL_KERNELS = ("route", "permute", "route_tr_plan", "gateup", "down", "combine", "dh", "dswiglu", "dwd", "dx",
                "dx_combine", "dw1")
 
 
@@ -43,7 +43,11 @@ def kernel_work(name, wl, M, e_act, es):
     if name == "down":
         return 2.0 * M * H * I, es * (1.0 * e_act * H * I + M * I + M * H)
     if name == "dh":
+        if es == 2:  # bf16: the dA' GEMM writes fp32 dA'; the dSwiGLU kernel does the rest
+            return 2.0 * M * H * I, es * (1.0 * e_act * H * I + N * H) + 4.0 * M * I
         return 2.0 * M * H * I, es * (1.0 * e_act * H * I + N * H + 5.0 * M * I) + 4.0 * M * ((I + 127) // 128)
+    if name == "dswiglu" and es == 2:  # reads dA' (fp32), G, U, w; writes dG, dU, A', dS
+        return 0.0, 4.0 * M * I + es * 5.0 * M * I + 8.0 * M
     if name == "dx":
         return 4.0 * M * H * I, es * (2.0 * e_act * I * H + 2.0 * M * I + M * H)
     if name == "dwd":
@@ -237,7 +241,7 @@ def main():
         res["gemm_pct_peak"] = round(100.0 * res["gemm_tflops"] / peak, 2)
         res["fwd_ms"] = round(sum(kern_ms.get(n, 0.0) for n in ("route", "permute", "route_tr_plan", "gateup",
                                                                   "down", "combine")), 4)
-        res["bwd_ms"] = round(sum(kern_ms.get(n, 0.0) for n in ("dh", "ds_reduce", "dwd", "dx", "dx_combine",
+        res["bwd_ms"] = round(sum(kern_ms.get(n, 0.0) for n in ("dh", "dswiglu", "dwd", "dx", "dx_combine",
                                                                   "dw1")), 4)
         kinfo = {}
         for n in names:

@@ -31,7 +31,7 @@ EXPORTED_SYMBOLS = (
 
 # kernel ids of the measurement hook (moe_kernel_id in include/moe.h)
 KERNEL_IDS = {"gateup": 0, "down": 1, "dh": 2, "dx": 3, "dwd": 4, "dw1": 5, "combine": 6, "dx_combine": 7,
-              "route": 8, "permute": 9, "route_tr_plan": 10, "ds_reduce": 11}
+              "route": 8, "permute": 9, "route_tr_plan": 10, "dswiglu": 11}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None

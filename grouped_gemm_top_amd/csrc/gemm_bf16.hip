@@ -66,7 +66,6 @@ constexpr int BM = 256, BN = 256, BK = 32;
 constexpr int NSTG = 4;        // LDS ring depth (stages)
 constexpr int AHEAD = NSTG - 1;
 constexpr int OPB = 16384;     // bytes of one operand per stage
-constexpr int STG = 2 * OPB;   // bytes per stage
 constexpr int TOKB = 256;      // bytes per token slot (64 row indices)
 constexpr int QN = 16;         // ring of dynamically assigned tile indices (a power of two)
 
@@ -85,7 +84,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 template <int K> struct KT;
 template <> struct KT<GATEUP> { static constexpr bool A_KC = true, B_KC = true, VK = false, GA = true, GB = false; static constexpr int ST = 32, MI = 5; };
 template <> struct KT<DOWN> { static constexpr bool A_KC = true, B_KC = true, VK = false, GA = false, GB = false; static constexpr int ST = 16, MI = 5; };
-template <> struct KT<DH> { static constexpr bool A_KC = true, B_KC = false, VK = false, GA = true, GB = false; static constexpr int ST = 96, MI = 4; };
+template <> struct KT<DH> { static constexpr bool A_KC = true, B_KC = false, VK = false, GA = true, GB = false; static constexpr int ST = 40, MI = 5; };
 template <> struct KT<DX> { static constexpr bool A_KC = true, B_KC = false, VK = false, GA = false, GB = false; static constexpr int ST = 16, MI = 5; };
 template <> struct KT<DWD> { static constexpr bool A_KC = false, B_KC = false, VK = true, GA = true, GB = false; static constexpr int ST = 16, MI = 4; };
 template <> struct KT<DW1> { static constexpr bool A_KC = false, B_KC = false, VK = true, GA = false, GB = true; static constexpr int ST = 16, MI = 4; };
@@ -533,6 +532,16 @@ __device__ __forceinline__ void stage_write_pk(char* st, const u32x2 (&blk)[8], 
     *reinterpret_cast<u32x2*>(st + c * 256 + pos * 16 + (g & 1) * 8) = blk[j];
   }
 }
+// fp32 columns 64h .. 64h+63 of a 16-row block (blk[4h .. 4h+3]) as rows of 256 bytes, 16-byte
+// chunk q (columns 4q .. 4q+3 of the half) of row r at position q ^ r; read back with stage_read
+__device__ __forceinline__ void stage_write_f32(char* st, const f32x4 (&blk)[8], int h, int L) {
+  const int c = L & 15, g = L >> 4;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int pos = (4 * jj + g) ^ c;
+    *reinterpret_cast<f32x4*>(st + c * 256 + pos * 16) = blk[4 * h + jj];
+  }
+}
 // the 16 bytes (8 columns, chunk L & 15) of row 4p + (L >> 4) of the staged block
 __device__ __forceinline__ uint4 stage_read(const char* st, int p, int L) {
   const int row = 4 * p + (L >> 4), q = L & 15;
@@ -545,8 +554,8 @@ __device__ __forceinline__ void st16(rsrc_t r, uint32_t off, const uint4& v) {
 // acc[i][j][v] = C[m = 16(4i + wm) + (L & 15)][n = wn*128 + 16j + 4(L >> 4) + v]
 // `st`: this wavefront's 4 KB of LDS staging, free for the duration of the epilogue.
 template <int KIND>
-__device__ __forceinline__ void epilogue(const Args& a, const Tile& c, f32x4 (&acc)[KT<KIND>::MI][8], float* s_red, int wm,
-                                         int wn, int L_, int nMg, int nTN, char* st) {
+__device__ __forceinline__ void epilogue(const Args& a, const Tile& c, f32x4 (&acc)[KT<KIND>::MI][8], int wm, int wn,
+                                         int L_, int nMg, char* st) {
   // The lane's address arithmetic depends only on kernel constants; an opaque copy of the lane
   // index keeps the compiler from computing it once for the whole kernel and holding the
   // results in registers across the k-loop (where they would push the MFMA loop into spills).
@@ -554,7 +563,6 @@ __device__ __forceinline__ void epilogue(const Args& a, const Tile& c, f32x4 (&a
   asm volatile("" : "+v"(L));
   const int H = a.H, I = a.I;
   constexpr int MI = KT<KIND>::MI;
-  const int cl = L & 15, g = L >> 4;
   const long long rb = (long long)c.roff + (long long)c.mt * Geo<KIND>::BMK;
   if constexpr (KIND == GATEUP) {
     const rsrc_t rh = gg::mkr_off(a.out0, rb * 2 * I * 2, (long long)c.mlen * 2 * I * 2);
@@ -603,87 +611,23 @@ __device__ __forceinline__ void epilogue(const Args& a, const Tile& c, f32x4 (&a
       }
     }
   } else if constexpr (KIND == DH) {
-    const rsrc_t rhc = gg::mkr_off(a.hcache, rb * 2 * I * 2, (long long)c.mlen * 2 * I * 2);
-    const rsrc_t rdh = gg::mkr_off(a.out0, rb * 2 * I * 2, (long long)c.mlen * 2 * I * 2);
-    const rsrc_t rap = gg::mkr_off(a.out1, rb * I * 2, (long long)c.mlen * I * 2);
-    const rsrc_t rw = gg::mkr_off(a.row_w, rb * 4, (long long)c.mlen * 4);
-    const int c0 = c.nt * BN + wn * 128;  // first of this wavefront's 128 columns of I
-    // G and U of row block i, in the accumulator layout, packed two bf16 per register until
-    // used; the next block's loads are issued before this block's stores, so waiting for
-    // them never waits for the stores
-    u32x2 Gp[8], Up[8];
-    float wr;
-    auto load_gu = [&](int i) __attribute__((always_inline)) {
-      const uint32_t m = (uint32_t)(16 * (4 * i + wm) + cl);
-      wr = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rw, m * 4u, 0, 0));
-      const uint32_t hrow = m * (uint32_t)(2 * I) * 2u;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int ii = c0 + 16 * j + 4 * g;
-        const bool iv = ii < I;
-        Gp[j] = __builtin_amdgcn_raw_buffer_load_b64(rhc, iv ? hrow + (uint32_t)ii * 2u : OOB, 0, 0);
-        Up[j] = __builtin_amdgcn_raw_buffer_load_b64(rhc, iv ? hrow + (uint32_t)(I + ii) * 2u : OOB, 0, 0);
-      }
-    };
-    float dsum[MI];
-    load_gu(0);
+    // dA' in fp32 for the dSwiGLU kernel that follows; each block goes through the staging
+    // area in two halves of 64 columns: 16 lanes store 256 contiguous bytes of one row, rows
+    // >= mlen lie past the descriptor's range
+    const rsrc_t ro = gg::mkr_off(a.out0, rb * I * 4, (long long)c.mlen * I * 4);
+    const int c0 = c.nt * BN + wn * 128;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
-      u32x2 dgp[8], dup[8], app[8];
-      float ds = 0.f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float dg[4], du[4], ap[4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const uint32_t gw = Gp[j][v >> 1], uw = Up[j][v >> 1];
-          const float gg_ = __uint_as_float((v & 1) ? (gw & 0xFFFF0000u) : (gw << 16));
-          const float u = __uint_as_float((v & 1) ? (uw & 0xFFFF0000u) : (uw << 16));
-          const float sg = sigm(gg_);
-          const float silu = gg_ * sg;
-          const float act = silu * u;
-          const float dap = acc[i][j][v];
-          ds += dap * act;
-          const float da = wr * dap;
-          dg[v] = da * u * sg * (1.0f + gg_ * (1.0f - sg));
-          du[v] = da * silu;
-          ap[v] = wr * act;
-        }
-        dgp[j] = u32x2{pk2(dg[0], dg[1]), pk2(dg[2], dg[3])};
-        dup[j] = u32x2{pk2(du[0], du[1]), pk2(du[2], du[3])};
-        app[j] = u32x2{pk2(ap[0], ap[1]), pk2(ap[2], ap[3])};
-      }
-      ds += __shfl_xor(ds, 16);
-      ds += __shfl_xor(ds, 32);
-      dsum[i] = ds;
-      if (i < MI - 1) load_gu(i + 1);
-      // dG, dU and A' of the block through the staging area: 16 lanes store 256 contiguous
-      // bytes of one row; rows >= mlen lie past the descriptors' ranges
-      const int q = L & 15, col = c0 + 8 * q;
-      const bool cv = col < I;
-#pragma unroll
-      for (int o = 0; o < 3; ++o) {
-        stage_write_pk(st, o == 0 ? dgp : (o == 1 ? dup : app), L);
+      for (int h = 0; h < 2; ++h) {
+        stage_write_f32(st, acc[i], h, L);
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           const uint4 v = stage_read(st, p, L);
           const uint32_t m = (uint32_t)(16 * (4 * i + wm) + 4 * p + (L >> 4));
-          if (o == 2) st16(rap, cv ? m * (uint32_t)I * 2u + (uint32_t)col * 2u : OOB, v);
-          else st16(rdh, cv ? m * (uint32_t)(2 * I) * 2u + (uint32_t)(o * I + col) * 2u : OOB, v);
+          const int col = c0 + 64 * h + 4 * (L & 15);
+          st16(ro, col < I ? m * (uint32_t)I * 4u + (uint32_t)col * 4u : OOB, v);
         }
-      }
-    }
-    // the two wavefronts of a row block hold the two column halves: wn 0 adds wn 1's half
-    if (wn == 1 && L < 16) {
-#pragma unroll
-      for (int i = 0; i < MI; ++i) s_red[16 * (4 * i + wm) + L] = dsum[i];
-    }
-    lds_barrier();
-    if (wn == 0 && L < 16) {
-#pragma unroll
-      for (int i = 0; i < MI; ++i) {
-        const int m = 16 * (4 * i + wm) + L;
-        if (m < c.mlen) a.dspart[(size_t)(rb + m) * nTN + c.nt] = dsum[i] + s_red[m];
       }
     }
   } else if constexpr (KIND == DWD) {
@@ -752,7 +696,6 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
   __shared__ int s_sched[1025];
   __shared__ int s_q[QN];
   __shared__ int s_wsum[9];
-  __shared__ float s_red[G::BMK];
 
   const int tid = threadIdx.x, L = tid & 63;
   const int w = ufl(tid >> 6);
@@ -775,7 +718,6 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
   }
   S.nMg = (a.I + BM - 1) / BM;
   S.nM = KIND == DWD ? (a.H + BM - 1) / BM : 2 * S.nMg;
-  const int nTN = (a.I + BN - 1) / BN;
 
   // ---- tile list from the device-resident counts ----
   if constexpr (!T::VK) {
@@ -849,7 +791,7 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
   S.decode(a, Cc, 0);
   if constexpr (T::VK) {
     while (Cc.valid && Cc.nk == 0) {
-      epilogue<KIND>(a, Cc, acc, s_red, wm, wn, L, S.nMg, nTN, s_ring + w * 4096);
+      epilogue<KIND>(a, Cc, acc, wm, wn, L, S.nMg, s_ring + w * 4096);
       S.decode(a, Cc, Cc.it + 1);
     }
   }
@@ -1012,6 +954,22 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
 #pragma unroll
             for (int j = 0; j < 8; ++j) acc[i][j] = mma(fb[j], fa[i], acc[i][j]);
           }
+      } else if constexpr (KIND == DH) {
+        // (fewer live fragments, for the register budget of the dSwiGLU epilogue) all A
+        // fragments first, then the B fragments one column block ahead
+        bf16x8 fa[G::MI];
+#pragma unroll
+        for (int i = 0; i < G::MI; ++i) fa[i] = frag_a(i);
+        bf16x8 fb = frag_b(0);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          bf16x8 fn;
+          if (j + 1 < 8) fn = frag_b(j + 1);
+#pragma unroll
+          for (int i = 0; i < G::MI; ++i)
+            if (i == 0 || nb > 64 * i) acc[i][j] = mma(fb, fa[i], acc[i][j]);
+          if (j + 1 < 8) fb = fn;
+        }
       } else {
         // all B fragments first, then the A fragments one row block ahead: block i + 1's read
         // is in flight during block i's MFMAs
@@ -1054,7 +1012,7 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
       // that refill it are issued only after the next step's barrier
       char* st = s_ring + (s & (NSTG - 1)) * G::STGK + w * 4096;
       lds_barrier();
-      epilogue<KIND>(a, Cc, acc, s_red, wm, wn, L, S.nMg, nTN, st);
+      epilogue<KIND>(a, Cc, acc, wm, wn, L, S.nMg, st);
       ++h0;
 #pragma unroll
       for (int i = 0; i < G::MI; ++i)
@@ -1063,7 +1021,7 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
       S.decode(a, Cc, Cc.it + 1);
       if constexpr (T::VK) {
         while (Cc.valid && Cc.nk == 0) {
-          epilogue<KIND>(a, Cc, acc, s_red, wm, wn, L, S.nMg, nTN, st);
+          epilogue<KIND>(a, Cc, acc, wm, wn, L, S.nMg, st);
           ++h0;
           S.decode(a, Cc, Cc.it + 1);
         }

@@ -222,7 +222,7 @@ moe_status moe_layer_bwd(moe_dtype dt, const void* dout, const void* x, const vo
 typedef enum moe_kernel_id {
   MOE_K_GATEUP = 0,      /* forward gate/up grouped GEMM + SwiGLU epilogue */
   MOE_K_DOWN = 1,        /* forward down grouped GEMM */
-  MOE_K_DH = 2,          /* backward dH kernel (dSwiGLU, dS partials, A') */
+  MOE_K_DH = 2,          /* backward dH kernel: bf16 the dA' grouped GEMM; fp32 with the dSwiGLU epilogue */
   MOE_K_DX = 3,          /* backward dX grouped GEMM (expert rows) */
   MOE_K_DWD = 4,         /* backward dW_down varlen-K GEMM */
   MOE_K_DW1 = 5,         /* backward dW_gate / dW_up varlen-K GEMM */
@@ -231,7 +231,7 @@ typedef enum moe_kernel_id {
   MOE_K_ROUTE = 8,       /* top-k router kernel */
   MOE_K_PERMUTE = 9,     /* histogram + scan + scatter of moe_permute */
   MOE_K_ROUTE_TR_PLAN = 10, /* the token-rounding plan kernels after the router */
-  MOE_K_DS_REDUCE = 11,  /* ordered reduction of the dS partials */
+  MOE_K_DSWIGLU = 11,    /* bf16: dSwiGLU, A' and dS from dA'; fp32: ordered sum of the dS partials */
   MOE_K_COUNT = 12
 } moe_kernel_id;
 
