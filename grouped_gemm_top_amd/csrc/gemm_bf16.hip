@@ -127,12 +127,11 @@ __device__ __forceinline__ i32x4 sgpr4(const i32x4& r) {
 // valid lane's voff + soff inside its tensor, and gives masked lanes a voff at or beyond the
 // descriptor range, so both operands of a masked access fail the range check.
 __device__ __forceinline__ void dma16(const i32x4& r, uint32_t m0, uint32_t voff, uint32_t soff) {
-  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(sgpr4(r)),
-               "s"(ufl((int)soff)), "{m0}"(ufl((int)m0))
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(r), "s"(soff), "{m0}"(m0)
                : "memory");
 }
 __device__ __forceinline__ void dma4(const i32x4& r, uint32_t m0, uint32_t voff) {
-  asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(sgpr4(r)), "{m0}"(ufl((int)m0))
+  asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(sgpr4(r)), "{m0}"(m0)
                : "memory");
 }
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -412,6 +411,9 @@ struct Loader {
   // whose K is not a multiple of 32 builds every lane's offset and masks k >= K.
   __device__ __forceinline__ void issue(const Args& a, const Tile& c, uint32_t mS, const int* tok, int w, int L) {
     const int H = a.H, I = a.I;
+    // the descriptors in SGPRs once per step (the inline assembly takes them as scalar operands)
+    const i32x4 rA = sgpr4(this->rA), rB = sgpr4(this->rB);
+    const i32x4 rB2 = (KIND == GATEUP || KIND == DX) ? sgpr4(this->rB2) : rB;
     const int k0 = c.kt * BK;
     const uint32_t mA = mS + (uint32_t)(2 * w) * 1024u;
     const uint32_t mB = mS + (uint32_t)G::OPA + (uint32_t)(2 * w) * 1024u;
@@ -906,8 +908,8 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
     h1 = h0;
     h0 = 0;
 
-#ifndef MOE_DMA_LATE
-    {
+    // ---- this step's loads (three steps ahead) and the MFMAs of step s ----
+    auto issue_block = [&]() __attribute__((always_inline)) {
       int tn = 0;
       if constexpr (GATHER) {
         tn = tok_issue(Tk, s + 2 * AHEAD);
@@ -918,91 +920,82 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
       if constexpr (!GATHER) lead_moved(Ld, false);
       t2 = t1;
       t1 = tn;
-    }
-#endif
-
-    // ---- MFMAs of step s ----
-    // row block i of this wavefront (rows 16(4i + wm) ..) takes part while it starts below
-    // mlen; a short tile's blocks are spread over all four SIMDs
-    if (Cc.mlen > 16 * wm) {
-      const int nb = Cc.mlen - 16 * wm;
-      // opaque copies: the per-fragment LDS positions derived from these are recomputed each
-      // step rather than held in registers across the loop
-      int kco = kc_off, k0o = mn_k0, ffo = mn_ff, bo = mn_b;
-      asm volatile("" : "+v"(kco), "+v"(k0o), "+v"(ffo), "+v"(bo));
-      const char* sa = s_ring + (s & (NSTG - 1)) * G::STGK;
-      const char* sb = sa + G::OPA;
-      auto frag_a = [&](int i) __attribute__((always_inline)) {
-        if constexpr (T::A_KC) return frag_kc(sa, 16 * (4 * i + wm), kco);
-        else return frag_mn(sa, 16 * (4 * i + wm), k0o, ffo, bo);
-      };
-      auto frag_b = [&](int j) __attribute__((always_inline)) {
-        if constexpr (T::B_KC) return frag_kc(sb, wn * 128 + 16 * j, kco);
-        else return frag_mn(sb, wn * 128 + 16 * j, k0o, ffo, bo);
-      };
-      // a row block at or past mlen skips its MFMAs (its fragment holds rows of no group)
-      if constexpr (G::MI == 4) {
-        // every fragment read first, then the MFMAs
-        bf16x8 fa[4], fb[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) fb[j] = frag_b(j);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) fa[i] = frag_a(i);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (i == 0 || nb > 64 * i) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) acc[i][j] = mma(fb[j], fa[i], acc[i][j]);
+    };
+    auto mma_block = [&]() __attribute__((always_inline)) {
+      // row block i of this wavefront (rows 16(4i + wm) ..) takes part while it starts below
+      // mlen; a short tile's blocks are spread over all four SIMDs
+      if (Cc.mlen > 16 * wm) {
+        const int nb = Cc.mlen - 16 * wm;
+        // opaque copies: the per-fragment LDS positions derived from these are recomputed each
+        // step rather than held in registers across the loop
+        int kco = kc_off, k0o = mn_k0, ffo = mn_ff, bo = mn_b;
+        asm volatile("" : "+v"(kco), "+v"(k0o), "+v"(ffo), "+v"(bo));
+        const char* sa = s_ring + (s & (NSTG - 1)) * G::STGK;
+        const char* sb = sa + G::OPA;
+        auto frag_a = [&](int i) __attribute__((always_inline)) {
+          if constexpr (T::A_KC) return frag_kc(sa, 16 * (4 * i + wm), kco);
+          else return frag_mn(sa, 16 * (4 * i + wm), k0o, ffo, bo);
+        };
+        auto frag_b = [&](int j) __attribute__((always_inline)) {
+          if constexpr (T::B_KC) return frag_kc(sb, wn * 128 + 16 * j, kco);
+          else return frag_mn(sb, wn * 128 + 16 * j, k0o, ffo, bo);
+        };
+        // a row block at or past mlen skips its MFMAs (its fragment holds rows of no group)
+        if constexpr (G::MI == 4) {
+          // every fragment read first, then the MFMAs
+          bf16x8 fa[4], fb[8];
+  #pragma unroll
+          for (int j = 0; j < 8; ++j) fb[j] = frag_b(j);
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) fa[i] = frag_a(i);
+  #pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (i == 0 || nb > 64 * i) {
+  #pragma unroll
+              for (int j = 0; j < 8; ++j) acc[i][j] = mma(fb[j], fa[i], acc[i][j]);
+            }
+        } else if constexpr (KIND == DH) {
+          // (fewer live fragments, for the register budget of the dSwiGLU epilogue) all A
+          // fragments first, then the B fragments one column block ahead
+          bf16x8 fa[G::MI];
+  #pragma unroll
+          for (int i = 0; i < G::MI; ++i) fa[i] = frag_a(i);
+          bf16x8 fb = frag_b(0);
+  #pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            bf16x8 fn;
+            if (j + 1 < 8) fn = frag_b(j + 1);
+  #pragma unroll
+            for (int i = 0; i < G::MI; ++i)
+              if (i == 0 || nb > 64 * i) acc[i][j] = mma(fb, fa[i], acc[i][j]);
+            if (j + 1 < 8) fb = fn;
           }
-      } else if constexpr (KIND == DH) {
-        // (fewer live fragments, for the register budget of the dSwiGLU epilogue) all A
-        // fragments first, then the B fragments one column block ahead
-        bf16x8 fa[G::MI];
-#pragma unroll
-        for (int i = 0; i < G::MI; ++i) fa[i] = frag_a(i);
-        bf16x8 fb = frag_b(0);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          bf16x8 fn;
-          if (j + 1 < 8) fn = frag_b(j + 1);
-#pragma unroll
-          for (int i = 0; i < G::MI; ++i)
-            if (i == 0 || nb > 64 * i) acc[i][j] = mma(fb, fa[i], acc[i][j]);
-          if (j + 1 < 8) fb = fn;
-        }
-      } else {
-        // all B fragments first, then the A fragments one row block ahead: block i + 1's read
-        // is in flight during block i's MFMAs
-        bf16x8 fb[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) fb[j] = frag_b(j);
-        bf16x8 fa = frag_a(0);
-#pragma unroll
-        for (int i = 0; i < G::MI; ++i) {
-          bf16x8 fn;
-          if (i + 1 < G::MI) fn = frag_a(i + 1);
-          if (i == 0 || nb > 64 * i) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) acc[i][j] = mma(fb[j], fa, acc[i][j]);
+        } else {
+          // all B fragments first, then the A fragments one row block ahead: block i + 1's read
+          // is in flight during block i's MFMAs
+          bf16x8 fb[8];
+  #pragma unroll
+          for (int j = 0; j < 8; ++j) fb[j] = frag_b(j);
+          bf16x8 fa = frag_a(0);
+  #pragma unroll
+          for (int i = 0; i < G::MI; ++i) {
+            bf16x8 fn;
+            if (i + 1 < G::MI) fn = frag_a(i + 1);
+            if (i == 0 || nb > 64 * i) {
+  #pragma unroll
+              for (int j = 0; j < 8; ++j) acc[i][j] = mma(fb[j], fa, acc[i][j]);
+            }
+            if (i + 1 < G::MI) fa = fn;
           }
-          if (i + 1 < G::MI) fa = fn;
         }
       }
-    }
-#ifdef MOE_DMA_LATE
-    {
-      int tn = 0;
-      if constexpr (GATHER) {
-        tn = tok_issue(Tk, s + 2 * AHEAD);
-        S.next(a, Tk, true);
-        lead_moved(Tk, false);
-      }
-      load_issue(s + AHEAD);
-      if constexpr (!GATHER) lead_moved(Ld, false);
-      t2 = t1;
-      t1 = tn;
-    }
-#endif
+    };
+    // The two wavefronts of a SIMD (wn = 0 and 1) take the two halves in opposite orders, so
+    // one's load issue and bookkeeping overlap the other's MFMAs instead of both waiting on
+    // the same phase.
+    if (wn == 0) issue_block();
+    mma_block();
+    if (wn != 0) issue_block();
 
     // ---- advance the compute cursor; finish a tile after its last step ----
     if (Cc.kt + 1 < Cc.nk) {
