@@ -10,6 +10,8 @@ from .oracle import (  # noqa: F401
     lib_path,
     pairs_from_plan,
     pairs_from_topk,
+    router_bwd,
+    router_logits,
     permute,
     route_topk,
     threads,

@@ -485,3 +485,118 @@ ORACLE_EXPORT int oracle_layer_bwd(const float* dout, const float* x, const floa
   free(A); free(DG); free(DU);
   return fail ? -2 : 0;
 }
+
+/* ------------------------------------------------------------------------------------
+ * Router logits.
+ * [DEP] "1) Router" maps the [N,H] hidden states to per-expert scores; the score of
+ * expert e is a linear function of the token's hidden state:
+ *   logits[t,e] = sum_h x[t,h] * W_r[h,e]   (+ bias[e] when bias is not NULL)
+ * accumulated in real in ascending h, rounded once to fp32.  W_r is [H,E].
+ * ---------------------------------------------------------------------------------- */
+ORACLE_EXPORT int oracle_router_logits(const float* x, const float* wr, const float* bias, int N, int H, int E,
+                                       float* logits) {
+  if (N < 0 || H < 1 || E < 1 || !x || !wr || !logits) return -1;
+#pragma omp parallel for schedule(static)
+  for (int t = 0; t < N; ++t)
+    for (int e = 0; e < E; ++e) {
+      real s = 0;
+      for (int h = 0; h < H; ++h) s += (real)x[(size_t)t * H + h] * (real)wr[(size_t)h * E + e];
+      if (bias) s += (real)bias[e];
+      logits[(size_t)t * E + e] = (float)s;
+    }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------------------
+ * Router backward (the gradient of the combine weights back to the router's inputs).
+ * The pages stop at dS, the gradient with respect to the combine weights ([SM] "3 기여 ①":
+ * dS = <dA', A>); training the router needs the rest, written out here from the weights'
+ * definition.  For token t with top-k set K (idx[t,0..k-1]) and z = logits[t,:] + bias:
+ *   every final pair f = (t, e_f) has weight   w_f(z) = exp(z_{e_f}) / sum_{j in K} exp(z_j)
+ * (the renormalised top-k softmax; for token-rounding plans the same expression, P_e / S_t,
+ * also gives the padded pairs' weights, and dropped pairs simply have no f).  With
+ * q_m = exp(z_m) / sum_{j in K} exp(z_j):
+ *   dw_f / dz_m = w_f * ([m == e_f] - q_m * [m in K])
+ *   dz[t,m]     = sum_f dS_f * dw_f / dz_m          (computed literally, f and m loops)
+ * and, because z = x W_r + bias:
+ *   dbias[m]    = sum_t dz[t,m]
+ *   dW_r[h,m]   = sum_t x[t,h] * dz[t,m]
+ *   dx[t,h]     = sum_m dz[t,m] * W_r[h,m]        (the router's share of dx only)
+ * The pairs (pair_t, pair_e, pair_ds) list every final pair once; w_f is recomputed from z in
+ * real (the plan's fp32 weight is that value rounded).  Outputs are double; dz [N,E],
+ * dwr [H,E], dx [N,H], dbias [E]; any of dwr, dx, dbias may be NULL.
+ * ---------------------------------------------------------------------------------- */
+ORACLE_EXPORT int oracle_router_bwd(const float* logits, const float* bias, int N, int E, int k,
+                                    const int32_t* idx, int P, const int32_t* pair_t, const int32_t* pair_e,
+                                    const float* pair_ds, const float* x, const float* wr, int H, double* dz,
+                                    double* dwr, double* dx, double* dbias) {
+  if (N < 0 || E < 1 || k < 1 || k > E || P < 0 || H < 1 || !logits || !idx || !dz) return -1;
+  if (P > 0 && (!pair_t || !pair_e || !pair_ds)) return -1;
+  if ((dwr || dx) && (!x || !wr)) return -1;
+  if (check_pairs(N, E, P, pair_t, pair_e)) return -1;
+  int32_t *tptr, *tlist;
+  if (group_pairs(P, pair_t, N, &tptr, &tlist)) return -2;
+  int fail = 0;
+#pragma omp parallel
+  {
+    real* z = (real*)malloc(sizeof(real) * (size_t)E);
+    real* q = (real*)malloc(sizeof(real) * (size_t)E);  /* q_m, zero outside K */
+    if (!z || !q) {
+#pragma omp atomic write
+      fail = 1;
+    } else {
+#pragma omp for schedule(static)
+      for (int t = 0; t < N; ++t) {
+        for (int e = 0; e < E; ++e) {
+          const float zf = bias ? logits[(size_t)t * E + e] + bias[e] : logits[(size_t)t * E + e];
+          z[e] = (real)zf;
+          q[e] = 0;
+        }
+        real zmax = z[idx[(size_t)t * k]];
+        for (int j = 1; j < k; ++j)
+          if (z[idx[(size_t)t * k + j]] > zmax) zmax = z[idx[(size_t)t * k + j]];
+        real sk = 0;
+        for (int j = 0; j < k; ++j) sk += exp(z[idx[(size_t)t * k + j]] - zmax);
+        for (int j = 0; j < k; ++j) q[idx[(size_t)t * k + j]] = exp(z[idx[(size_t)t * k + j]] - zmax) / sk;
+        for (int m = 0; m < E; ++m) {
+          real s = 0;
+          for (int c = tptr[t]; c < tptr[t + 1]; ++c) {
+            const int f = tlist[c], ef = pair_e[f];
+            const real wf = exp(z[ef] - zmax) / sk;
+            const real dwdz = wf * ((m == ef ? (real)1 : (real)0) - q[m]);
+            s += (real)pair_ds[f] * dwdz;
+          }
+          dz[(size_t)t * E + m] = (double)s;
+        }
+      }
+    }
+    free(z); free(q);
+  }
+  free(tptr); free(tlist);
+  if (fail) return -2;
+  if (dbias)
+    for (int m = 0; m < E; ++m) {
+      real s = 0;
+      for (int t = 0; t < N; ++t) s += (real)dz[(size_t)t * E + m];
+      dbias[m] = (double)s;
+    }
+  if (dwr) {
+#pragma omp parallel for schedule(static)
+    for (int h = 0; h < H; ++h)
+      for (int m = 0; m < E; ++m) {
+        real s = 0;
+        for (int t = 0; t < N; ++t) s += (real)x[(size_t)t * H + h] * (real)dz[(size_t)t * E + m];
+        dwr[(size_t)h * E + m] = (double)s;
+      }
+  }
+  if (dx) {
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < N; ++t)
+      for (int h = 0; h < H; ++h) {
+        real s = 0;
+        for (int m = 0; m < E; ++m) s += (real)dz[(size_t)t * E + m] * (real)wr[(size_t)h * E + m];
+        dx[(size_t)t * H + h] = (double)s;
+      }
+  }
+  return 0;
+}

@@ -60,8 +60,14 @@ def _lib(real: str = "f64"):
     lib.oracle_layer_bwd.argtypes = [_f32p, _f32p, _f32p, _f32p, _f32p, ctypes.c_int,
                                      ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                      _i32p, _i32p, _f32p, _f64p, _f64p, _f64p, _f64p, _f64p]
+    lib.oracle_router_logits.argtypes = [_f32p, _f32p, _f32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         _f32p]
+    lib.oracle_router_bwd.argtypes = [_f32p, _f32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p,
+                                      ctypes.c_int, _i32p, _i32p, _f32p, _f32p, _f32p, ctypes.c_int,
+                                      _f64p, _f64p, _f64p, _f64p]
     for fn in ("oracle_route_topk", "oracle_permute", "oracle_token_round", "oracle_layer_fwd",
-               "oracle_layer_bwd", "oracle_real_bytes", "oracle_threads"):
+               "oracle_layer_bwd", "oracle_router_logits", "oracle_router_bwd", "oracle_real_bytes",
+               "oracle_threads"):
         getattr(lib, fn).restype = ctypes.c_int
     _LIBS[real] = lib
     return lib
@@ -199,4 +205,44 @@ def layer_bwd(dout, x, wg, wu, wd, pair_t, pair_e, pair_w, want=("dx", "dwg", "d
                                        _p(pair_e, _i32p), _p(pair_w, _f32p),
                                        *[_p(res[n], _f64p) for n in ("dx", "dwg", "dwu", "dwd", "ds")]),
            "oracle_layer_bwd")
+    return {n: v for n, v in res.items() if v is not None}
+
+
+def router_logits(x, wr, bias=None, real="f64"):
+    """logits [N,E] float32 = x @ W_r (+ bias), accumulated in `real`, rounded once."""
+    x, wr = _f32(x), _f32(wr)
+    N, H = x.shape
+    E = wr.shape[1]
+    bias = None if bias is None else _f32(bias)
+    out = np.empty((N, E), np.float32)
+    _check(_lib(real).oracle_router_logits(_p(x, _f32p), _p(wr, _f32p), _p(bias, _f32p), N, H, E,
+                                           _p(out, _f32p)),
+           "oracle_router_logits")
+    return out
+
+
+def router_bwd(logits, bias, idx, pair_t, pair_e, pair_ds, x=None, wr=None,
+               want=("dz", "dwr", "dx", "dbias"), real="f64"):
+    """Router backward from the per-pair gradients dS (one entry per final pair).
+    Returns float64 dz [N,E] and, as requested, dwr [H,E], dx [N,H] (router share only),
+    dbias [E]."""
+    logits = _f32(logits)
+    N, E = logits.shape
+    idx = _i32(idx)
+    k = idx.shape[1]
+    bias = None if bias is None else _f32(bias)
+    pair_t, pair_e, pair_ds = _i32(pair_t), _i32(pair_e), _f32(pair_ds)
+    H = 1
+    if x is not None:
+        x, wr = _f32(x), _f32(wr)
+        H = x.shape[1]
+    res = {"dz": np.empty((N, E), np.float64)}
+    res["dwr"] = np.empty((H, E), np.float64) if ("dwr" in want and x is not None) else None
+    res["dx"] = np.empty((N, H), np.float64) if ("dx" in want and x is not None) else None
+    res["dbias"] = np.empty((E,), np.float64) if "dbias" in want else None
+    _check(_lib(real).oracle_router_bwd(_p(logits, _f32p), _p(bias, _f32p), N, E, k, _p(idx, _i32p),
+                                        len(pair_t), _p(pair_t, _i32p), _p(pair_e, _i32p),
+                                        _p(pair_ds, _f32p), _p(x, _f32p), _p(wr, _f32p), H,
+                                        *[_p(res[n], _f64p) for n in ("dz", "dwr", "dx", "dbias")]),
+           "oracle_router_bwd")
     return {n: v for n, v in res.items() if v is not None}

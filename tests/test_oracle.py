@@ -441,3 +441,156 @@ def test_token_round_config5_counts():
     assert np.all(r % wl.mtile == 0)
     assert np.all(np.abs(r - c) <= wl.mtile // 2)
     assert pl["offsets"][-1] <= wl.N * wl.k + wl.E * wl.mtile // 2
+
+
+# ----------------------------------------------------------------------------- router
+# The router's forward weights, written in float64 numpy for finite differences: for a token
+# with top-k set K and logits z, the final pair (t, e) weighs exp(z_e) / sum_{j in K} exp(z_j).
+# The oracle's backward is pinned against central differences of this forward; the forward
+# itself is pinned against the oracle's routing outputs (route_topk's weights, and the
+# token-rounding plan's row weights).
+
+def _pair_weights(z, K, pe):
+    zmax = max(z[j] for j in K)
+    sk = sum(math.exp(z[j] - zmax) for j in K)
+    return np.array([math.exp(z[e] - zmax) / sk for e in pe])
+
+
+def _loss(z_rows, idx, pt, pe, ds):
+    """sum over final pairs of dS_f * w_f(z)"""
+    tot = 0.0
+    for t in range(z_rows.shape[0]):
+        sel = np.nonzero(pt == t)[0]
+        if len(sel) == 0:
+            continue
+        w = _pair_weights(z_rows[t], list(idx[t]), pe[sel])
+        tot += float(np.dot(ds[sel].astype(np.float64), w))
+    return tot
+
+
+def _fd_dz(z, idx, pt, pe, ds, eps=1e-6):
+    N, E = z.shape
+    g = np.zeros((N, E))
+    for t in range(N):
+        for m in range(E):
+            zp = z.astype(np.float64).copy()
+            zm = zp.copy()
+            zp[t, m] += eps
+            zm[t, m] -= eps
+            g[t, m] = (_loss(zp, idx, pt, pe, ds) - _loss(zm, idx, pt, pe, ds)) / (2 * eps)
+    return g
+
+
+def test_router_logits_matmul_and_one_hot():
+    rng = np.random.default_rng(21)
+    N, H, E = 9, 13, 7
+    x = rng.standard_normal((N, H)).astype(np.float32)
+    wr = rng.standard_normal((H, E)).astype(np.float32)
+    b = rng.standard_normal(E).astype(np.float32)
+    lg = oracle.router_logits(x, wr, b)
+    ref = (x.astype(np.float64) @ wr.astype(np.float64) + b).astype(np.float32)
+    np.testing.assert_array_equal(lg, ref)
+    # one-hot rows select rows of W_r exactly
+    xo = np.zeros((H, H), np.float32)
+    xo[np.arange(H), np.arange(H)] = 1.0
+    np.testing.assert_array_equal(oracle.router_logits(xo, wr), wr)
+
+
+def test_router_bwd_worked_example_top2():
+    # weights 0.7 and 0.3 on experts 0 and 2 ('EP: Expert를 나누고 토큰 보내기', section '여러
+    # Expert의 결과도 같은 토큰으로 돌아오기'); with dS = (1, 0) the closed form of the
+    # renormalised softmax gives dz_0 = 0.7 (1 - 0.7) = 0.21 and dz_2 = 0.3 (0 - 0.7) = -0.21
+    g = _golden("ep_combine_top2.json")
+    E = g["E"]
+    lg = np.full((1, E), -30.0, np.float32)
+    for e, wt in zip(g["experts"], g["weights"]):
+        lg[0, e] = math.log(wt)
+    idx, w, _ = oracle.route_topk(lg, None, g["k"])
+    pt, pe, _ = oracle.pairs_from_topk(idx, w)
+    r = oracle.router_bwd(lg, None, idx, pt, pe, np.array([1.0, 0.0], np.float32))
+    np.testing.assert_allclose(r["dz"][0], [0.21, 0.0, -0.21, 0.0], atol=1e-7)
+    # dS = (0, 1): dz_0 = 0.7 (0 - 0.3), dz_2 = 0.3 (1 - 0.3)
+    r = oracle.router_bwd(lg, None, idx, pt, pe, np.array([0.0, 1.0], np.float32))
+    np.testing.assert_allclose(r["dz"][0], [-0.21, 0.0, 0.21, 0.0], atol=1e-7)
+    # k = 1: the weight is identically one, so no gradient reaches z
+    idx1, w1, _ = oracle.route_topk(lg, None, 1)
+    pt1, pe1, _ = oracle.pairs_from_topk(idx1, w1)
+    r = oracle.router_bwd(lg, None, idx1, pt1, pe1, np.array([5.0], np.float32))
+    np.testing.assert_array_equal(r["dz"], 0.0)
+
+
+def test_router_bwd_topk_finite_differences():
+    rng = np.random.default_rng(22)
+    N, E, k = 5, 6, 3
+    lg = rng.standard_normal((N, E)).astype(np.float32)
+    idx, w, _ = oracle.route_topk(lg, None, k)
+    pt, pe, pw = oracle.pairs_from_topk(idx, w)
+    # the numpy forward reproduces the oracle's routing weights
+    for t in range(N):
+        np.testing.assert_allclose(_pair_weights(lg[t].astype(np.float64), list(idx[t]), idx[t]), w[t], rtol=2e-7)
+    ds = rng.standard_normal(len(pt)).astype(np.float32)
+    r = oracle.router_bwd(lg, None, idx, pt, pe, ds)
+    np.testing.assert_allclose(r["dz"], _fd_dz(lg, idx, pt, pe, ds), rtol=1e-6, atol=1e-8)
+    # shift invariance: the weights do not change when every z of a token moves together
+    np.testing.assert_allclose(r["dz"].sum(axis=1), 0.0, atol=1e-12)
+    # zero outside the chosen experts
+    mask = np.zeros((N, E), bool)
+    mask[np.repeat(np.arange(N), k), idx.reshape(-1)] = True
+    assert np.all(r["dz"][~mask] == 0.0)
+
+
+def test_router_bwd_token_rounding_finite_differences():
+    # a token-rounding plan has padded pairs (outside K, weight P_e / S_t) and dropped pairs
+    # (in K, no final pair): both enter only through the normaliser over K
+    rng = np.random.default_rng(23)
+    N, E, k, mtile = 12, 4, 2, 4
+    lg = rng.standard_normal((N, E)).astype(np.float32)
+    idx, w, probs = oracle.route_topk(lg, None, k, want_probs=True)
+    pl = oracle.token_round(probs, idx, mtile)
+    pt, pe, pw = oracle.pairs_from_plan(pl, E)
+    assert np.any(pl["row_pair"] < 0), "the case needs a padded pair"
+    routed = {(t, e) for t in range(N) for e in idx[t]}
+    assert len(routed - set(zip(pt.tolist(), pe.tolist()))) > 0, "the case needs a dropped pair"
+    # the plan's weights are this forward's values
+    for f in range(len(pt)):
+        wf = _pair_weights(lg[pt[f]].astype(np.float64), list(idx[pt[f]]), [pe[f]])[0]
+        np.testing.assert_allclose(pw[f], wf, rtol=1e-6)
+    ds = rng.standard_normal(len(pt)).astype(np.float32)
+    r = oracle.router_bwd(lg, None, idx, pt, pe, ds)
+    np.testing.assert_allclose(r["dz"], _fd_dz(lg, idx, pt, pe, ds), rtol=1e-6, atol=1e-8)
+    np.testing.assert_allclose(r["dz"].sum(axis=1), 0.0, atol=1e-12)
+
+
+def test_router_bwd_parameter_gradients_finite_differences():
+    # end to end: z = x W_r + b, L = sum_f dS_f w_f(z); differences in x, W_r and b
+    rng = np.random.default_rng(24)
+    N, H, E, k = 4, 5, 6, 2
+    x = rng.standard_normal((N, H)).astype(np.float32)
+    wr = rng.standard_normal((H, E)).astype(np.float32)
+    b = (0.5 * rng.standard_normal(E)).astype(np.float32)
+    lg = oracle.router_logits(x, wr)
+    idx, w, _ = oracle.route_topk(lg, b, k)
+    pt, pe, pw = oracle.pairs_from_topk(idx, w)
+    ds = rng.standard_normal(len(pt)).astype(np.float32)
+    r = oracle.router_bwd(lg, b, idx, pt, pe, ds, x, wr)
+
+    def loss(xx, ww, bb):
+        z = xx @ ww + bb
+        # the selection stays the one the gradient was taken at
+        assert all(set(np.argsort(-z[t], kind="stable")[:k]) == set(idx[t]) for t in range(N))
+        return _loss(z, idx, pt, pe, ds)
+
+    X, Wr, B = x.astype(np.float64), wr.astype(np.float64), b.astype(np.float64)
+    eps = 1e-6
+    for (name, arr, shape) in (("dx", X, (N, H)), ("dwr", Wr, (H, E)), ("dbias", B, (E,))):
+        g = np.zeros(shape)
+        for ix in np.ndindex(*shape):
+            ap, am = arr.copy(), arr.copy()
+            ap[ix] += eps
+            am[ix] -= eps
+            args_p = [X, Wr, B]
+            args_m = [X, Wr, B]
+            pos = {"dx": 0, "dwr": 1, "dbias": 2}[name]
+            args_p[pos], args_m[pos] = ap, am
+            g[ix] = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+        np.testing.assert_allclose(r[name], g, rtol=2e-5, atol=1e-7)
