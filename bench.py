@@ -266,6 +266,51 @@ def main():
             res["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2), "peak": peak,
                                "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": traffic,
                                "algorithmic_flops": f, "us": round(kern_ms[dom] * 1e3, 2)}
+    # The router's own product and backward (logits = x W_r + bias; dS -> dlogits, dW_r, dbias
+    # and the router's share of dx), timed on their own after the layer: the layer's metric
+    # starts from the logits, as the workload defines it.
+    if args.kernel_events:
+        wr = torch.from_numpy(T.wr).to(dev)
+        lg_r = torch.empty((N, E), dtype=torch.float32, device=dev)
+        dlg = torch.empty((N, E), dtype=torch.float32, device=dev)
+        dwr = torch.empty((H, E), dtype=torch.float32, device=dev)
+        dbias = torch.empty((E,), dtype=torch.float32, device=dev)
+        dx_r = torch.empty_like(dx)
+        ws_r = torch.empty(G.workspace_bytes(G.OP_ROUTER_BWD, dt_code, N, E, k, H, 8, 0), dtype=torch.uint8,
+                           device=dev)
+        ws_l = torch.empty(G.workspace_bytes(G.OP_ROUTER_LOGITS, dt_code, N, E, 1, H, 8, 0), dtype=torch.uint8,
+                           device=dev)
+
+        def router_step():
+            G.router_logits(x, wr, bias, logits=lg_r, ws=ws_l)
+            G.router_bwd(logits, idx, plan, ds, x, wr, bias=bias, dx_in=dx, dx_out=dx_r, dlogits=dlg, dw_r=dwr,
+                         dbias=dbias, ws=ws_r)
+
+        for _ in range(args.warmup):
+            router_step()
+        rnames = ("router_logits", "router_dz", "router_dx", "router_dw")
+        rev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.steps)] for n in rnames}
+        for pairs in rev.values():
+            for a_, b_ in pairs:
+                a_.record()
+                b_.record()
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            for n in rnames:
+                G.set_kernel_events(n, *rev[n][i])
+            router_step()
+        torch.cuda.synchronize()
+        for n in rnames:
+            G.set_kernel_events(n, None, None)
+        r_us = {n: round(float(np.mean([a_.elapsed_time(b_) for a_, b_ in rev[n]])) * 1e3, 2) for n in rnames}
+        fl = 2.0 * N * H * E
+        res["router"] = {
+            "note": "router logits product and router backward, timed separately (not in ms_per_step)",
+            "kernels_us": r_us,
+            "logits_tflops": round(fl / (r_us["router_logits"] * 1e-6) / 1e12, 2),
+            "bwd_us": round(r_us["router_dz"] + r_us["router_dx"] + r_us["router_dw"], 2),
+        }
     pad = float(sum(((c + 127) // 128) * 128 for c in counts)) / max(M, 1) - 1.0
     res["padded_row_fraction_tile128"] = round(pad, 4)
 

@@ -21,17 +21,18 @@ __all__ = [
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, 1, 2, 3, 4
 MOE_F32, MOE_BF16 = 0, 1
 PLAN_TOPK, PLAN_TR = 0, 1
-OP_PERMUTE, OP_ROUTE_TR, OP_GEMM_FWD, OP_LAYER_BWD = 0, 1, 2, 3
+OP_PERMUTE, OP_ROUTE_TR, OP_GEMM_FWD, OP_LAYER_BWD, OP_ROUTER_BWD, OP_ROUTER_LOGITS = 0, 1, 2, 3, 4, 5
 
 EXPORTED_SYMBOLS = (
     "moe_plan_rows_cap", "moe_workspace_bytes", "moe_last_error", "moe_route_topk", "moe_permute",
     "moe_route_token_rounding", "moe_grouped_gemm_fwd", "moe_unpermute_combine", "moe_layer_bwd",
-    "moe_set_kernel_events",
+    "moe_router_logits", "moe_router_bwd", "moe_set_kernel_events",
 )
 
 # kernel ids of the measurement hook (moe_kernel_id in include/moe.h)
 KERNEL_IDS = {"gateup": 0, "down": 1, "dh": 2, "dx": 3, "dwd": 4, "dw1": 5, "combine": 6, "dx_combine": 7,
-              "route": 8, "permute": 9, "route_tr_plan": 10, "dswiglu": 11}
+              "route": 8, "permute": 9, "route_tr_plan": 10, "dswiglu": 11, "router_logits": 12,
+              "router_dz": 13, "router_dx": 14, "router_dw": 15}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -83,9 +84,12 @@ def lib():
     L.moe_unpermute_combine.argtypes = [ctypes.c_int, vp, i32, pp, vp, vp, vp]
     L.moe_layer_bwd.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, i32, i32, pp, vp, vp, vp, vp, vp, vp,
                                 vp, sz, vp]
+    L.moe_router_logits.argtypes = [ctypes.c_int, vp, vp, vp, i32, i32, i32, vp, vp, sz, vp]
+    L.moe_router_bwd.argtypes = [ctypes.c_int, vp, vp, vp, pp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_set_kernel_events.argtypes = [i32, vp, vp]
     for fn in ("moe_route_topk", "moe_permute", "moe_route_token_rounding", "moe_grouped_gemm_fwd",
-               "moe_unpermute_combine", "moe_layer_bwd", "moe_set_kernel_events"):
+               "moe_unpermute_combine", "moe_layer_bwd", "moe_router_logits", "moe_router_bwd",
+               "moe_set_kernel_events"):
         getattr(L, fn).restype = ctypes.c_int
     _LIB = L
     return L
@@ -271,3 +275,48 @@ def layer_bwd(dout, x, w_gate, w_up, w_down, plan: Plan, hcache, dx=None, dw_gat
                                _ptr(hcache), _ptr(dx), _ptr(dw_gate), _ptr(dw_up), _ptr(dw_down), _ptr(ds),
                                _ptr(ws), nb, _stream(stream)))
     return dict(dx=dx, dw_gate=dw_gate, dw_up=dw_up, dw_down=dw_down, ds=ds)
+
+
+def router_logits(x, w_r, bias=None, logits=None, ws=None, stream=None):
+    """logits [N,E] fp32 = x @ w_r (+ bias); x [N,H] (bf16 or fp32), w_r fp32 [H,E]."""
+    import torch
+    N, H = x.shape
+    E = w_r.shape[1]
+    dt = _dtype_code(x)
+    logits = logits if logits is not None else torch.empty((N, E), dtype=torch.float32, device=x.device)
+    nb = workspace_bytes(OP_ROUTER_LOGITS, dt, N, E, 1, H, 8, 0)
+    ws = _ws(nb, x.device, ws)
+    _check(lib().moe_router_logits(dt, _ptr(x), _ptr(w_r), _ptr(bias), N, H, E, _ptr(logits), _ptr(ws), nb,
+                                   _stream(stream)))
+    return logits
+
+
+def router_bwd(logits, topk_idx, plan: Plan, ds, x, w_r, bias=None, dx_in=None, dx_out=None, dlogits=None,
+               dw_r=None, dbias=None, want_dx=True, want_dw=True, want_dbias=True, ws=None, stream=None):
+    """Router backward from dS (moe_layer_bwd's ds) -> dict(dlogits, dx, dw_r, dbias).
+    dx = dx_in + the router's share (dx_in defaults to zeros; dx_out may be dx_in)."""
+    import torch
+    N, H = x.shape
+    E = logits.shape[1]
+    dt = _dtype_code(x)
+    dev = x.device
+    dlogits = dlogits if dlogits is not None else torch.empty((N, E), dtype=torch.float32, device=dev)
+    if want_dx:
+        dx_in = dx_in if dx_in is not None else torch.zeros_like(x)
+        dx_out = dx_out if dx_out is not None else torch.empty_like(x)
+    else:
+        dx_in = dx_out = None
+    if want_dw:
+        dw_r = dw_r if dw_r is not None else torch.empty((H, E), dtype=torch.float32, device=dev)
+    else:
+        dw_r = None
+    if want_dbias:
+        dbias = dbias if dbias is not None else torch.empty((E,), dtype=torch.float32, device=dev)
+    else:
+        dbias = None
+    nb = workspace_bytes(OP_ROUTER_BWD, dt, plan.N, plan.E, plan.k, H, 8, 0) if (want_dw or want_dbias) else 0
+    ws = _ws(nb, dev, ws) if nb else None
+    _check(lib().moe_router_bwd(dt, _ptr(logits), _ptr(bias), _ptr(topk_idx), plan.c, _ptr(ds), _ptr(x), _ptr(w_r),
+                                H, _ptr(dx_in), _ptr(dx_out), _ptr(dlogits), _ptr(dw_r), _ptr(dbias), _ptr(ws), nb,
+                                _stream(stream)))
+    return dict(dlogits=dlogits, dx=dx_out, dw_r=dw_r, dbias=dbias)

@@ -129,6 +129,12 @@ size_t moe_workspace_bytes(moe_op op, moe_dtype dt, int32_t N, int32_t E, int32_
     case MOE_OP_LAYER_BWD:
       if (check_dtype(dt) != MOE_OK || check_hi(H, I) != MOE_OK || M_cap < 0) return 0;
       return moe::layer_bwd_ws_bytes(dt, N, M_cap, H, I);
+    case MOE_OP_ROUTER_BWD:
+      if (check_dtype(dt) != MOE_OK || H < 1) return 0;
+      return moe::router_bwd_ws_bytes(N, H, E);
+    case MOE_OP_ROUTER_LOGITS:
+      if (check_dtype(dt) != MOE_OK || H < 1) return 0;
+      return moe::router_logits_ws_bytes(N, H, E);
   }
   return 0;
 }
@@ -251,6 +257,47 @@ moe_status moe_layer_bwd(moe_dtype dt, const void* dout, const void* x, const vo
   return hip_status(moe::launch_layer_bwd(dt, dout, x, w_gate, w_up, w_down, H, I, *plan, hcache, dx, dw_gate,
                                           dw_up, dw_down, ds, ws, (hipStream_t)stream),
                     "moe_layer_bwd");
+}
+
+moe_status moe_router_logits(moe_dtype dt, const void* x, const float* w_r, const float* bias, int32_t N,
+                             int32_t H, int32_t E, float* logits, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  moe_status st;
+  if ((st = check_dtype(dt)) != MOE_OK) return st;
+  REQUIRE(N >= 0, MOE_EINVAL, "N must be >= 0 (got %d)", N);
+  REQUIRE(E >= 1 && E <= 1024, MOE_EINVAL, "E must be in [1, 1024] (got %d)", E);
+  REQUIRE(H >= 1, MOE_EINVAL, "H must be >= 1 (got %d)", H);
+  REQUIRE((int64_t)N * H < ((int64_t)1 << 40) && (int64_t)N * E < ((int64_t)1 << 40), MOE_EINVAL, "N too large");
+  REQUIRE(N == 0 || (x && w_r && logits), MOE_EINVAL, "NULL x/w_r/logits");
+  const size_t need = moe::router_logits_ws_bytes(N, H, E);
+  REQUIRE(ws_bytes >= need, MOE_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  REQUIRE(ws != nullptr, MOE_EINVAL, "NULL workspace");
+  return hip_status(moe::launch_router_logits(dt, x, w_r, bias, N, H, E, logits, ws, (hipStream_t)stream),
+                    "moe_router_logits");
+}
+
+moe_status moe_router_bwd(moe_dtype dt, const float* logits, const float* bias, const int32_t* topk_idx,
+                          const moe_plan* plan, const float* ds, const void* x, const float* w_r, int32_t H,
+                          const void* dx_in, void* dx_out, float* dlogits, float* dw_r, float* dbias, void* ws,
+                          size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  moe_status st;
+  if ((st = check_dtype(dt)) != MOE_OK) return st;
+  if ((st = check_plan(plan)) != MOE_OK) return st;
+  REQUIRE(H >= 1, MOE_EINVAL, "H must be >= 1 (got %d)", H);
+  const int32_t N = plan->N;
+  REQUIRE(N == 0 || (logits && topk_idx && dlogits), MOE_EINVAL, "NULL logits/topk_idx/dlogits");
+  REQUIRE(N == 0 || plan->M_cap == 0 || ds, MOE_EINVAL, "NULL ds");
+  REQUIRE(!dx_out || (dx_in && w_r), MOE_EINVAL, "dx_out needs dx_in and w_r");
+  REQUIRE(!(dw_r || dbias) || N == 0 || x, MOE_EINVAL, "dw_r / dbias need x");
+  if (dw_r || dbias) {
+    const size_t need = moe::router_bwd_ws_bytes(N, H, plan->E);
+    REQUIRE(ws_bytes >= need, MOE_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+    REQUIRE(ws != nullptr, MOE_EINVAL, "NULL workspace");
+  }
+  return hip_status(moe::launch_router_bwd(dt, logits, bias, topk_idx, *plan, ds, x, w_r, H, dx_in, dx_out, dlogits,
+                                           dw_r, dbias, ws, (hipStream_t)stream),
+                    "moe_router_bwd");
 }
 
 }  // extern "C"

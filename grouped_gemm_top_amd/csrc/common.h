@@ -78,6 +78,14 @@ hipError_t launch_combine(moe_dtype dt, const void* y, int H, const moe_plan& p,
 size_t gemm_fwd_ws_bytes(moe_dtype dt, int M_cap, int I);
 hipError_t launch_gemm_fwd(moe_dtype dt, const void* x, const void* wg, const void* wu, const void* wd, int H,
                            int I, const moe_plan& p, void* hcache, void* y, void* ws, hipStream_t s);
+size_t router_bwd_ws_bytes(int N, int H, int E);
+size_t router_logits_ws_bytes(int N, int H, int E);
+hipError_t launch_router_logits(moe_dtype dt, const void* x, const float* wr, const float* bias, int N, int H, int E,
+                                float* logits, void* ws, hipStream_t s);
+hipError_t launch_router_bwd(moe_dtype dt, const float* logits, const float* bias, const int32_t* idx,
+                             const moe_plan& p, const float* ds, const void* x, const float* wr, int H,
+                             const void* dx_in, void* dx_out, float* dlogits, float* dwr, float* dbias, void* ws,
+                             hipStream_t s);
 size_t layer_bwd_ws_bytes(moe_dtype dt, int N, int M_cap, int H, int I);
 hipError_t launch_layer_bwd(moe_dtype dt, const void* dout, const void* x, const void* wg, const void* wu,
                             const void* wd, int H, int I, const moe_plan& p, const void* hcache, void* dx,

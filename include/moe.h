@@ -64,7 +64,9 @@ typedef enum moe_op {
   MOE_OP_PERMUTE = 0,
   MOE_OP_ROUTE_TR = 1,
   MOE_OP_GEMM_FWD = 2,
-  MOE_OP_LAYER_BWD = 3
+  MOE_OP_LAYER_BWD = 3,
+  MOE_OP_ROUTER_BWD = 4,
+  MOE_OP_ROUTER_LOGITS = 5
 } moe_op;
 
 /*
@@ -210,6 +212,43 @@ moe_status moe_layer_bwd(moe_dtype dt, const void* dout, const void* x, const vo
                          void* stream);
 
 /*
+ * Router logits.  [DEP] "1) Router" maps the [N,H] hidden states to per-expert scores; the
+ * score is linear in the hidden state:
+ *   logits[t,e] = sum_h x[t,h] * w_r[h,e]  (+ bias[e] when bias is not NULL)
+ * accumulated in fp32 in a fixed order (the h range is cut into slices whose partial sums are
+ * added in slice order; bitwise reproducible).  x [N,H] of dtype dt; w_r fp32 [H,E]; bias
+ * fp32 [E] or NULL; logits fp32 [N,E] (written).  Requires 1 <= E <= 1024, H >= 1.
+ * Workspace: moe_workspace_bytes(MOE_OP_ROUTER_LOGITS, dt, N, E, 1, H, 0, 0).
+ */
+moe_status moe_router_logits(moe_dtype dt, const void* x, const float* w_r, const float* bias, int32_t N,
+                             int32_t H, int32_t E, float* logits, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Router backward: from dS, the gradient of the combine weights (moe_layer_bwd's ds), to
+ * the router's logits, weight, bias and input.  The pages stop at dS ([SM] "3 기여 ①");
+ * the rest follows from the weights' definition.  For token t with top-k set K
+ * (topk_idx[t,:], the selection of the same logits and bias) and z = logits[t,:] + bias,
+ * every final pair f = (t, e_f) of the plan has weight w_f = exp(z_{e_f}) / sum_{j in K}
+ * exp(z_j): the renormalised top-k softmax ([DEP] "1) Router"), and for token-rounding
+ * plans P_e / S_t ([SM] "5 기여 ③"), the same expression (padded pairs lie outside K,
+ * dropped pairs have no row).  With q_m = exp(z_m) / sum_{j in K} exp(z_j):
+ *   dlogits[t,m] = sum_f dS_f w_f ([m == e_f] - q_m [m in K])    (also d bias-shifted z)
+ *   dx_out[t,h]  = dx_in[t,h] + sum_m dlogits[t,m] w_r[h,m]       (NULL dx_out skips it)
+ *   dw_r[h,m]    = sum_t x[t,h] dlogits[t,m]                      (NULL skips it)
+ *   dbias[m]     = sum_t dlogits[t,m]                             (NULL skips it)
+ * w_f is the plan's row_w; dS_f is ds[t*k+j] (top-k plans, row_pair = t*k+j) or ds[r] (token
+ * rounding, row order), the layout moe_layer_bwd writes.  logits, dlogits fp32 [N,E]; bias
+ * fp32 [E] or NULL; topk_idx int32 [N,k]; x, dx_in, dx_out [N,H] of dtype dt (dx_out may be
+ * dx_in: in place); w_r fp32 [H,E]; dw_r fp32 [H,E]; dbias fp32 [E].  Everything is written
+ * fresh, in a fixed order (bitwise reproducible).  Workspace: moe_workspace_bytes(
+ * MOE_OP_ROUTER_BWD, dt, N, E, k, H, 0, 0) when dw_r or dbias is requested, else none.
+ */
+moe_status moe_router_bwd(moe_dtype dt, const float* logits, const float* bias, const int32_t* topk_idx,
+                          const moe_plan* plan, const float* ds, const void* x, const float* w_r, int32_t H,
+                          const void* dx_in, void* dx_out, float* dlogits, float* dw_r, float* dbias,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Measurement hook (for benchmarks and profilers, not needed for computing): kernels of
  * the library, identified by moe_kernel_id.  After moe_set_kernel_events(id, start, stop)
  * with two hipEvent_t handles (passed as void*), every later launch of that kernel records
@@ -232,7 +271,11 @@ typedef enum moe_kernel_id {
   MOE_K_PERMUTE = 9,     /* histogram + scan + scatter of moe_permute */
   MOE_K_ROUTE_TR_PLAN = 10, /* the token-rounding plan kernels after the router */
   MOE_K_DSWIGLU = 11,    /* bf16: dSwiGLU, A' and dS from dA'; fp32: ordered sum of the dS partials */
-  MOE_K_COUNT = 12
+  MOE_K_ROUTER_LOGITS = 12, /* moe_router_logits */
+  MOE_K_ROUTER_DZ = 13,  /* moe_router_bwd: dz from dS */
+  MOE_K_ROUTER_DX = 14,  /* moe_router_bwd: dx_out = dx_in + dz W_r^T */
+  MOE_K_ROUTER_DW = 15,  /* moe_router_bwd: dW_r and dbias (sliced product + ordered reduction) */
+  MOE_K_COUNT = 16
 } moe_kernel_id;
 
 moe_status moe_set_kernel_events(int32_t kernel_id, void* start_event, void* stop_event);

@@ -55,6 +55,9 @@ def test_workspace_bytes(L):
         assert L.moe_workspace_bytes(op, G.MOE_BF16, 4096, 128, 0, 2048, 512, 32768) == 0  # k = 0
     assert L.moe_workspace_bytes(G.OP_GEMM_FWD, G.MOE_BF16, 64, 8, 2, 60, 32, 128) == 0     # H % 8
     assert L.moe_workspace_bytes(G.OP_LAYER_BWD, 9, 64, 8, 2, 64, 32, 128) == 0            # dtype
+    # the router backward's workspace holds the sliced dW_r / dbias partial sums
+    assert L.moe_workspace_bytes(G.OP_ROUTER_BWD, G.MOE_BF16, 4096, 128, 8, 2048, 0, 0) >= 2049 * 128 * 4
+    assert L.moe_workspace_bytes(G.OP_ROUTER_BWD, 9, 4096, 128, 8, 2048, 0, 0) == 0         # dtype
     # forward workspace holds the activation A [M_cap, I]
     assert L.moe_workspace_bytes(G.OP_GEMM_FWD, G.MOE_BF16, 4096, 128, 8, 2048, 512, 32768) >= 32768 * 512 * 2
 
