@@ -13,15 +13,17 @@
 //
 // Design:
 //  * One workgroup of 512 threads (8 wavefronts, 4 along M x 2 along N) per compute unit
-//    owns a 256x256 output tile; wavefront (wm, wn) computes the 16-row blocks 16(4i + wm),
-//    i = 0..3, times 128 columns with v_mfma_f32_16x16x32_bf16 (4 x 8 blocks of 16x16).
-//    Wavefront w runs on SIMD w % 4 = wm, so interleaving the row blocks spreads a short
-//    tile's work over all four SIMDs; blocks at or past the tile's row count are skipped.
+//    owns a (64 MI) x 256 output tile (MI = 5 for the varlen-M kinds, so that a group of up
+//    to 320 rows is one M-tile; MI = 4 for the varlen-K kinds); wavefront (wm, wn) computes
+//    the 16-row blocks 16(4i + wm), i < MI, times 128 columns with v_mfma_f32_16x16x32_bf16
+//    (MI x 8 blocks of 16x16).  Wavefront w runs on SIMD w % 4 = wm, so interleaving the row
+//    blocks spreads a short tile's work over all four SIMDs; blocks at or past the tile's
+//    row count are skipped.
 //    The grid is persistent: one workgroup per CU walks its share of the tile list.
 //  * Operands go from HBM straight into LDS with buffer_load ... lds (no VGPR staging).
-//    LDS holds a ring of 4 stages of k = 32 (16 KB per operand and stage); the loads run
-//    three k-steps ahead of the MFMAs, across tile boundaries, so a tile's prologue overlaps
-//    the previous tile's last steps and its epilogue.
+//    LDS holds a ring of 4 stages of k = 32 (64 MI rows of A and 16 KB of B per stage); the
+//    loads run three k-steps ahead of the MFMAs, across tile boundaries, so a tile's prologue
+//    overlaps the previous tile's last steps and its epilogue.
 //  * K-contiguous operands are stored as 64-byte rows, chunk c of row r at c ^ ((r >> 2) & 3),
 //    and read as one 16-byte fragment per lane.  K-strided operands (the backward's weights,
 //    both varlen-K operands) are stored in their natural layout, k-rows of 512 bytes with
