@@ -5,6 +5,7 @@ package.  The product path (the HIP library and its binding) never touches it.
 """
 from .oracle import (  # noqa: F401
     build,
+    capacity_plan,
     layer_bwd,
     layer_fwd,
     lib_path,

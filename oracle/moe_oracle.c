@@ -231,6 +231,84 @@ ORACLE_EXPORT int oracle_token_round(const float* probs, const int32_t* idx, int
 }
 
 /* ------------------------------------------------------------------------------------
+ * Capacity plan (drop policy of the capacity-based layout).
+ * [DEP] "Drop/Padding 방식": the tokens assigned to each expert are lined up and cut at the
+ * expert's capacity C; the rest are dropped (padding up to C only matters for the dense
+ * E x C x H layout; this plan keeps the ragged layout, so nothing is padded).  The line-up
+ * order is the drop policy the same section names (Megatron-LM's "probs" or "position"):
+ *   policy 0 (position): token index ascending
+ *   policy 1 (probs)   : P[t,e] descending, then token index ascending
+ * Kept pairs keep their top-k weight w[t,j] (no renormalisation); rows ascend by token within
+ * an expert; row_pair = t*k + j; tok_ptr / tok_rows list each token's kept rows.  `probs` is
+ * read only by policy 1.  Returns the row count M (>= 0) or < 0 on error.
+ * ---------------------------------------------------------------------------------- */
+typedef struct { int t; int j; float p; } cap_cand;
+static int cap_policy;
+static int cap_cmp(const void* a, const void* b) {
+  const cap_cand* x = (const cap_cand*)a;
+  const cap_cand* y = (const cap_cand*)b;
+  if (cap_policy == 1 && x->p != y->p) return x->p > y->p ? -1 : 1;
+  return x->t < y->t ? -1 : (x->t > y->t ? 1 : 0);
+}
+static int cap_tok_cmp(const void* a, const void* b) {
+  const cap_cand* x = (const cap_cand*)a;
+  const cap_cand* y = (const cap_cand*)b;
+  return x->t < y->t ? -1 : (x->t > y->t ? 1 : 0);
+}
+
+ORACLE_EXPORT int oracle_capacity_plan(const float* probs, const int32_t* idx, const float* w, int N, int E, int k,
+                                       int C, int policy, int M_cap, int32_t* counts, int32_t* offsets,
+                                       int32_t* row_token, float* row_w, int32_t* row_pair, int32_t* tok_ptr,
+                                       int32_t* tok_rows) {
+  if (N < 0 || E < 1 || k < 1 || k > E || C < 0 || (policy != 0 && policy != 1) || !idx || !w || !counts ||
+      !offsets || !row_token || !row_w || !row_pair || !tok_ptr || !tok_rows)
+    return -1;
+  if (policy == 1 && !probs) return -1;
+  cap_cand* cand = (cap_cand*)malloc(sizeof(cap_cand) * ((size_t)N + 1));
+  int32_t* tcount = (int32_t*)calloc((size_t)N + 1, sizeof(int32_t));
+  if (!cand || !tcount) { free(cand); free(tcount); return -2; }
+  cap_policy = policy;
+  int32_t r = 0;
+  for (int e = 0; e < E; ++e) {
+    /* the tokens assigned to expert e, lined up by the policy */
+    int n = 0;
+    for (int t = 0; t < N; ++t)
+      for (int j = 0; j < k; ++j)
+        if (idx[(size_t)t * k + j] == e) {
+          cand[n].t = t;
+          cand[n].j = j;
+          cand[n].p = policy == 1 ? probs[(size_t)t * E + e] : 0.f;
+          ++n;
+        }
+    qsort(cand, (size_t)n, sizeof(cap_cand), cap_cmp);
+    const int keep = n < C ? n : C;
+    /* the kept ones, in token order */
+    qsort(cand, (size_t)keep, sizeof(cap_cand), cap_tok_cmp);
+    offsets[e] = r;
+    if (r + keep > M_cap) { free(cand); free(tcount); return -1; }
+    for (int q = 0; q < keep; ++q) {
+      const int t = cand[q].t, j = cand[q].j;
+      row_token[r] = t;
+      row_w[r] = w[(size_t)t * k + j];
+      row_pair[r] = t * k + j;
+      tcount[t]++;
+      ++r;
+    }
+    counts[e] = keep;
+  }
+  offsets[E] = r;
+  tok_ptr[0] = 0;
+  for (int t = 0; t < N; ++t) tok_ptr[t + 1] = tok_ptr[t] + tcount[t];
+  memset(tcount, 0, sizeof(int32_t) * ((size_t)N + 1));
+  for (int32_t q = 0; q < r; ++q) {
+    const int t = row_token[q];
+    tok_rows[tok_ptr[t] + tcount[t]++] = q;
+  }
+  free(cand); free(tcount);
+  return (int)r;
+}
+
+/* ------------------------------------------------------------------------------------
  * Expert MLP pieces shared by forward and backward (plain definitions).
  * The expert is the SwiGLU MLP named by [GG] "적용" step (6) (gate -> up -> down) and
  * [SM] "4.2 Epilogue 융합" (SwiGLU): a_i = silu(g_i) * u_i with silu(g) = g * sigmoid(g).

@@ -60,13 +60,17 @@ def _lib(real: str = "f64"):
     lib.oracle_layer_bwd.argtypes = [_f32p, _f32p, _f32p, _f32p, _f32p, ctypes.c_int,
                                      ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                      _i32p, _i32p, _f32p, _f64p, _f64p, _f64p, _f64p, _f64p]
+    lib.oracle_capacity_plan.argtypes = [_f32p, _i32p, _f32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p, _i32p, _i32p, _f32p,
+                                         _i32p, _i32p, _i32p]
     lib.oracle_router_logits.argtypes = [_f32p, _f32p, _f32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                          _f32p]
     lib.oracle_router_bwd.argtypes = [_f32p, _f32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p,
                                       ctypes.c_int, _i32p, _i32p, _f32p, _f32p, _f32p, ctypes.c_int,
                                       _f64p, _f64p, _f64p, _f64p]
     for fn in ("oracle_route_topk", "oracle_permute", "oracle_token_round", "oracle_layer_fwd",
-               "oracle_layer_bwd", "oracle_router_logits", "oracle_router_bwd", "oracle_real_bytes",
+               "oracle_layer_bwd", "oracle_router_logits", "oracle_router_bwd", "oracle_capacity_plan",
+               "oracle_real_bytes",
                "oracle_threads"):
         getattr(lib, fn).restype = ctypes.c_int
     _LIBS[real] = lib
@@ -149,6 +153,26 @@ def token_round(probs, idx, mtile, mcap=None):
                                            for n in ("counts", "offsets", "row_token", "row_w",
                                                      "row_pair", "tok_ptr", "tok_rows")]),
                "oracle_token_round")
+    for n in ("row_token", "row_w", "row_pair", "tok_rows"):
+        pl[n] = pl[n][:m].copy()
+    return pl
+
+
+def capacity_plan(idx, w, E, C, policy, probs=None):
+    """Capacity plan: each expert keeps at most C of its assigned tokens, lined up by token
+    index (policy 0, "position") or by P[t,e] descending then token (policy 1, "probs").
+    Arrays are trimmed to the actual row count M."""
+    idx = _i32(idx)
+    w = _f32(w)
+    N, k = idx.shape
+    mcap = max(N * k, 1)
+    pl = _plan_arrays(N, E, mcap)
+    pp = None if probs is None else _f32(probs)
+    m = _check(_lib().oracle_capacity_plan(_p(pp, _f32p), _p(idx, _i32p), _p(w, _f32p), N, E, k, C, policy, mcap,
+                                           *[_p(pl[n], _i32p if pl[n].dtype == np.int32 else _f32p)
+                                             for n in ("counts", "offsets", "row_token", "row_w",
+                                                       "row_pair", "tok_ptr", "tok_rows")]),
+               "oracle_capacity_plan")
     for n in ("row_token", "row_w", "row_pair", "tok_rows"):
         pl[n] = pl[n][:m].copy()
     return pl

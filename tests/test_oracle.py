@@ -594,3 +594,66 @@ def test_router_bwd_parameter_gradients_finite_differences():
             args_p[pos], args_m[pos] = ap, am
             g[ix] = (loss(*args_p) - loss(*args_m)) / (2 * eps)
         np.testing.assert_allclose(r[name], g, rtol=2e-5, atol=1e-7)
+
+
+# ----------------------------------------------------------------------------- capacity plan
+
+def _brute_capacity(idx, w, E, C, policy, probs):
+    """Independent: per expert, Python sort of its (t, j) pairs by the policy key, keep C."""
+    N, k = idx.shape
+    rows = []
+    counts = []
+    for e in range(E):
+        pairs = [(t, j) for t in range(N) for j in range(k) if idx[t, j] == e]
+        key = (lambda tj: tj[0]) if policy == 0 else (lambda tj: (-float(probs[tj[0], e]), tj[0]))
+        kept = sorted(sorted(pairs, key=key)[:C])
+        counts.append(len(kept))
+        rows += [(t, j, float(w[t, j])) for t, j in kept]
+    return np.array(counts), rows
+
+
+def test_golden_ep_imbalance_capacity():
+    g = _golden("ep_imbalance_capacity2.json")
+    lg = _logits_for_choice(g["choice"], g["E"])
+    idx, w, _ = oracle.route_topk(lg, None, g["k"])
+    pl = oracle.capacity_plan(idx, w, g["E"], g["capacity"], 0)
+    ex = g["expected"]
+    np.testing.assert_array_equal(pl["counts"], ex["counts"])
+    np.testing.assert_array_equal(pl["offsets"], ex["offsets"])
+    np.testing.assert_array_equal(pl["row_token"], ex["row_token"])
+    kept = set(pl["row_token"].tolist())
+    assert sorted(set(range(len(g["choice"]))) - kept) == ex["dropped_tokens"]
+
+
+@pytest.mark.parametrize("policy", [0, 1])
+def test_capacity_brute_force(policy):
+    rng = np.random.default_rng(31 + policy)
+    for N, E, k, C in ((40, 6, 2, 9), (64, 8, 3, 20), (17, 5, 5, 3), (30, 4, 1, 0)):
+        lg = rng.standard_normal((N, E)).astype(np.float32)
+        if policy == 1:
+            lg[: N // 3] = np.round(lg[: N // 3])  # ties in P: token order decides
+        idx, w, probs = oracle.route_topk(lg, None, k, want_probs=True)
+        pl = oracle.capacity_plan(idx, w, E, C, policy, probs)
+        counts, rows = _brute_capacity(idx, w, E, C, policy, probs)
+        np.testing.assert_array_equal(pl["counts"], counts)
+        np.testing.assert_array_equal(pl["counts"], np.minimum(np.bincount(idx.reshape(-1), minlength=E), C))
+        np.testing.assert_array_equal(pl["row_token"], [r[0] for r in rows])
+        np.testing.assert_array_equal(pl["row_pair"], [r[0] * k + r[1] for r in rows])
+        np.testing.assert_array_equal(pl["row_w"], np.array([r[2] for r in rows], np.float32))
+        # token lists: the kept rows of each token, ascending
+        for t in range(N):
+            rs = pl["tok_rows"][pl["tok_ptr"][t]:pl["tok_ptr"][t + 1]]
+            assert np.all(np.diff(rs) > 0) and np.all(pl["row_token"][rs] == t)
+        assert pl["tok_ptr"][-1] == len(rows)
+
+
+def test_capacity_without_drops_is_the_topk_plan():
+    rng = np.random.default_rng(33)
+    N, E, k = 50, 7, 3
+    idx, w, probs = oracle.route_topk(rng.standard_normal((N, E)).astype(np.float32), None, k, want_probs=True)
+    cmax = int(np.bincount(idx.reshape(-1), minlength=E).max())
+    ref = oracle.permute(idx, w, E)
+    for policy in (0, 1):
+        pl = oracle.capacity_plan(idx, w, E, cmax, policy, probs)
+        for n in ref:
+            np.testing.assert_array_equal(pl[n], ref[n], err_msg=n)
