@@ -111,6 +111,12 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=4096,
                     help="tokens in the CPU-oracle baseline sample (0 disables it)")
     ap.add_argument("--kernel-events", type=int, default=1, help="record per-kernel HIP events (1/0)")
+    ap.add_argument("--routing", choices=("workload", "capacity"), default="workload",
+                    help="capacity: route with a capacity plan (each expert keeps at most "
+                         "C = ceil(factor * N * k / E) tokens) instead of the workload's routing")
+    ap.add_argument("--capacity-factor", type=float, default=1.0)
+    ap.add_argument("--cap-policy", type=int, choices=(0, 1), default=0,
+                    help="capacity drop policy: 0 keeps the first C tokens, 1 the C most probable")
     ap.add_argument("--mode", choices=("layer", "copy"), default="layer",
                     help="copy: time a plain 1 GiB device-to-device copy (the calibration run for the "
                          "FETCH_SIZE / WRITE_SIZE counters)")
@@ -158,22 +164,32 @@ def main():
     bias = None if T.bias is None else torch.from_numpy(T.bias).to(dev)
     N, H, I, E, k = wl.N, wl.H, wl.I, wl.E, wl.k
     tr = wl.routing == "tr"
+    cap = args.routing == "capacity"
+    if cap:
+        import math
+        if tr:
+            print("--routing capacity replaces top-k routing; this workload uses token rounding", file=sys.stderr)
+            sys.exit(2)
+        C = int(math.ceil(args.capacity_factor * N * k / E))
     dt_code = G.MOE_BF16 if wl.dtype == "bf16" else G.MOE_F32
     es = 2 if wl.dtype == "bf16" else 4
 
     # every buffer allocated once, outside the timed region
-    plan = G.Plan(N, E, k, kind=G.PLAN_TR if tr else G.PLAN_TOPK, mtile=wl.mtile if tr else 0)
+    if cap:
+        plan = G.Plan(N, E, k, kind=G.PLAN_CAP, mtile=C)
+    else:
+        plan = G.Plan(N, E, k, kind=G.PLAN_TR if tr else G.PLAN_TOPK, mtile=wl.mtile if tr else 0)
     idx = torch.empty((N, k), dtype=torch.int32, device=dev)
     wts = torch.empty((N, k), dtype=torch.float32, device=dev)
-    probs = torch.empty((N, E), dtype=torch.float32, device=dev) if tr else None
+    probs = torch.empty((N, E), dtype=torch.float32, device=dev) if (tr or cap) else None
     mc = max(plan.M_cap, 1)
     hcache = torch.empty((mc, 2 * I), dtype=x.dtype, device=dev)
     y = torch.empty((mc, H), dtype=x.dtype, device=dev)
     out = torch.empty((N, H), dtype=x.dtype, device=dev)
     dx = torch.empty_like(x)
     dwg, dwu, dwd = torch.empty_like(wg), torch.empty_like(wu), torch.empty_like(wd)
-    ds = torch.empty((mc,) if tr else (N, k), dtype=torch.float32, device=dev)
-    ws_route = torch.empty(G.workspace_bytes(G.OP_ROUTE_TR if tr else G.OP_PERMUTE, dt_code, N, E, k),
+    ds = torch.empty((mc,) if (tr or cap) else (N, k), dtype=torch.float32, device=dev)
+    ws_route = torch.empty(G.workspace_bytes(G.OP_ROUTE_TR if (tr or cap) else G.OP_PERMUTE, dt_code, N, E, k),
                            dtype=torch.uint8, device=dev)
     ws_fwd = torch.empty(G.workspace_bytes(G.OP_GEMM_FWD, dt_code, N, E, k, H, I, plan.M_cap), dtype=torch.uint8,
                          device=dev)
@@ -184,6 +200,9 @@ def main():
         if tr:
             G.route_token_rounding(logits, k, wl.mtile, bias=bias, plan=plan, ws=ws_route, idx=idx, w=wts,
                                    probs=probs)
+        elif cap:
+            G.route_capacity(logits, k, C, args.cap_policy, bias=bias, plan=plan, ws=ws_route, idx=idx, w=wts,
+                             probs=probs)
         else:
             G.route_topk(logits, k, bias=bias, idx=idx, w=wts)
             G.permute(idx, wts, E, plan=plan, ws=ws_route)
@@ -210,7 +229,8 @@ def main():
 
     # Per-kernel durations: the same steps again, each kernel bracketed by HIP events on its
     # launch stream (the library's hook).
-    names = [n for n in ALL_KERNELS if not (tr and n == "permute") and not (not tr and n == "route_tr_plan")]
+    rt = tr or cap  # routing through the rounding / capacity plan kernels
+    names = [n for n in ALL_KERNELS if not (rt and n == "permute") and not (not rt and n == "route_tr_plan")]
     evs = {}
     if args.kernel_events:
         evs = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -241,7 +261,8 @@ def main():
         "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic (seeded gaussian inputs, see workloads.py)",
-        "config": {"workload": wl.name, "N": N, "H": H, "I": I, "E": E, "k": k, "routing": wl.routing,
+        "config": {"workload": wl.name, "N": N, "H": H, "I": I, "E": E, "k": k,
+                   "routing": "capacity" if cap else wl.routing,
                    "rows": M, "active_experts": e_act, "parallelism": "single GPU"},
         "pct_peak": round(100.0 * tflops / peak, 2),
     }
@@ -324,13 +345,19 @@ def main():
         }
     pad = float(sum(((c + 127) // 128) * 128 for c in counts)) / max(M, 1) - 1.0
     res["padded_row_fraction_tile128"] = round(pad, 4)
+    if cap:
+        res["config"].update({"capacity_factor": args.capacity_factor, "capacity": C,
+                              "cap_policy": "probs" if args.cap_policy else "position"})
+        res["capacity"] = {"dropped_pairs": N * k - M, "dropped_fraction": round((N * k - M) / (N * k), 4),
+                           "dense_layout_rows": E * C, "dense_padding_rows": E * C - M,
+                           "dense_padding_fraction": round((E * C - M) / max(E * C, 1), 4)}
 
-    if args.cpu_tokens > 0 and not tr:
+    if args.cpu_tokens > 0 and not tr and not cap:
         print(f"# cpu baseline on {args.cpu_tokens} tokens", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(T, idx.cpu().numpy(), wts.cpu().numpy(),
                                            min(args.cpu_tokens, N))
     elif args.cpu_tokens > 0:
-        print("# cpu baseline on token-rounding plan", file=sys.stderr, flush=True)
+        print("# cpu baseline on the routing plan", file=sys.stderr, flush=True)
         import oracle
         hp = plan.host()
         pt, pe, pw = oracle.pairs_from_plan(hp, E)

@@ -12,20 +12,23 @@ import os
 
 __all__ = [
     "MoEError", "lib", "lib_path", "Plan", "route_topk", "permute", "route_token_rounding",
-    "grouped_gemm_fwd", "unpermute_combine", "layer_bwd", "workspace_bytes", "plan_rows_cap",
-    "MOE_OK", "MOE_EINVAL", "MOE_EUNSUPPORTED", "MOE_EWORKSPACE", "MOE_EHIP",
-    "OP_PERMUTE", "OP_ROUTE_TR", "OP_GEMM_FWD", "OP_LAYER_BWD", "PLAN_TOPK", "PLAN_TR",
+    "route_capacity", "grouped_gemm_fwd", "unpermute_combine", "layer_bwd", "router_logits", "router_bwd",
+    "workspace_bytes", "plan_rows_cap", "MOE_OK", "MOE_EINVAL", "MOE_EUNSUPPORTED", "MOE_EWORKSPACE",
+    "MOE_EHIP", "OP_PERMUTE", "OP_ROUTE_TR", "OP_GEMM_FWD", "OP_LAYER_BWD", "OP_ROUTER_BWD",
+    "OP_ROUTER_LOGITS", "PLAN_TOPK", "PLAN_TR", "PLAN_CAP", "CAP_POSITION", "CAP_PROBS",
     "EXPORTED_SYMBOLS", "KERNEL_IDS", "set_kernel_events",
 ]
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, 1, 2, 3, 4
 MOE_F32, MOE_BF16 = 0, 1
-PLAN_TOPK, PLAN_TR = 0, 1
+PLAN_TOPK, PLAN_TR, PLAN_CAP = 0, 1, 2
+CAP_POSITION, CAP_PROBS = 0, 1
 OP_PERMUTE, OP_ROUTE_TR, OP_GEMM_FWD, OP_LAYER_BWD, OP_ROUTER_BWD, OP_ROUTER_LOGITS = 0, 1, 2, 3, 4, 5
 
 EXPORTED_SYMBOLS = (
     "moe_plan_rows_cap", "moe_workspace_bytes", "moe_last_error", "moe_route_topk", "moe_permute",
-    "moe_route_token_rounding", "moe_grouped_gemm_fwd", "moe_unpermute_combine", "moe_layer_bwd",
+    "moe_route_token_rounding", "moe_route_capacity", "moe_grouped_gemm_fwd", "moe_unpermute_combine",
+    "moe_layer_bwd",
     "moe_router_logits", "moe_router_bwd", "moe_set_kernel_events",
 )
 
@@ -80,6 +83,7 @@ def lib():
     L.moe_route_topk.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp]
     L.moe_permute.argtypes = [vp, vp, i32, i32, i32, pp, vp, sz, vp]
     L.moe_route_token_rounding.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, pp, vp, sz, vp]
+    L.moe_route_capacity.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, pp, vp, sz, vp]
     L.moe_grouped_gemm_fwd.argtypes = [ctypes.c_int, vp, vp, vp, vp, i32, i32, pp, vp, vp, vp, sz, vp]
     L.moe_unpermute_combine.argtypes = [ctypes.c_int, vp, i32, pp, vp, vp, vp]
     L.moe_layer_bwd.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, i32, i32, pp, vp, vp, vp, vp, vp, vp,
@@ -87,7 +91,8 @@ def lib():
     L.moe_router_logits.argtypes = [ctypes.c_int, vp, vp, vp, i32, i32, i32, vp, vp, sz, vp]
     L.moe_router_bwd.argtypes = [ctypes.c_int, vp, vp, vp, pp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_set_kernel_events.argtypes = [i32, vp, vp]
-    for fn in ("moe_route_topk", "moe_permute", "moe_route_token_rounding", "moe_grouped_gemm_fwd",
+    for fn in ("moe_route_topk", "moe_permute", "moe_route_token_rounding", "moe_route_capacity",
+               "moe_grouped_gemm_fwd",
                "moe_unpermute_combine", "moe_layer_bwd", "moe_router_logits", "moe_router_bwd",
                "moe_set_kernel_events"):
         getattr(L, fn).restype = ctypes.c_int
@@ -147,7 +152,7 @@ class Plan:
     def __init__(self, N: int, E: int, k: int, kind: int = PLAN_TOPK, mtile: int = 0, device="cuda"):
         import torch
         self.N, self.E, self.k, self.kind = N, E, k, kind
-        self.mtile = mtile if kind == PLAN_TR else 0
+        self.mtile = mtile if kind in (PLAN_TR, PLAN_CAP) else 0  # capacity plans: the capacity
         self.M_cap = plan_rows_cap(kind, N, E, k, self.mtile)
         i32 = dict(dtype=torch.int32, device=device)
         mc = max(self.M_cap, 1)
@@ -222,6 +227,24 @@ def route_token_rounding(logits, k: int, mtile: int, bias=None, plan: Plan | Non
     ws = _ws(nb, dev, ws)
     _check(lib().moe_route_token_rounding(_ptr(logits), _ptr(bias), N, E, k, mtile, _ptr(idx), _ptr(w),
                                           _ptr(probs), plan.c, _ptr(ws), nb, _stream(stream)))
+    return plan, idx, w, probs
+
+
+def route_capacity(logits, k: int, capacity: int, policy: int = CAP_POSITION, bias=None, plan: Plan | None = None,
+                   ws=None, idx=None, w=None, probs=None, stream=None):
+    """-> (plan, topk_idx, topk_w, probs): top-k routing, then each expert keeps at most
+    `capacity` of its tokens (policy CAP_POSITION: token order; CAP_PROBS: largest P first)."""
+    import torch
+    N, E = logits.shape
+    dev = logits.device
+    plan = plan or Plan(N, E, k, kind=PLAN_CAP, mtile=capacity, device=dev)
+    idx = idx if idx is not None else torch.empty((N, k), dtype=torch.int32, device=dev)
+    w = w if w is not None else torch.empty((N, k), dtype=torch.float32, device=dev)
+    probs = probs if probs is not None else torch.empty((N, E), dtype=torch.float32, device=dev)
+    nb = workspace_bytes(OP_ROUTE_TR, MOE_BF16, N, E, k)
+    ws = _ws(nb, dev, ws)
+    _check(lib().moe_route_capacity(_ptr(logits), _ptr(bias), N, E, k, capacity, policy, _ptr(idx), _ptr(w),
+                                    _ptr(probs), plan.c, _ptr(ws), nb, _stream(stream)))
     return plan, idx, w, probs
 
 

@@ -54,8 +54,9 @@ moe_status check_plan(const moe_plan* p) {
   REQUIRE(p != nullptr, MOE_EINVAL, "plan is NULL");
   moe_status st = check_dims(p->N, p->E, p->k);
   if (st != MOE_OK) return st;
-  REQUIRE(p->kind == MOE_PLAN_TOPK || p->kind == MOE_PLAN_TR, MOE_EINVAL, "unknown plan kind %d", p->kind);
-  const int64_t need = moe_plan_rows_cap(p->kind, p->N, p->E, p->k, p->kind == MOE_PLAN_TR ? p->mtile : 0);
+  REQUIRE(p->kind == MOE_PLAN_TOPK || p->kind == MOE_PLAN_TR || p->kind == MOE_PLAN_CAP, MOE_EINVAL,
+          "unknown plan kind %d", p->kind);
+  const int64_t need = moe_plan_rows_cap(p->kind, p->N, p->E, p->k, p->kind == MOE_PLAN_TOPK ? 0 : p->mtile);
   REQUIRE(need >= 0, MOE_EINVAL, "invalid plan dimensions");
   REQUIRE(p->M_cap >= need, MOE_EINVAL, "plan M_cap %d < required %lld", p->M_cap, (long long)need);
   REQUIRE(p->counts && p->offsets && p->tok_ptr, MOE_EINVAL, "plan has a NULL counts/offsets/tok_ptr array");
@@ -113,6 +114,11 @@ int64_t moe_plan_rows_cap(int32_t kind, int32_t N, int32_t E, int32_t k, int32_t
   if (kind == MOE_PLAN_TR) {
     if (mtile < 1) return -1;
     return (int64_t)N * k + (int64_t)E * (mtile / 2);
+  }
+  if (kind == MOE_PLAN_CAP) {  // mtile holds the capacity
+    if (mtile < 0) return -1;
+    const int64_t a = (int64_t)N * k, b = (int64_t)E * mtile;
+    return a < b ? a : b;
   }
   return -1;
 }
@@ -193,9 +199,39 @@ moe_status moe_route_token_rounding(const float* logits, const float* bias, int3
   moe::kernel_event(MOE_K_ROUTE, 1, s);
   if (e != hipSuccess) return hip_status(e, "moe_route_token_rounding/route");
   moe::kernel_event(MOE_K_ROUTE_TR_PLAN, 0, s);
-  e = moe::launch_token_round(topk_idx, probs, tok_norm, N, E, k, mtile, *plan, ws, s);
+  e = moe::launch_token_round(topk_idx, probs, tok_norm, nullptr, N, E, k, 0, mtile, 1, *plan, ws, s);
   moe::kernel_event(MOE_K_ROUTE_TR_PLAN, 1, s);
   return hip_status(e, "moe_route_token_rounding");
+}
+
+moe_status moe_route_capacity(const float* logits, const float* bias, int32_t N, int32_t E, int32_t k,
+                              int32_t capacity, int32_t policy, int32_t* topk_idx, float* topk_w, float* probs,
+                              const moe_plan* plan, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  moe_status st = check_dims(N, E, k);
+  if (st != MOE_OK) return st;
+  REQUIRE(capacity >= 0, MOE_EINVAL, "capacity must be >= 0 (got %d)", capacity);
+  REQUIRE(policy == MOE_CAP_POSITION || policy == MOE_CAP_PROBS, MOE_EINVAL, "unknown capacity policy %d", policy);
+  if ((st = check_plan(plan)) != MOE_OK) return st;
+  REQUIRE(plan->kind == MOE_PLAN_CAP && plan->mtile == capacity, MOE_EINVAL,
+          "a capacity plan needs kind MOE_PLAN_CAP with the capacity in its mtile field");
+  REQUIRE(plan->N == N && plan->E == E && plan->k == k, MOE_EINVAL, "plan dimensions differ from the call");
+  REQUIRE(N == 0 || (logits && topk_idx && topk_w && probs), MOE_EINVAL, "NULL logits/topk_idx/topk_w/probs");
+  const size_t need = moe::tr_ws_bytes(N, E);
+  REQUIRE(ws_bytes >= need, MOE_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  REQUIRE(ws != nullptr, MOE_EINVAL, "NULL workspace");
+  const size_t nb = ((size_t)N + 255) / 256;
+  float* tok_norm = (float*)((char*)ws + (((nb * E * 4) + 255) & ~(size_t)255));
+  hipStream_t s = (hipStream_t)stream;
+  moe::kernel_event(MOE_K_ROUTE, 0, s);
+  hipError_t e = moe::launch_route_topk(logits, bias, N, E, k, topk_idx, topk_w, probs, tok_norm, s);
+  moe::kernel_event(MOE_K_ROUTE, 1, s);
+  if (e != hipSuccess) return hip_status(e, "moe_route_capacity/route");
+  moe::kernel_event(MOE_K_ROUTE_TR_PLAN, 0, s);
+  e = moe::launch_token_round(topk_idx, probs, tok_norm, topk_w, N, E, k, 1, capacity,
+                              policy == MOE_CAP_PROBS ? 1 : 0, *plan, ws, s);
+  moe::kernel_event(MOE_K_ROUTE_TR_PLAN, 1, s);
+  return hip_status(e, "moe_route_capacity");
 }
 
 moe_status moe_grouped_gemm_fwd(moe_dtype dt, const void* x, const void* w_gate, const void* w_up,

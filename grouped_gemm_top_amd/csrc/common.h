@@ -71,8 +71,11 @@ size_t permute_ws_bytes(int N, int E);
 hipError_t launch_permute(const int32_t* idx, const float* w, int N, int E, int k, const moe_plan& p,
                           void* ws, hipStream_t s);
 size_t tr_ws_bytes(int N, int E);
-hipError_t launch_token_round(const int32_t* idx, const float* probs, const float* tok_norm, int N, int E,
-                              int k, int mtile, const moe_plan& p, void* ws, hipStream_t s);
+// cap = 0: token rounding with granule param; cap = 1: capacity plan with capacity param, keys with
+// (use_p = 1) or without (0) the score, row weights from topk_w
+hipError_t launch_token_round(const int32_t* idx, const float* probs, const float* tok_norm, const float* topk_w,
+                              int N, int E, int k, int cap, int param, int use_p, const moe_plan& p, void* ws,
+                              hipStream_t s);
 hipError_t launch_combine(moe_dtype dt, const void* y, int H, const moe_plan& p, const float* row_w,
                           void* out, hipStream_t s);
 size_t gemm_fwd_ws_bytes(moe_dtype dt, int M_cap, int I);

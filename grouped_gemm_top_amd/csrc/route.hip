@@ -121,6 +121,9 @@ hipError_t launch_route_topk(const float* logits, const float* bias, int N, int 
 //   k_tr_select  one block per expert: radix-select the r_e-th largest key, keep every key
 //                >= it, compact in token order -> rows of expert e
 //   k_tr_tokcount / scan / k_tr_tokfill   token-major row lists
+// The capacity plan ([DEP] "Drop/Padding 방식": each expert's tokens lined up and cut at the
+// capacity C, the rest dropped) runs the same kernels with r_e = min(c_e, C), the key's score
+// left out for the position order, and each kept row taking its pair's top-k weight.
 // ---------------------------------------------------------------------------------------
 __device__ __forceinline__ int block_excl_scan_1024(int v, int* s_wave, int* total) {
   // 1024 threads = 16 wavefronts; returns the exclusive prefix of v in thread order
@@ -149,8 +152,9 @@ __device__ __forceinline__ int block_excl_scan_1024(int v, int* s_wave, int* tot
   return res;
 }
 
+// cap = 0: token rounding, r_e = mtile-rounded c_e; cap = 1: capacity, r_e = min(c_e, param)
 __global__ __launch_bounds__(1024) void k_tr_sizes(const int32_t* __restrict__ bcnt, int nb, int N, int E,
-                                                   int mtile, int32_t* __restrict__ counts,
+                                                   int param, int cap, int32_t* __restrict__ counts,
                                                    int32_t* __restrict__ offsets) {
   __shared__ int s_wave[17];
   const int e = threadIdx.x;
@@ -158,9 +162,14 @@ __global__ __launch_bounds__(1024) void k_tr_sizes(const int32_t* __restrict__ b
   if (e < E) {
     int c = 0;
     for (int b = 0; b < nb; ++b) c += bcnt[(size_t)b * E + e];
-    const int rmax = mtile * (N / mtile);
-    r = mtile * ((c + mtile / 2) / mtile);
-    if (r > rmax) r = rmax;
+    if (cap) {
+      r = c < param ? c : param;
+    } else {
+      const int mtile = param;
+      const int rmax = mtile * (N / mtile);
+      r = mtile * ((c + mtile / 2) / mtile);
+      if (r > rmax) r = rmax;
+    }
     counts[e] = r;
   }
   int total;
@@ -169,15 +178,16 @@ __global__ __launch_bounds__(1024) void k_tr_sizes(const int32_t* __restrict__ b
   if (e == 0) offsets[E] = total;
 }
 
+// use_p = 0 leaves the score out of the key (the capacity plan's position order)
 __global__ __launch_bounds__(256) void k_tr_keys(const float* __restrict__ probs, const int32_t* __restrict__ idx,
-                                                 int N, int E, int k, uint64_t* __restrict__ keys) {
+                                                 int N, int E, int k, int use_p, uint64_t* __restrict__ keys) {
   __shared__ uint32_t s_p[64][65];
   __shared__ uint8_t s_r[64][64];
   const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
   for (int q = threadIdx.x; q < 64 * 64; q += 256) {
     const int tl = q >> 6, el = q & 63;
     const int t = t0 + tl, e = e0 + el;
-    s_p[tl][el] = (t < N && e < E) ? (__float_as_uint(probs[(size_t)t * E + e]) & 0x7FFFFFFFu) : 0u;
+    s_p[tl][el] = (use_p && t < N && e < E) ? (__float_as_uint(probs[(size_t)t * E + e]) & 0x7FFFFFFFu) : 0u;
     s_r[tl][el] = 0;
   }
   __syncthreads();
@@ -199,8 +209,9 @@ __global__ __launch_bounds__(256) void k_tr_keys(const float* __restrict__ probs
   }
 }
 
+// topk_w != NULL (capacity plans): a kept row takes its pair's top-k weight as it is
 __global__ __launch_bounds__(1024) void k_tr_select(const uint64_t* __restrict__ keys, const float* __restrict__ probs,
-                                                    const float* __restrict__ tok_norm,
+                                                    const float* __restrict__ tok_norm, const float* __restrict__ topk_w,
                                                     const int32_t* __restrict__ idx, int N, int E, int k,
                                                     const int32_t* __restrict__ counts,
                                                     const int32_t* __restrict__ offsets,
@@ -210,13 +221,14 @@ __global__ __launch_bounds__(1024) void k_tr_select(const uint64_t* __restrict__
   __shared__ int s_wave[17];
   __shared__ unsigned long long s_prefix;
   __shared__ int s_remaining;
+  __shared__ int s_done;
   const int e = blockIdx.x;
   const int r = counts[e];
   const int off = offsets[e];
   const uint64_t* ke = keys + (size_t)e * N;
   uint64_t thr = ~0ull;  // select nothing unless r > 0
   if (r > 0) {
-    if (threadIdx.x == 0) { s_prefix = 0ull; s_remaining = r; }
+    if (threadIdx.x == 0) { s_prefix = 0ull; s_remaining = r; s_done = 0; }
     uint64_t mask = 0ull;
     for (int pass = 0; pass < 8; ++pass) {
       const int shift = 56 - 8 * pass;
@@ -228,21 +240,22 @@ __global__ __launch_bounds__(1024) void k_tr_select(const uint64_t* __restrict__
         if ((key & mask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], 1);
       }
       __syncthreads();
-      if (threadIdx.x == 0) {
-        int cum = 0;
-        const int rem = s_remaining;
-        for (int b = 255; b >= 0; --b) {
-          const int c = s_hist[b];
-          if (cum + c >= rem) {
-            s_prefix = prefix | ((uint64_t)b << shift);
-            s_remaining = rem - cum;
-            break;
-          }
-          cum += c;
-        }
+      // the bin holding the rem-th largest key: thread q takes bin 255 - q, so its exclusive
+      // prefix is the count of keys in the bins above; exactly one bin crosses rem
+      const int rem = s_remaining;
+      const int bq = 255 - (int)threadIdx.x;
+      const int hq = threadIdx.x < 256 ? s_hist[bq] : 0;
+      int tot;
+      const int above = block_excl_scan_1024(hq, s_wave, &tot);
+      if (threadIdx.x < 256 && above < rem && above + hq >= rem) {
+        s_prefix = prefix | ((uint64_t)bq << shift);
+        s_remaining = rem - above;
+        // every key of the bin is needed: the threshold with zero low bits is already exact
+        if (above + hq == rem) s_done = 1;
       }
       mask |= 0xFFull << shift;
       __syncthreads();
+      if (s_done) break;
     }
     thr = s_prefix;
   }
@@ -257,10 +270,10 @@ __global__ __launch_bounds__(1024) void k_tr_select(const uint64_t* __restrict__
         const int row = off + run + pos;
         row_of[(size_t)e * N + t] = row;
         row_token[row] = t;
-        row_w[row] = probs[(size_t)t * E + e] / tok_norm[t];
         int pair = -1;
         for (int j = 0; j < k; ++j)
           if (idx[(size_t)t * k + j] == e) { pair = t * k + j; break; }
+        row_w[row] = (topk_w && pair >= 0) ? topk_w[pair] : probs[(size_t)t * E + e] / tok_norm[t];
         row_pair[row] = pair;
       } else {
         row_of[(size_t)e * N + t] = -1;
@@ -270,13 +283,21 @@ __global__ __launch_bounds__(1024) void k_tr_select(const uint64_t* __restrict__
   }
 }
 
+// Token-major row lists from row_of [E, N].  One block per 64 tokens; thread (g, tl) covers
+// token t0 + tl and the experts of quarter g (e in [g E/4, (g+1) E/4)), so every load reads 64
+// consecutive tokens of one expert.
 __global__ __launch_bounds__(256) void k_tr_tokcount(const int32_t* __restrict__ row_of, int N, int E,
                                                      int32_t* __restrict__ tcount) {
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  if (t >= N) return;
+  __shared__ int s_c[4][64];
+  const int tl = threadIdx.x & 63, g = threadIdx.x >> 6;
+  const int t = blockIdx.x * 64 + tl;
+  const int e0 = g * E / 4, e1 = (g + 1) * E / 4;
   int c = 0;
-  for (int e = 0; e < E; ++e) c += row_of[(size_t)e * N + t] >= 0;
-  tcount[t] = c;
+  if (t < N)
+    for (int e = e0; e < e1; ++e) c += row_of[(size_t)e * N + t] >= 0;
+  s_c[g][tl] = c;
+  __syncthreads();
+  if (g == 0 && t < N) tcount[t] = s_c[0][tl] + s_c[1][tl] + s_c[2][tl] + s_c[3][tl];
 }
 
 // exclusive scan of tcount[0..N) into tok_ptr[0..N]; one block of 1024 threads
@@ -295,13 +316,24 @@ __global__ __launch_bounds__(1024) void k_scan_tokens(const int32_t* __restrict_
   if (threadIdx.x == 0) tok_ptr[N] = run;
 }
 
+// the kept rows of each token in ascending expert order: quarter g writes after the rows of
+// quarters 0 .. g-1
 __global__ __launch_bounds__(256) void k_tr_tokfill(const int32_t* __restrict__ row_of, int N, int E,
                                                     const int32_t* __restrict__ tok_ptr,
                                                     int32_t* __restrict__ tok_rows) {
-  const int t = blockIdx.x * 256 + threadIdx.x;
+  __shared__ int s_c[4][64];
+  const int tl = threadIdx.x & 63, g = threadIdx.x >> 6;
+  const int t = blockIdx.x * 64 + tl;
+  const int e0 = g * E / 4, e1 = (g + 1) * E / 4;
+  int c = 0;
+  if (t < N)
+    for (int e = e0; e < e1; ++e) c += row_of[(size_t)e * N + t] >= 0;
+  s_c[g][tl] = c;
+  __syncthreads();
   if (t >= N) return;
   int p = tok_ptr[t];
-  for (int e = 0; e < E; ++e) {
+  for (int q = 0; q < g; ++q) p += s_c[q][tl];
+  for (int e = e0; e < e1; ++e) {
     const int r = row_of[(size_t)e * N + t];
     if (r >= 0) tok_rows[p++] = r;
   }
@@ -318,8 +350,9 @@ size_t tr_ws_bytes(int N, int E) {
          align256((size_t)E * N * 4) + align256((size_t)N * 4) + 256;
 }
 
-hipError_t launch_token_round(const int32_t* idx, const float* probs, const float* tok_norm, int N, int E,
-                              int k, int mtile, const moe_plan& p, void* ws, hipStream_t s) {
+hipError_t launch_token_round(const int32_t* idx, const float* probs, const float* tok_norm, const float* topk_w,
+                              int N, int E, int k, int cap, int param, int use_p, const moe_plan& p, void* ws,
+                              hipStream_t s) {
   const int nb = (N + 255) / 256;
   char* w = (char*)ws;
   int32_t* bcnt = (int32_t*)w;
@@ -334,21 +367,22 @@ hipError_t launch_token_round(const int32_t* idx, const float* probs, const floa
   if (N > 0) {
     if ((err = launch_perm_hist(idx, N, E, k, bcnt, s)) != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(k_tr_sizes, dim3(1), dim3(1024), 0, s, bcnt, nb, N, E, mtile, p.counts, p.offsets);
+  hipLaunchKernelGGL(k_tr_sizes, dim3(1), dim3(1024), 0, s, bcnt, nb, N, E, param, cap, p.counts, p.offsets);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (N > 0) {
-    hipLaunchKernelGGL(k_tr_keys, dim3((N + 63) / 64, (E + 63) / 64), dim3(256), 0, s, probs, idx, N, E, k, keys);
+    hipLaunchKernelGGL(k_tr_keys, dim3((N + 63) / 64, (E + 63) / 64), dim3(256), 0, s, probs, idx, N, E, k, use_p,
+                       keys);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL(k_tr_select, dim3(E), dim3(1024), 0, s, keys, probs, tok_norm, idx, N, E, k, p.counts,
+    hipLaunchKernelGGL(k_tr_select, dim3(E), dim3(1024), 0, s, keys, probs, tok_norm, topk_w, idx, N, E, k, p.counts,
                        p.offsets, row_of, p.row_token, p.row_w, p.row_pair);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL(k_tr_tokcount, dim3((N + 255) / 256), dim3(256), 0, s, row_of, N, E, tcount);
+    hipLaunchKernelGGL(k_tr_tokcount, dim3((N + 63) / 64), dim3(256), 0, s, row_of, N, E, tcount);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   hipLaunchKernelGGL(k_scan_tokens, dim3(1), dim3(1024), 0, s, tcount, N, p.tok_ptr);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (N > 0) {
-    hipLaunchKernelGGL(k_tr_tokfill, dim3((N + 255) / 256), dim3(256), 0, s, row_of, N, E, p.tok_ptr, p.tok_rows);
+    hipLaunchKernelGGL(k_tr_tokfill, dim3((N + 63) / 64), dim3(256), 0, s, row_of, N, E, p.tok_ptr, p.tok_rows);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   return hipSuccess;

@@ -41,8 +41,9 @@ class Workload:
     bias: str = "none"    # "none" | "normal" | "zipf"
     bias_std: float = 0.0
     zipf_s: float = 0.0
-    routing: str = "topk"  # "topk" | "tr" (token rounding)
+    routing: str = "topk"  # "topk" | "tr" (token rounding) | "cap" (capacity: mtile = C)
     mtile: int = 128
+    cap_policy: int = 0    # capacity plans: 0 keeps the first C tokens, 1 the C most probable
     seed: int = 0
     w_std: float = 0.02
     extra: dict = field(default_factory=dict, compare=False)
@@ -174,6 +175,6 @@ def generate(wl: Workload, seed: int | None = None, weights: bool = True) -> Ten
 
 
 def custom(name="custom", N=256, H=128, I=96, E=8, k=2, dtype="bf16", bias="none", bias_std=0.0,
-           zipf_s=0.0, routing="topk", mtile=128, seed=7) -> Workload:
+           zipf_s=0.0, routing="topk", mtile=128, seed=7, cap_policy=0) -> Workload:
     return Workload(name, N=N, H=H, I=I, E=E, k=k, dtype=dtype, bias=bias, bias_std=bias_std,
-                    zipf_s=zipf_s, routing=routing, mtile=mtile, seed=seed)
+                    zipf_s=zipf_s, routing=routing, mtile=mtile, seed=seed, cap_policy=cap_policy)

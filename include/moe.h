@@ -57,8 +57,14 @@ typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
 typedef enum moe_plan_kind {
   MOE_PLAN_TOPK = 0,     /* plain top-k: exactly N*k rows */
-  MOE_PLAN_TR = 1        /* token rounding: per-expert rows rounded to multiples of mtile */
+  MOE_PLAN_TR = 1,       /* token rounding: per-expert rows rounded to multiples of mtile */
+  MOE_PLAN_CAP = 2       /* capacity: at most mtile (= the capacity C) rows per expert */
 } moe_plan_kind;
+
+typedef enum moe_cap_policy {
+  MOE_CAP_POSITION = 0,  /* keep an expert's first C tokens in token order */
+  MOE_CAP_PROBS = 1      /* keep its C tokens of largest probability P[t,e] (ties: lower token) */
+} moe_cap_policy;
 
 typedef enum moe_op {
   MOE_OP_PERMUTE = 0,
@@ -91,7 +97,7 @@ typedef struct moe_plan {
   int32_t kind;      /* moe_plan_kind */
   int32_t N, E, k;
   int32_t M_cap;
-  int32_t mtile;     /* MOE_PLAN_TR only (rounding granule); 0 for top-k */
+  int32_t mtile;     /* MOE_PLAN_TR: rounding granule; MOE_PLAN_CAP: capacity C; 0 for top-k */
   int32_t* counts;
   int32_t* offsets;
   int32_t* row_token;
@@ -102,8 +108,9 @@ typedef struct moe_plan {
 } moe_plan;
 
 /* Row capacity a plan of this kind needs: N*k for top-k; N*k + E*(mtile/2) for token
- * rounding (rounding to the nearest multiple adds at most mtile/2 rows per expert).
- * Returns -1 for invalid arguments.  Host-only, no GPU needed. */
+ * rounding (rounding to the nearest multiple adds at most mtile/2 rows per expert);
+ * min(N*k, E*C) for a capacity plan (mtile = C).  Returns -1 for invalid arguments.
+ * Host-only, no GPU needed. */
 int64_t moe_plan_rows_cap(int32_t kind, int32_t N, int32_t E, int32_t k, int32_t mtile);
 
 /* Bytes of workspace an operation needs (host-only, no GPU needed).  M_cap is the plan's
@@ -160,6 +167,23 @@ moe_status moe_route_token_rounding(const float* logits, const float* bias, int3
                                     void* stream);
 
 /*
+ * Capacity routing: top-k (as moe_route_topk, writing topk_idx, topk_w and probs), then the
+ * plan of the capacity-based layout of [DEP] "Drop/Padding 방식": the tokens assigned to each
+ * expert are lined up and cut at the capacity C, the rest dropped.  The line-up order is the
+ * drop policy that section names: MOE_CAP_POSITION (token order) or MOE_CAP_PROBS (P[t,e]
+ * descending, then token order).  The plan stays ragged (rows ascending by token within an
+ * expert, nothing padded: the dense E x C x H layout's padding is only a size), kept rows keep
+ * their top-k weight (row_w = topk_w[t*k+j], no renormalisation), row_pair = t*k+j, and
+ * tok_ptr / tok_rows list each token's kept rows (a token may keep fewer than k, or none).
+ * moe_layer_bwd writes ds in row order for these plans, as for token rounding.  The plan
+ * must have kind MOE_PLAN_CAP, mtile = capacity and M_cap >= moe_plan_rows_cap(); the row
+ * count sits on the device in offsets[E].  Workspace: moe_workspace_bytes(MOE_OP_ROUTE_TR, ...).
+ */
+moe_status moe_route_capacity(const float* logits, const float* bias, int32_t N, int32_t E, int32_t k,
+                              int32_t capacity, int32_t policy, int32_t* topk_idx, float* topk_w, float* probs,
+                              const moe_plan* plan, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Grouped expert MLP forward: for every row r of expert e (token t = row_token[r]),
  *   G = x[t] W_gate[e]^T,  U = x[t] W_up[e]^T        (variable-M grouped GEMM, gate and up
  *                                                      share the group sizes, [GG] "적용" (6))
@@ -202,7 +226,8 @@ moe_status moe_unpermute_combine(moe_dtype dt, const void* y, int32_t H, const m
  * ([SM] "4 기여 ②": varlen-M / varlen-K grouped GEMMs, gathers fused in the backward too.)
  *   dout, x [N,H]; hcache [M_cap,2I]; dx [N,H]; dw_gate, dw_up [E,I,H]; dw_down [E,H,I]
  *   (experts without rows get zeros); ds fp32: [N,k] in (t,j) order for top-k plans,
- *   [M_cap] in row order for token-rounding plans.  dx excludes the router's own path.
+ *   [M_cap] in row order for token-rounding and capacity plans.  dx excludes the router's
+ *   own path.
  * Workspace: moe_workspace_bytes(MOE_OP_LAYER_BWD, ...).
  */
 moe_status moe_layer_bwd(moe_dtype dt, const void* dout, const void* x, const void* w_gate,
@@ -237,7 +262,7 @@ moe_status moe_router_logits(moe_dtype dt, const void* x, const float* w_r, cons
  *   dw_r[h,m]    = sum_t x[t,h] dlogits[t,m]                      (NULL skips it)
  *   dbias[m]     = sum_t dlogits[t,m]                             (NULL skips it)
  * w_f is the plan's row_w; dS_f is ds[t*k+j] (top-k plans, row_pair = t*k+j) or ds[r] (token
- * rounding, row order), the layout moe_layer_bwd writes.  logits, dlogits fp32 [N,E]; bias
+ * rounding and capacity plans, row order), the layout moe_layer_bwd writes.  logits, dlogits fp32 [N,E]; bias
  * fp32 [E] or NULL; topk_idx int32 [N,k]; x, dx_in, dx_out [N,H] of dtype dt (dx_out may be
  * dx_in: in place); w_r fp32 [H,E]; dw_r fp32 [H,E]; dbias fp32 [E].  Everything is written
  * fresh, in a fixed order (bitwise reproducible).  Workspace: moe_workspace_bytes(

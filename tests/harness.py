@@ -21,6 +21,8 @@ def log(msg):
 def rel_err(got, ref):
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
+    if ref.size == 0:
+        return 0.0
     den = np.abs(ref).max()
     num = np.abs(got - ref).max()
     if den == 0:
@@ -58,6 +60,8 @@ def run_gpu(T: W.Tensors, D=None):
     D = D or upload(T)
     if wl.routing == "tr":
         plan, idx, w, probs = G.route_token_rounding(D["logits"], wl.k, wl.mtile, bias=D["bias"])
+    elif wl.routing == "cap":
+        plan, idx, w, probs = G.route_capacity(D["logits"], wl.k, wl.mtile, wl.cap_policy, bias=D["bias"])
     else:
         idx, w, probs = G.route_topk(D["logits"], wl.k, bias=D["bias"], want_probs=True)
         plan = G.permute(idx, w, wl.E)
@@ -95,6 +99,9 @@ def check_routing(T: W.Tensors, res: dict):
     if wl.routing == "tr":
         # bit-exact given the GPU's own probabilities and indices
         op = oracle.token_round(res["probs"], res["idx"], wl.mtile)
+    elif wl.routing == "cap":
+        # bit-exact given the GPU's own indices, weights (copied bitwise) and probabilities
+        op = oracle.capacity_plan(res["idx"], res["w"], wl.E, wl.mtile, wl.cap_policy, res["probs"])
     else:
         op = oracle.permute(idx, w, wl.E)
         # row weights are bitwise copies of the GPU's route weights
@@ -153,7 +160,7 @@ def check_layer(T: W.Tensors, res: dict, toks=None, exps=None):
     errs["out"] = rel_err(res["out"][toks], out[toks])
     g = oracle.layer_bwd(T.dout, T.x, T.wg, T.wu, T.wd, tt, te, tw, want=("dx", "ds"))
     errs["dx"] = rel_err(res["dx"][toks], g["dx"][toks])
-    if wl.routing == "tr":
+    if wl.routing in ("tr", "cap"):
         gds = res["ds"][tr]
     else:
         gds = res["ds"].reshape(-1)[res["plan"]["row_pair"][tr]]

@@ -152,6 +152,47 @@ def test_token_rounding_small_mtile():
     assert not bad, (errs, bad)
 
 
+@pytest.mark.parametrize("policy", [0, 1])
+def test_capacity_plan(policy):
+    """Capacity plans with drops (C below the busiest experts' counts), compared in full."""
+    wl = W.custom("cap-small", N=500, H=128, I=64, E=10, k=2, dtype="bf16",
+                  routing="cap", mtile=90, cap_policy=policy, seed=12)
+    T = W.generate(wl)
+    res = run_gpu(T)
+    check_routing(T, res)
+    c = res["plan"]["counts"]
+    assert c.max() == 90 and int(c.sum()) < 500 * 2
+    errs, bad = check_layer(T, res)
+    log(f"[capacity policy {policy}] {errs}")
+    assert not bad, (errs, bad)
+
+
+def test_capacity_zero_drops_everything():
+    """C = 0: no rows; out, dx and every dW are zero."""
+    wl = W.custom("cap-zero", N=64, H=64, I=32, E=4, k=2, dtype="bf16", routing="cap", mtile=0, seed=16)
+    T = W.generate(wl)
+    res = run_gpu(T)
+    check_routing(T, res)
+    assert int(res["plan"]["offsets"][-1]) == 0
+    for n in ("out", "dx", "dwg", "dwu", "dwd"):
+        assert not np.any(res[n]), n
+
+
+@pytest.mark.parametrize("policy", [0, 1])
+def test_capacity_headline_layer(policy):
+    """The headline layer (E=128, H=2048, I=512, k=8, N=4096) with capacity factor 1
+    (C = N k / E = 256), on a sample of tokens and experts."""
+    import dataclasses
+    wl = dataclasses.replace(W.CONFIGS[2], name="headline-cap", routing="cap", mtile=256, cap_policy=policy)
+    T = W.generate(wl)
+    res = run_gpu(T)
+    check_routing(T, res)
+    toks, exps = sample(T, res, 256, 6)
+    errs, bad = check_layer(T, res, toks, exps)
+    log(f"[capacity headline policy {policy}] {errs}")
+    assert not bad, (errs, bad)
+
+
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
 def test_config(cfg):
     wl = W.CONFIGS[cfg]

@@ -49,6 +49,9 @@ def _router_case(T, tag):
     if wl.routing == "tr":
         plan, idx, w, probs = G.route_token_rounding(D["logits"], wl.k, wl.mtile, bias=D["bias"])
         ds = torch.from_numpy(res["ds"]).to("cuda")
+    elif wl.routing == "cap":
+        plan, idx, w, probs = G.route_capacity(D["logits"], wl.k, wl.mtile, wl.cap_policy, bias=D["bias"])
+        ds = torch.from_numpy(res["ds"]).to("cuda")
     else:
         idx, w, probs = G.route_topk(D["logits"], wl.k, bias=D["bias"], want_probs=True)
         plan = G.permute(idx, w, wl.E)
@@ -65,7 +68,7 @@ def _router_case(T, tag):
     # oracle, given the GPU's dS per final pair (pairs in row order)
     pl = res["plan"]
     pt, pe, _ = oracle.pairs_from_plan(pl, wl.E)
-    if wl.routing == "tr":
+    if wl.routing in ("tr", "cap"):
         pds = res["ds"][:len(pt)]
     else:
         pds = res["ds"].reshape(-1)[pl["row_pair"]]
@@ -126,3 +129,11 @@ def test_router_empty_input():
 def test_router_config(cfg):
     # the full-size layer the benchmark times (E=128, H=2048, I=512, k=8, N=4096), in full
     _router_case(W.generate(W.CONFIGS[cfg]), f"config {cfg}")
+
+
+def test_router_capacity_plan():
+    # dropped pairs (inside the top-k set, without a row) enter only through the normaliser
+    wl = W.custom("cap", N=600, H=64, I=32, E=10, k=2, dtype="bf16", routing="cap", mtile=96, cap_policy=1,
+                  seed=15)
+    res, r1, ref = _router_case(W.generate(wl), "capacity")
+    assert int(res["plan"]["offsets"][-1]) < 600 * 2, "the case needs dropped pairs"
