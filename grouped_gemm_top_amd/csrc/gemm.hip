@@ -835,12 +835,6 @@ __global__ __launch_bounds__(NTHR, 2) void k_grouped_gemm(Args a, const int32_t*
   }
 }
 
-// Zero the tile counters of the dynamically scheduled grouped GEMMs of one call (a kernel
-// rather than a memset, so the call can be captured into a graph).
-__global__ __launch_bounds__(256) void k_zero_qctr(int* __restrict__ q, int n) {
-  for (int i = threadIdx.x; i < n; i += 256) q[i] = 0;
-}
-
 // dSwiGLU of the bf16 path, one wavefront per expert row r (rows at or past M only clear dS in
 // row order).  From the row's fp32 dA' (the dH GEMM's output), its cached G, U and its routing
 // weight w ("SonicMoE" section "3 기여 ①": only [G | U] is cached; dS = <dA', A>):
@@ -964,17 +958,9 @@ static hipError_t run(const gg::Args& a, long long max_tiles, hipStream_t s) {
   return hipGetLastError();
 }
 
-// tile counters of one call: two dynamically scheduled launches x 8 XCDs, 16 ints apart
-constexpr int QCTR_INTS = 2 * 8 * 16;
-
-static hipError_t zero_qctr(int* q, hipStream_t s) {
-  hipLaunchKernelGGL(gg::k_zero_qctr, dim3(1), dim3(256), 0, s, q, QCTR_INTS);
-  return hipGetLastError();
-}
-
 size_t gemm_fwd_ws_bytes(moe_dtype dt, int M_cap, int I) {
   const size_t es = dt == MOE_BF16 ? 2 : 4;
-  return align256((size_t)M_cap * I * es) + align256(QCTR_INTS * 4) + 256;
+  return align256((size_t)M_cap * I * es) + 256;
 }
 
 template <typename T>
@@ -988,12 +974,9 @@ static hipError_t gemm_fwd_t(const void* x, const void* wg, const void* wu, cons
   a.out0 = hcache; a.out1 = act;
   hipError_t err;
   if constexpr (std::is_same<T, bf16_t>::value) {
-    int* q = (int*)((char*)ws + align256((size_t)p.M_cap * I * sizeof(T)));
-    if ((err = zero_qctr(q, s)) != hipSuccess) return err;
     const long long mt = (long long)(p.M_cap + 255) / 256 + p.E;
-    a.qctr = q;
     if ((err = run_gemm_bf16<gg::GATEUP>(a, mt * ((I + 127) / 128), s)) != hipSuccess) return err;
-    a.act = act; a.out0 = y; a.out1 = nullptr; a.qctr = q + QCTR_INTS / 2;
+    a.act = act; a.out0 = y; a.out1 = nullptr;
     return run_gemm_bf16<gg::DOWN>(a, mt * ((H + 255) / 256), s);
   } else {
     const long long mt = (long long)(p.M_cap + gg::BM - 1) / gg::BM + p.E;
@@ -1016,7 +999,7 @@ size_t layer_bwd_ws_bytes(moe_dtype dt, int N, int M_cap, int H, int I) {
   // fp32: the dH kernel's dS partials; bf16: the dH GEMM's fp32 dA'
   const size_t part = dt == MOE_BF16 ? (size_t)M_cap * I * 4 : (size_t)M_cap * nTN * 4;
   return align256((size_t)M_cap * 2 * I * es) + align256((size_t)M_cap * I * es) +
-         align256((size_t)M_cap * H * es) + align256(part) + align256(QCTR_INTS * 4) + 256;
+         align256((size_t)M_cap * H * es) + align256(part) + 256;
 }
 
 template <typename T>
@@ -1036,7 +1019,6 @@ static hipError_t layer_bwd_t(const void* dout, const void* x, const void* wg, c
   w += align256((size_t)p.M_cap * H * es);
   float* dspart = (float*)w;  // fp32: dS partials; bf16: dA' [M_cap, I] in fp32
   w += align256((size_t)p.M_cap * (BF ? I : nTN) * 4);
-  int* q = (int*)w;
 
   gg::Args a{};
   a.x = x; a.wg = wg; a.wu = wu; a.wd = wd; a.dout = dout; a.hcache = hcache;
@@ -1059,11 +1041,8 @@ static hipError_t layer_bwd_t(const void* dout, const void* x, const void* wg, c
   if constexpr (BF) {
     // dA' = dOut[t] W_down^T (varlen-M GEMM, fp32 out), then the dSwiGLU kernel:
     // dH = [dG | dU], A' = w A and dS
-    if ((err = zero_qctr(q, s)) != hipSuccess) return err;
-    a.qctr = q;
     a.out0 = dspart; a.out1 = nullptr;
     if ((err = launch(KDH{}, mt * nTN)) != hipSuccess) return err;
-    a.qctr = nullptr;
     if (p.M_cap > 0) {
       kernel_event(MOE_K_DSWIGLU, 0, s);
       hipLaunchKernelGGL(gg::k_dswiglu_bf16, dim3((p.M_cap + 3) / 4), dim3(256), 0, s, dspart,
@@ -1089,9 +1068,7 @@ static hipError_t layer_bwd_t(const void* dout, const void* x, const void* wg, c
   if ((err = launch(KDWD{}, (long long)p.E * ((H + tm - 1) / tm) * nTN)) != hipSuccess) return err;
   // dXe = dH [W_gate; W_up]   (varlen-M), then the unweighted combine to token order
   a.dh = dh; a.out0 = dxe;
-  if constexpr (BF) a.qctr = q + QCTR_INTS / 2;
   if ((err = launch(KDX{}, mt * ((H + tn - 1) / tn))) != hipSuccess) return err;
-  a.qctr = nullptr;
   kernel_event(MOE_K_DX_COMBINE, 0, s);
   err = launch_combine(sizeof(T) == 2 ? MOE_BF16 : MOE_F32, dxe, H, p, nullptr, dx, s);
   kernel_event(MOE_K_DX_COMBINE, 1, s);

@@ -22,16 +22,19 @@
 //    The grid is persistent: one workgroup per CU walks its share of the tile list.
 //  * Operands go from HBM straight into LDS with buffer_load ... lds (no VGPR staging).
 //    LDS holds a ring of 4 stages of k = 32 (64 MI rows of A and 16 KB of B per stage); the
-//    loads run three k-steps ahead of the MFMAs, across tile boundaries, so a tile's prologue
-//    overlaps the previous tile's last steps and its epilogue.
+//    loads run three k-steps ahead of the MFMAs.  Varlen-M tiles run one after another: the
+//    next tile's first three steps are issued right after the finished tile's epilogue,
+//    without waiting for its stores.  Varlen-K tiles (many short ones for small groups) share
+//    one pipeline that runs across tile boundaries.
 //  * K-contiguous operands are stored as 64-byte rows, chunk c of row r at c ^ ((r >> 2) & 3),
 //    and read as one 16-byte fragment per lane.  K-strided operands (the backward's weights,
 //    both varlen-K operands) are stored in their natural layout, k-rows of 512 bytes with
 //    chunk c at c ^ f(k), and read with ds_read_b64_tr_b16, which transposes 4x16 blocks of
 //    16-bit values across each group of 16 lanes; two such reads make one MFMA fragment.
 //    Both placements spread every read over all LDS banks.
-//  * Gathered rows (x and dOut through row_token) need the token of each row: a small per-
-//    wavefront ring in LDS is filled by 4-byte LDS loads six steps ahead of use.
+//  * Gathered rows (x and dOut through row_token) need the token of each row: per wavefront,
+//    4-byte LDS loads fetch a varlen-M tile's tokens a whole tile ahead, and a varlen-K step's
+//    six steps ahead, into small slots in LDS.
 //  * Loads never branch: a buffer offset beyond the descriptor range returns zeros, which
 //    masks rows past a group's end, K tails and steps past the last tile.  Every step issues
 //    the same number of loads, so the wait for step s is an immediate vmcnt equal to the
@@ -40,12 +43,10 @@
 //  * Varlen-M tiles are ordered (expert, n-tile, m-tile) so tiles that share a weight slice
 //    run together; varlen-K tiles are ordered heaviest expert first.  Each XCD gets
 //    contiguous runs of the tile list, so neighbouring tiles share its L2.
-//  * Varlen-M tile costs vary (a group's last m-tile holds its leftover rows), so the
-//    bf16 varlen-M kinds balance dynamically: each XCD owns an eighth of the tile list, its
-//    workgroups take the first rounds in a fixed order and then draw further tiles from an
-//    XCD-local counter (one atomic add per tile).  Every tile is still computed by one
-//    workgroup in a fixed k order, so results stay bitwise reproducible; no reduction uses
-//    atomics.
+//  * The schedule is static (round r of the grid takes the next G tiles); every tile is
+//    computed by one workgroup in a fixed k order, so results are bitwise reproducible, and no
+//    reduction uses atomics.  (A dynamic variant, where each XCD's workgroups drew their last
+//    tiles from an XCD-local counter, measured slower on the ragged layers it was meant for.)
 #include "gemm_common.h"
 
 namespace moe {
@@ -69,7 +70,6 @@ constexpr int NSTG = 4;        // LDS ring depth (stages)
 constexpr int AHEAD = NSTG - 1;
 constexpr int OPB = 16384;     // bytes of one operand per stage
 constexpr int TOKB = 256;      // bytes per token slot (64 row indices)
-constexpr int QN = 16;         // ring of dynamically assigned tile indices (a power of two)
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -162,21 +162,18 @@ template <int N>
 __device__ __forceinline__ void vm_wait_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
-// The wait for step s of a wavefront that issues NLW loads per step: the memory instructions it
-// issued after step s's loads are the two later steps' loads, the token loads among them (ts,
-// varlen-M gathers) and the stores of the ne epilogues in between (at least ST each).
-// Rounding an allowance down only makes the wait stricter.
+// The wait for step s of a wavefront that issues NLW loads per step (varlen-K): the memory
+// instructions it issued after step s's loads are the two later steps' loads and the stores of
+// the ne epilogues in between (at least ST each).  Rounding an allowance down only makes the
+// wait stricter.
 template <int NLW, int ST>
-__device__ __forceinline__ void step_wait(int ne, int ts) {
+__device__ __forceinline__ void step_wait(int ne) {
   constexpr int X0 = 2 * NLW;
   constexpr int X1 = (X0 + ST) < 63 ? (X0 + ST) : 63;
   constexpr int X2 = (X0 + 2 * ST) < 63 ? (X0 + 2 * ST) : 63;
   constexpr int X3 = (X0 + 3 * ST) < 63 ? (X0 + 3 * ST) : 63;
-  if (ne == 0) {
-    if (ts == 0) vm_wait_barrier<X0>();
-    else if (ts == 1) vm_wait_barrier<X0 + 1>();
-    else vm_wait_barrier<X0 + 2>();
-  } else if (ne == 1) vm_wait_barrier<X1>();
+  if (ne == 0) vm_wait_barrier<X0>();
+  else if (ne == 1) vm_wait_barrier<X1>();
   else if (ne == 2) vm_wait_barrier<X2>();
   else vm_wait_barrier<X3>();
 }
@@ -193,23 +190,15 @@ struct Sched {
   using T = KT<KIND>;
   static constexpr int BMK = Geo<KIND>::BMK;
   const int* s_sched;  // LDS: varlen-M tile prefix [E+1]; varlen-K expert order [E]
-  const int* s_q;      // LDS: tile index of the workgroup's j-th tile at [j & (QN - 1)] (dynamic)
   int total, G, per, xcd, slot, E, nN, nMg, nM;
-  // dynamic schedule (varlen-M): this XCD owns tiles [lo, hi); its workgroups take rounds
-  // 0 .. R-1 statically (tile lo + j*per + slot) and the rest from the XCD's counter
-  int dyn, lo, hi, R;
 
+  // Tile `it` of this workgroup: round it of the grid, where XCD x takes the run
+  // [x per, (x + 1) per) of the round's G tiles and its workgroups one tile each.
   __device__ __forceinline__ void decode(const Args& a, Tile& c, int it) const {
     c.it = it;
     c.kt = 0;
-    long long tl;
-    if (dyn) {
-      tl = it < R ? (long long)lo + (long long)it * per + slot : (long long)ufl(s_q[it & (QN - 1)]);
-      c.valid = tl >= 0 && tl < (long long)hi;
-    } else {
-      tl = (long long)it * G + (long long)xcd * per + slot;
-      c.valid = tl < (long long)total;
-    }
+    const long long tl = (long long)it * G + (long long)xcd * per + slot;
+    c.valid = tl < (long long)total;
     if (!c.valid) {
       c.e = 0; c.roff = 0; c.mt = 0; c.nt = 0; c.mlen = 0; c.K = 0; c.nk = 0;
       return;
@@ -681,6 +670,15 @@ __device__ __forceinline__ bf16x8 frag_mn(const char* op, int x0, int mn_k0, int
   return __builtin_bit_cast(bf16x8, p);
 }
 
+// The wait before a varlen-M step: `later` of the tile's following steps (at most two, P
+// memory instructions each) were issued after this step's loads.
+template <int P>
+__device__ __forceinline__ void mstep_wait(int later) {
+  if (later >= 2) vm_wait_barrier<2 * P>();
+  else if (later == 1) vm_wait_barrier<P>();
+  else vm_wait_barrier<0>();
+}
+
 // ------------------------------------------------------------------ the kernel
 template <int KIND>
 __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __restrict__ counts,
@@ -691,14 +689,13 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
   using G = Geo<KIND>;
   constexpr bool GATHER = T::GA || T::GB;
   // memory instructions per step and wavefront: 4 operand loads (plus one more A load on
-  // wavefronts w < NA - 16), plus the token load that varlen-K kinds issue every step
-  // (varlen-M kinds issue theirs only at tile starts and count them separately)
+  // wavefronts w < NA - 16), plus the token load that gathered varlen-K kinds issue every
+  // step (varlen-M kinds issue theirs once per tile, before the tile's step loads)
   constexpr int NLW = 4 + (T::VK && GATHER ? 1 : 0);
 
   __shared__ __attribute__((aligned(1024))) char s_ring[NSTG * G::STGK];
   __shared__ __attribute__((aligned(256))) int s_tok[8 * NSTG * (TOKB / 4)];
   __shared__ int s_sched[1025];
-  __shared__ int s_q[QN];
   __shared__ int s_wsum[9];
 
   const int tid = threadIdx.x, L = tid & 63;
@@ -708,8 +705,6 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
 
   Sched<KIND> S;
   S.s_sched = s_sched;
-  S.s_q = s_q;
-  S.dyn = 0;
   S.E = E;
   S.G = gridDim.x;
   S.per = S.G >> 3;
@@ -760,12 +755,6 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
     if (tid == 0) s_sched[E] = s_wsum[8];
     S.total = ufl(s_wsum[8]);
     __syncthreads();
-    if (a.qctr != nullptr) {
-      S.dyn = 1;
-      S.lo = (int)((long long)S.total * S.xcd / 8);
-      S.hi = (int)((long long)S.total * (S.xcd + 1) / 8);
-      S.R = max(1, S.total / S.G - 1);
-    }
   } else {
     // heaviest expert first: rank_e = #{f : c_f > c_e or (c_f == c_e and f < e)}
     int* s_cnt = reinterpret_cast<int*>(s_ring);  // the ring is free until the first load
@@ -790,17 +779,6 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // ---- compute cursor; tiles without k-steps (empty experts, varlen-K) only write zeros ----
-  Tile Cc;
-  S.decode(a, Cc, 0);
-  if constexpr (T::VK) {
-    while (Cc.valid && Cc.nk == 0) {
-      epilogue<KIND>(a, Cc, acc, wm, wn, L, S.nMg, s_ring + w * 4096);
-      S.decode(a, Cc, Cc.it + 1);
-    }
-  }
-  if (!Cc.valid) return;
-
   // per-lane fragment addressing
   const int kc_off = (L & 15) * 64 + ((((L >> 4) ^ kc_swz(L & 15)) & 3) << 4);
   const int mn_m = L & 15, mn_g = L >> 4;
@@ -808,224 +786,253 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
   const int mn_ff = 2 * ((mn_m >> 2) | ((mn_g & 1) << 2));
   const int mn_b = (mn_m >> 1) & 1;
 
+  // The MFMAs of one k-step from the stage at `sa`: this wavefront's row blocks 16(4i + wm)
+  // that start below the tile's row count (nb = mlen - 16 wm > 64 i; a block at or past it
+  // holds rows of no group and is skipped) times its 128 columns.
+  auto mma_stage = [&](const char* sa, int nb) __attribute__((always_inline)) {
+    // opaque copies: the per-fragment LDS positions derived from these are recomputed each
+    // step rather than held in registers across the loop
+    int kco = kc_off, k0o = mn_k0, ffo = mn_ff, bo = mn_b;
+    asm volatile("" : "+v"(kco), "+v"(k0o), "+v"(ffo), "+v"(bo));
+    const char* sb = sa + G::OPA;
+    auto frag_a = [&](int i) __attribute__((always_inline)) {
+      if constexpr (T::A_KC) return frag_kc(sa, 16 * (4 * i + wm), kco);
+      else return frag_mn(sa, 16 * (4 * i + wm), k0o, ffo, bo);
+    };
+    auto frag_b = [&](int j) __attribute__((always_inline)) {
+      if constexpr (T::B_KC) return frag_kc(sb, wn * 128 + 16 * j, kco);
+      else return frag_mn(sb, wn * 128 + 16 * j, k0o, ffo, bo);
+    };
+    if constexpr (G::MI == 4) {
+      // every fragment read first, then the MFMAs
+      bf16x8 fa[4], fb[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) fb[j] = frag_b(j);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fa[i] = frag_a(i);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (i == 0 || nb > 64 * i) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[i][j] = mma(fb[j], fa[i], acc[i][j]);
+        }
+    } else if constexpr (KIND == DH) {
+      // (fewer live fragments, for the register budget of the dSwiGLU epilogue) all A
+      // fragments first, then the B fragments one column block ahead
+      bf16x8 fa[G::MI];
+#pragma unroll
+      for (int i = 0; i < G::MI; ++i) fa[i] = frag_a(i);
+      bf16x8 fb = frag_b(0);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        bf16x8 fn;
+        if (j + 1 < 8) fn = frag_b(j + 1);
+#pragma unroll
+        for (int i = 0; i < G::MI; ++i)
+          if (i == 0 || nb > 64 * i) acc[i][j] = mma(fb, fa[i], acc[i][j]);
+        if (j + 1 < 8) fb = fn;
+      }
+    } else {
+      // all B fragments first, then the A fragments one row block ahead: block i + 1's read
+      // is in flight during block i's MFMAs
+      bf16x8 fb[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) fb[j] = frag_b(j);
+      bf16x8 fa = frag_a(0);
+#pragma unroll
+      for (int i = 0; i < G::MI; ++i) {
+        bf16x8 fn;
+        if (i + 1 < G::MI) fn = frag_a(i + 1);
+        if (i == 0 || nb > 64 * i) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[i][j] = mma(fb[j], fa, acc[i][j]);
+        }
+        if (i + 1 < G::MI) fa = fn;
+      }
+    }
+  };
+
   Loader<KIND> ld;
   ld.init(w, L);
   const i32x4 rtok = dmadesc(a.row_token, 4LL * (long long)a.M_cap);
-  int* my_tok = s_tok + w * NSTG * (TOKB / 4);  // this wavefront's token ring
+  int* my_tok = s_tok + w * NSTG * (TOKB / 4);  // this wavefront's token slots
   const uint32_t tok_m0 = lds_addr(my_tok);
   const uint32_t ring_m0 = lds_addr(s_ring);  // stage 0
 
-  // token load for cursor t at step index s: per step (varlen-K), or at a tile's first step
-  // (varlen-M, which then returns 1: the number of loads it issued)
-  auto tok_issue = [&](const Tile& t, int s) __attribute__((always_inline)) -> int {
-    const uint32_t m0 = tok_m0 + (uint32_t)(s & (NSTG - 1)) * TOKB;
-    if constexpr (T::VK) {
-      dma4(rtok, m0, t.valid ? (uint32_t)(t.roff + t.kt * BK + 4 * w + L) * 4u : OOB);
-      return 1;
-    } else {
-      if (t.valid && t.kt == 0) {
+  if constexpr (!T::VK) {
+    // ---- varlen-M: this workgroup's tiles one after another ----
+    // Every tile has k-steps (groups without rows have no tiles).  A tile's step loads follow
+    // the previous tile's epilogue without a drain: the vmcnt wait of its first step also
+    // covers those older stores.  Its tokens (gathered A) were loaded into LDS during the
+    // previous tile, before that tile's step loads, so the previous tile's last wait (vmcnt 0)
+    // has seen them land; tokens alternate between two slots (tile it uses slot it & 1).
+    auto tok_load = [&](const Tile& t) __attribute__((always_inline)) {
+      if constexpr (T::GA) {
         // lane L: the token of row 16w + (L & 15) + 128 (L >> 4), i.e. of A instruction
         // w + 8 (L >> 4) (rows past the tile's instructions are never used)
-        dma4(rtok, m0, (uint32_t)(t.roff + t.mt * G::BMK + 16 * w + (L & 15) + 128 * (L >> 4)) * 4u);
-        return 1;
+        if (t.valid)
+          dma4(rtok, tok_m0 + (uint32_t)(t.it & 1) * TOKB,
+               (uint32_t)(t.roff + t.mt * G::BMK + 16 * w + (L & 15) + 128 * (L >> 4)) * 4u);
       }
-      return 0;
-    }
-  };
-  Tile Ld = Cc, Tk = Cc;
-  auto load_issue = [&](int s) __attribute__((always_inline)) {
-    const int* tk = my_tok + (s & (NSTG - 1)) * (TOKB / 4);
-    if (Ld.kt == 0) ld.setup(a, Ld, tk, w, L, S.nMg);
-    ld.issue(a, Ld, ring_m0 + (uint32_t)(s & (NSTG - 1)) * G::STGK, tk, w, L);
-    S.next(a, Ld, true);
-  };
-  // Dynamic schedule: when the leading cursor (Tk for gathered kinds, else Ld) starts the tile
-  // before sequence index f_next, wavefront 0 takes tile f_next from the XCD's counter and
-  // stores its index in s_q.  Waiting for the atomic also waits for wavefront 0's loads in
-  // flight, so it happens once per dynamic tile only.  The index reaches the other
-  // wavefronts through the next barrier (sync: a barrier right here, where several cursor
-  // steps follow without one, as in the prologue).
-  int f_next = S.R;
-  auto lead_moved = [&](const Tile& lead, bool sync) __attribute__((always_inline)) {
-    if constexpr (!T::VK) {
-      if (S.dyn && lead.valid && lead.it + 1 == f_next) {
-        if (w == 0) {
-          if (L == 0) {
-            const int v = __hip_atomic_fetch_add(a.qctr + 16 * S.xcd, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const long long t = (long long)S.lo + (long long)S.R * S.per + v;
-            s_q[f_next & (QN - 1)] = t < (long long)S.hi ? (int)t : -1;
-          }
-          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        }
-        ++f_next;
-        if (sync) lds_barrier();
-      }
-    }
-  };
-  if constexpr (GATHER) lead_moved(Tk, true);
-  else lead_moved(Ld, true);
-
-  // ---- prologue: tokens of steps 0..2 resident, loads of steps 0..2 in flight ----
-  // t1, t2: token loads issued with the last and the second-to-last step's loads (varlen-M)
-  int t1 = 0, t2 = 0;
-  if constexpr (GATHER) {
-#pragma unroll 1
-    for (int s = 0; s < AHEAD; ++s) {
-      tok_issue(Tk, s);
-      S.next(a, Tk, true);
-      lead_moved(Tk, true);
-    }
-    vm_drain();
-  }
-#pragma unroll 1
-  for (int s = 0; s < AHEAD; ++s) {
-    int tn = 0;
-    if constexpr (GATHER) {
-      tn = tok_issue(Tk, s + AHEAD);
-      S.next(a, Tk, true);
-      lead_moved(Tk, true);
-    }
-    load_issue(s);
-    if constexpr (!GATHER) lead_moved(Ld, true);
-    t2 = t1;
-    t1 = tn;
-  }
-
-  // epilogues issued after the loads of the last three steps (their stores are younger)
-  int h0 = 0, h1 = 0, h2 = 0;
-
-#pragma unroll 1
-  for (int s = 0;; ++s) {
-    // step s's loads (issued three steps ago) have landed for every wavefront, and every
-    // wavefront is done with the stage that the loads below overwrite
-    const int ne = h0 + h1 + h2;
-    const int ts = (T::GA && !T::VK) ? t1 + t2 : 0;  // varlen-K: the token loads are part of NLW
-    if constexpr (G::NA > 16) {
-      if (w < G::NA - 16) step_wait<NLW + 1, T::ST>(ne, ts);
-      else step_wait<NLW, T::ST>(ne, ts);
-    } else {
-      step_wait<NLW, T::ST>(ne, ts);
-    }
-    h2 = h1;
-    h1 = h0;
-    h0 = 0;
-
-    // ---- this step's loads (three steps ahead) and the MFMAs of step s ----
-    auto issue_block = [&]() __attribute__((always_inline)) {
-      int tn = 0;
-      if constexpr (GATHER) {
-        tn = tok_issue(Tk, s + 2 * AHEAD);
-        S.next(a, Tk, true);
-        lead_moved(Tk, false);
-      }
-      load_issue(s + AHEAD);
-      if constexpr (!GATHER) lead_moved(Ld, false);
-      t2 = t1;
-      t1 = tn;
     };
-    auto mma_block = [&]() __attribute__((always_inline)) {
-      // row block i of this wavefront (rows 16(4i + wm) ..) takes part while it starts below
-      // mlen; a short tile's blocks are spread over all four SIMDs
-      if (Cc.mlen > 16 * wm) {
-        const int nb = Cc.mlen - 16 * wm;
-        // opaque copies: the per-fragment LDS positions derived from these are recomputed each
-        // step rather than held in registers across the loop
-        int kco = kc_off, k0o = mn_k0, ffo = mn_ff, bo = mn_b;
-        asm volatile("" : "+v"(kco), "+v"(k0o), "+v"(ffo), "+v"(bo));
-        const char* sa = s_ring + (s & (NSTG - 1)) * G::STGK;
-        const char* sb = sa + G::OPA;
-        auto frag_a = [&](int i) __attribute__((always_inline)) {
-          if constexpr (T::A_KC) return frag_kc(sa, 16 * (4 * i + wm), kco);
-          else return frag_mn(sa, 16 * (4 * i + wm), k0o, ffo, bo);
-        };
-        auto frag_b = [&](int j) __attribute__((always_inline)) {
-          if constexpr (T::B_KC) return frag_kc(sb, wn * 128 + 16 * j, kco);
-          else return frag_mn(sb, wn * 128 + 16 * j, k0o, ffo, bo);
-        };
-        // a row block at or past mlen skips its MFMAs (its fragment holds rows of no group)
-        if constexpr (G::MI == 4) {
-          // every fragment read first, then the MFMAs
-          bf16x8 fa[4], fb[8];
-  #pragma unroll
-          for (int j = 0; j < 8; ++j) fb[j] = frag_b(j);
-  #pragma unroll
-          for (int i = 0; i < 4; ++i) fa[i] = frag_a(i);
-  #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (i == 0 || nb > 64 * i) {
-  #pragma unroll
-              for (int j = 0; j < 8; ++j) acc[i][j] = mma(fb[j], fa[i], acc[i][j]);
-            }
-        } else if constexpr (KIND == DH) {
-          // (fewer live fragments, for the register budget of the dSwiGLU epilogue) all A
-          // fragments first, then the B fragments one column block ahead
-          bf16x8 fa[G::MI];
-  #pragma unroll
-          for (int i = 0; i < G::MI; ++i) fa[i] = frag_a(i);
-          bf16x8 fb = frag_b(0);
-  #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            bf16x8 fn;
-            if (j + 1 < 8) fn = frag_b(j + 1);
-  #pragma unroll
-            for (int i = 0; i < G::MI; ++i)
-              if (i == 0 || nb > 64 * i) acc[i][j] = mma(fb, fa[i], acc[i][j]);
-            if (j + 1 < 8) fb = fn;
-          }
+    // the first min(AHEAD, nk) steps of tile t, whose first step takes ring stage gs
+    auto issue_first = [&](const Tile& t, int gs) __attribute__((always_inline)) {
+#pragma unroll 1
+      for (int q = 0; q < AHEAD; ++q)
+        if (q < t.nk) {
+          Tile u = t;
+          u.kt = q;
+          ld.issue(a, u, ring_m0 + (uint32_t)((gs + q) & (NSTG - 1)) * G::STGK, my_tok, w, L);
+        }
+    };
+    {
+      Tile C0;
+      S.decode(a, C0, 0);
+      if (!C0.valid) return;
+      tok_load(C0);
+      vm_drain();
+    }
+    int gs = 0;  // ring sequence number of the current tile's first step
+#pragma unroll 1
+    for (int it = 0;; ++it) {
+      Tile Cc;
+      S.decode(a, Cc, it);
+      if (!Cc.valid) break;
+      ld.setup(a, Cc, my_tok + (it & 1) * (TOKB / 4), w, L, S.nMg);
+      {
+        Tile Cn;
+        S.decode(a, Cn, it + 1);
+        tok_load(Cn);
+      }
+      issue_first(Cc, gs);
+      const int nk = Cc.nk;
+      const int nb = Cc.mlen - 16 * wm;
+#pragma unroll 1
+      for (int kt = 0; kt < nk; ++kt) {
+        // step kt's loads have landed for every wavefront, and every wavefront is done with
+        // the stage that the loads below refill (the stage of step kt - 1)
+        const int later = min(2, nk - 1 - kt);
+        if constexpr (G::NA > 16) {
+          if (w < G::NA - 16) mstep_wait<NLW + 1>(later);
+          else mstep_wait<NLW>(later);
         } else {
-          // all B fragments first, then the A fragments one row block ahead: block i + 1's read
-          // is in flight during block i's MFMAs
-          bf16x8 fb[8];
-  #pragma unroll
-          for (int j = 0; j < 8; ++j) fb[j] = frag_b(j);
-          bf16x8 fa = frag_a(0);
-  #pragma unroll
-          for (int i = 0; i < G::MI; ++i) {
-            bf16x8 fn;
-            if (i + 1 < G::MI) fn = frag_a(i + 1);
-            if (i == 0 || nb > 64 * i) {
-  #pragma unroll
-              for (int j = 0; j < 8; ++j) acc[i][j] = mma(fb[j], fa, acc[i][j]);
-            }
-            if (i + 1 < G::MI) fa = fn;
-          }
+          mstep_wait<NLW>(later);
         }
+        if (kt + AHEAD < nk) {
+          Tile u = Cc;
+          u.kt = kt + AHEAD;
+          ld.issue(a, u, ring_m0 + (uint32_t)((gs + kt + AHEAD) & (NSTG - 1)) * G::STGK, my_tok, w, L);
+        }
+        if (nb > 0) mma_stage(s_ring + ((gs + kt) & (NSTG - 1)) * G::STGK, nb);
       }
-    };
-    // The two wavefronts of a SIMD (wn = 0 and 1) take the two halves in opposite orders, so
-    // one's load issue and bookkeeping overlap the other's MFMAs instead of both waiting on
-    // the same phase.
-    if (wn == 0) issue_block();
-    mma_block();
-    if (wn != 0) issue_block();
-
-    // ---- advance the compute cursor; finish a tile after its last step ----
-    if (Cc.kt + 1 < Cc.nk) {
-      ++Cc.kt;
-    } else {
-      // the stage of step s is free once every wavefront has read its fragments; the loads
-      // that refill it are issued only after the next step's barrier
-      char* st = s_ring + (s & (NSTG - 1)) * G::STGK + w * 4096;
+      // every wavefront is done with the ring; the last step's stage stages the epilogue
+      char* st = s_ring + ((gs + nk - 1) & (NSTG - 1)) * G::STGK + w * 4096;
       lds_barrier();
       epilogue<KIND>(a, Cc, acc, wm, wn, L, S.nMg, st);
-      ++h0;
 #pragma unroll
       for (int i = 0; i < G::MI; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      gs += nk;
+    }
+    vm_drain();
+  } else {
+    // ---- varlen-K: one pipeline over the workgroup's tiles, three steps ahead ----
+    // Tiles without k-steps (empty groups) only write zeros.
+    Tile Cc;
+    S.decode(a, Cc, 0);
+    while (Cc.valid && Cc.nk == 0) {
+      epilogue<KIND>(a, Cc, acc, wm, wn, L, S.nMg, s_ring + w * 4096);
       S.decode(a, Cc, Cc.it + 1);
-      if constexpr (T::VK) {
+    }
+    if (!Cc.valid) return;
+
+    // the token load of cursor t at step index s (gathered kinds, every step)
+    auto tok_issue = [&](const Tile& t, int s) __attribute__((always_inline)) {
+      const uint32_t m0 = tok_m0 + (uint32_t)(s & (NSTG - 1)) * TOKB;
+      dma4(rtok, m0, t.valid ? (uint32_t)(t.roff + t.kt * BK + 4 * w + L) * 4u : OOB);
+    };
+    Tile Ld = Cc, Tk = Cc;
+    auto load_issue = [&](int s) __attribute__((always_inline)) {
+      const int* tk = my_tok + (s & (NSTG - 1)) * (TOKB / 4);
+      if (Ld.kt == 0) ld.setup(a, Ld, tk, w, L, S.nMg);
+      ld.issue(a, Ld, ring_m0 + (uint32_t)(s & (NSTG - 1)) * G::STGK, tk, w, L);
+      S.next(a, Ld, true);
+    };
+
+    // ---- prologue: tokens of steps 0..2 resident, loads of steps 0..2 in flight ----
+    if constexpr (GATHER) {
+#pragma unroll 1
+      for (int s = 0; s < AHEAD; ++s) {
+        tok_issue(Tk, s);
+        S.next(a, Tk, true);
+      }
+      vm_drain();
+    }
+#pragma unroll 1
+    for (int s = 0; s < AHEAD; ++s) {
+      if constexpr (GATHER) {
+        tok_issue(Tk, s + AHEAD);
+        S.next(a, Tk, true);
+      }
+      load_issue(s);
+    }
+
+    // epilogues issued after the loads of the last three steps (their stores are younger)
+    int h0 = 0, h1 = 0, h2 = 0;
+
+#pragma unroll 1
+    for (int s = 0;; ++s) {
+      // step s's loads (issued three steps ago) have landed for every wavefront, and every
+      // wavefront is done with the stage that the loads below overwrite
+      const int ne = h0 + h1 + h2;
+      static_assert(G::NA == 16, "varlen-K: every wavefront issues NLW loads per step");
+      step_wait<NLW, T::ST>(ne);
+      h2 = h1;
+      h1 = h0;
+      h0 = 0;
+
+      // ---- this step's loads (three steps ahead) and the MFMAs of step s ----
+      auto issue_block = [&]() __attribute__((always_inline)) {
+        if constexpr (GATHER) {
+          tok_issue(Tk, s + 2 * AHEAD);
+          S.next(a, Tk, true);
+        }
+        load_issue(s + AHEAD);
+      };
+      // The two wavefronts of a SIMD (wn = 0 and 1) take the two halves in opposite orders,
+      // so one's load issue and bookkeeping overlap the other's MFMAs instead of both waiting
+      // on the same phase.
+      if (wn == 0) issue_block();
+      if (Cc.mlen > 16 * wm) mma_stage(s_ring + (s & (NSTG - 1)) * G::STGK, Cc.mlen - 16 * wm);
+      if (wn != 0) issue_block();
+
+      // ---- advance the compute cursor; finish a tile after its last step ----
+      if (Cc.kt + 1 < Cc.nk) {
+        ++Cc.kt;
+      } else {
+        // the stage of step s is free once every wavefront has read its fragments; the loads
+        // that refill it are issued only after the next step's barrier
+        char* st = s_ring + (s & (NSTG - 1)) * G::STGK + w * 4096;
+        lds_barrier();
+        epilogue<KIND>(a, Cc, acc, wm, wn, L, S.nMg, st);
+        ++h0;
+#pragma unroll
+        for (int i = 0; i < G::MI; ++i)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        S.decode(a, Cc, Cc.it + 1);
         while (Cc.valid && Cc.nk == 0) {
           epilogue<KIND>(a, Cc, acc, wm, wn, L, S.nMg, st);
           ++h0;
           S.decode(a, Cc, Cc.it + 1);
         }
+        if (!Cc.valid) break;
       }
-      if (!Cc.valid) break;
     }
+    // loads past the last tile (all masked) must land before the workgroup's LDS is released
+    vm_drain();
   }
-  // loads past the last tile (all masked) must land before the workgroup's LDS is released
-  vm_drain();
 }
 
 }  // namespace g4

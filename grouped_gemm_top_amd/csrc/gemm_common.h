@@ -25,9 +25,6 @@ struct Args {
   const int32_t* offsets;
   const int32_t* row_token;
   const float* row_w;
-  // bf16 varlen-M kinds: eight tile counters (one per XCD, 16 ints apart), zero when the
-  // kernel starts; null selects the fully static schedule
-  int* qctr;
   int E, H, I;
   int N, M_cap;
 };
