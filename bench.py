@@ -60,6 +60,14 @@ def kernel_work(name, wl, M, e_act, es):
     return 0.0, 0.0
 
 
+def layer_bytes(wl, M, e_act, es):
+    """Algorithmic HBM bytes of one forward + backward step: weights of the active experts read
+    in the forward and the backward, dW written for every expert, x, out, dOut and dX once,
+    hcache, A, dH and A' traffic (14 M I) and Y and dXe each written and read (4 M H)."""
+    N, H, I, E = wl.N, wl.H, wl.I, wl.E
+    return float(es) * ((6.0 * e_act + 3.0 * E) * H * I + 4.0 * N * H + 14.0 * M * I + 4.0 * M * H)
+
+
 def load_traffic(name, workload):
     """HBM bytes per launch of kernel `name`, from the rocprofv3 FETCH_SIZE / WRITE_SIZE passes
     summarised in profiles/traffic_<workload>.txt.  Returned only while the kernel's source file
@@ -117,9 +125,11 @@ def main():
     ap.add_argument("--capacity-factor", type=float, default=1.0)
     ap.add_argument("--cap-policy", type=int, choices=(0, 1), default=0,
                     help="capacity drop policy: 0 keeps the first C tokens, 1 the C most probable")
-    ap.add_argument("--mode", choices=("layer", "copy"), default="layer",
+    ap.add_argument("--mode", choices=("layer", "copy", "peak"), default="layer",
                     help="copy: time a plain 1 GiB device-to-device copy (the calibration run for the "
-                         "FETCH_SIZE / WRITE_SIZE counters)")
+                         "FETCH_SIZE / WRITE_SIZE counters); peak: only the measured device peaks "
+                         "(dense bf16 MFMA and HBM streaming probes)")
+    ap.add_argument("--peaks", type=int, default=1, help="measure the device peaks after the layer (1/0)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -149,6 +159,13 @@ def main():
         dt = (time.perf_counter() - t0) / args.steps
         print(json.dumps({"mode": "copy", "bytes_read": nbytes, "bytes_written": nbytes, "launches": args.steps,
                           "ms": round(dt * 1e3, 4), "gbs": round(2 * nbytes / dt / 1e9, 1)}), flush=True)
+        return
+    if args.mode == "peak":
+        from grouped_gemm_top_amd import probe
+        pk = probe.measure_peaks()
+        pk.update({"mode": "peak", "published_mfma_bf16_tflops": PEAK_BF16_TFLOPS,
+                   "published_hbm_gbs": PEAK_HBM_GBS})
+        print(json.dumps(pk), flush=True)
         return
     G.lib()
     wl = W.CONFIGS[args.config]
@@ -343,6 +360,22 @@ def main():
             "logits_tflops": round(fl / (r_us["router_logits"] * 1e-6) / 1e12, 2),
             "bwd_us": round(r_us["router_dz"] + r_us["router_dx"] + r_us["router_dw"], 2),
         }
+    # The bound the whole step can reach: the larger of its FLOPs at the MFMA peak and its
+    # algorithmic bytes (every tensor touched once per pass) at the HBM peak.
+    lb = layer_bytes(wl, M, e_act, es)
+    t_bound = max(flops / (peak * 1e12), lb / (PEAK_HBM_GBS * 1e9))
+    res["attainable"] = {"algorithmic_bytes": lb, "t_bound_ms": round(t_bound * 1e3, 4),
+                         "bound": "hbm" if lb / (PEAK_HBM_GBS * 1e9) >= flops / (peak * 1e12) else "mfma",
+                         "frac_of_bound": round(t_bound / (ms * 1e-3), 4),
+                         "max_pct_of_mfma_peak": round(100.0 * flops / (peak * 1e12) / t_bound, 2)}
+    if args.peaks:
+        from grouped_gemm_top_amd import probe
+        pk = probe.measure_peaks()
+        pk["note"] = ("measured with the probes of libmoe_probe.so (inline-asm MFMA loop on registers; "
+                      "16-byte streaming copy and read of 1 GiB); roofline.peak stays the published figure")
+        res["measured_peaks"] = pk
+        res["pct_of_measured_mfma_peak"] = round(100.0 * tflops / max(pk["mfma_bf16_16x16x32_tflops"],
+                                                                      pk["mfma_bf16_32x32x16_tflops"]), 2)
     pad = float(sum(((c + 127) // 128) * 128 for c in counts)) / max(M, 1) - 1.0
     res["padded_row_fraction_tile128"] = round(pad, 4)
     if cap:

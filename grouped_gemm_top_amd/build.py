@@ -1,4 +1,5 @@
-"""Build libmoe.so (all HIP sources under csrc/) for gfx950 with hipcc, in-tree."""
+"""Build libmoe.so (all HIP sources under csrc/) and libmoe_probe.so (the measurement probes
+under csrc/probe/) for gfx950 with hipcc, in-tree."""
 from __future__ import annotations
 
 import glob
@@ -12,6 +13,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmoe.so")
+PROBE_LIB = os.path.join(HERE, "libmoe_probe.so")
 BUILD = os.path.join(ROOT, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -28,13 +30,9 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    """Compile every source (always) and link libmoe.so.  Returns the library path."""
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
-
+def _compile_link(srcs, lib, tag, verbose, jobs):
     def compile_one(src):
-        obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+        obj = os.path.join(BUILD, tag + os.path.basename(src) + ".o")
         cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
@@ -49,12 +47,20 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
 
     with ThreadPoolExecutor(max(1, min(jobs, len(srcs)))) as ex:
         objs = list(ex.map(compile_one, srcs))
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False, jobs: int = 8) -> str:
+    """Compile every source (always) and link libmoe.so and libmoe_probe.so.  Returns the
+    path of libmoe.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    _compile_link(sources(), LIB, "", verbose, jobs)
+    _compile_link(sorted(glob.glob(os.path.join(CSRC, "probe", "*.hip"))), PROBE_LIB, "probe_", verbose, jobs)
     return LIB
 
 

@@ -1,0 +1,111 @@
+// peak_probe.hip -- measurement probes: dense bf16 MFMA throughput and HBM streaming
+// bandwidth on gfx950 (the peaks the layer's kernels are compared against).
+#include <hip/hip_runtime.h>
+
+#include "moe_probe.h"
+
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// Each wavefront keeps eight (shape 0) or four (shape 1) accumulators in flight, so
+// consecutive MFMAs never depend on each other and the matrix core issues back to back.
+// Operands are small integers, so every sum is exact and stays far from overflow.  The MFMAs
+// are written as inline assembly on VGPR operands: as builtins the compiler places these few
+// accumulators in AGPRs and copies them around every iteration, which is not what a peak
+// probe should time.
+template <int SHAPE>
+__global__ __launch_bounds__(256) void k_mfma_peak(float* __restrict__ sink, int iters) {
+  const int tid = blockIdx.x * 256 + threadIdx.x;
+  bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(float)((threadIdx.x + i) & 3);
+    b[i] = (__bf16)(float)((3 * threadIdx.x + i) & 3);
+  }
+  float s = 0.f;
+  if constexpr (SHAPE == 0) {
+    f32x4 acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    asm volatile("s_nop 7" ::: "memory");  // the VALU writes of acc settle before the MFMAs read it
+#pragma unroll 1
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc[j]) : "v"(a), "v"(b));
+    }
+    asm volatile("s_nop 15" ::: "memory");  // the last MFMA results land before VALU reads
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+  } else {
+    f32x16 acc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
+    asm volatile("s_nop 7" ::: "memory");
+#pragma unroll 1
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc[j]) : "v"(a), "v"(b));
+    }
+    asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s += acc[j][v];
+  }
+  sink[tid] = s;
+}
+
+__global__ __launch_bounds__(256) void k_copy16(const uint4* __restrict__ src, uint4* __restrict__ dst, size_t n) {
+  const size_t stride = (size_t)gridDim.x * 256;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) dst[i] = src[i];
+}
+
+__global__ __launch_bounds__(256) void k_read16(const uint4* __restrict__ src, size_t n, uint32_t* __restrict__ sink) {
+  const size_t stride = (size_t)gridDim.x * 256;
+  uint32_t x = 0;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) {
+    const uint4 v = src[i];
+    x ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  sink[(size_t)blockIdx.x * 256 + threadIdx.x] = x;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+extern "C" int moe_probe_mfma_bf16(int shape, int blocks, int iters, float* sink, void* stream) {
+  if (sink == nullptr || (shape != 0 && shape != 1) || blocks < 1 || blocks > 65536 || iters < 1 ||
+      iters > (1 << 24))
+    return 1;
+  hipStream_t s = (hipStream_t)stream;
+  if (shape == 0) hipLaunchKernelGGL(k_mfma_peak<0>, dim3(blocks), dim3(256), 0, s, sink, iters);
+  else hipLaunchKernelGGL(k_mfma_peak<1>, dim3(blocks), dim3(256), 0, s, sink, iters);
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+extern "C" int moe_probe_copy(const void* src, void* dst, size_t bytes, int blocks, void* stream) {
+  if (src == nullptr || dst == nullptr || bytes % 16 != 0 || !aligned16(src) || !aligned16(dst) || blocks < 1 ||
+      blocks > 65536)
+    return 1;
+  if (bytes == 0) return 0;
+  hipLaunchKernelGGL(k_copy16, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const uint4*)src, (uint4*)dst,
+                     bytes / 16);
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+extern "C" int moe_probe_read(const void* src, size_t bytes, int blocks, uint32_t* sink, void* stream) {
+  if (src == nullptr || sink == nullptr || bytes % 16 != 0 || !aligned16(src) || blocks < 1 || blocks > 65536)
+    return 1;
+  if (bytes == 0) return 0;
+  hipLaunchKernelGGL(k_read16, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const uint4*)src, bytes / 16,
+                     sink);
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}

@@ -148,3 +148,29 @@ def test_layer_bwd_errors(L):
     assert call(ds=None) == G.MOE_EINVAL
     assert call(H=12) == G.MOE_EUNSUPPORTED
     assert call(plan=_plan(M_cap=3)) == G.MOE_EINVAL
+
+
+def test_probe_library_exports_and_validation():
+    """libmoe_probe.so (the measurement probes): exports what include/moe_probe.h declares and
+    rejects bad arguments with status 1 before queueing anything."""
+    from grouped_gemm_top_amd import probe
+    if not os.path.exists(probe.lib_path()):
+        import grouped_gemm_top_amd.build as B
+        B.build()
+    P = probe.lib()
+    src = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "moe_probe.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", src)))
+    assert set(names) == set(probe.PROBE_SYMBOLS)
+    for n in names:
+        assert hasattr(P, n), n
+    f = ctypes.c_void_p(FAKE)
+    assert P.moe_probe_mfma_bf16(2, 8, 10, f, None) == 1        # unknown shape
+    assert P.moe_probe_mfma_bf16(0, 0, 10, f, None) == 1        # no blocks
+    assert P.moe_probe_mfma_bf16(0, 8, 0, f, None) == 1         # no iterations
+    assert P.moe_probe_mfma_bf16(0, 8, 10, None, None) == 1     # NULL sink
+    assert P.moe_probe_copy(f, f, 24, 8, None) == 1             # not a multiple of 16
+    assert P.moe_probe_copy(ctypes.c_void_p(FAKE + 4), f, 32, 8, None) == 1  # misaligned
+    assert P.moe_probe_copy(f, None, 32, 8, None) == 1
+    assert P.moe_probe_copy(f, f, 0, 8, None) == 0              # empty: nothing to queue
+    assert P.moe_probe_read(f, 32, 8, None, None) == 1
+    assert P.moe_probe_read(f, 32, 70000, f, None) == 1         # too many blocks
