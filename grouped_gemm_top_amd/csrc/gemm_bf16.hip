@@ -65,10 +65,9 @@ using gg::DWD;
 using gg::DW1;
 
 constexpr int NT = 512;        // threads per workgroup
-constexpr int BM = 256, BN = 256, BK = 32;
-constexpr int NSTG = 4;        // LDS ring depth (stages)
+constexpr int BM = 256, BN = 256, BK = 32;  // varlen-K tiles; k = 32 per stage
+constexpr int NSTG = 4;        // varlen-K LDS ring depth (stages)
 constexpr int AHEAD = NSTG - 1;
-constexpr int OPB = 16384;     // bytes of one operand per stage
 constexpr int TOKB = 256;      // bytes per token slot (64 row indices)
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -91,11 +90,18 @@ template <> struct KT<DX> { static constexpr bool A_KC = true, B_KC = false, VK 
 template <> struct KT<DWD> { static constexpr bool A_KC = false, B_KC = false, VK = true, GA = true, GB = false; static constexpr int ST = 16, MI = 4; };
 template <> struct KT<DW1> { static constexpr bool A_KC = false, B_KC = false, VK = true, GA = false, GB = true; static constexpr int ST = 16, MI = 4; };
 
-// Per-kind tile geometry: BMK rows per M-tile; a stage holds OPA bytes of A (BMK rows of 64
-// bytes, or 32 k-rows of 512 bytes when A is K-strided) then OPB bytes of B; NA: A load
-// instructions per stage (16 rows of 64 bytes each).
+// Per-kind tile geometry: BMK rows per M-tile; a stage covers BKS values of k and holds OPA
+// bytes of A then OPB bytes of B; NST stages form the LDS ring.
+//  varlen-M: k = 64 per stage, so a K-contiguous row of a stage is 128 bytes, one whole cache
+//            line (with k = 32 every line was fetched twice, half of it each time); two stages
+//            of 72 KB.  K-strided B: 64 k-rows of 512 bytes.
+//  varlen-K: k = 32 per stage, both operands K-strided (32 k-rows of 512 bytes); four stages.
+//            NA: A load instructions per stage (16 rows of 64 bytes each).
 template <int KIND> struct Geo {
-  static constexpr int MI = KT<KIND>::MI, BMK = 64 * MI, OPA = BMK * 64, STGK = OPA + OPB, NA = BMK / 16;
+  static constexpr bool VK = KT<KIND>::VK;
+  static constexpr int MI = KT<KIND>::MI, BMK = 64 * MI;
+  static constexpr int BKS = VK ? BK : 64, NST = VK ? NSTG : 2;
+  static constexpr int OPA = BMK * 2 * BKS, OPB = BN * 2 * BKS, STGK = OPA + OPB, NA = BMK / 16;
 };
 
 // LDS loads.  They are written as inline assembly on purpose: the compiler then does not
@@ -241,7 +247,7 @@ struct Sched {
       }
       c.K = a.counts[e];
     }
-    c.nk = (c.K + BK - 1) / BK;
+    c.nk = (c.K + Geo<KIND>::BKS - 1) / Geo<KIND>::BKS;
   }
   // Step forward; at a tile's end move to the next tile (skipping tiles without k-steps
   // when skip_empty is set).
@@ -280,82 +286,106 @@ struct Loader {
   using T = KT<KIND>;
   using G = Geo<KIND>;
   i32x4 rA, rB, rB2;          // descriptors; rB2: the up-projection half (GATEUP rows, DX k-rows)
-  uint32_t vA[3], vB[2];      // this lane's byte offsets at k = 0 (OOB when masked)
-  uint32_t colA[2], colB[2];  // K-strided: column byte offsets (OOB when masked)
+  uint32_t vA[5], vB[4];      // this lane's byte offsets at k = 0 (OOB when masked)
+  uint32_t colA[2], colB[4];  // K-strided: column byte offsets (OOB when masked)
   int kc_c;                   // k-chunk this lane loads (K-contiguous)
-  int mn_k[2], mn_c[2];       // k-row and column chunk this lane loads (K-strided)
+  int mn_k[4], mn_c[4];       // k-row and column chunk this lane loads (K-strided)
 
+  // Varlen-M stages (k = 64): K-contiguous rows of 128 bytes, chunk c of row r at position
+  // c ^ ((r >> 1) & 7); instruction q of wavefront w fills the kilobyte w + 8q of an operand:
+  // rows 8(w + 8q) + (L >> 3) (lane position L & 7) or, K-strided, k-rows 2(w + 8q) + (L >> 5)
+  // (lane position L & 31).  A has 5 such instructions per wavefront (BMK = 320 rows), B 4.
+  // Varlen-K stages (k = 32): instruction q (0, 1) fills kilobyte 2w + q; K-strided only.
   __device__ __forceinline__ void init(int w, int L) {
-    kc_c = (L & 3) ^ kc_swz(L >> 2);  // the row of this lane is (2w+q)*16 + (L >> 2)
+    if constexpr (!T::VK) {
+      // row 8(w + 8q) + (L >> 3): (r >> 1) & 7 = (4 (w & 1) + (L >> 4)) & 7 for every q
+      kc_c = (L & 7) ^ ((4 * (w & 1) + (L >> 4)) & 7);
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      mn_k[q] = (2 * w + q) * 2 + (L >> 5);
-      mn_c[q] = (L & 31) ^ mn_f(mn_k[q]);
+      for (int q = 0; q < 4; ++q) {
+        mn_k[q] = 2 * (w + 8 * q) + (L >> 5);
+        mn_c[q] = (L & 31) ^ mn_f(mn_k[q]);
+      }
+    } else {
+      kc_c = 0;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        mn_k[q] = (2 * w + q) * 2 + (L >> 5);
+        mn_c[q] = (L & 31) ^ mn_f(mn_k[q]);
+      }
     }
   }
 
   // per-tile state; tok = this wavefront's token slot of the tile's first step
   __device__ __forceinline__ void setup(const Args& a, const Tile& c, const int* tok, int w, int L, int nMg) {
     const int H = a.H, I = a.I;
-    uint32_t rowA[3], rowB[2];  // K-contiguous: row byte offsets (OOB when masked)
-    const int kr[2] = {(2 * w) * 16 + (L >> 2), (2 * w + 1) * 16 + (L >> 2)};
-    const long long rb = (long long)c.roff + (long long)c.mt * G::BMK;  // first row of an M-tile
-    // K-contiguous A: instruction w + 8q (q < 3, while below NA) loads rows 16(w + 8q) + 0..15
-    int ka[3];
+    if constexpr (!T::VK) {
+      uint32_t rowA[5], rowB[4];  // K-contiguous: row byte offsets (OOB when masked)
+      const long long rb = (long long)c.roff + (long long)c.mt * G::BMK;  // first row of the M-tile
 #pragma unroll
-    for (int q = 0; q < 3; ++q) ka[q] = (w + 8 * q < G::NA) ? 16 * (w + 8 * q) + (L >> 2) : 1 << 30;
-    if constexpr (KIND == GATEUP || KIND == DH) {
-      rA = dmadesc(KIND == GATEUP ? a.x : a.dout, (long long)a.N * H * 2);
-#pragma unroll
-      for (int q = 0; q < 3; ++q) {
-        const int t = tok[(L >> 2) + 16 * q];
-        rowA[q] = (c.valid && ka[q] < c.mlen) ? (uint32_t)t * (uint32_t)H * 2u : OOB;
+      for (int q = 0; q < 5; ++q) {
+        const int r = 8 * (w + 8 * q) + (L >> 3);  // < 320
+        const bool ok = c.valid && r < c.mlen;
+        if constexpr (KIND == GATEUP || KIND == DH) {
+          const int t = tok[8 * q + (L >> 3)];
+          rowA[q] = ok ? (uint32_t)t * (uint32_t)H * 2u : OOB;
+        } else if constexpr (KIND == DOWN) {
+          rowA[q] = ok ? (uint32_t)r * (uint32_t)I * 2u : OOB;
+        } else {  // DX: rows of dH = [dG | dU]
+          rowA[q] = ok ? (uint32_t)r * (uint32_t)(2 * I) * 2u : OOB;
+        }
       }
+      if constexpr (KIND == GATEUP || KIND == DH) rA = dmadesc(KIND == GATEUP ? a.x : a.dout, (long long)a.N * H * 2);
+      if constexpr (KIND == DOWN) rA = dmadesc_off(a.act, rb * I * 2, (long long)c.mlen * I * 2);
+      if constexpr (KIND == DX) rA = dmadesc_off(a.dh, rb * 2 * I * 2, (long long)c.mlen * 2 * I * 2);
+      if constexpr (KIND == GATEUP) {
+        // tile row n = 8w + 64q + (L >> 3): rows 64..127 of each 128-row half are up-projection
+        // rows (q odd), for i = 128 nt + 64 (q >> 1) + (n & 63)
+        const long long es = (long long)c.e * I * H * 2;
+        rB = dmadesc_off(a.wg, es, (long long)I * H * 2);
+        rB2 = dmadesc_off(a.wu, es, (long long)I * H * 2);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int i = c.nt * 128 + (q >> 1) * 64 + 8 * w + (L >> 3);
+          rowB[q] = c.valid ? (uint32_t)i * (uint32_t)H * 2u : OOB;  // i >= I lies past the range
+        }
+      } else if constexpr (KIND == DOWN) {
+        rB = dmadesc_off(a.wd, (long long)c.e * H * I * 2, (long long)H * I * 2);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = c.nt * BN + 8 * (w + 8 * q) + (L >> 3);
+          rowB[q] = (c.valid && n < H) ? (uint32_t)n * (uint32_t)I * 2u : OOB;
+        }
+      } else if constexpr (KIND == DH) {
+        rB = dmadesc_off(a.wd, (long long)c.e * H * I * 2, (long long)H * I * 2);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = c.nt * BN + 8 * mn_c[q];
+          colB[q] = (c.valid && col < I) ? (uint32_t)col * 2u : OOB;
+          vB[q] = colB[q] + (uint32_t)mn_k[q] * (uint32_t)I * 2u;
+        }
+      } else {  // DX
+        const long long es = (long long)c.e * I * H * 2;
+        rB = dmadesc_off(a.wg, es, (long long)I * H * 2);
+        rB2 = dmadesc_off(a.wu, es, (long long)I * H * 2);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = c.nt * BN + 8 * mn_c[q];
+          colB[q] = (c.valid && col < H) ? (uint32_t)col * 2u : OOB;
+          vB[q] = colB[q] + (uint32_t)mn_k[q] * (uint32_t)H * 2u;
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 5; ++q) vA[q] = rowA[q] + 16u * (uint32_t)kc_c;  // OOB stays OOB: no wrap
+      if constexpr (T::B_KC) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) vB[q] = rowB[q] + 16u * (uint32_t)kc_c;
+      }
+      rA = sgpr4(rA);
+      rB = sgpr4(rB);
+      if constexpr (KIND == GATEUP || KIND == DX) rB2 = sgpr4(rB2);
+      return;
     }
-    if constexpr (KIND == GATEUP) {
-      const long long es = (long long)c.e * I * H * 2;
-      const i32x4 rg = dmadesc_off(a.wg, es, (long long)I * H * 2);
-      const i32x4 ru = dmadesc_off(a.wu, es, (long long)I * H * 2);
-      // rows 64..127 of each 128-row half are up-projection rows
-      rB = (((2 * w) & 7) >= 4) ? ru : rg;
-      rB2 = (((2 * w + 1) & 7) >= 4) ? ru : rg;
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int n = kr[q];
-        const int i = c.nt * 128 + (n >> 7) * 64 + (n & 63);
-        rowB[q] = c.valid ? (uint32_t)i * (uint32_t)H * 2u : OOB;  // i >= I lies past the range
-      }
-    } else if constexpr (KIND == DOWN) {
-      rA = dmadesc_off(a.act, rb * I * 2, (long long)c.mlen * I * 2);
-      rB = dmadesc_off(a.wd, (long long)c.e * H * I * 2, (long long)H * I * 2);
-#pragma unroll
-      for (int q = 0; q < 3; ++q) rowA[q] = (c.valid && ka[q] < c.mlen) ? (uint32_t)ka[q] * (uint32_t)I * 2u : OOB;
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int n = c.nt * BN + kr[q];
-        rowB[q] = (c.valid && n < H) ? (uint32_t)n * (uint32_t)I * 2u : OOB;
-      }
-    } else if constexpr (KIND == DH) {
-      rB = dmadesc_off(a.wd, (long long)c.e * H * I * 2, (long long)H * I * 2);
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int col = c.nt * BN + 8 * mn_c[q];
-        colB[q] = (c.valid && col < I) ? (uint32_t)col * 2u : OOB;
-      }
-    } else if constexpr (KIND == DX) {
-      rA = dmadesc_off(a.dh, rb * 2 * I * 2, (long long)c.mlen * 2 * I * 2);
-      const long long es = (long long)c.e * I * H * 2;
-      rB = dmadesc_off(a.wg, es, (long long)I * H * 2);
-      rB2 = dmadesc_off(a.wu, es, (long long)I * H * 2);
-#pragma unroll
-      for (int q = 0; q < 3; ++q)
-        rowA[q] = (c.valid && ka[q] < c.mlen) ? (uint32_t)ka[q] * (uint32_t)(2 * I) * 2u : OOB;
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int col = c.nt * BN + 8 * mn_c[q];
-        colB[q] = (c.valid && col < H) ? (uint32_t)col * 2u : OOB;
-      }
-    } else if constexpr (KIND == DWD) {
+    if constexpr (KIND == DWD) {
       rA = dmadesc(a.dout, (long long)a.N * H * 2);
       rB = dmadesc_off(a.act, (long long)c.roff * I * 2, (long long)c.K * I * 2);
 #pragma unroll
@@ -380,120 +410,110 @@ struct Loader {
     }
     // offsets at k = 0 for the steps without a K tail (OOB stays OOB: no 32-bit wrap)
 #pragma unroll
-    for (int q = 0; q < 3; ++q)
-      if constexpr (T::A_KC) vA[q] = rowA[q] + 16u * (uint32_t)kc_c;
-#pragma unroll
     for (int q = 0; q < 2; ++q) {
-      if constexpr (T::B_KC) vB[q] = rowB[q] + 16u * (uint32_t)kc_c;
-      if constexpr (KIND == DH) vB[q] = colB[q] + (uint32_t)mn_k[q] * (uint32_t)I * 2u;
-      if constexpr (KIND == DX) vB[q] = colB[q] + (uint32_t)mn_k[q] * (uint32_t)H * 2u;
       if constexpr (KIND == DWD) vB[q] = colB[q] + (uint32_t)mn_k[q] * (uint32_t)I * 2u;
       if constexpr (KIND == DW1) vA[q] = colA[q] + (uint32_t)mn_k[q] * (uint32_t)(2 * I) * 2u;
     }
     rA = sgpr4(rA);
     rB = sgpr4(rB);
-    if constexpr (KIND == GATEUP || KIND == DX) rB2 = sgpr4(rB2);
   }
 
-  // The operand loads of step c.kt.  mS: LDS address of the step's stage; this wavefront's
-  // kilobytes are A: (w + 8q) (K-contiguous) or 2w, 2w+1 (K-strided), B: OPA + 2w, 2w+1.
-  // tok: the step's token slot (varlen-K gathers).
+  // The operand loads of step c.kt.  mS: LDS address of the step's stage (see init for which
+  // kilobytes this wavefront fills).  tok: the step's token slot (varlen-K gathers).
   // A step without a K tail adds the k advance as the uniform offset; the last step of a tile
-  // whose K is not a multiple of 32 builds every lane's offset and masks k >= K.
+  // whose K is not a multiple of the stage's k builds every lane's offset and masks k >= K.
   __device__ __forceinline__ void issue(const Args& a, const Tile& c, uint32_t mS, const int* tok, int w, int L) {
     const int H = a.H, I = a.I;
     // the descriptors in SGPRs once per step (the inline assembly takes them as scalar operands)
     const i32x4 rA = sgpr4(this->rA), rB = sgpr4(this->rB);
     const i32x4 rB2 = (KIND == GATEUP || KIND == DX) ? sgpr4(this->rB2) : rB;
-    const int k0 = c.kt * BK;
-    const uint32_t mA = mS + (uint32_t)(2 * w) * 1024u;
-    const uint32_t mB = mS + (uint32_t)G::OPA + (uint32_t)(2 * w) * 1024u;
-    // the uniform advance is only used where it is non-negative and keeps every lane inside
-    // its row: no K tail, and (dX) no stage that straddles the gate / up boundary at k = I
-    bool fast = k0 + BK <= c.K;
-    if constexpr (KIND == DX) fast = fast && (k0 + BK <= I || k0 >= I);
-    if (fast) {
-      if constexpr (T::A_KC) {
+    const int k0 = c.kt * G::BKS;
+    if constexpr (!T::VK) {
+      const uint32_t mB = mS + (uint32_t)G::OPA;
+      // the uniform advance is only used where it is non-negative and keeps every lane inside
+      // its row: no K tail, and (dX) no stage that straddles the gate / up boundary at k = I
+      bool fast = k0 + G::BKS <= c.K;
+      if constexpr (KIND == DX) fast = fast && (k0 + G::BKS <= I || k0 >= I);
+      if (fast) {
         const uint32_t so = (uint32_t)k0 * 2u;
 #pragma unroll
-        for (int q = 0; q < 3; ++q)
-          if (w + 8 * q < G::NA) dma16(rA, mS + (uint32_t)(w + 8 * q) * 1024u, vA[q], so);
-        if constexpr (T::B_KC) {
-          dma16(rB, mB, vB[0], so);
-          dma16(KIND == GATEUP ? rB2 : rB, mB + 1024, vB[1], so);
+        for (int q = 0; q < 5; ++q) dma16(rA, mS + (uint32_t)(w + 8 * q) * 1024u, vA[q], so);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t m = mB + (uint32_t)(w + 8 * q) * 1024u;
+          if constexpr (KIND == GATEUP) dma16((q & 1) ? rB2 : rB, m, vB[q], so);
+          if constexpr (KIND == DOWN) dma16(rB, m, vB[q], so);
+          if constexpr (KIND == DH) dma16(rB, m, vB[q], (uint32_t)k0 * (uint32_t)I * 2u);
+          if constexpr (KIND == DX) {
+            const bool up = k0 >= I;  // the whole stage lies in one half
+            dma16(up ? rB2 : rB, m, vB[q], (uint32_t)(k0 - (up ? I : 0)) * (uint32_t)H * 2u);
+          }
         }
+        return;
       }
-      if constexpr (KIND == DH) {
-        const uint32_t so = (uint32_t)k0 * (uint32_t)I * 2u;
-        dma16(rB, mB, vB[0], so);
-        dma16(rB, mB + 1024, vB[1], so);
-      } else if constexpr (KIND == DX) {
+      // K tail (or a dX stage across k = I): full per-lane offsets, k >= K masked
+      const bool kv = k0 + 8 * kc_c < c.K;
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const int kb = k0 + (2 * w + q) * 2;  // both k-rows of this instruction: same half
-          const bool up = kb >= I;
-          dma16(up ? rB2 : rB, mB + q * 1024, vB[q], (uint32_t)(k0 - (up ? I : 0)) * (uint32_t)H * 2u);
+      for (int q = 0; q < 5; ++q)
+        dma16(rA, mS + (uint32_t)(w + 8 * q) * 1024u, kv ? vA[q] + (uint32_t)k0 * 2u : OOB, 0u);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t m = mB + (uint32_t)(w + 8 * q) * 1024u;
+        if constexpr (KIND == GATEUP) dma16((q & 1) ? rB2 : rB, m, kv ? vB[q] + (uint32_t)k0 * 2u : OOB, 0u);
+        if constexpr (KIND == DOWN) dma16(rB, m, kv ? vB[q] + (uint32_t)k0 * 2u : OOB, 0u);
+        if constexpr (KIND == DH) {
+          const uint32_t k = (uint32_t)(k0 + mn_k[q]);
+          dma16(rB, m, colB[q] + k * (uint32_t)I * 2u, 0u);  // k >= H lies past the range
         }
-      } else if constexpr (KIND == DWD) {
-        const uint32_t so = (uint32_t)k0 * (uint32_t)I * 2u;
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const uint32_t t = (uint32_t)tok[2 * q + (L >> 5)];
-          dma16(rA, mA + q * 1024, t * (uint32_t)H * 2u + colA[q], 0u);
-          dma16(rB, mB + q * 1024, vB[q], so);
-        }
-      } else if constexpr (KIND == DW1) {
-        const uint32_t so = (uint32_t)k0 * (uint32_t)(2 * I) * 2u;
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const uint32_t t = (uint32_t)tok[2 * q + (L >> 5)];
-          dma16(rA, mA + q * 1024, vA[q], so);
-          dma16(rB, mB + q * 1024, t * (uint32_t)H * 2u + colB[q], 0u);
+        if constexpr (KIND == DX) {
+          // both k-rows of an instruction lie in the same half (I is a multiple of 8), so the
+          // half follows from the instruction's first k-row (wavefront-uniform)
+          const bool up = k0 + 2 * (w + 8 * q) >= I;
+          const uint32_t k = (uint32_t)(k0 + mn_k[q] - (up ? I : 0));
+          dma16(up ? rB2 : rB, m, colB[q] + k * (uint32_t)H * 2u, 0u);  // k >= 2I: past the range
         }
       }
       return;
-    }
-    // K tail (or a dX stage across k = I): full per-lane offsets, k >= K masked
-    if constexpr (T::A_KC) {
-      const int kk = k0 + 8 * kc_c;
-      const bool kv = kk < c.K;
+    } else {
+      const uint32_t mA = mS + (uint32_t)(2 * w) * 1024u;
+      const uint32_t mB = mS + (uint32_t)G::OPA + (uint32_t)(2 * w) * 1024u;
+      if (k0 + BK <= c.K) {
+        if constexpr (KIND == DWD) {
+          const uint32_t so = (uint32_t)k0 * (uint32_t)I * 2u;
 #pragma unroll
-      for (int q = 0; q < 3; ++q)
-        if (w + 8 * q < G::NA) dma16(rA, mS + (uint32_t)(w + 8 * q) * 1024u, kv ? vA[q] + (uint32_t)k0 * 2u : OOB, 0u);
-      if constexpr (T::B_KC) {
-        dma16(rB, mB, kv ? vB[0] + (uint32_t)k0 * 2u : OOB, 0u);
-        dma16(KIND == GATEUP ? rB2 : rB, mB + 1024, kv ? vB[1] + (uint32_t)k0 * 2u : OOB, 0u);
+          for (int q = 0; q < 2; ++q) {
+            const uint32_t t = (uint32_t)tok[2 * q + (L >> 5)];
+            dma16(rA, mA + q * 1024, t * (uint32_t)H * 2u + colA[q], 0u);
+            dma16(rB, mB + q * 1024, vB[q], so);
+          }
+        } else {  // DW1
+          const uint32_t so = (uint32_t)k0 * (uint32_t)(2 * I) * 2u;
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const uint32_t t = (uint32_t)tok[2 * q + (L >> 5)];
+            dma16(rA, mA + q * 1024, vA[q], so);
+            dma16(rB, mB + q * 1024, t * (uint32_t)H * 2u + colB[q], 0u);
+          }
+        }
+        return;
       }
-    }
-    if constexpr (KIND == DH) {
+      // K tail: every lane's own offset, k-rows >= K masked
+      if constexpr (KIND == DWD) {
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const uint32_t k = (uint32_t)(k0 + mn_k[q]);
-        dma16(rB, mB + q * 1024, colB[q] + k * (uint32_t)I * 2u, 0u);  // k >= H lies past the range
-      }
-    } else if constexpr (KIND == DX) {
+        for (int q = 0; q < 2; ++q) {
+          const int r = k0 + mn_k[q];
+          const uint32_t t = (uint32_t)tok[2 * q + (L >> 5)];
+          dma16(rA, mA + q * 1024, r < c.K ? t * (uint32_t)H * 2u + colA[q] : OOB, 0u);
+          dma16(rB, mB + q * 1024, colB[q] + (uint32_t)r * (uint32_t)I * 2u, 0u);
+        }
+      } else {  // DW1
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int kb = k0 + (2 * w + q) * 2;
-        const bool up = kb >= I;
-        const uint32_t k = (uint32_t)(k0 + mn_k[q] - (up ? I : 0));
-        dma16(up ? rB2 : rB, mB + q * 1024, colB[q] + k * (uint32_t)H * 2u, 0u);  // k >= 2I: past the range
-      }
-    } else if constexpr (KIND == DWD) {
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int r = k0 + mn_k[q];
-        const uint32_t t = (uint32_t)tok[2 * q + (L >> 5)];
-        dma16(rA, mA + q * 1024, r < c.K ? t * (uint32_t)H * 2u + colA[q] : OOB, 0u);
-        dma16(rB, mB + q * 1024, colB[q] + (uint32_t)r * (uint32_t)I * 2u, 0u);
-      }
-    } else if constexpr (KIND == DW1) {
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int r = k0 + mn_k[q];
-        const uint32_t t = (uint32_t)tok[2 * q + (L >> 5)];
-        dma16(rA, mA + q * 1024, colA[q] + (uint32_t)r * (uint32_t)(2 * I) * 2u, 0u);
-        dma16(rB, mB + q * 1024, r < c.K ? t * (uint32_t)H * 2u + colB[q] : OOB, 0u);
+        for (int q = 0; q < 2; ++q) {
+          const int r = k0 + mn_k[q];
+          const uint32_t t = (uint32_t)tok[2 * q + (L >> 5)];
+          dma16(rA, mA + q * 1024, colA[q] + (uint32_t)r * (uint32_t)(2 * I) * 2u, 0u);
+          dma16(rB, mB + q * 1024, r < c.K ? t * (uint32_t)H * 2u + colB[q] : OOB, 0u);
+        }
       }
     }
   }
@@ -655,12 +675,14 @@ __device__ __forceinline__ void epilogue(const Args& a, const Tile& c, f32x4 (&a
 }
 
 // ------------------------------------------------------------------ fragments
-// K-contiguous fragment of rows r0 .. r0+15: lane reads row r0 + (L & 15), k-chunk L >> 4.
-__device__ __forceinline__ bf16x8 frag_kc(const char* op, int r0, int kc_off) {
-  return *reinterpret_cast<const bf16x8*>(op + r0 * 64 + kc_off);
+// K-contiguous fragment of rows r0 .. r0+15 (varlen-M stages, rows of 128 bytes): lane reads
+// row r0 + (L & 15), k-chunk 4 sub + (L >> 4) of the stage's eight; kc_off: the lane's offset
+// for sub = 0 (sub = 1 flips bit 2 of the chunk position, offset bit 6).
+__device__ __forceinline__ bf16x8 frag_kc(const char* op, int r0, int sub, int kc_off) {
+  return *reinterpret_cast<const bf16x8*>(op + r0 * 128 + (kc_off ^ (64 * sub)));
 }
 // K-strided fragment of columns x0 .. x0+15 (x0 a multiple of 16): two transposing reads of
-// k-rows 8(L>>4) + 0..3 and + 4..7.
+// k-rows 8(L>>4) + 0..3 and + 4..7 (mn_k0 includes the 32-row offset of a second k-substep).
 __device__ __forceinline__ bf16x8 frag_mn(const char* op, int x0, int mn_k0, int mn_f_, int mn_b) {
   const int pos = ((((x0 >> 3) ^ mn_f_) | mn_b) << 4);
   typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -693,7 +715,7 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
   // step (varlen-M kinds issue theirs once per tile, before the tile's step loads)
   constexpr int NLW = 4 + (T::VK && GATHER ? 1 : 0);
 
-  __shared__ __attribute__((aligned(1024))) char s_ring[NSTG * G::STGK];
+  __shared__ __attribute__((aligned(1024))) char s_ring[G::NST * G::STGK];
   __shared__ __attribute__((aligned(256))) int s_tok[8 * NSTG * (TOKB / 4)];
   __shared__ int s_sched[1025];
   __shared__ int s_wsum[9];
@@ -779,28 +801,29 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // per-lane fragment addressing
-  const int kc_off = (L & 15) * 64 + ((((L >> 4) ^ kc_swz(L & 15)) & 3) << 4);
+  // per-lane fragment addressing (K-contiguous rows: chunk c of row r at c ^ ((r >> 1) & 7))
+  const int kc_off = (L & 15) * 128 + ((((L >> 4) ^ ((L >> 1) & 7)) & 7) << 4);
   const int mn_m = L & 15, mn_g = L >> 4;
   const int mn_k0 = (8 * mn_g + (mn_m >> 2)) * 512 + 8 * (mn_m & 1);
   const int mn_ff = 2 * ((mn_m >> 2) | ((mn_g & 1) << 2));
   const int mn_b = (mn_m >> 1) & 1;
 
-  // The MFMAs of one k-step from the stage at `sa`: this wavefront's row blocks 16(4i + wm)
-  // that start below the tile's row count (nb = mlen - 16 wm > 64 i; a block at or past it
-  // holds rows of no group and is skipped) times its 128 columns.
-  auto mma_stage = [&](const char* sa, int nb) __attribute__((always_inline)) {
+  // The MFMAs of one k-substep (k = 32; sub: which 32 of a varlen-M stage) from the stage at
+  // `sa`: this wavefront's row blocks 16(4i + wm) that start below the tile's row count
+  // (nb = mlen - 16 wm > 64 i; a block at or past it holds rows of no group and is skipped)
+  // times its 128 columns.
+  auto mma_stage = [&](const char* sa, int nb, int sub) __attribute__((always_inline)) {
     // opaque copies: the per-fragment LDS positions derived from these are recomputed each
     // step rather than held in registers across the loop
-    int kco = kc_off, k0o = mn_k0, ffo = mn_ff, bo = mn_b;
+    int kco = kc_off, k0o = mn_k0 + sub * (32 * 512), ffo = mn_ff, bo = mn_b;
     asm volatile("" : "+v"(kco), "+v"(k0o), "+v"(ffo), "+v"(bo));
     const char* sb = sa + G::OPA;
     auto frag_a = [&](int i) __attribute__((always_inline)) {
-      if constexpr (T::A_KC) return frag_kc(sa, 16 * (4 * i + wm), kco);
+      if constexpr (T::A_KC) return frag_kc(sa, 16 * (4 * i + wm), sub, kco);
       else return frag_mn(sa, 16 * (4 * i + wm), k0o, ffo, bo);
     };
     auto frag_b = [&](int j) __attribute__((always_inline)) {
-      if constexpr (T::B_KC) return frag_kc(sb, wn * 128 + 16 * j, kco);
+      if constexpr (T::B_KC) return frag_kc(sb, wn * 128 + 16 * j, sub, kco);
       else return frag_mn(sb, wn * 128 + 16 * j, k0o, ffo, bo);
     };
     if constexpr (G::MI == 4) {
@@ -861,29 +884,27 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
 
   if constexpr (!T::VK) {
     // ---- varlen-M: this workgroup's tiles one after another ----
-    // Every tile has k-steps (groups without rows have no tiles).  A tile's step loads follow
-    // the previous tile's epilogue without a drain: the vmcnt wait of its first step also
-    // covers those older stores.  Its tokens (gathered A) were loaded into LDS during the
-    // previous tile, before that tile's step loads, so the previous tile's last wait (vmcnt 0)
-    // has seen them land; tokens alternate between two slots (tile it uses slot it & 1).
+    // Two stages of k = 64: the loads of step kt + 1 are issued right after step kt's wait and
+    // fill the stage that step kt - 1 used, during step kt's MFMAs.  Every tile has k-steps
+    // (groups without rows have no tiles).  A tile's first step load follows the previous
+    // tile's epilogue without a drain: the vmcnt wait of its first step also covers those
+    // older stores.  Its tokens (gathered A) were loaded into LDS during the previous tile,
+    // before that tile's step loads, so the previous tile's last wait (vmcnt 0) has seen them
+    // land; tokens alternate between two slots (tile it uses slot it & 1).
+    static_assert(G::NST == 2, "varlen-M: two stages");
     auto tok_load = [&](const Tile& t) __attribute__((always_inline)) {
       if constexpr (T::GA) {
-        // lane L: the token of row 16w + (L & 15) + 128 (L >> 4), i.e. of A instruction
-        // w + 8 (L >> 4) (rows past the tile's instructions are never used)
+        // lane L: the token of row 8(w + 8(L >> 3)) + (L & 7), i.e. of A instruction L >> 3 of
+        // this wavefront (instructions past the tile's five are never used)
         if (t.valid)
           dma4(rtok, tok_m0 + (uint32_t)(t.it & 1) * TOKB,
-               (uint32_t)(t.roff + t.mt * G::BMK + 16 * w + (L & 15) + 128 * (L >> 4)) * 4u);
+               (uint32_t)(t.roff + t.mt * G::BMK + 8 * w + 64 * (L >> 3) + (L & 7)) * 4u);
       }
     };
-    // the first min(AHEAD, nk) steps of tile t, whose first step takes ring stage gs
-    auto issue_first = [&](const Tile& t, int gs) __attribute__((always_inline)) {
-#pragma unroll 1
-      for (int q = 0; q < AHEAD; ++q)
-        if (q < t.nk) {
-          Tile u = t;
-          u.kt = q;
-          ld.issue(a, u, ring_m0 + (uint32_t)((gs + q) & (NSTG - 1)) * G::STGK, my_tok, w, L);
-        }
+    auto issue_step = [&](const Tile& t, int kt, int stage) __attribute__((always_inline)) {
+      Tile u = t;
+      u.kt = kt;
+      ld.issue(a, u, ring_m0 + (uint32_t)(stage & 1) * G::STGK, my_tok, w, L);
     };
     {
       Tile C0;
@@ -904,29 +925,23 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
         S.decode(a, Cn, it + 1);
         tok_load(Cn);
       }
-      issue_first(Cc, gs);
+      issue_step(Cc, 0, gs);
       const int nk = Cc.nk;
       const int nb = Cc.mlen - 16 * wm;
 #pragma unroll 1
       for (int kt = 0; kt < nk; ++kt) {
-        // step kt's loads have landed for every wavefront, and every wavefront is done with
-        // the stage that the loads below refill (the stage of step kt - 1)
-        const int later = min(2, nk - 1 - kt);
-        if constexpr (G::NA > 16) {
-          if (w < G::NA - 16) mstep_wait<NLW + 1>(later);
-          else mstep_wait<NLW>(later);
-        } else {
-          mstep_wait<NLW>(later);
+        // step kt's loads (and everything older) have landed for every wavefront, and every
+        // wavefront is done with the stage that the loads below refill (the stage of step kt - 1)
+        vm_wait_barrier<0>();
+        if (kt + 1 < nk) issue_step(Cc, kt + 1, gs + kt + 1);
+        if (nb > 0) {
+          const char* sa = s_ring + ((gs + kt) & 1) * G::STGK;
+          mma_stage(sa, nb, 0);
+          mma_stage(sa, nb, 1);
         }
-        if (kt + AHEAD < nk) {
-          Tile u = Cc;
-          u.kt = kt + AHEAD;
-          ld.issue(a, u, ring_m0 + (uint32_t)((gs + kt + AHEAD) & (NSTG - 1)) * G::STGK, my_tok, w, L);
-        }
-        if (nb > 0) mma_stage(s_ring + ((gs + kt) & (NSTG - 1)) * G::STGK, nb);
       }
       // every wavefront is done with the ring; the last step's stage stages the epilogue
-      char* st = s_ring + ((gs + nk - 1) & (NSTG - 1)) * G::STGK + w * 4096;
+      char* st = s_ring + ((gs + nk - 1) & 1) * G::STGK + w * 4096;
       lds_barrier();
       epilogue<KIND>(a, Cc, acc, wm, wn, L, S.nMg, st);
 #pragma unroll
@@ -1004,7 +1019,7 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
       // so one's load issue and bookkeeping overlap the other's MFMAs instead of both waiting
       // on the same phase.
       if (wn == 0) issue_block();
-      if (Cc.mlen > 16 * wm) mma_stage(s_ring + (s & (NSTG - 1)) * G::STGK, Cc.mlen - 16 * wm);
+      if (Cc.mlen > 16 * wm) mma_stage(s_ring + (s & (NSTG - 1)) * G::STGK, Cc.mlen - 16 * wm, 0);
       if (wn != 0) issue_block();
 
       // ---- advance the compute cursor; finish a tile after its last step ----
