@@ -886,11 +886,11 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
     // ---- varlen-M: this workgroup's tiles one after another ----
     // Two stages of k = 64: the loads of step kt + 1 are issued right after step kt's wait and
     // fill the stage that step kt - 1 used, during step kt's MFMAs.  Every tile has k-steps
-    // (groups without rows have no tiles).  A tile's first step load follows the previous
-    // tile's epilogue without a drain: the vmcnt wait of its first step also covers those
-    // older stores.  Its tokens (gathered A) were loaded into LDS during the previous tile,
-    // before that tile's step loads, so the previous tile's last wait (vmcnt 0) has seen them
-    // land; tokens alternate between two slots (tile it uses slot it & 1).
+    // (groups without rows have no tiles).  A tile's loader is set up and its first step
+    // issued before the previous tile's epilogue, so those loads overlap the epilogue and the
+    // epilogue's stores drain during the first step.  A tile's tokens (gathered A) are loaded
+    // into LDS a tile earlier, before that earlier tile's first step, so they have landed by
+    // its first wait; tokens alternate between two slots (tile it uses slot it & 1).
     static_assert(G::NST == 2, "varlen-M: two stages");
     auto tok_load = [&](const Tile& t) __attribute__((always_inline)) {
       if constexpr (T::GA) {
@@ -907,32 +907,34 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
       ld.issue(a, u, ring_m0 + (uint32_t)(stage & 1) * G::STGK, my_tok, w, L);
     };
     {
-      Tile C0;
+      Tile C0, C1;
       S.decode(a, C0, 0);
       if (!C0.valid) return;
       tok_load(C0);
       vm_drain();
+      ld.setup(a, C0, my_tok, w, L, S.nMg);
+      S.decode(a, C1, 1);
+      tok_load(C1);
+      issue_step(C0, 0, 0);
     }
     int gs = 0;  // ring sequence number of the current tile's first step
+    int ep = 0;  // an epilogue's stores were issued after the current tile's first step
 #pragma unroll 1
     for (int it = 0;; ++it) {
+      // tile `it`: its loader is set up and its first step's loads are in flight
       Tile Cc;
       S.decode(a, Cc, it);
       if (!Cc.valid) break;
-      ld.setup(a, Cc, my_tok + (it & 1) * (TOKB / 4), w, L, S.nMg);
-      {
-        Tile Cn;
-        S.decode(a, Cn, it + 1);
-        tok_load(Cn);
-      }
-      issue_step(Cc, 0, gs);
       const int nk = Cc.nk;
       const int nb = Cc.mlen - 16 * wm;
 #pragma unroll 1
       for (int kt = 0; kt < nk; ++kt) {
-        // step kt's loads (and everything older) have landed for every wavefront, and every
-        // wavefront is done with the stage that the loads below refill (the stage of step kt - 1)
-        vm_wait_barrier<0>();
+        // step kt's loads have landed for every wavefront (at the first step, the previous
+        // tile's epilogue stores, issued after them, may still be in flight: at least ST
+        // instructions), and every wavefront is done with the stage that the loads below
+        // refill (the stage of step kt - 1)
+        if (kt == 0 && ep) vm_wait_barrier<T::ST>();
+        else vm_wait_barrier<0>();
         if (kt + 1 < nk) issue_step(Cc, kt + 1, gs + kt + 1);
         if (nb > 0) {
           const char* sa = s_ring + ((gs + kt) & 1) * G::STGK;
@@ -940,15 +942,29 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
           mma_stage(sa, nb, 1);
         }
       }
-      // every wavefront is done with the ring; the last step's stage stages the epilogue
+      // every wavefront is done with the ring: the last step's stage stages the epilogue, the
+      // other takes the next tile's first step, issued before the epilogue so that its wait
+      // does not include the epilogue's stores
       char* st = s_ring + ((gs + nk - 1) & 1) * G::STGK + w * 4096;
       lds_barrier();
+      gs += nk;
+      {
+        Tile Cn;
+        S.decode(a, Cn, it + 1);
+        if (Cn.valid) {
+          ld.setup(a, Cn, my_tok + ((it + 1) & 1) * (TOKB / 4), w, L, S.nMg);
+          Tile Cnn;
+          S.decode(a, Cnn, it + 2);
+          tok_load(Cnn);
+          issue_step(Cn, 0, gs);
+        }
+      }
       epilogue<KIND>(a, Cc, acc, wm, wn, L, S.nMg, st);
 #pragma unroll
       for (int i = 0; i < G::MI; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      gs += nk;
+      ep = 1;
     }
     vm_drain();
   } else {
