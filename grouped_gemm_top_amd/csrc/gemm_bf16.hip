@@ -168,20 +168,27 @@ template <int N>
 __device__ __forceinline__ void vm_wait_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
-// The wait for step s of a wavefront that issues NLW loads per step (varlen-K): the memory
-// instructions it issued after step s's loads are the two later steps' loads and the stores of
-// the ne epilogues in between (at least ST each).  Rounding an allowance down only makes the
-// wait stricter.
+// The wait for step s + 1 at step s of a wavefront that issues NLW loads per step (varlen-K):
+// the memory instructions it issued after step s + 1's loads are the next step's loads and the
+// stores of the ne epilogues in between (at least ST each).  Rounding an allowance down only
+// makes the wait stricter.
+// The wavefront's LDS reads are complete too: the fragments it read from the stage that the
+// loads after the barrier overwrite may not have fed any MFMA (a wavefront without rows in the
+// tile reads them all the same).
+template <int N>
+__device__ __forceinline__ void vm_lds_wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
 template <int NLW, int ST>
 __device__ __forceinline__ void step_wait(int ne) {
-  constexpr int X0 = 2 * NLW;
+  constexpr int X0 = NLW;
   constexpr int X1 = (X0 + ST) < 63 ? (X0 + ST) : 63;
   constexpr int X2 = (X0 + 2 * ST) < 63 ? (X0 + 2 * ST) : 63;
   constexpr int X3 = (X0 + 3 * ST) < 63 ? (X0 + 3 * ST) : 63;
-  if (ne == 0) vm_wait_barrier<X0>();
-  else if (ne == 1) vm_wait_barrier<X1>();
-  else if (ne == 2) vm_wait_barrier<X2>();
-  else vm_wait_barrier<X3>();
+  if (ne == 0) vm_lds_wait_barrier<X0>();
+  else if (ne == 1) vm_lds_wait_barrier<X1>();
+  else if (ne == 2) vm_lds_wait_barrier<X2>();
+  else vm_lds_wait_barrier<X3>();
 }
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 __device__ __forceinline__ void vm_drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -826,20 +833,7 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
       if constexpr (T::B_KC) return frag_kc(sb, wn * 128 + 16 * j, sub, kco);
       else return frag_mn(sb, wn * 128 + 16 * j, k0o, ffo, bo);
     };
-    if constexpr (G::MI == 4) {
-      // every fragment read first, then the MFMAs
-      bf16x8 fa[4], fb[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) fb[j] = frag_b(j);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) fa[i] = frag_a(i);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (i == 0 || nb > 64 * i) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) acc[i][j] = mma(fb[j], fa[i], acc[i][j]);
-        }
-    } else if constexpr (KIND == DH) {
+    if constexpr (KIND == DH) {
       // (fewer live fragments, for the register budget of the dSwiGLU epilogue) all A
       // fragments first, then the B fragments one column block ahead
       bf16x8 fa[G::MI];
@@ -873,6 +867,27 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
         if (i + 1 < G::MI) fa = fn;
       }
     }
+  };
+
+  // Varlen-K step: fa / fb hold this step's fragments, read during the previous step.  The
+  // MFMAs go column block by column block; once a column's four MFMAs are issued its B
+  // fragment is refilled with the next step's from the stage at `sn`, and after the last
+  // column the A fragments are, so the next step's LDS reads overlap this step's MFMAs
+  // instead of preceding them.  Every block is computed: a varlen-K tile's rows are weight
+  // rows (h or i), ragged only in the last M-tile of a matrix, and the epilogue never stores
+  // a row at or past the matrix's end, so what such blocks compute is discarded.
+  auto mma_pf = [&](bf16x8 (&fa)[4], bf16x8 (&fb)[8], const char* sn) __attribute__((always_inline)) {
+    int k0o = mn_k0, ffo = mn_ff, bo = mn_b;
+    asm volatile("" : "+v"(k0o), "+v"(ffo), "+v"(bo));
+    const char* sbn = sn + G::OPA;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i][j] = mma(fb[j], fa[i], acc[i][j]);
+      fb[j] = frag_mn(sbn, wn * 128 + 16 * j, k0o, ffo, bo);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[i] = frag_mn(sn, 16 * (4 * i + wm), k0o, ffo, bo);
   };
 
   Loader<KIND> ld;
@@ -1009,21 +1024,34 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
       load_issue(s);
     }
 
-    // epilogues issued after the loads of the last three steps (their stores are younger)
-    int h0 = 0, h1 = 0, h2 = 0;
+    // epilogues issued after the loads of the last two steps (their stores are younger)
+    int h0 = 0, h1 = 0;
+
+    // step 0's loads have landed (the loads of steps 1 and 2 and their token loads were issued
+    // after them); its fragments go to registers
+    bf16x8 fa[4], fb[8];
+    vm_wait_barrier<2 * NLW>();
+    {
+      const char* s0 = s_ring;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) fb[j] = frag_mn(s0 + G::OPA, wn * 128 + 16 * j, mn_k0, mn_ff, mn_b);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fa[i] = frag_mn(s0, 16 * (4 * i + wm), mn_k0, mn_ff, mn_b);
+    }
 
 #pragma unroll 1
     for (int s = 0;; ++s) {
-      // step s's loads (issued three steps ago) have landed for every wavefront, and every
-      // wavefront is done with the stage that the loads below overwrite
-      const int ne = h0 + h1 + h2;
+      // step s + 1's loads (issued two steps ago) have landed for every wavefront, and every
+      // wavefront is done with the stage that the loads below overwrite (step s - 1's, whose
+      // fragments were read before step s - 1's MFMAs)
+      const int ne = h0 + h1;
       static_assert(G::NA == 16, "varlen-K: every wavefront issues NLW loads per step");
       step_wait<NLW, T::ST>(ne);
-      h2 = h1;
       h1 = h0;
       h0 = 0;
 
-      // ---- this step's loads (three steps ahead) and the MFMAs of step s ----
+      // ---- this step's loads (three steps ahead), the MFMAs of step s and the fragment
+      // reads of step s + 1 ----
       auto issue_block = [&]() __attribute__((always_inline)) {
         if constexpr (GATHER) {
           tok_issue(Tk, s + 2 * AHEAD);
@@ -1035,7 +1063,7 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
       // so one's load issue and bookkeeping overlap the other's MFMAs instead of both waiting
       // on the same phase.
       if (wn == 0) issue_block();
-      if (Cc.mlen > 16 * wm) mma_stage(s_ring + (s & (NSTG - 1)) * G::STGK, Cc.mlen - 16 * wm, 0);
+      mma_pf(fa, fb, s_ring + ((s + 1) & (NSTG - 1)) * G::STGK);
       if (wn != 0) issue_block();
 
       // ---- advance the compute cursor; finish a tile after its last step ----
