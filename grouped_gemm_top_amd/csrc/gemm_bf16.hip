@@ -168,27 +168,9 @@ template <int N>
 __device__ __forceinline__ void vm_wait_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
-// The wait for step s + 1 at step s of a wavefront that issues NLW loads per step (varlen-K):
-// the memory instructions it issued after step s + 1's loads are the next step's loads and the
-// stores of the ne epilogues in between (at least ST each).  Rounding an allowance down only
-// makes the wait stricter.
-// The wavefront's LDS reads are complete too: the fragments it read from the stage that the
-// loads after the barrier overwrite may not have fed any MFMA (a wavefront without rows in the
-// tile reads them all the same).
 template <int N>
-__device__ __forceinline__ void vm_lds_wait_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
-}
-template <int NLW, int ST>
-__device__ __forceinline__ void step_wait(int ne) {
-  constexpr int X0 = NLW;
-  constexpr int X1 = (X0 + ST) < 63 ? (X0 + ST) : 63;
-  constexpr int X2 = (X0 + 2 * ST) < 63 ? (X0 + 2 * ST) : 63;
-  constexpr int X3 = (X0 + 3 * ST) < 63 ? (X0 + 3 * ST) : 63;
-  if (ne == 0) vm_lds_wait_barrier<X0>();
-  else if (ne == 1) vm_lds_wait_barrier<X1>();
-  else if (ne == 2) vm_lds_wait_barrier<X2>();
-  else vm_lds_wait_barrier<X3>();
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 __device__ __forceinline__ void vm_drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -294,7 +276,7 @@ struct Loader {
   using G = Geo<KIND>;
   i32x4 rA, rB, rB2;          // descriptors; rB2: the up-projection half (GATEUP rows, DX k-rows)
   uint32_t vA[5], vB[4];      // this lane's byte offsets at k = 0 (OOB when masked)
-  uint32_t colA[2], colB[4];  // K-strided: column byte offsets (OOB when masked)
+  uint32_t colA[4], colB[4];  // K-strided: column byte offsets (OOB when masked)
   int kc_c;                   // k-chunk this lane loads (K-contiguous)
   int mn_k[4], mn_c[4];       // k-row and column chunk this lane loads (K-strided)
 
@@ -302,7 +284,8 @@ struct Loader {
   // c ^ ((r >> 1) & 7); instruction q of wavefront w fills the kilobyte w + 8q of an operand:
   // rows 8(w + 8q) + (L >> 3) (lane position L & 7) or, K-strided, k-rows 2(w + 8q) + (L >> 5)
   // (lane position L & 31).  A has 5 such instructions per wavefront (BMK = 320 rows), B 4.
-  // Varlen-K stages (k = 32): instruction q (0, 1) fills kilobyte 2w + q; K-strided only.
+  // Varlen-K stages (k = 32): only wavefronts 0-3 load; instruction q (0..3) of wavefront w
+  // fills kilobyte 4w + q of each operand, k-rows 2(4w + q) + (L >> 5); K-strided only.
   __device__ __forceinline__ void init(int w, int L) {
     if constexpr (!T::VK) {
       // row 8(w + 8q) + (L >> 3): (r >> 1) & 7 = (4 (w & 1) + (L >> 4)) & 7 for every q
@@ -315,8 +298,8 @@ struct Loader {
     } else {
       kc_c = 0;
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        mn_k[q] = (2 * w + q) * 2 + (L >> 5);
+      for (int q = 0; q < 4; ++q) {
+        mn_k[q] = (4 * w + q) * 2 + (L >> 5);
         mn_c[q] = (L & 31) ^ mn_f(mn_k[q]);
       }
     }
@@ -396,7 +379,7 @@ struct Loader {
       rA = dmadesc(a.dout, (long long)a.N * H * 2);
       rB = dmadesc_off(a.act, (long long)c.roff * I * 2, (long long)c.K * I * 2);
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
+      for (int q = 0; q < 4; ++q) {
         const int ca = c.mt * BM + 8 * mn_c[q];
         colA[q] = (c.valid && ca < H) ? (uint32_t)ca * 2u : OOB;
         const int cb = c.nt * BN + 8 * mn_c[q];
@@ -408,7 +391,7 @@ struct Loader {
       rA = dmadesc_off(a.dh, (long long)c.roff * 2 * I * 2, (long long)c.K * 2 * I * 2);
       rB = dmadesc(a.x, (long long)a.N * H * 2);
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
+      for (int q = 0; q < 4; ++q) {
         const int ma = m0 + 8 * mn_c[q];
         colA[q] = (c.valid && ma < I) ? (uint32_t)(seg * I + ma) * 2u : OOB;
         const int cb = c.nt * BN + 8 * mn_c[q];
@@ -417,7 +400,7 @@ struct Loader {
     }
     // offsets at k = 0 for the steps without a K tail (OOB stays OOB: no 32-bit wrap)
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < 4; ++q) {
       if constexpr (KIND == DWD) vB[q] = colB[q] + (uint32_t)mn_k[q] * (uint32_t)I * 2u;
       if constexpr (KIND == DW1) vA[q] = colA[q] + (uint32_t)mn_k[q] * (uint32_t)(2 * I) * 2u;
     }
@@ -482,21 +465,22 @@ struct Loader {
       }
       return;
     } else {
-      const uint32_t mA = mS + (uint32_t)(2 * w) * 1024u;
-      const uint32_t mB = mS + (uint32_t)G::OPA + (uint32_t)(2 * w) * 1024u;
+      const uint32_t mA = mS + (uint32_t)(4 * w) * 1024u;
+      const uint32_t mB = mS + (uint32_t)G::OPA + (uint32_t)(4 * w) * 1024u;
       if (k0 + BK <= c.K) {
+        // (only wavefronts 0-3 issue loads: the uniform offset goes to an SGPR explicitly)
         if constexpr (KIND == DWD) {
-          const uint32_t so = (uint32_t)k0 * (uint32_t)I * 2u;
+          const uint32_t so = (uint32_t)ufl(k0 * I * 2);
 #pragma unroll
-          for (int q = 0; q < 2; ++q) {
+          for (int q = 0; q < 4; ++q) {
             const uint32_t t = (uint32_t)tok[2 * q + (L >> 5)];
             dma16(rA, mA + q * 1024, t * (uint32_t)H * 2u + colA[q], 0u);
             dma16(rB, mB + q * 1024, vB[q], so);
           }
         } else {  // DW1
-          const uint32_t so = (uint32_t)k0 * (uint32_t)(2 * I) * 2u;
+          const uint32_t so = (uint32_t)ufl(k0 * 2 * I * 2);
 #pragma unroll
-          for (int q = 0; q < 2; ++q) {
+          for (int q = 0; q < 4; ++q) {
             const uint32_t t = (uint32_t)tok[2 * q + (L >> 5)];
             dma16(rA, mA + q * 1024, vA[q], so);
             dma16(rB, mB + q * 1024, t * (uint32_t)H * 2u + colB[q], 0u);
@@ -507,7 +491,7 @@ struct Loader {
       // K tail: every lane's own offset, k-rows >= K masked
       if constexpr (KIND == DWD) {
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
+        for (int q = 0; q < 4; ++q) {
           const int r = k0 + mn_k[q];
           const uint32_t t = (uint32_t)tok[2 * q + (L >> 5)];
           dma16(rA, mA + q * 1024, r < c.K ? t * (uint32_t)H * 2u + colA[q] : OOB, 0u);
@@ -515,7 +499,7 @@ struct Loader {
         }
       } else {  // DW1
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
+        for (int q = 0; q < 4; ++q) {
           const int r = k0 + mn_k[q];
           const uint32_t t = (uint32_t)tok[2 * q + (L >> 5)];
           dma16(rA, mA + q * 1024, colA[q] + (uint32_t)r * (uint32_t)(2 * I) * 2u, 0u);
@@ -681,6 +665,90 @@ __device__ __forceinline__ void epilogue(const Args& a, const Tile& c, f32x4 (&a
   }
 }
 
+// Varlen-K output addressing: row 4p + (L >> 4) and columns 8 (L & 15) .. + 7 of 16-row block
+// i of wavefront (wm, wn) in tile c: the descriptor of the weight gradient it belongs to and
+// the byte offset (OOB past the matrix).  DWD: rows h, columns i of dW_down[e]; DW1: rows i
+// of dW_gate[e] (M-tiles below nMg) or dW_up[e], columns h.
+template <int KIND>
+__device__ __forceinline__ uint32_t vk_out(const Args& a, const Tile& c, int i, int p, int wm, int wn, int nMg,
+                                           int L, rsrc_t& ro) {
+  const int H = a.H, I = a.I;
+  const int n = c.nt * BN + wn * 128 + (L & 15) * 8;
+  if constexpr (KIND == DWD) {
+    ro = gg::mkr_off(a.out0, (long long)c.e * H * I * 2, (long long)H * I * 2);
+    const int m = c.mt * BM + 16 * (4 * i + wm) + 4 * p + (L >> 4);  // h
+    return (m < H && n < I) ? (uint32_t)m * (uint32_t)I * 2u + (uint32_t)n * 2u : OOB;
+  } else {
+    const int seg = c.mt >= nMg;
+    const int m = (c.mt - seg * nMg) * BM + 16 * (4 * i + wm) + 4 * p + (L >> 4);  // i
+    ro = gg::mkr_off(seg ? a.out1 : a.out0, (long long)c.e * I * H * 2, (long long)I * H * 2);
+    return (m < I && n < H) ? (uint32_t)m * (uint32_t)H * 2u + (uint32_t)n * 2u : OOB;
+  }
+}
+
+// Varlen-K epilogue.  Wavefronts 0-3 (wn = 0) issue every operand load and no store;
+// wavefronts 4-7 (wn = 1) issue every store.  Loads and stores of a wavefront complete in
+// issue order on one counter, so a wavefront that stored a tile's results would have to wait
+// for those stores to drain before it could wait for any load issued after them; split this
+// way, the loaders' waits never include a store.
+//  part 1 (every wavefront, after an LDS barrier): a loader writes its four blocks as bf16 to
+//    `pst` (4 KB per block; stage_write placement); a storer stores its own blocks through
+//    its 4 KB slot `own`.
+//  part 2 (storers, after a second barrier): the partner loader's (w - 4) blocks from its `pst`.
+// An empty group's tile (zero = true) stores zeros for both and uses no LDS.
+template <int KIND>
+__device__ __forceinline__ void vk_epilogue1(const Args& a, const Tile& c, f32x4 (&acc)[4][8], int wm, int wn,
+                                             int L_, int nMg, char* pst, char* own) {
+  int L = L_;
+  asm volatile("" : "+v"(L));
+  if (wn == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) stage_write(pst + i * 4096, acc[i], L);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      stage_write(own, acc[i], L);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint4 v = stage_read(own, p, L);
+        rsrc_t ro;
+        const uint32_t off = vk_out<KIND>(a, c, i, p, wm, 1, nMg, L, ro);
+        st16(ro, off, v);
+      }
+    }
+  }
+}
+template <int KIND>
+__device__ __forceinline__ void vk_epilogue2(const Args& a, const Tile& c, int wm, int L_, int nMg, const char* pst) {
+  int L = L_;
+  asm volatile("" : "+v"(L));
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint4 v = stage_read(pst + i * 4096, p, L);
+      rsrc_t ro;
+      const uint32_t off = vk_out<KIND>(a, c, i, p, wm, 0, nMg, L, ro);
+      st16(ro, off, v);
+    }
+}
+template <int KIND>
+__device__ __forceinline__ void vk_zero(const Args& a, const Tile& c, int wm, int L_, int nMg) {
+  int L = L_;
+  asm volatile("" : "+v"(L));
+  const uint4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int wn = 0; wn < 2; ++wn)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        rsrc_t ro;
+        const uint32_t off = vk_out<KIND>(a, c, i, p, wm, wn, nMg, L, ro);
+        st16(ro, off, z);
+      }
+}
+
 // ------------------------------------------------------------------ fragments
 // K-contiguous fragment of rows r0 .. r0+15 (varlen-M stages, rows of 128 bytes): lane reads
 // row r0 + (L & 15), k-chunk 4 sub + (L >> 4) of the stage's eight; kc_off: the lane's offset
@@ -717,15 +785,12 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
   using T = KT<KIND>;
   using G = Geo<KIND>;
   constexpr bool GATHER = T::GA || T::GB;
-  // memory instructions per step and wavefront: 4 operand loads (plus one more A load on
-  // wavefronts w < NA - 16), plus the token load that gathered varlen-K kinds issue every
-  // step (varlen-M kinds issue theirs once per tile, before the tile's step loads)
-  constexpr int NLW = 4 + (T::VK && GATHER ? 1 : 0);
 
   __shared__ __attribute__((aligned(1024))) char s_ring[G::NST * G::STGK];
   __shared__ __attribute__((aligned(256))) int s_tok[8 * NSTG * (TOKB / 4)];
   __shared__ int s_sched[1025];
   __shared__ int s_wsum[9];
+  __shared__ __attribute__((aligned(256))) char s_stg[T::VK ? 4 * 4096 : 16];
 
   const int tid = threadIdx.x, L = tid & 63;
   const int w = ufl(tid >> 6);
@@ -984,19 +1049,24 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
     vm_drain();
   } else {
     // ---- varlen-K: one pipeline over the workgroup's tiles, three steps ahead ----
-    // Tiles without k-steps (empty groups) only write zeros.
+    // Wavefronts 0-3 (wn = 0) issue every load (operands and tokens), wavefronts 4-7 every
+    // store (see vk_epilogue1); all eight compute.  Tiles without k-steps (empty groups) only
+    // write zeros.
+    const bool loader = wn == 0;
+    char* s_own = s_stg + wm * 4096;  // a storer's staging slot
     Tile Cc;
     S.decode(a, Cc, 0);
     while (Cc.valid && Cc.nk == 0) {
-      epilogue<KIND>(a, Cc, acc, wm, wn, L, S.nMg, s_ring + w * 4096);
+      if (!loader) vk_zero<KIND>(a, Cc, wm, L, S.nMg);
       S.decode(a, Cc, Cc.it + 1);
     }
     if (!Cc.valid) return;
 
-    // the token load of cursor t at step index s (gathered kinds, every step)
+    // the token load of cursor t at step index s (gathered kinds, every step): loader w takes
+    // the rows 8w .. 8w + 63 of the step (its loads use rows 8w .. 8w + 7)
     auto tok_issue = [&](const Tile& t, int s) __attribute__((always_inline)) {
       const uint32_t m0 = tok_m0 + (uint32_t)(s & (NSTG - 1)) * TOKB;
-      dma4(rtok, m0, t.valid ? (uint32_t)(t.roff + t.kt * BK + 4 * w + L) * 4u : OOB);
+      dma4(rtok, m0, t.valid ? (uint32_t)(t.roff + t.kt * BK + 8 * w + L) * 4u : OOB);
     };
     Tile Ld = Cc, Tk = Cc;
     auto load_issue = [&](int s) __attribute__((always_inline)) {
@@ -1005,92 +1075,89 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
       ld.issue(a, Ld, ring_m0 + (uint32_t)(s & (NSTG - 1)) * G::STGK, tk, w, L);
       S.next(a, Ld, true);
     };
+    // memory instructions a loader issues per step: 8 operand loads and the token load
+    constexpr int NLK = 8 + (GATHER ? 1 : 0);
+    static_assert(G::NA == 16, "varlen-K: four loaders, eight loads each per step");
 
-    // ---- prologue: tokens of steps 0..2 resident, loads of steps 0..2 in flight ----
-    if constexpr (GATHER) {
+    // ---- prologue (loaders): tokens of steps 0..2 resident, loads of steps 0..2 in flight ----
+    if (loader) {
+      if constexpr (GATHER) {
+#pragma unroll 1
+        for (int s = 0; s < AHEAD; ++s) {
+          tok_issue(Tk, s);
+          S.next(a, Tk, true);
+        }
+        vm_drain();
+      }
 #pragma unroll 1
       for (int s = 0; s < AHEAD; ++s) {
-        tok_issue(Tk, s);
-        S.next(a, Tk, true);
+        if constexpr (GATHER) {
+          tok_issue(Tk, s + AHEAD);
+          S.next(a, Tk, true);
+        }
+        load_issue(s);
       }
-      vm_drain();
+      // step 0's loads have landed (the loads of steps 1 and 2 and their token loads were
+      // issued after them)
+      vm_wait<2 * NLK>();
     }
-#pragma unroll 1
-    for (int s = 0; s < AHEAD; ++s) {
-      if constexpr (GATHER) {
-        tok_issue(Tk, s + AHEAD);
-        S.next(a, Tk, true);
-      }
-      load_issue(s);
-    }
-
-    // epilogues issued after the loads of the last two steps (their stores are younger)
-    int h0 = 0, h1 = 0;
-
-    // step 0's loads have landed (the loads of steps 1 and 2 and their token loads were issued
-    // after them); its fragments go to registers
+    lds_barrier();
     bf16x8 fa[4], fb[8];
-    vm_wait_barrier<2 * NLW>();
     {
-      const char* s0 = s_ring;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) fb[j] = frag_mn(s0 + G::OPA, wn * 128 + 16 * j, mn_k0, mn_ff, mn_b);
+      for (int j = 0; j < 8; ++j) fb[j] = frag_mn(s_ring + G::OPA, wn * 128 + 16 * j, mn_k0, mn_ff, mn_b);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) fa[i] = frag_mn(s0, 16 * (4 * i + wm), mn_k0, mn_ff, mn_b);
+      for (int i = 0; i < 4; ++i) fa[i] = frag_mn(s_ring, 16 * (4 * i + wm), mn_k0, mn_ff, mn_b);
     }
 
 #pragma unroll 1
     for (int s = 0;; ++s) {
-      // step s + 1's loads (issued two steps ago) have landed for every wavefront, and every
-      // wavefront is done with the stage that the loads below overwrite (step s - 1's, whose
-      // fragments were read before step s - 1's MFMAs)
-      const int ne = h0 + h1;
-      static_assert(G::NA == 16, "varlen-K: every wavefront issues NLW loads per step");
-      step_wait<NLW, T::ST>(ne);
-      h1 = h0;
-      h0 = 0;
+      // step s + 1's loads (issued two steps ago; only the next step's were issued after
+      // them) have landed, and every wavefront's LDS reads are complete, in particular those
+      // of the stage the loads below overwrite (step s - 1's)
+      if (loader) vm_wait<NLK>();
+      lds_barrier();
 
       // ---- this step's loads (three steps ahead), the MFMAs of step s and the fragment
       // reads of step s + 1 ----
-      auto issue_block = [&]() __attribute__((always_inline)) {
+      if (loader) {
         if constexpr (GATHER) {
           tok_issue(Tk, s + 2 * AHEAD);
           S.next(a, Tk, true);
         }
         load_issue(s + AHEAD);
-      };
-      // The two wavefronts of a SIMD (wn = 0 and 1) take the two halves in opposite orders,
-      // so one's load issue and bookkeeping overlap the other's MFMAs instead of both waiting
-      // on the same phase.
-      if (wn == 0) issue_block();
+      }
       mma_pf(fa, fb, s_ring + ((s + 1) & (NSTG - 1)) * G::STGK);
-      if (wn != 0) issue_block();
 
       // ---- advance the compute cursor; finish a tile after its last step ----
       if (Cc.kt + 1 < Cc.nk) {
         ++Cc.kt;
-      } else {
-        // the stage of step s is free once every wavefront has read its fragments; the loads
-        // that refill it are issued only after the next step's barrier
-        char* st = s_ring + (s & (NSTG - 1)) * G::STGK + w * 4096;
-        lds_barrier();
-        epilogue<KIND>(a, Cc, acc, wm, wn, L, S.nMg, st);
-        ++h0;
-#pragma unroll
-        for (int i = 0; i < G::MI; ++i)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        S.decode(a, Cc, Cc.it + 1);
-        while (Cc.valid && Cc.nk == 0) {
-          epilogue<KIND>(a, Cc, acc, wm, wn, L, S.nMg, st);
-          ++h0;
-          S.decode(a, Cc, Cc.it + 1);
-        }
-        if (!Cc.valid) break;
+        continue;
       }
+      // Stages s and s + 1 are free: every wavefront's reads of them are complete after the
+      // barrier below, and the loads that refill them are issued after the barriers of steps
+      // s + 1 and s + 2.  Loader w stages its blocks in the 16 KB at (w & 1) 16 KB of stage
+      // s + (w >> 1).
+      auto pst_of = [&](int v) __attribute__((always_inline)) {
+        return s_ring + ((s + (v >> 1)) & (NSTG - 1)) * G::STGK + (v & 1) * 16384;
+      };
+      lds_barrier();
+      vk_epilogue1<KIND>(a, Cc, acc, wm, wn, L, S.nMg, pst_of(wm), s_own);
+      lds_barrier();
+      if (!loader) vk_epilogue2<KIND>(a, Cc, wm, L, S.nMg, pst_of(wm));
+#pragma unroll
+      for (int i = 0; i < G::MI; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      S.decode(a, Cc, Cc.it + 1);
+      while (Cc.valid && Cc.nk == 0) {
+        if (!loader) vk_zero<KIND>(a, Cc, wm, L, S.nMg);
+        S.decode(a, Cc, Cc.it + 1);
+      }
+      if (!Cc.valid) break;
     }
     // loads past the last tile (all masked) must land before the workgroup's LDS is released
-    vm_drain();
+    if (loader) vm_drain();
   }
 }
 
