@@ -21,12 +21,13 @@
 //    row count are skipped.
 //    The grid is persistent: one workgroup per CU walks its share of the tile list.
 //  * Operands go from HBM straight into LDS with buffer_load ... lds (no VGPR staging).
-//    LDS holds a ring of 4 stages of k = 32 (64 MI rows of A and 16 KB of B per stage); the
-//    loads run three k-steps ahead of the MFMAs.  Varlen-M tiles run one after another: the
-//    next tile's first three steps are issued right after the finished tile's epilogue,
-//    without waiting for its stores.  Varlen-K tiles (many short ones for small groups) share
-//    one pipeline that runs across tile boundaries.
-//  * K-contiguous operands are stored as 64-byte rows, chunk c of row r at c ^ ((r >> 2) & 3),
+//    Varlen-M kinds: two stages of k = 64 (every K-contiguous row of a stage is one whole
+//    128-byte line); each tile runs its own loop, loads one step ahead of the MFMAs, and the
+//    next tile's first step is issued before the finished tile's epilogue.  Varlen-K kinds
+//    (many short tiles for small groups): four stages of k = 32 in one pipeline that runs
+//    across tile boundaries, loads three steps ahead; only wavefronts 0-3 load and only
+//    wavefronts 4-7 store (vk_epilogue1).
+//  * K-contiguous operands are stored as 128-byte rows, chunk c of row r at c ^ ((r >> 1) & 7),
 //    and read as one 16-byte fragment per lane.  K-strided operands (the backward's weights,
 //    both varlen-K operands) are stored in their natural layout, k-rows of 512 bytes with
 //    chunk c at c ^ f(k), and read with ds_read_b64_tr_b16, which transposes 4x16 blocks of
@@ -37,9 +38,9 @@
 //    six steps ahead, into small slots in LDS.
 //  * Loads never branch: a buffer offset beyond the descriptor range returns zeros, which
 //    masks rows past a group's end, K tails and steps past the last tile.  Every step issues
-//    the same number of loads, so the wait for step s is an immediate vmcnt equal to the
-//    number of memory instructions issued after step s's loads (the later steps' loads plus
-//    the stores of any epilogue in between); a raw s_barrier then publishes the stage.
+//    the same number of loads, and a wavefront's loads and stores complete in issue order, so
+//    the wait for a step is an immediate vmcnt equal to the number of memory instructions
+//    issued after that step's loads; a raw s_barrier then publishes the stage.
 //  * Varlen-M tiles are ordered (expert, n-tile, m-tile) so tiles that share a weight slice
 //    run together; varlen-K tiles are ordered heaviest expert first.  Each XCD gets
 //    contiguous runs of the tile list, so neighbouring tiles share its L2.
@@ -255,20 +256,10 @@ struct Sched {
 };
 
 // ------------------------------------------------------------------ operand loads
-// Instruction q (0, 1) of wavefront w fills bytes [(2w+q)*1024, +1024) of an operand's stage
-// area; lane L writes the 16 bytes at offset 16 L of that kilobyte.
-//  K-contiguous: rows (2w+q)*16 + (L >> 2), position L & 3 holds k-chunk (L & 3) ^ ((L >> 4) & 3).
-//  K-strided:    k-row (2w+q)*2 + (L >> 5), position L & 31 holds column chunk (L & 31) ^ f(k).
+// A load instruction fills one kilobyte of an operand's stage area; lane L writes the 16
+// bytes at offset 16 L of it (which kilobyte and which rows: Loader).  K-strided k-rows of
+// 512 bytes hold column chunk c at position c ^ f(k).
 __device__ __forceinline__ int mn_f(int k) { return 2 * ((k & 3) | (((k >> 3) & 1) << 2)); }
-// K-contiguous placement: chunk c of 64-byte row r sits at position c ^ kc_swz(r).
-#ifndef MOE_KC_SWZ
-#define MOE_KC_SWZ 2
-#endif
-__device__ __forceinline__ int kc_swz(int r) {
-  if (MOE_KC_SWZ == 1) return (r >> 1) & 3;
-  if (MOE_KC_SWZ == 2) return ((r >> 2) & 3) ^ ((r >> 1) & 2);
-  return (r >> 2) & 3;
-}
 
 template <int KIND>
 struct Loader {
