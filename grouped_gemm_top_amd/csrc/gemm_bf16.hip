@@ -1006,12 +1006,13 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
         // refill (the stage of step kt - 1)
         if (kt == 0 && ep) vm_wait_barrier<T::ST>();
         else vm_wait_barrier<0>();
-        if (kt + 1 < nk) issue_step(Cc, kt + 1, gs + kt + 1);
-        if (nb > 0) {
-          const char* sa = s_ring + ((gs + kt) & 1) * G::STGK;
-          mma_stage(sa, nb, 0);
-          mma_stage(sa, nb, 1);
-        }
+        // the two wavefronts of a SIMD issue the next step's loads at different points (before
+        // and after their first k-substep), so one issues loads while the other runs MFMAs
+        const char* sa = s_ring + ((gs + kt) & 1) * G::STGK;
+        if (wn == 0 && kt + 1 < nk) issue_step(Cc, kt + 1, gs + kt + 1);
+        if (nb > 0) mma_stage(sa, nb, 0);
+        if (wn != 0 && kt + 1 < nk) issue_step(Cc, kt + 1, gs + kt + 1);
+        if (nb > 0) mma_stage(sa, nb, 1);
       }
       // every wavefront is done with the ring: the last step's stage stages the epilogue, the
       // other takes the next tile's first step, issued before the epilogue so that its wait
