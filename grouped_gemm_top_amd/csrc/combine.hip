@@ -7,7 +7,10 @@
 //
 //   out[t] = sum over r in tok_rows[tok_ptr[t] .. tok_ptr[t+1]) of row_w[r] * y[r]
 // One workgroup per token, 16-byte vectors along H, fp32 accumulation in ascending row
-// order (deterministic, no atomics).  Pure HBM streaming: each y row is read once.
+// order (deterministic, no atomics).  Pure HBM streaming: each y row is read once.  A thread
+// loads the vectors of up to RB rows before it accumulates any of them, so RB loads per lane
+// are in flight instead of one (with one load at a time the kernel is bound by memory
+// latency, not bandwidth); the sum still runs row by row in ascending order.
 #include "common.h"
 
 namespace moe {
@@ -17,6 +20,7 @@ __global__ __launch_bounds__(256) void k_combine(const T* __restrict__ y, int H,
                                                  const int32_t* __restrict__ tok_rows,
                                                  const float* __restrict__ row_w, T* __restrict__ out) {
   constexpr int VEC = 16 / sizeof(T);
+  constexpr int RB = 8;
   const int t = blockIdx.x;
   const int q0 = tok_ptr[t], q1 = tok_ptr[t + 1];
   const int nv = H / VEC;
@@ -24,13 +28,24 @@ __global__ __launch_bounds__(256) void k_combine(const T* __restrict__ y, int H,
     float acc[VEC];
 #pragma unroll
     for (int c = 0; c < VEC; ++c) acc[c] = 0.f;
-    for (int q = q0; q < q1; ++q) {
-      const int r = tok_rows[q];
-      const float wr = row_w ? row_w[r] : 1.0f;
-      const uint4 raw = *reinterpret_cast<const uint4*>(y + (size_t)r * H + (size_t)v * VEC);
-      const T* vals = reinterpret_cast<const T*>(&raw);
+    for (int qb = q0; qb < q1; qb += RB) {
+      uint4 raw[RB];
+      float wr[RB];
 #pragma unroll
-      for (int c = 0; c < VEC; ++c) acc[c] += wr * to_f32<T>(vals[c]);
+      for (int u = 0; u < RB; ++u) {
+        // past the token's last row the load repeats that row, and the sum below skips it
+        const int r = tok_rows[min(qb + u, q1 - 1)];
+        wr[u] = row_w ? row_w[r] : 1.0f;
+        raw[u] = *reinterpret_cast<const uint4*>(y + (size_t)r * H + (size_t)v * VEC);
+      }
+#pragma unroll
+      for (int u = 0; u < RB; ++u) {
+        if (qb + u < q1) {  // uniform across the workgroup
+          const T* vals = reinterpret_cast<const T*>(&raw[u]);
+#pragma unroll
+          for (int c = 0; c < VEC; ++c) acc[c] += wr[u] * to_f32<T>(vals[c]);
+        }
+      }
     }
     uint4 o;
     T* ov = reinterpret_cast<T*>(&o);
