@@ -1063,20 +1063,24 @@ static hipError_t layer_bwd_t(const void* dout, const void* x, const void* wg, c
       if ((err = hipGetLastError()) != hipSuccess) return err;
     }
   }
+  // The two weight-gradient kernels run first and dX last: each writes its dW (805 MB in all
+  // at the headline shape) through the caches, and those lines drain to HBM while the next
+  // kernels run.  Following dW_g/u directly, the next step's gate/up GEMM measured 22 us
+  // slower; the dX GEMM absorbs the drain at a smaller cost.
   // dW_down = sum_r dOut[t]^T A'   (varlen-K)
   a.act = aprime; a.out0 = dwd; a.out1 = nullptr;
   if ((err = launch(KDWD{}, (long long)p.E * ((H + tm - 1) / tm) * nTN)) != hipSuccess) return err;
+  // dW_gate, dW_up = sum_r dH^T x[t]   (varlen-K)
+  a.dh = dh; a.out0 = dwg; a.out1 = dwu;
+  const long long mtw = BF ? 2LL * ((I + 255) / 256) : (2LL * I + 127) / 128;
+  if ((err = launch(KDW1{}, (long long)p.E * mtw * ((H + tn - 1) / tn))) != hipSuccess) return err;
   // dXe = dH [W_gate; W_up]   (varlen-M), then the unweighted combine to token order
-  a.dh = dh; a.out0 = dxe;
+  a.out0 = dxe; a.out1 = nullptr;
   if ((err = launch(KDX{}, mt * ((H + tn - 1) / tn))) != hipSuccess) return err;
   kernel_event(MOE_K_DX_COMBINE, 0, s);
   err = launch_combine(sizeof(T) == 2 ? MOE_BF16 : MOE_F32, dxe, H, p, nullptr, dx, s);
   kernel_event(MOE_K_DX_COMBINE, 1, s);
-  if (err != hipSuccess) return err;
-  // dW_gate, dW_up = sum_r dH^T x[t]   (varlen-K)
-  a.out0 = dwg; a.out1 = dwu;
-  const long long mtw = BF ? 2LL * ((I + 255) / 256) : (2LL * I + 127) / 128;
-  return launch(KDW1{}, (long long)p.E * mtw * ((H + tn - 1) / tn));
+  return err;
 }
 
 hipError_t launch_layer_bwd(moe_dtype dt, const void* dout, const void* x, const void* wg, const void* wu,
