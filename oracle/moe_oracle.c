@@ -508,7 +508,7 @@ ORACLE_EXPORT int oracle_layer_bwd(const float* dout, const float* x, const floa
     free(tptr); free(tlist);
   }
 
-  /* phase 3, per expert: weight gradients */
+  /* phase 3, per expert and output row: weight gradients */
   if (dwg || dwu || dwd) {
     int32_t *eptr, *elist;
     if (group_pairs(P, pair_e, E, &eptr, &elist)) { free(A); free(DG); free(DU); return -2; }
@@ -519,40 +519,45 @@ ORACLE_EXPORT int oracle_layer_bwd(const float* dout, const float* x, const floa
 #pragma omp atomic write
         fail = 1;
       } else {
+/* one work item per output row: dW_down[e] row h (items 0 .. H-1 of expert e) or the
+         * rows i of dW_gate[e] and dW_up[e] (items H .. H+I-1); each row is summed over the
+         * expert's pairs in pair order */
 #pragma omp for schedule(dynamic, 1)
-        for (int e = 0; e < E; ++e) {
-          if (dwd)
-            for (int h = 0; h < H; ++h) {
-              for (int i = 0; i < I; ++i) acc[i] = 0;
-              for (int q = eptr[e]; q < eptr[e + 1]; ++q) {
-                const int p = elist[q];
-                const real dyh = (real)pair_w[p] * (real)dout[(size_t)pair_t[p] * H + h];
-                const real* a = A + (size_t)p * I;
-                for (int i = 0; i < I; ++i) acc[i] += dyh * a[i];
-              }
-              for (int i = 0; i < I; ++i) dwd[((size_t)e * H + h) * I + i] = (double)acc[i];
+        for (long wi = 0; wi < (long)E * (H + I); ++wi) {
+          const int e = (int)(wi / (H + I)), r = (int)(wi % (H + I));
+          if (r < H) {
+            const int h = r;
+            if (!dwd) continue;
+            for (int i = 0; i < I; ++i) acc[i] = 0;
+            for (int q = eptr[e]; q < eptr[e + 1]; ++q) {
+              const int p = elist[q];
+              const real dyh = (real)pair_w[p] * (real)dout[(size_t)pair_t[p] * H + h];
+              const real* a = A + (size_t)p * I;
+              for (int i = 0; i < I; ++i) acc[i] += dyh * a[i];
             }
-          for (int i = 0; i < I; ++i) {
-            if (dwg) {
-              for (int h = 0; h < H; ++h) acc[h] = 0;
-              for (int q = eptr[e]; q < eptr[e + 1]; ++q) {
-                const int p = elist[q];
-                const float* xt = x + (size_t)pair_t[p] * H;
-                const real d = DG[(size_t)p * I + i];
-                for (int h = 0; h < H; ++h) acc[h] += d * (real)xt[h];
-              }
-              for (int h = 0; h < H; ++h) dwg[((size_t)e * I + i) * H + h] = (double)acc[h];
+            for (int i = 0; i < I; ++i) dwd[((size_t)e * H + h) * I + i] = (double)acc[i];
+            continue;
+          }
+          const int i = r - H;
+          if (dwg) {
+            for (int h = 0; h < H; ++h) acc[h] = 0;
+            for (int q = eptr[e]; q < eptr[e + 1]; ++q) {
+              const int p = elist[q];
+              const float* xt = x + (size_t)pair_t[p] * H;
+              const real d = DG[(size_t)p * I + i];
+              for (int h = 0; h < H; ++h) acc[h] += d * (real)xt[h];
             }
-            if (dwu) {
-              for (int h = 0; h < H; ++h) acc[h] = 0;
-              for (int q = eptr[e]; q < eptr[e + 1]; ++q) {
-                const int p = elist[q];
-                const float* xt = x + (size_t)pair_t[p] * H;
-                const real d = DU[(size_t)p * I + i];
-                for (int h = 0; h < H; ++h) acc[h] += d * (real)xt[h];
-              }
-              for (int h = 0; h < H; ++h) dwu[((size_t)e * I + i) * H + h] = (double)acc[h];
+            for (int h = 0; h < H; ++h) dwg[((size_t)e * I + i) * H + h] = (double)acc[h];
+          }
+          if (dwu) {
+            for (int h = 0; h < H; ++h) acc[h] = 0;
+            for (int q = eptr[e]; q < eptr[e + 1]; ++q) {
+              const int p = elist[q];
+              const float* xt = x + (size_t)pair_t[p] * H;
+              const real d = DU[(size_t)p * I + i];
+              for (int h = 0; h < H; ++h) acc[h] += d * (real)xt[h];
             }
+            for (int h = 0; h < H; ++h) dwu[((size_t)e * I + i) * H + h] = (double)acc[h];
           }
         }
       }

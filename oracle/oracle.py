@@ -23,7 +23,9 @@ _f64p = ctypes.POINTER(ctypes.c_double)
 
 
 def lib_path(real: str = "f64") -> str:
-    return os.path.join(_HERE, f"liboracle_{real}.so")
+    """The oracle library; ORACLE_LIB_DIR (set only by the sanitizer tests) names a directory
+    holding another build of the same source, e.g. with AddressSanitizer."""
+    return os.path.join(os.environ.get("ORACLE_LIB_DIR") or _HERE, f"liboracle_{real}.so")
 
 
 def build(verbose: bool = False) -> None:
@@ -31,7 +33,7 @@ def build(verbose: bool = False) -> None:
     for real, ctype in (("f64", "double"), ("f32", "float")):
         out = lib_path(real)
         tmp = out + ".tmp"
-        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", f"-DORACLE_REAL={ctype}",
+        cmd = ["gcc", "-O3", "-fopenmp", "-fPIC", "-shared", f"-DORACLE_REAL={ctype}",
                "-fvisibility=hidden", _SRC, "-o", tmp, "-lm"]
         if verbose:
             print(" ".join(cmd))
@@ -44,7 +46,10 @@ def _lib(real: str = "f64"):
     if real in _LIBS:
         return _LIBS[real]
     path = lib_path(real)
-    if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC):
+    if os.environ.get("ORACLE_LIB_DIR"):
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing")
+    elif not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC):
         build()
     lib = ctypes.CDLL(path)
     lib.oracle_route_topk.argtypes = [_f32p, _f32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
