@@ -11,7 +11,8 @@ import ctypes
 import os
 
 __all__ = [
-    "MoEError", "lib", "lib_path", "Plan", "route_topk", "permute", "route_token_rounding",
+    "MoEError", "lib", "lib_path", "load_library", "Plan", "route_topk", "permute",
+    "route_token_rounding",
     "route_capacity", "grouped_gemm_fwd", "unpermute_combine", "layer_bwd", "router_logits", "router_bwd",
     "workspace_bytes", "plan_rows_cap", "MOE_OK", "MOE_EINVAL", "MOE_EUNSUPPORTED", "MOE_EWORKSPACE",
     "MOE_EHIP", "OP_PERMUTE", "OP_ROUTE_TR", "OP_GEMM_FWD", "OP_LAYER_BWD", "OP_ROUTER_BWD",
@@ -42,9 +43,8 @@ _LIB = None
 
 
 def lib_path() -> str:
-    """The in-tree libmoe.so; MOE_LIBRARY may name another build of the same sources (used
-    only to compare kernel variants side by side)."""
-    return os.environ.get("MOE_LIBRARY") or os.path.join(_HERE, "libmoe.so")
+    """The in-tree libmoe.so (built by ``grouped_gemm_top_amd.build``)."""
+    return os.path.join(_HERE, "libmoe.so")
 
 
 class MoEError(RuntimeError):
@@ -71,6 +71,13 @@ def lib():
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -m grouped_gemm_top_amd.build` "
                            "(there is no fallback path)")
+    _LIB = load_library(path)
+    return _LIB
+
+
+def load_library(path: str):
+    """ctypes handle of a build of libmoe.so at `path` with every entry point's signature set
+    (lib() uses it for the in-tree library; the host-sanitizer tests for their own build)."""
     L = ctypes.CDLL(path)
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     pp = ctypes.POINTER(CPlan)
@@ -91,12 +98,12 @@ def lib():
     L.moe_router_logits.argtypes = [ctypes.c_int, vp, vp, vp, i32, i32, i32, vp, vp, sz, vp]
     L.moe_router_bwd.argtypes = [ctypes.c_int, vp, vp, vp, pp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_set_kernel_events.argtypes = [i32, vp, vp]
-    for fn in ("moe_route_topk", "moe_permute", "moe_route_token_rounding", "moe_route_capacity",
+    for fn in ("moe_route_topk", "moe_permute", "moe_route_token_rounding",
+               "moe_route_capacity",
                "moe_grouped_gemm_fwd",
                "moe_unpermute_combine", "moe_layer_bwd", "moe_router_logits", "moe_router_bwd",
                "moe_set_kernel_events"):
         getattr(L, fn).restype = ctypes.c_int
-    _LIB = L
     return L
 
 
@@ -149,20 +156,25 @@ def workspace_bytes(op: int, dtype_code: int, N: int, E: int, k: int, H: int = 8
 class Plan:
     """Device arrays of a routing plan (see moe_plan in include/moe.h), allocated with torch."""
 
-    def __init__(self, N: int, E: int, k: int, kind: int = PLAN_TOPK, mtile: int = 0, device="cuda"):
+    def __init__(self, N: int, E: int, k: int, kind: int = PLAN_TOPK, mtile: int = 0, device="cuda",
+                 alloc=None):
+        """alloc(name, numel, dtype) -> 1-D device tensor, if given, supplies the arrays
+        (default: torch.empty on `device`)."""
         import torch
         self.N, self.E, self.k, self.kind = N, E, k, kind
         self.mtile = mtile if kind in (PLAN_TR, PLAN_CAP) else 0  # capacity plans: the capacity
         self.M_cap = plan_rows_cap(kind, N, E, k, self.mtile)
-        i32 = dict(dtype=torch.int32, device=device)
+        if alloc is None:
+            alloc = lambda name, n, dt: torch.empty(n, dtype=dt, device=device)  # noqa: E731
+        i32 = torch.int32
         mc = max(self.M_cap, 1)
-        self.counts = torch.empty(E, **i32)
-        self.offsets = torch.empty(E + 1, **i32)
-        self.row_token = torch.empty(mc, **i32)
-        self.row_w = torch.empty(mc, dtype=torch.float32, device=device)
-        self.row_pair = torch.empty(mc, **i32)
-        self.tok_ptr = torch.empty(N + 1, **i32)
-        self.tok_rows = torch.empty(mc, **i32)
+        self.counts = alloc("counts", E, i32)
+        self.offsets = alloc("offsets", E + 1, i32)
+        self.row_token = alloc("row_token", mc, i32)
+        self.row_w = alloc("row_w", mc, torch.float32)
+        self.row_pair = alloc("row_pair", mc, i32)
+        self.tok_ptr = alloc("tok_ptr", N + 1, i32)
+        self.tok_rows = alloc("tok_rows", mc, i32)
         self._c = CPlan(kind, N, E, k, self.M_cap, self.mtile, *(t.data_ptr() for t in (
             self.counts, self.offsets, self.row_token, self.row_w, self.row_pair, self.tok_ptr,
             self.tok_rows)))

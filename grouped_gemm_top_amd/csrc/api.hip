@@ -67,6 +67,25 @@ moe_status check_plan(const moe_plan* p) {
 
 int64_t mcap_of(const moe_plan* p) { return p->M_cap; }
 
+// The GEMM kernels address a tensor through one buffer descriptor with 32-bit byte offsets
+// (an offset of 2^31 or more marks a masked lane), so every tensor one descriptor covers must
+// stay below 2 GiB: x and dOut [N,H], one expert's weight or weight-gradient matrix [I,H],
+// the row-ordered activations (hcache and dH [M_cap, 2I], A and A' [M_cap, I]) and the plan's
+// row arrays (4 M_cap bytes).
+constexpr int64_t kDescBytes = 0x7FFFFFFF;
+moe_status check_desc_sizes(moe_dtype dt, int64_t N, int64_t H, int64_t I, int64_t M_cap) {
+  const int64_t es = dt == MOE_BF16 ? 2 : 4;
+  REQUIRE(N * H * es <= kDescBytes, MOE_EUNSUPPORTED, "x/dout [N=%lld, H=%lld] must be < 2 GiB", (long long)N,
+          (long long)H);
+  REQUIRE(I * H * es <= kDescBytes, MOE_EUNSUPPORTED, "one expert's weight matrix [I=%lld, H=%lld] must be < 2 GiB",
+          (long long)I, (long long)H);
+  REQUIRE(M_cap * 2 * I * es <= kDescBytes, MOE_EUNSUPPORTED,
+          "row activations [M_cap=%lld, 2I=%lld] must be < 2 GiB", (long long)M_cap, (long long)(2 * I));
+  REQUIRE(M_cap * 4 <= kDescBytes, MOE_EUNSUPPORTED, "plan row arrays (M_cap=%lld) must be < 2 GiB",
+          (long long)M_cap);
+  return MOE_OK;
+}
+
 }  // namespace
 
 namespace moe {
@@ -247,6 +266,7 @@ moe_status moe_grouped_gemm_fwd(moe_dtype dt, const void* x, const void* w_gate,
   REQUIRE(aligned16(x) && aligned16(w_gate) && aligned16(w_up) && aligned16(w_down) && aligned16(hcache) &&
               aligned16(y) && aligned16(ws),
           MOE_EUNSUPPORTED, "tensors and workspace must be 16-byte aligned");
+  if ((st = check_desc_sizes(dt, plan->N, H, I, plan->M_cap)) != MOE_OK) return st;
   const size_t need = moe::gemm_fwd_ws_bytes(dt, (int)mcap_of(plan), I);
   REQUIRE(ws_bytes >= need, MOE_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   REQUIRE(ws != nullptr, MOE_EINVAL, "NULL workspace");
@@ -287,6 +307,7 @@ moe_status moe_layer_bwd(moe_dtype dt, const void* dout, const void* x, const vo
               aligned16(hcache) && aligned16(dx) && aligned16(dw_gate) && aligned16(dw_up) && aligned16(dw_down) &&
               aligned16(ws),
           MOE_EUNSUPPORTED, "tensors and workspace must be 16-byte aligned");
+  if ((st = check_desc_sizes(dt, plan->N, H, I, plan->M_cap)) != MOE_OK) return st;
   const size_t need = moe::layer_bwd_ws_bytes(dt, plan->N, (int)mcap_of(plan), H, I);
   REQUIRE(ws_bytes >= need, MOE_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   REQUIRE(ws != nullptr, MOE_EINVAL, "NULL workspace");

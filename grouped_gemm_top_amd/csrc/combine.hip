@@ -6,6 +6,7 @@
 //   [DEP] "Deep EP", section "3) Combine" (weighted sum of the k expert outputs per token)
 //
 //   out[t] = sum over r in tok_rows[tok_ptr[t] .. tok_ptr[t+1]) of row_w[r] * y[r]
+// (slots holding -1, pairs the plan skipped, add nothing)
 // One workgroup per token, 16-byte vectors along H, fp32 accumulation in ascending row
 // order (deterministic, no atomics).  Pure HBM streaming: each y row is read once.  A thread
 // loads the vectors of up to RB rows before it accumulates any of them, so RB loads per lane
@@ -31,16 +32,20 @@ __global__ __launch_bounds__(256) void k_combine(const T* __restrict__ y, int H,
     for (int qb = q0; qb < q1; qb += RB) {
       uint4 raw[RB];
       float wr[RB];
+      uint32_t live = 0u;  // bit u: slot qb + u is one of the token's rows
 #pragma unroll
       for (int u = 0; u < RB; ++u) {
-        // past the token's last row the load repeats that row, and the sum below skips it
+        // past the token's last row the load repeats that row, and the sum below skips it; a
+        // slot of -1 (a pair the plan skipped) loads row 0 and is skipped too
         const int r = tok_rows[min(qb + u, q1 - 1)];
-        wr[u] = row_w ? row_w[r] : 1.0f;
-        raw[u] = *reinterpret_cast<const uint4*>(y + (size_t)r * H + (size_t)v * VEC);
+        const int rr = r < 0 ? 0 : r;
+        if (qb + u < q1 && r >= 0) live |= 1u << u;
+        wr[u] = row_w ? row_w[rr] : 1.0f;
+        raw[u] = *reinterpret_cast<const uint4*>(y + (size_t)rr * H + (size_t)v * VEC);
       }
 #pragma unroll
       for (int u = 0; u < RB; ++u) {
-        if (qb + u < q1) {  // uniform across the workgroup
+        if (live & (1u << u)) {  // uniform across the workgroup
           const T* vals = reinterpret_cast<const T*>(&raw[u]);
 #pragma unroll
           for (int c = 0; c < VEC; ++c) acc[c] += wr[u] * to_f32<T>(vals[c]);

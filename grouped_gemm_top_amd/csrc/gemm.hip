@@ -1063,10 +1063,10 @@ static hipError_t layer_bwd_t(const void* dout, const void* x, const void* wg, c
       if ((err = hipGetLastError()) != hipSuccess) return err;
     }
   }
-  // The two weight-gradient kernels run first and dX last: each writes its dW (805 MB in all
-  // at the headline shape) through the caches, and those lines drain to HBM while the next
-  // kernels run.  Following dW_g/u directly, the next step's gate/up GEMM measured 22 us
-  // slower; the dX GEMM absorbs the drain at a smaller cost.
+  // The two weight-gradient kernels run first and dX last.  The bf16 kernels store their dW
+  // (805 MB in all at the headline shape) with the non-temporal policy, since no later kernel
+  // of the step reads it; of the orders measured with those stores this one is the fastest
+  // (with dW_g/u last, the write-back of its output had slowed the next step's gate/up GEMM).
   // dW_down = sum_r dOut[t]^T A'   (varlen-K)
   a.act = aprime; a.out0 = dwd; a.out1 = nullptr;
   if ((err = launch(KDWD{}, (long long)p.E * ((H + tm - 1) / tm) * nTN)) != hipSuccess) return err;

@@ -15,6 +15,12 @@
 //                   and one popcount), so rows of an expert ascend by token; also writes the
 //                   token-major row lists
 // Integer counting only: the plan is bit-exact and independent of scheduling.
+//
+// A pair (t, j) makes a row only if its expert id is in [0, E) and no earlier slot of the
+// same token names the same expert; other pairs (which the router never produces) are
+// skipped by every kernel here, so the plan stays consistent: counts and offsets count the
+// rows made, token t's rows fill tok_rows[t k ..] in ascending row order and its remaining
+// slots hold -1.
 #include "common.h"
 
 namespace moe {
@@ -23,6 +29,15 @@ constexpr int kPT = 256;  // threads per block
 constexpr int kTB = 64;   // tokens per block of the top-k permute (one 64-bit mask per expert)
 
 // per-block expert histogram; pair p of the block is (token p / k, slot p % k), read in order
+// Pair j of a token (slots `it`) makes a row: its expert id is in range and is the first
+// occurrence of that id among the token's slots.
+__device__ __forceinline__ bool pair_makes_row(const int32_t* it, int j, int e, int E) {
+  if (e < 0 || e >= E) return false;
+  for (int x = 0; x < j; ++x)
+    if (it[x] == e) return false;
+  return true;
+}
+
 template <int TB>
 __global__ __launch_bounds__(kPT) void k_perm_hist(const int32_t* __restrict__ idx, int N, int E, int k,
                                                    int32_t* __restrict__ bcnt) {
@@ -33,8 +48,8 @@ __global__ __launch_bounds__(kPT) void k_perm_hist(const int32_t* __restrict__ i
   const int np = (int)(min((long long)TB, (long long)N - t0) * k);
   const int32_t* ib = idx + t0 * k;
   for (int q = threadIdx.x; q < np; q += kPT) {
-    const int e = ib[q];
-    if (e >= 0 && e < E) atomicAdd(&s_cnt[e], 1);
+    const int e = ib[q], tl = q / k;
+    if (pair_makes_row(ib + (size_t)tl * k, q - tl * k, e, E)) atomicAdd(&s_cnt[e], 1);
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += kPT) bcnt[(size_t)blockIdx.x * E + e] = s_cnt[e];
@@ -114,8 +129,11 @@ __global__ __launch_bounds__(kPT) void k_perm_scatter(const int32_t* __restrict_
                                                       int32_t* __restrict__ row_token, float* __restrict__ row_w,
                                                       int32_t* __restrict__ row_pair, int32_t* __restrict__ tok_ptr,
                                                       int32_t* __restrict__ tok_rows) {
-  __shared__ uint32_t s_bits[1024 * 2];  // expert e: tokens 0-31 and 32-63 of the block
+  __shared__ uint32_t s_bits[1024 * 2];         // expert e: tokens 0-31 and 32-63 of the block
+  __shared__ uint32_t s_texp[kTB * (1024 / 32)];  // token tl: its experts, EW words of 32 ids
+  const int EW = (E + 31) >> 5;
   for (int q = threadIdx.x; q < 2 * E; q += kPT) s_bits[q] = 0u;
+  for (int q = threadIdx.x; q < kTB * EW; q += kPT) s_texp[q] = 0u;
   __syncthreads();
   const int t0 = blockIdx.x * kTB;
   const int nt = min(kTB, N - t0);
@@ -123,28 +141,42 @@ __global__ __launch_bounds__(kPT) void k_perm_scatter(const int32_t* __restrict_
   const int32_t* ib = idx + (size_t)t0 * k;
   for (int q = threadIdx.x; q < np; q += kPT) {
     const int e = ib[q], tl = q / k;
-    if (e >= 0 && e < E) atomicOr(&s_bits[2 * e + (tl >> 5)], 1u << (tl & 31));
+    if (e >= 0 && e < E) {  // (a repeated id sets the same bits again)
+      atomicOr(&s_bits[2 * e + (tl >> 5)], 1u << (tl & 31));
+      atomicOr(&s_texp[tl * EW + (e >> 5)], 1u << (e & 31));
+    }
   }
   if (threadIdx.x < nt) tok_ptr[t0 + threadIdx.x] = (t0 + threadIdx.x) * k;
   __syncthreads();
   const int32_t* bb = bbase + (size_t)blockIdx.x * E;
   for (int q = threadIdx.x; q < np; q += kPT) {
     const int e = ib[q];
-    if (e < 0 || e >= E) continue;
     const int tl = q / k, j = q - tl * k;
+    const int t = t0 + tl;
+    const uint32_t* tx = s_texp + tl * EW;
+    if (!pair_makes_row(ib + (size_t)tl * k, j, e, E)) {
+      // a skipped pair: the token's slots past its rows hold -1 (slot j is one of them when
+      // j >= the number of distinct in-range experts of the token)
+      int nrow = 0;
+      for (int x = 0; x < EW; ++x) nrow += __popc(tx[x]);
+      if (j >= nrow) tok_rows[(size_t)t * k + j] = -1;
+      continue;
+    }
     const uint32_t lo = s_bits[2 * e], hi = s_bits[2 * e + 1];
     const int rank = tl < 32 ? __popc(lo & ((1u << tl) - 1u)) : __popc(lo) + __popc(hi & ((1u << (tl - 32)) - 1u));
     const int row = bb[e] + rank;
-    const int t = t0 + tl;
     row_token[row] = t;
     row_w[row] = w[(size_t)t * k + j];
     row_pair[row] = t * k + j;
     // rows ascend with the expert id, so the token-major position is the number of this
-    // token's experts with a smaller id
-    const int32_t* it = ib + (size_t)tl * k;
-    int pos = 0;
-    for (int x = 0; x < k; ++x) pos += (it[x] < e);
+    // token's distinct experts with a smaller id; slots past the token's rows are filled with
+    // -1 above, and a token whose k experts are distinct and in range has exactly k rows
+    int pos = __popc(tx[e >> 5] & ((1u << (e & 31)) - 1u));
+    for (int x = 0; x < (e >> 5); ++x) pos += __popc(tx[x]);
     tok_rows[(size_t)t * k + pos] = row;
+    int nrow = pos + __popc(tx[e >> 5] >> (e & 31));
+    for (int x = (e >> 5) + 1; x < EW; ++x) nrow += __popc(tx[x]);
+    if (j >= nrow) tok_rows[(size_t)t * k + j] = -1;
   }
 }
 

@@ -197,6 +197,7 @@ __global__ __launch_bounds__(256) void k_router_dz(const float* __restrict__ log
   float c = 0.f;
   for (int q = r0 + L; q < r1; q += 64) {
     const int r = p.tok_rows[q];
+    if (r < 0) continue;  // a slot of a pair the plan skipped
     // the expert owning row r: the last e with offsets[e] <= r
     int lo = 0, hi = E;
     while (hi - lo > 1) {

@@ -26,6 +26,11 @@
  *    Contractions accumulate in fp32.
  *  - H and I must be multiples of 8 and every data pointer 16-byte aligned, else
  *    MOE_EUNSUPPORTED.  1 <= k <= E <= 1024; N >= 0 (N == 0 is a valid empty call).
+ *  - Size limit of the grouped-GEMM calls (moe_grouped_gemm_fwd, moe_layer_bwd): their
+ *    kernels address each of these tensors with 32-bit byte offsets, so each must be smaller
+ *    than 2 GiB, else MOE_EUNSUPPORTED: x and dout (N*H elements), one expert's weight or
+ *    weight-gradient matrix (I*H elements), the row activations hcache and dH (M_cap*2I
+ *    elements) and the plan's row arrays (4*M_cap bytes).
  *  - Outputs are always overwritten, never accumulated into.
  *  - Errors: arguments are validated before anything is queued; on failure nothing is
  *    queued and moe_last_error() describes the problem.  MOE_EHIP reports a launch error
@@ -88,10 +93,12 @@ typedef enum moe_op {
  *   row_pair  int32 [M_cap]   t*k + j for the row made from topk slot j of token t;
  *                             -1 for a row added by token rounding (padding)
  *   tok_ptr   int32 [N+1]     token t owns tok_rows[tok_ptr[t] .. tok_ptr[t+1]-1]
- *   tok_rows  int32 [M_cap]   rows of each token, ascending
+ *   tok_rows  int32 [M_cap]   rows of each token, ascending (then -1 in the slots of pairs
+ *                             moe_permute skipped, see there)
  *
  * M_cap is the row capacity of the row arrays, of hcache/y and of the bwd row buffers;
- * use moe_plan_rows_cap().  For MOE_PLAN_TOPK M = N*k exactly and tok_ptr[t] = t*k.
+ * use moe_plan_rows_cap().  For MOE_PLAN_TOPK tok_ptr[t] = t*k, and M = N*k exactly when
+ * every pair is valid (always, for the router's own selection).
  */
 typedef struct moe_plan {
   int32_t kind;      /* moe_plan_kind */
@@ -142,9 +149,16 @@ moe_status moe_route_topk(const float* logits, const float* bias, int32_t N, int
  * Permute: build the top-k routing plan from topk_idx/topk_w without moving activations
  * ([GG] "적용" steps (1)-(3): flatten, sort by expert, bincount).  A stable counting sort:
  * rows of expert e appear in ascending token order.  Requires plan->kind == MOE_PLAN_TOPK,
- * plan->N/E/k equal to the arguments, plan->M_cap >= N*k, every topk_idx value in [0,E)
- * and the k experts of a token distinct (as moe_route_topk produces); other inputs give
- * an unspecified but memory-safe plan.  Workspace: moe_workspace_bytes(MOE_OP_PERMUTE, ...).
+ * plan->N/E/k equal to the arguments and plan->M_cap >= N*k.
+ * Pairs that cannot make a row are skipped, so every plan this call writes is consistent and
+ * safe to pass on: a pair (t, j) makes a row only if topk_idx[t,j] is in [0,E) and no slot
+ * j' < j of token t names the same expert (moe_route_topk never produces another kind).  For
+ * a skipped pair no row exists: counts and offsets count only the rows made (offsets[E] = M
+ * <= N*k; plan rows M .. N*k-1 are not written), tok_ptr[t] = t*k still, token t's rows fill
+ * tok_rows[t*k ..] in ascending row order and its remaining slots hold -1 (the combine skips
+ * them), and moe_layer_bwd leaves ds[t*k+j] of that pair unwritten.  moe_router_bwd, which
+ * reads topk_idx itself, still needs the router's own (valid) selection.
+ * Workspace: moe_workspace_bytes(MOE_OP_PERMUTE, ...).
  */
 moe_status moe_permute(const int32_t* topk_idx, const float* topk_w, int32_t N, int32_t E, int32_t k,
                        const moe_plan* plan, void* ws, size_t ws_bytes, void* stream);

@@ -15,6 +15,7 @@ from .oracle import (  # noqa: F401
     router_logits,
     permute,
     route_topk,
+    set_threads,
     threads,
     token_round,
 )

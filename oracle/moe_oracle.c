@@ -39,6 +39,14 @@ typedef ORACLE_REAL real;
 
 ORACLE_EXPORT int oracle_real_bytes(void) { return (int)sizeof(real); }
 
+/* Number of OpenMP threads later parallel regions of this library use, when called from the
+ * thread that calls the library (n >= 1); returns the resulting count. */
+int oracle_threads(void);
+ORACLE_EXPORT int oracle_set_threads(int n) {
+  if (n >= 1) omp_set_num_threads(n);
+  return oracle_threads();
+}
+
 /* Number of OpenMP threads a parallel region of this library uses. */
 ORACLE_EXPORT int oracle_threads(void) {
   int n = 1;

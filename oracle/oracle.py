@@ -73,7 +73,8 @@ def _lib(real: str = "f64"):
     lib.oracle_router_bwd.argtypes = [_f32p, _f32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p,
                                       ctypes.c_int, _i32p, _i32p, _f32p, _f32p, _f32p, ctypes.c_int,
                                       _f64p, _f64p, _f64p, _f64p]
-    for fn in ("oracle_route_topk", "oracle_permute", "oracle_token_round", "oracle_layer_fwd",
+    lib.oracle_set_threads.argtypes = [ctypes.c_int]
+    for fn in ("oracle_set_threads", "oracle_route_topk", "oracle_permute", "oracle_token_round", "oracle_layer_fwd",
                "oracle_layer_bwd", "oracle_router_logits", "oracle_router_bwd", "oracle_capacity_plan",
                "oracle_real_bytes",
                "oracle_threads"):
@@ -85,6 +86,11 @@ def _lib(real: str = "f64"):
 def threads(real: str = "f64") -> int:
     """OpenMP threads the oracle's parallel loops use."""
     return int(_lib(real).oracle_threads())
+
+
+def set_threads(n: int, real: str = "f64") -> int:
+    """Use n OpenMP threads in later calls (from this thread); returns the resulting count."""
+    return int(_lib(real).oracle_set_threads(int(n)))
 
 
 def _p(a, t):

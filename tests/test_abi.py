@@ -23,6 +23,11 @@ def _declared():
 
 @pytest.fixture(scope="module")
 def L():
+    # MOE_ABI_TEST_LIB: another build of the same sources to run these checks on (the
+    # host-AddressSanitizer build of tests/test_asan.py)
+    other = os.environ.get("MOE_ABI_TEST_LIB")
+    if other:
+        return G.load_library(other)
     if not os.path.exists(G.lib_path()):
         import grouped_gemm_top_amd.build as B
         B.build()
@@ -148,6 +153,36 @@ def test_layer_bwd_errors(L):
     assert call(ds=None) == G.MOE_EINVAL
     assert call(H=12) == G.MOE_EUNSUPPORTED
     assert call(plan=_plan(M_cap=3)) == G.MOE_EINVAL
+
+
+def test_descriptor_size_limits(L):
+    """Every tensor one kernel buffer descriptor covers must stay below 2 GiB (32-bit byte
+    offsets); larger shapes are refused with MOE_EUNSUPPORTED before anything is queued, by
+    both grouped-GEMM calls, and shapes just inside the limit pass this check (the calls then
+    stop at the workspace check, since the fake workspace is too small)."""
+    f = ctypes.c_void_p(FAKE)
+
+    def calls(dt, N, H, I, E=8, k=2):
+        p = _plan(N=N, E=E, k=k)
+        fwd = L.moe_grouped_gemm_fwd(dt, f, f, f, f, H, I, ctypes.byref(p), f, f, f, 1, None)
+        bwd = L.moe_layer_bwd(dt, f, f, f, f, f, H, I, ctypes.byref(p), f, f, f, f, f, f, f, 1, None)
+        return fwd, bwd
+
+    E2 = G.MOE_EUNSUPPORTED
+    # x / dout [N, H]: 2^31 bytes exactly (N * H * 2)
+    assert calls(G.MOE_BF16, 65536, 16384, 8) == (E2, E2)
+    assert "x/dout" in _err(L)
+    assert calls(G.MOE_BF16, 65535, 16384, 8) == (G.MOE_EWORKSPACE, G.MOE_EWORKSPACE)
+    # the same N*H is over the limit in fp32 (4-byte elements)
+    assert calls(G.MOE_F32, 32768, 16384, 8) == (E2, E2)
+    # one expert's weight matrix [I, H]
+    assert calls(G.MOE_BF16, 8, 32768, 32768) == (E2, E2)
+    assert "weight matrix" in _err(L)
+    # row activations [M_cap, 2I]: M_cap = N k = 2^20 rows, 2I = 1024 -> 2^31 bytes
+    assert calls(G.MOE_BF16, 1 << 19, 8, 512) == (E2, E2)
+    assert "row activations" in _err(L)
+    assert calls(G.MOE_BF16, 1 << 19, 8, 504) == (G.MOE_EWORKSPACE, G.MOE_EWORKSPACE)
+    # (the plan's row arrays, 4 M_cap bytes, stay below the limit whenever [M_cap, 2I] does)
 
 
 def test_probe_library_exports_and_validation():

@@ -7,16 +7,22 @@
 * two runs are bitwise identical.
 The five workloads run at full size; configurations 1 and 2 are compared in full, the
 larger ones on a sample (rows are independent given the weights, so a sampled token's out,
-dx and dS and a sampled expert's dW are exact comparisons)."""
+dx and dS and a sampled expert's dW are exact comparisons): 1024 tokens, every token of the
+two lightest non-empty experts among them, and dW of 16 experts (the heaviest, the lightest
+non-empty, up to two empty ones, the rest random).  Top-k workloads are compared end to end
+against the oracle's own routing plan and weights from the logits; token-rounding and
+capacity plans against the oracle run on the GPU plan, which is first checked bit-exact given
+the GPU's probabilities.  Every buffer of a run carries guard bands that are checked after
+each call."""
 import numpy as np
 import pytest
 
 from grouped_gemm_top_amd import workloads as W
-from harness import bitwise_equal, check_layer, check_routing, log, run_gpu, sample, upload
+from harness import Guards, bitwise_equal, check_layer, check_routing, log, rel_err, run_gpu, sample, upload
 
 pytestmark = pytest.mark.gpu
 
-SAMPLES = {3: (256, 6), 4: (1024, 16), 5: (512, 8)}
+SAMPLES = {3: (1024, 16), 4: (1024, 16), 5: (1024, 16)}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -40,6 +46,115 @@ def test_ragged_tiles(dtype):
     errs, bad = check_layer(T, res)
     log(f"[ragged {dtype}] {errs}")
     assert not bad, bad
+
+
+def test_ragged_k_tails_bf16():
+    """bf16 with H and I not multiples of 64 (H = 200, I = 72): the K tails of every kernel
+    (the last k-step of gate/up and dH over H, of down over I, of dX over 2I) and ragged N
+    tails, with several experts and ragged row counts; compared in full."""
+    wl = W.custom("ktails", N=300, H=200, I=72, E=6, k=2, dtype="bf16", bias="normal", bias_std=0.4, seed=21)
+    T = W.generate(wl)
+    res = run_gpu(T)
+    check_routing(T, res)
+    errs, bad = check_layer(T, res)
+    log(f"[k tails] {errs}")
+    assert not bad, bad
+
+
+def _plan_model(idx, w, E):
+    """CPU model of the top-k plan moe_permute documents for any topk_idx: pair (t, j) makes a
+    row only if its id is in [0, E) and no earlier slot of the token names it; rows by expert,
+    then token; token t's rows ascending in tok_rows[t k ..], then -1."""
+    N, k = idx.shape
+    valid = np.zeros((N, k), bool)
+    for t in range(N):
+        seen = set()
+        for j in range(k):
+            e = int(idx[t, j])
+            if 0 <= e < E and e not in seen:
+                valid[t, j] = True
+                seen.add(e)
+    rows = [(int(idx[t, j]), t, j) for t in range(N) for j in range(k) if valid[t, j]]
+    rows.sort()
+    counts = np.bincount([r[0] for r in rows], minlength=E).astype(np.int32)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    tok_rows = np.full(N * k, -1, np.int32)
+    fill = np.zeros(N, np.int64)
+    for r, (e, t, j) in enumerate(rows):
+        tok_rows[t * k + fill[t]] = r
+        fill[t] += 1
+    return dict(counts=counts, offsets=offsets, row_token=np.array([t for _, t, _ in rows], np.int32),
+                row_w=np.array([w[t, j] for _, t, j in rows], np.float32),
+                row_pair=np.array([t * k + j for _, t, j in rows], np.int32),
+                tok_ptr=(np.arange(N + 1) * k).astype(np.int32), tok_rows=tok_rows)
+
+
+def test_permute_skips_invalid_pairs():
+    """topk_idx with repeated and out-of-range expert ids (which the router never produces):
+    the plan matches the documented skipping rule exactly, and the layer run on it matches the
+    oracle on the pairs that made rows.  Guard bands around every buffer stay intact."""
+    import torch
+    import grouped_gemm_top_amd as G
+    wl = W.custom("invalid-idx", N=300, H=128, I=64, E=12, k=4, dtype="bf16", seed=23)
+    T = W.generate(wl)
+    N, E, k, H, I = wl.N, wl.E, wl.k, wl.H, wl.I
+    rng = np.random.default_rng(5)
+    idx = rng.integers(-2, E + 2, size=(N, k)).astype(np.int32)
+    idx[::7, 1] = idx[::7, 0]                      # repeats inside a token
+    idx[::11] = rng.integers(0, E, size=(len(idx[::11]), 1))  # a token with one expert in every slot
+    idx[5] = np.arange(k)                          # a token with k valid distinct experts
+    idx[6] = -1                                    # a token with no valid slot
+    w = rng.random((N, k)).astype(np.float32)
+    ref = _plan_model(idx, w, E)
+    assert 0 < ref["offsets"][-1] < N * k
+    g = Guards()
+    D = upload(T, g)
+    didx = g.upload("topk_idx", idx)
+    dw = g.upload("topk_w", w)
+    plan = G.Plan(N, E, k, alloc=lambda name, n, dt: g.alloc("plan." + name, (n,), dt))
+    ws = g.alloc("ws_permute", (G.workspace_bytes(G.OP_PERMUTE, G.MOE_BF16, N, E, k),), torch.uint8)
+    # fill the plan's rows with a pattern, so rows past M that the call must not write are seen
+    for t in (plan.row_token, plan.row_pair, plan.tok_rows):
+        t.fill_(-7)
+    G.permute(didx, dw, E, plan=plan, ws=ws)
+    g.check("permute")
+    m = int(ref["offsets"][-1])
+    for n in ("counts", "offsets", "tok_ptr"):
+        np.testing.assert_array_equal(getattr(plan, n).cpu().numpy(), ref[n], err_msg=n)
+    for n in ("row_token", "row_w", "row_pair"):
+        got = getattr(plan, n).cpu().numpy()
+        np.testing.assert_array_equal(got[:m], ref[n], err_msg=n)
+    assert np.all(plan.row_token.cpu().numpy()[m:] == -7)
+    np.testing.assert_array_equal(plan.tok_rows.cpu().numpy(), ref["tok_rows"])
+    hc = g.alloc("hcache", (N * k, 2 * I), torch.bfloat16)
+    y = g.alloc("y", (N * k, H), torch.bfloat16)
+    wsf = g.alloc("ws_fwd", (G.workspace_bytes(G.OP_GEMM_FWD, G.MOE_BF16, N, E, k, H, I, N * k),), torch.uint8)
+    G.grouped_gemm_fwd(D["x"], D["wg"], D["wu"], D["wd"], plan, hcache=hc, y=y, ws=wsf)
+    out = g.alloc("out", (N, H), torch.bfloat16)
+    G.unpermute_combine(y, plan, out=out)
+    g.check("forward")
+    ds = g.alloc("ds", (N, k), torch.float32)
+    ds.fill_(123.0)
+    wsb = g.alloc("ws_bwd", (G.workspace_bytes(G.OP_LAYER_BWD, G.MOE_BF16, N, E, k, H, I, N * k),), torch.uint8)
+    bw = dict(dx=g.alloc("dx", (N, H), torch.bfloat16), dw_gate=g.alloc("dwg", (E, I, H), torch.bfloat16),
+              dw_up=g.alloc("dwu", (E, I, H), torch.bfloat16), dw_down=g.alloc("dwd", (E, H, I), torch.bfloat16))
+    G.layer_bwd(D["dout"], D["x"], D["wg"], D["wu"], D["wd"], plan, hc, ds=ds, ws=wsb, **bw)
+    g.check("layer_bwd")
+    import oracle
+    pt, pe, pw = oracle.pairs_from_plan(ref, E)
+    o = oracle.layer_fwd(T.x, T.wg, T.wu, T.wd, pt, pe, pw)
+    gr = oracle.layer_bwd(T.dout, T.x, T.wg, T.wu, T.wd, pt, pe, pw)
+    dsg = ds.cpu().numpy().reshape(-1)
+    errs = {"out": rel_err(out.float().cpu().numpy(), o), "dx": rel_err(bw["dx"].float().cpu().numpy(), gr["dx"]),
+            "dwg": rel_err(bw["dw_gate"].float().cpu().numpy(), gr["dwg"]),
+            "dwu": rel_err(bw["dw_up"].float().cpu().numpy(), gr["dwu"]),
+            "dwd": rel_err(bw["dw_down"].float().cpu().numpy(), gr["dwd"]),
+            "ds": rel_err(dsg[ref["row_pair"]], gr["ds"])}
+    log(f"[invalid idx] rows {m} of {N * k}: {errs}")
+    assert all(v <= 1e-2 for v in errs.values()), errs
+    # ds of a skipped pair is left unwritten
+    skipped = np.setdiff1d(np.arange(N * k), ref["row_pair"])
+    assert np.all(dsg[skipped] == 123.0)
 
 
 def _run_choice(choice, E, H=64, I=32, dtype="bf16", seed=3, k=None):
