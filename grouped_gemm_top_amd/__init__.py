@@ -11,7 +11,7 @@ import ctypes
 import os
 
 __all__ = [
-    "MoEError", "lib", "lib_path", "load_library", "Plan", "route_topk", "permute",
+    "MoEError", "lib", "lib_path", "load_library", "Plan", "route_topk", "permute", "permute_noalloc",
     "route_token_rounding",
     "route_capacity", "grouped_gemm_fwd", "unpermute_combine", "layer_bwd", "router_logits", "router_bwd",
     "workspace_bytes", "plan_rows_cap", "MOE_OK", "MOE_EINVAL", "MOE_EUNSUPPORTED", "MOE_EWORKSPACE",
@@ -28,6 +28,7 @@ OP_PERMUTE, OP_ROUTE_TR, OP_GEMM_FWD, OP_LAYER_BWD, OP_ROUTER_BWD, OP_ROUTER_LOG
 
 EXPORTED_SYMBOLS = (
     "moe_plan_rows_cap", "moe_workspace_bytes", "moe_last_error", "moe_route_topk", "moe_permute",
+    "moe_permute_noalloc",
     "moe_route_token_rounding", "moe_route_capacity", "moe_grouped_gemm_fwd", "moe_unpermute_combine",
     "moe_layer_bwd",
     "moe_router_logits", "moe_router_bwd", "moe_set_kernel_events",
@@ -89,6 +90,7 @@ def load_library(path: str):
     L.moe_last_error.restype = ctypes.c_char_p
     L.moe_route_topk.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp]
     L.moe_permute.argtypes = [vp, vp, i32, i32, i32, pp, vp, sz, vp]
+    L.moe_permute_noalloc.argtypes = [vp, vp, i32, i32, i32, pp, vp]
     L.moe_route_token_rounding.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, pp, vp, sz, vp]
     L.moe_route_capacity.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, pp, vp, sz, vp]
     L.moe_grouped_gemm_fwd.argtypes = [ctypes.c_int, vp, vp, vp, vp, i32, i32, pp, vp, vp, vp, sz, vp]
@@ -98,7 +100,7 @@ def load_library(path: str):
     L.moe_router_logits.argtypes = [ctypes.c_int, vp, vp, vp, i32, i32, i32, vp, vp, sz, vp]
     L.moe_router_bwd.argtypes = [ctypes.c_int, vp, vp, vp, pp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_set_kernel_events.argtypes = [i32, vp, vp]
-    for fn in ("moe_route_topk", "moe_permute", "moe_route_token_rounding",
+    for fn in ("moe_route_topk", "moe_permute", "moe_permute_noalloc", "moe_route_token_rounding",
                "moe_route_capacity",
                "moe_grouped_gemm_fwd",
                "moe_unpermute_combine", "moe_layer_bwd", "moe_router_logits", "moe_router_bwd",
@@ -222,6 +224,14 @@ def permute(topk_idx, topk_w, E: int, plan: Plan | None = None, ws=None, stream=
     nb = workspace_bytes(OP_PERMUTE, MOE_BF16, N, E, k)
     ws = _ws(nb, topk_idx.device, ws)
     _check(lib().moe_permute(_ptr(topk_idx), _ptr(topk_w), N, E, k, plan.c, _ptr(ws), nb, _stream(stream)))
+    return plan
+
+
+def permute_noalloc(topk_idx, topk_w, E: int, plan: Plan, stream=None) -> Plan:
+    """moe_permute_noalloc: the permute with the library's fixed scratch instead of a
+    workspace; `plan` (caller-allocated) is required, so this call allocates nothing."""
+    N, k = topk_idx.shape
+    _check(lib().moe_permute_noalloc(_ptr(topk_idx), _ptr(topk_w), N, E, k, plan.c, _stream(stream)))
     return plan
 
 

@@ -194,6 +194,28 @@ moe_status moe_permute(const int32_t* topk_idx, const float* topk_w, int32_t N, 
   return hip_status(e, "moe_permute");
 }
 
+moe_status moe_permute_noalloc(const int32_t* topk_idx, const float* topk_w, int32_t N, int32_t E, int32_t k,
+                               const moe_plan* plan, void* stream) {
+  g_err[0] = 0;
+  moe_status st = check_dims(N, E, k);
+  if (st != MOE_OK) return st;
+  if ((st = check_plan(plan)) != MOE_OK) return st;
+  REQUIRE(plan->kind == MOE_PLAN_TOPK, MOE_EINVAL, "moe_permute_noalloc needs a top-k plan");
+  REQUIRE(plan->N == N && plan->E == E && plan->k == k, MOE_EINVAL, "plan dimensions differ from the call");
+  REQUIRE(N == 0 || (topk_idx && topk_w), MOE_EINVAL, "NULL topk_idx/topk_w");
+  const size_t need = moe::permute_ws_bytes(N, E);
+  REQUIRE(need <= moe::permute_scratch_bytes(), MOE_EUNSUPPORTED,
+          "moe_permute_noalloc: N=%d, E=%d need %zu bytes of scratch, more than its fixed %zu", N, E, need,
+          moe::permute_scratch_bytes());
+  void* scratch = nullptr;
+  hipError_t e = moe::permute_scratch(&scratch);
+  if (e != hipSuccess) return hip_status(e, "moe_permute_noalloc: scratch address");
+  moe::kernel_event(MOE_K_PERMUTE, 0, (hipStream_t)stream);
+  e = moe::launch_permute(topk_idx, topk_w, N, E, k, *plan, scratch, (hipStream_t)stream);
+  moe::kernel_event(MOE_K_PERMUTE, 1, (hipStream_t)stream);
+  return hip_status(e, "moe_permute_noalloc");
+}
+
 moe_status moe_route_token_rounding(const float* logits, const float* bias, int32_t N, int32_t E, int32_t k,
                                     int32_t mtile, int32_t* topk_idx, float* topk_w, float* probs,
                                     const moe_plan* plan, void* ws, size_t ws_bytes, void* stream) {

@@ -68,6 +68,8 @@ namespace moe {
 hipError_t launch_route_topk(const float* logits, const float* bias, int N, int E, int k, int32_t* idx,
                              float* w, float* probs, float* tok_norm, hipStream_t s);
 size_t permute_ws_bytes(int N, int E);
+size_t permute_scratch_bytes();
+hipError_t permute_scratch(void** out);  // device address of the no-alloc permute's scratch
 hipError_t launch_permute(const int32_t* idx, const float* w, int N, int E, int k, const moe_plan& p,
                           void* ws, hipStream_t s);
 size_t tr_ws_bytes(int N, int E);

@@ -21,6 +21,8 @@
 // skipped by every kernel here, so the plan stays consistent: counts and offsets count the
 // rows made, token t's rows fill tok_rows[t k ..] in ascending row order and its remaining
 // slots hold -1.
+#include <mutex>
+
 #include "common.h"
 
 namespace moe {
@@ -178,6 +180,37 @@ __global__ __launch_bounds__(kPT) void k_perm_scatter(const int32_t* __restrict_
     for (int x = (e >> 5) + 1; x < EW; ++x) nrow += __popc(tx[x]);
     if (j >= nrow) tok_rows[(size_t)t * k + j] = -1;
   }
+}
+
+// Scratch of moe_permute_noalloc: a fixed device array, one copy per GPU for the life of the
+// process, holding what the workspace holds for moe_permute (the per-block histogram and the
+// block bases, permute_ws_bytes(N, E) bytes).  Nothing in it needs clearing: k_perm_hist writes
+// every histogram entry and k_perm_scan every block base.  Calls that overlap on one GPU share
+// it and race.
+constexpr size_t kPermuteScratchBytes = size_t(4) << 20;
+static __device__ __attribute__((aligned(256))) char scratch[kPermuteScratchBytes];
+
+size_t permute_scratch_bytes() { return kPermuteScratchBytes; }
+
+// The device address of `scratch` on the current device, looked up once per device (the
+// array's name in host code is a host-side stand-in, not a device address).
+hipError_t permute_scratch(void** out) {
+  static std::mutex mu;
+  static void* addr[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 size_t permute_ws_bytes(int N, int E) {

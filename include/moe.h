@@ -164,6 +164,22 @@ moe_status moe_permute(const int32_t* topk_idx, const float* topk_w, int32_t N, 
                        const moe_plan* plan, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Permute without a workspace, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation): the same plan as
+ * moe_permute, bit for bit, with the workspace replaced by a fixed 4 MiB scratch array that
+ * the library holds on each GPU it runs on until the process ends.  Requires
+ * moe_workspace_bytes(MOE_OP_PERMUTE, ...) <= 4 MiB (N*E up to about 2^25: N = 131008 tokens
+ * at E = 256, 32704 at E = 1024), else MOE_EUNSUPPORTED and nothing is queued.  It calls no
+ * allocating routine.
+ * The scratch needs no clearing (every entry a call reads was written earlier in that call),
+ * and all calls on one GPU share it: calls that overlap on one GPU (on different streams or
+ * threads without ordering) race, so serialise them.  Arguments, plan and errors otherwise as
+ * moe_permute.
+ */
+moe_status moe_permute_noalloc(const int32_t* topk_idx, const float* topk_w, int32_t N, int32_t E, int32_t k,
+                               const moe_plan* plan, void* stream);
+
+/*
  * Token-rounding route ([SM] "5 기여 ③ Token Rounding 라우팅"): ordinary top-k first (as
  * moe_route_topk, writing topk_idx, topk_w and probs, all required), then per expert the
  * row count c_e is rounded to r_e = mtile * floor((c_e + mtile/2) / mtile), clamped to the

@@ -103,6 +103,19 @@ def test_permute_errors(L):
     assert L.moe_permute(None, f, 64, 8, 2, ctypes.byref(p), f, need, None) == G.MOE_EINVAL
 
 
+def test_permute_noalloc_errors(L):
+    """The no-allocation permute validates like moe_permute and refuses shapes whose histogram
+    would not fit its fixed 4 MiB scratch, before anything is queued."""
+    f = ctypes.c_void_p(FAKE)
+    p = _plan()
+    assert L.moe_permute_noalloc(f, f, 64, 8, 2, None, None) == G.MOE_EINVAL
+    assert L.moe_permute_noalloc(None, f, 64, 8, 2, ctypes.byref(p), None) == G.MOE_EINVAL
+    assert L.moe_permute_noalloc(f, f, 64, 8, 2, ctypes.byref(_plan(kind=G.PLAN_TR, mtile=16)), None) == G.MOE_EINVAL
+    big = _plan(N=131072, E=256, k=8)
+    assert L.moe_permute_noalloc(f, f, 131072, 256, 8, ctypes.byref(big), None) == G.MOE_EUNSUPPORTED
+    assert "scratch" in _err(L)
+
+
 def test_token_rounding_errors(L):
     f = ctypes.c_void_p(FAKE)
     p = _plan(kind=G.PLAN_TR, mtile=16)
