@@ -93,21 +93,61 @@ def load_traffic(name, workload):
         return None
 
 
-def cpu_baseline(T, idx, w, n_tokens):
-    """The fp64 oracle as it stands, on the pairs of the first n_tokens tokens, fwd + bwd."""
+def host_facts():
+    """The host the CPU baseline ran on: CPU model, logical CPUs, CPUs this process may use."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count(), "cpus_available": len(os.sched_getaffinity(0))}
+
+
+def cpu_baseline(T, pt, pe, pw, what, single_tokens):
+    """The fp32 oracle as it stands (plain C loops, -O3, OpenMP over the host's threads), the
+    layer forward then backward (out, dx, dW_gate, dW_up, dW_down, dS) on the given pairs;
+    then the same on one thread for the pairs of the first `single_tokens` tokens."""
     import oracle
     wl = T.wl
-    pt, pe, pw = oracle.pairs_from_topk(idx[:n_tokens], w[:n_tokens])
+    thr = oracle.threads("f32")
     t0 = time.perf_counter()
-    oracle.layer_fwd(T.x, T.wg, T.wu, T.wd, pt, pe, pw)
-    oracle.layer_bwd(T.dout, T.x, T.wg, T.wu, T.wd, pt, pe, pw)
-    dt = time.perf_counter() - t0
+    oracle.layer_fwd(T.x, T.wg, T.wu, T.wd, pt, pe, pw, real="f32")
+    t1 = time.perf_counter()
+    oracle.layer_bwd(T.dout, T.x, T.wg, T.wu, T.wd, pt, pe, pw, real="f32")
+    t2 = time.perf_counter()
     flops = 18.0 * len(pt) * wl.H * wl.I
-    return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": oracle.threads(), "kind": "oracle",
-            "sample": f"fp64 oracle fwd+bwd (out, dx, dW_gate, dW_up, dW_down, dS) on the {len(pt)} "
-                      f"(token, expert) pairs of the first {n_tokens} of {wl.N} tokens; "
-                      f"{dt:.1f} s; scaled by algorithmic FLOPs (18*pairs*H*I)",
-            "seconds": dt}
+    keep = pt < single_tokens
+    oracle.set_threads(1, "f32")
+    try:
+        s0 = time.perf_counter()
+        oracle.layer_fwd(T.x, T.wg, T.wu, T.wd, pt[keep], pe[keep], pw[keep], real="f32")
+        oracle.layer_bwd(T.dout, T.x, T.wg, T.wu, T.wd, pt[keep], pe[keep], pw[keep], real="f32")
+        s1 = time.perf_counter()
+    finally:
+        oracle.set_threads(thr, "f32")
+    sflops = 18.0 * int(keep.sum()) * wl.H * wl.I
+    res = {"value": flops / (t2 - t0) / 1e12, "unit": "TFLOPS", "cores": thr, "kind": "oracle",
+           "sample": f"fp32 oracle forward + backward on {what} ({len(pt)} (token, expert) pairs); "
+                     f"{t2 - t0:.1f} s on {thr} threads; TFLOPS = 18*pairs*H*I / time",
+           "fwd_s": round(t1 - t0, 3), "bwd_s": round(t2 - t1, 3), "layer_ms": round((t2 - t0) * 1e3, 1),
+           "single_thread": {"pairs": int(keep.sum()), "tokens": single_tokens, "seconds": round(s1 - s0, 3),
+                             "tflops": sflops / (s1 - s0) / 1e12 if s1 > s0 else None}}
+    res.update(host_facts())
+    return res
+
+
+def padded_fractions(counts, M):
+    """MFMA rows computed beyond the real rows, as a fraction of M, for the kernels' own
+    granules: varlen-M tiles skip 16-row blocks that start past a group's rows (so a group of
+    c rows costs 16*ceil(c/16)); varlen-K tiles run k-steps of 32 rows (32*ceil(c/32))."""
+    c = np.asarray(counts, np.int64)
+    m = max(int(M), 1)
+    return {"varlen_m_16row_blocks": round(float((16 * ((c + 15) // 16)).sum()) / m - 1.0, 5),
+            "varlen_k_32row_steps": round(float((32 * ((c + 31) // 32)).sum()) / m - 1.0, 5),
+            "fixed_128row_tiles": round(float((128 * ((c + 127) // 128)).sum()) / m - 1.0, 5)}
 
 
 def main():
@@ -118,6 +158,8 @@ def main():
     ap.add_argument("--config", type=int, default=2, help="workload number (1-5); 2 is the headline")
     ap.add_argument("--cpu-tokens", type=int, default=4096,
                     help="tokens in the CPU-oracle baseline sample (0 disables it)")
+    ap.add_argument("--cpu-single-tokens", type=int, default=256,
+                    help="tokens of the single-thread CPU-oracle run")
     ap.add_argument("--kernel-events", type=int, default=1, help="record per-kernel HIP events (1/0)")
     ap.add_argument("--routing", choices=("workload", "capacity"), default="workload",
                     help="capacity: route with a capacity plan (each expert keeps at most "
@@ -244,6 +286,19 @@ def main():
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
 
+    # Per-step durations: the same number of steps again, a HIP event on the current stream
+    # between consecutive steps (one event per step; no per-kernel hook).
+    sev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    for e_ in sev:
+        e_.record()
+    torch.cuda.synchronize()
+    sev[0].record()
+    for i in range(args.steps):
+        step()
+        sev[i + 1].record()
+    torch.cuda.synchronize()
+    step_ms = [sev[i].elapsed_time(sev[i + 1]) for i in range(args.steps)]
+
     # Per-kernel durations: the same steps again, each kernel bracketed by HIP events on its
     # launch stream (the library's hook).
     rt = tr or cap  # routing through the rounding / capacity plan kernels
@@ -282,6 +337,9 @@ def main():
                    "routing": "capacity" if cap else wl.routing,
                    "rows": M, "active_experts": e_act, "parallelism": "single GPU"},
         "pct_peak": round(100.0 * tflops / peak, 2),
+        "layer_ms": {"mean": round(ms, 4), "median": round(float(np.median(step_ms)), 4),
+                     "min": round(float(np.min(step_ms)), 4), "max": round(float(np.max(step_ms)), 4),
+                     "note": "mean: the timed steps; median/min/max: per-step HIP events over as many more steps"},
     }
     if kern_ms:
         gemm_ms = sum(kern_ms[n] for n in GEMMS)
@@ -376,8 +434,7 @@ def main():
         res["measured_peaks"] = pk
         res["pct_of_measured_mfma_peak"] = round(100.0 * tflops / max(pk["mfma_bf16_16x16x32_tflops"],
                                                                       pk["mfma_bf16_32x32x16_tflops"]), 2)
-    pad = float(sum(((c + 127) // 128) * 128 for c in counts)) / max(M, 1) - 1.0
-    res["padded_row_fraction_tile128"] = round(pad, 4)
+    res["padded_row_fraction"] = padded_fractions(counts, M)
     if cap:
         res["config"].update({"capacity_factor": args.capacity_factor, "capacity": C,
                               "cap_policy": "probs" if args.cap_policy else "position"})
@@ -385,24 +442,15 @@ def main():
                            "dense_layout_rows": E * C, "dense_padding_rows": E * C - M,
                            "dense_padding_fraction": round((E * C - M) / max(E * C, 1), 4)}
 
-    if args.cpu_tokens > 0 and not tr and not cap:
-        print(f"# cpu baseline on {args.cpu_tokens} tokens", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(T, idx.cpu().numpy(), wts.cpu().numpy(),
-                                           min(args.cpu_tokens, N))
-    elif args.cpu_tokens > 0:
-        print("# cpu baseline on the routing plan", file=sys.stderr, flush=True)
+    if args.cpu_tokens > 0:
         import oracle
-        hp = plan.host()
-        pt, pe, pw = oracle.pairs_from_plan(hp, E)
-        keep = pt < args.cpu_tokens
-        t0 = time.perf_counter()
-        oracle.layer_fwd(T.x, T.wg, T.wu, T.wd, pt[keep], pe[keep], pw[keep])
-        oracle.layer_bwd(T.dout, T.x, T.wg, T.wu, T.wd, pt[keep], pe[keep], pw[keep])
-        dtc = time.perf_counter() - t0
-        res["cpu_baseline"] = {"value": 18.0 * int(keep.sum()) * H * I / dtc / 1e12, "unit": "TFLOPS",
-                               "cores": oracle.threads(), "kind": "oracle",
-                               "sample": f"fp64 oracle fwd+bwd on the {int(keep.sum())} rows of the first "
-                                         f"{args.cpu_tokens} tokens; {dtc:.1f} s"}
+        nt = min(args.cpu_tokens, N)
+        print(f"# cpu baseline (fp32 oracle) on the rows of {nt} tokens", file=sys.stderr, flush=True)
+        pt, pe, pw = oracle.pairs_from_plan(plan.host(), E)
+        keep = pt < nt
+        what = (f"the whole workload" if nt == N else f"the rows of the first {nt} of {N} tokens") + \
+            (" (the GPU's routing plan)" if (tr or cap) else "")
+        res["cpu_baseline"] = cpu_baseline(T, pt[keep], pe[keep], pw[keep], what, min(args.cpu_single_tokens, nt))
     print(json.dumps(res), flush=True)
 
 
