@@ -77,6 +77,24 @@ __global__ __launch_bounds__(256) void k_read16(const uint4* __restrict__ src, s
   sink[(size_t)blockIdx.x * 256 + threadIdx.x] = x;
 }
 
+// One scaled fp8 MFMA per wavefront (case c = blockIdx.x): lane L passes its 32 bytes of A
+// and of B, its scale dwords (byte 0 selected) and a zero accumulator, and writes the four
+// floats it receives.  Formats: e4m3 for both operands.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+__global__ __launch_bounds__(64) void k_mfma_fp8_layout(const i32x8* __restrict__ a, const i32x8* __restrict__ b,
+                                                        const int* __restrict__ sa, const int* __restrict__ sb,
+                                                        f32x4* __restrict__ d) {
+  const int i = blockIdx.x * 64 + threadIdx.x;
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  d[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], b[i], z, 0, 0, 0, sa[i], 0, sb[i]);
+}
+
+// fp32 -> fp8 e4m3 with the conversion instruction the fp8 kernels use, two values per call
+__global__ __launch_bounds__(256) void k_cvt_fp8(const float* __restrict__ src, int n2, uint16_t* __restrict__ dst) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n2) dst[i] = (uint16_t)__builtin_amdgcn_cvt_pk_fp8_f32(src[2 * i], src[2 * i + 1], 0, false);
+}
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 }  // namespace
@@ -107,5 +125,21 @@ extern "C" int moe_probe_read(const void* src, size_t bytes, int blocks, uint32_
   if (bytes == 0) return 0;
   hipLaunchKernelGGL(k_read16, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const uint4*)src, bytes / 16,
                      sink);
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+extern "C" int moe_probe_mfma_fp8_layout(const uint8_t* a, const uint8_t* b, const uint32_t* sa, const uint32_t* sb,
+                                         int cases, float* d, void* stream) {
+  if (!a || !b || !sa || !sb || !d || cases < 1 || cases > 4096 || !aligned16(a) || !aligned16(b) || !aligned16(d))
+    return 1;
+  hipLaunchKernelGGL(k_mfma_fp8_layout, dim3(cases), dim3(64), 0, (hipStream_t)stream, (const i32x8*)a,
+                     (const i32x8*)b, (const int*)sa, (const int*)sb, (f32x4*)d);
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+extern "C" int moe_probe_cvt_fp8(const float* src, int n, uint8_t* dst, void* stream) {
+  if (!src || !dst || n < 2 || n % 2 != 0 || ((uintptr_t)dst & 1u)) return 1;
+  const int n2 = n / 2;
+  hipLaunchKernelGGL(k_cvt_fp8, dim3((n2 + 255) / 256), dim3(256), 0, (hipStream_t)stream, src, n2, (uint16_t*)dst);
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }

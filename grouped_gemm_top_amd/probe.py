@@ -9,7 +9,8 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 
-PROBE_SYMBOLS = ("moe_probe_mfma_bf16", "moe_probe_copy", "moe_probe_read")
+PROBE_SYMBOLS = ("moe_probe_mfma_bf16", "moe_probe_copy", "moe_probe_read", "moe_probe_mfma_fp8_layout",
+                 "moe_probe_cvt_fp8")
 FLOP_PER_ITER_WAVE = 131072  # eight 16x16x32 (or four 32x32x16) bf16 MFMAs
 
 
@@ -29,6 +30,8 @@ def lib():
         L.moe_probe_mfma_bf16.argtypes = [i32, i32, i32, vp, vp]
         L.moe_probe_copy.argtypes = [vp, vp, sz, i32, vp]
         L.moe_probe_read.argtypes = [vp, sz, i32, vp, vp]
+        L.moe_probe_mfma_fp8_layout.argtypes = [vp, vp, vp, vp, i32, vp, vp]
+        L.moe_probe_cvt_fp8.argtypes = [vp, i32, vp, vp]
         for n in PROBE_SYMBOLS:
             getattr(L, n).restype = i32
         _LIB = L
@@ -107,3 +110,22 @@ def measure_peaks(reps: int = 5) -> dict:
     out["read_gbs"] = round(best(lambda: read(src, sblocks, isink)) / 1e9, 1)
     del src, dst
     return out
+
+
+def mfma_fp8_layout(a, b, sa, sb, d, stream=None):
+    """Queue the scaled-fp8 MFMA lane-layout probe.  a, b: uint8 cuda [cases, 64, 32]; sa, sb:
+    int32 cuda [cases, 64]; d: float32 cuda [cases, 64, 4] (written)."""
+    cases = a.shape[0]
+    assert a.shape == (cases, 64, 32) and b.shape == a.shape and sa.shape == (cases, 64) and sb.shape == sa.shape
+    assert d.shape == (cases, 64, 4)
+    p = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    _check(lib().moe_probe_mfma_fp8_layout(p(a), p(b), p(sa), p(sb), cases, p(d), _stream(stream)),
+           "moe_probe_mfma_fp8_layout")
+
+
+def cvt_fp8(src, dst, stream=None):
+    """Queue the fp32 -> fp8 e4m3 conversion probe: dst (uint8 cuda) = codes of src (float32
+    cuda, even length)."""
+    assert src.numel() == dst.numel() and src.numel() % 2 == 0
+    _check(lib().moe_probe_cvt_fp8(ctypes.c_void_p(src.data_ptr()), src.numel(), ctypes.c_void_p(dst.data_ptr()),
+                                   _stream(stream)), "moe_probe_cvt_fp8")

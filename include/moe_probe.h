@@ -37,6 +37,19 @@ int moe_probe_copy(const void* src, void* dst, size_t bytes, int blocks, void* s
  * each thread's words to sink[blocks * 256] (uint32).  Same constraints as moe_probe_copy. */
 int moe_probe_read(const void* src, size_t bytes, int blocks, uint32_t* sink, void* stream);
 
+/* Lane-layout probe of the scaled fp8 matrix instruction (v_mfma_scale_f32_16x16x128_f8f6f4,
+ * e4m3 operands): one wavefront per case runs one instruction with a zero accumulator.
+ * For case c and lane L: a, b hold 32 bytes each at [(c*64 + L)*32] (the lane's operand
+ * registers), sa, sb one dword each at [c*64 + L] (the lane's scale registers, byte 0
+ * selected), and d receives the lane's four result floats at [(c*64 + L)*4].  1 <= cases <=
+ * 4096; a, b, d 16-byte aligned. */
+int moe_probe_mfma_fp8_layout(const uint8_t* a, const uint8_t* b, const uint32_t* sa, const uint32_t* sb,
+                              int cases, float* d, void* stream);
+
+/* fp32 -> fp8 e4m3 with the conversion instruction the fp8 kernels use (v_cvt_pk_fp8_f32):
+ * dst[i] = code of src[i], i < n; n even, dst 2-byte aligned. */
+int moe_probe_cvt_fp8(const float* src, int n, uint8_t* dst, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,7 +1,8 @@
 """The measurement probes of libmoe_probe.so on the GPU: the copy probe copies exactly, the
 read probe reads every word once (the XOR of its per-thread results equals the XOR of the
 buffer), and the MFMA probe's results are linear in its iteration count and equal to the
-closed form of its constant operands."""
+closed form of its constant operands.  Two probes pin behaviour the fp8 kernels rely on: the
+lane layout of the scaled fp8 matrix instruction and the rounding of the fp8 conversion."""
 import numpy as np
 import pytest
 
@@ -81,3 +82,74 @@ def test_mfma_probe_values(shape):
     assert np.array_equal(b, 7 * a)                 # linear in the iteration count
     want = _mfma_expected(shape, 1)
     assert np.array_equal(a, np.tile(want, blocks))  # the MFMA's closed form on these operands
+
+
+def _e4m3(code):
+    """Value of an OCP e4m3 code (sign, 4 exponent bits with bias 7, 3 mantissa bits; exponent
+    field 0 is subnormal; 0x7F / 0xFF are NaN)."""
+    code = np.asarray(code, np.int64)
+    e, m = (code >> 3) & 0xF, code & 7
+    v = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1 + m / 8.0) * 2.0 ** (e - 7))
+    v = np.where((code & 0x7F) == 0x7F, np.nan, v)
+    return np.where(code & 0x80, -v, v)
+
+
+def test_fp8_scaled_mfma_lane_layout():
+    """The scaled fp8 matrix instruction the fp8 grouped GEMMs use
+    (v_mfma_scale_f32_16x16x128_f8f6f4, e4m3 operands), checked on random exact-valued cases:
+    lane L holds, for row L % 16 of its operand, k = 16 (L / 16) + j in byte j < 16 and
+    k = 64 + 16 (L / 16) + (j - 16) in bytes 16..31; the block scale of (row L % 16, k block
+    L / 16 of 32) is byte 0 of lane L's scale register (2^(byte - 127)); the result row
+    4 (L / 16) + v (of the first operand) and column L % 16 (of the second) is float v of
+    lane L.  The kernels' LDS fragment reads and scale placement rely on exactly this."""
+    import torch
+    from grouped_gemm_top_amd import probe
+    rng = np.random.default_rng(11)
+    C = 16
+    codes = np.array([0x00, 0x30, 0x38, 0x3C, 0x40, 0x44, 0x48, 0x4C, 0xB0, 0xB8, 0xBC, 0xC0, 0xC8], np.uint8)
+    a = codes[rng.integers(0, len(codes), (C, 64, 32))]
+    b = codes[rng.integers(0, len(codes), (C, 64, 32))]
+    sa = rng.integers(122, 133, (C, 64)).astype(np.int64) | (rng.integers(0, 1 << 24, (C, 64)) << 8)
+    sb = rng.integers(122, 133, (C, 64)).astype(np.int64) | (rng.integers(0, 1 << 24, (C, 64)) << 8)
+    sa, sb = sa.astype(np.uint32).view(np.int32), sb.astype(np.uint32).view(np.int32)
+    d = torch.zeros((C, 64, 4), dtype=torch.float32, device="cuda")
+    probe.mfma_fp8_layout(torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda(), torch.from_numpy(sa).cuda(),
+                          torch.from_numpy(sb).cuda(), d)
+    torch.cuda.synchronize()
+    got = d.cpu().numpy()
+    L = np.arange(64)[:, None]
+    j = np.arange(32)[None, :]
+    k = np.where(j < 16, 16 * (L // 16) + j, 64 + 16 * (L // 16) + (j - 16))
+    for c in range(C):
+        A = np.zeros((16, 128))
+        B = np.zeros((16, 128))
+        A[np.broadcast_to(L % 16, k.shape), k] = _e4m3(a[c])
+        B[np.broadcast_to(L % 16, k.shape), k] = _e4m3(b[c])
+        SA = np.zeros((16, 4))
+        SB = np.zeros((16, 4))
+        SA[np.arange(64) % 16, np.arange(64) // 16] = 2.0 ** ((sa[c].view(np.uint32) & 0xFF).astype(np.float64) - 127)
+        SB[np.arange(64) % 16, np.arange(64) // 16] = 2.0 ** ((sb[c].view(np.uint32) & 0xFF).astype(np.float64) - 127)
+        D = (A * np.repeat(SA, 32, axis=1)) @ (B * np.repeat(SB, 32, axis=1)).T
+        want = np.array([[D[4 * (l // 16) + v, l % 16] for v in range(4)] for l in range(64)])
+        np.testing.assert_array_equal(got[c], want, err_msg=f"case {c}")
+
+
+def test_fp8_conversion_matches_rne():
+    """v_cvt_pk_fp8_f32, the conversion the fp8 kernels quantize with, rounds fp32 to e4m3 to
+    nearest, ties to even, like torch's float8_e4m3fn cast: every code, every midpoint and
+    its two neighbours, subnormals, signed zeros and random values in [-448, 448]."""
+    import torch
+    from grouped_gemm_top_amd import probe
+    rng = np.random.default_rng(12)
+    grid = _e4m3(np.arange(0, 0x7F))
+    mids = (grid[:-1] + grid[1:]) / 2
+    xs = np.concatenate([grid, mids, np.nextafter(mids.astype(np.float32), np.float32(0)),
+                         np.nextafter(mids.astype(np.float32), np.float32(1000)), rng.uniform(-448, 448, 30000),
+                         rng.uniform(-0.02, 0.02, 30000), [0.0, 2.0 ** -10, 2.0 ** -11, 448.0]])
+    xs = np.concatenate([xs, -xs]).astype(np.float32)
+    src = torch.from_numpy(xs).cuda()
+    dst = torch.zeros(len(xs), dtype=torch.uint8, device="cuda")
+    probe.cvt_fp8(src, dst)
+    torch.cuda.synchronize()
+    ref = torch.from_numpy(xs).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(dst.cpu().numpy(), ref)
