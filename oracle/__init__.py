@@ -8,12 +8,15 @@ from .oracle import (  # noqa: F401
     capacity_plan,
     layer_bwd,
     layer_fwd,
+    layer_fwd_mxfp8,
     lib_path,
+    mx_scale_cols,
     pairs_from_plan,
     pairs_from_topk,
     router_bwd,
     router_logits,
     permute,
+    quantize_mxfp8,
     route_topk,
     set_threads,
     threads,

@@ -691,3 +691,175 @@ ORACLE_EXPORT int oracle_router_bwd(const float* logits, const float* bias, int 
   }
   return 0;
 }
+
+/* ------------------------------------------------------------------------------------
+ * MX-FP8: the fine-grained FP8 grouped GEMM of [GG] "한계" (DeepSeek-V3's FP8 grouped GEMM:
+ * FP8 operands with scales for small blocks along the contraction dimension).  The pages name
+ * it but give no format; the reading here is the OCP microscaling (MX) FP8 layout:
+ *   element : e4m3 -- sign bit, 4 exponent bits with bias 7, 3 mantissa bits; exponent field
+ *             0 holds the subnormals (m/8) 2^-6; largest finite value 448; codes 0x7F and
+ *             0xFF are NaN (never produced here)
+ *   block   : 32 consecutive values along the contraction dimension (K) share one scale
+ *             X = 2^(c - 127), c an unsigned byte code
+ * Quantization rule (the pages give none): X is the smallest power of two with
+ * max |v| <= 448 X over the block (no value clips), its code limited to 0..254; each value is
+ * stored as v / X rounded to the nearest e4m3 value, ties to the even code.
+ * Layout of a quantized [rows, K] matrix: codes q [rows, K] (row-major, one byte each) and
+ * scale codes s [rows, KS] with KS = 4 ceil(K / 128): s[r, b] scales q[r, 32b .. 32b+31];
+ * entries b >= K / 32 are 0.  K must be a multiple of 32.
+ * ---------------------------------------------------------------------------------- */
+static double e4m3_value(uint8_t c) {
+  const int e = (c >> 3) & 0xF, m = c & 7;
+  const double v = e == 0 ? ldexp((double)m, -9) : ldexp(8.0 + m, e - 10);
+  return (c & 0x80) ? -v : v;
+}
+
+/* t rounded to the nearest e4m3 value, ties to the even code; requires |t| <= 448 */
+static uint8_t e4m3_round(double t) {
+  const uint8_t sign = signbit(t) ? 0x80 : 0;
+  const double a = fabs(t);
+  if (a < ldexp(1.0, -6)) {                 /* subnormal spacing 2^-9 (n = 8 is 2^-6, code 8) */
+    const double n = nearbyint(a * 512.0);  /* exact scaling; nearbyint rounds ties to even */
+    return sign | (uint8_t)n;
+  }
+  int ex;
+  frexp(a, &ex);                            /* a in [2^(ex-1), 2^ex) */
+  int e = ex - 1;
+  double n = nearbyint(ldexp(a, 3 - e));    /* mantissa steps of 2^(e-3): n in [8, 16] */
+  if (n == 16.0) { e += 1; n = 8.0; }
+  return sign | (uint8_t)(((e + 7) << 3) | ((int)n - 8));
+}
+
+/* scale exponent of a block: the smallest s in [-127, 127] with amax <= 448 * 2^s */
+static int mx_scale_exp(double amax) {
+  if (amax == 0.0) return -127;
+  int ex;
+  const double f = frexp(amax, &ex);        /* amax = f 2^ex, f in [0.5, 1); 448 = 0.875 2^9 */
+  int s = f <= 0.875 ? ex - 9 : ex - 8;
+  if (s < -127) s = -127;
+  if (s > 127) s = 127;
+  return s;
+}
+
+static int mx_ks(int K) { return 4 * ((K + 127) / 128); }
+
+/* quantize one row of K values (K multiple of 32) into codes q[K] and scale codes s[KS] */
+static void mx_quantize_row(const float* v, int K, uint8_t* q, uint8_t* s) {
+  const int KS = mx_ks(K);
+  for (int b = 0; b < KS; ++b) s[b] = 0;
+  for (int b = 0; b < K / 32; ++b) {
+    double amax = 0;
+    for (int j = 0; j < 32; ++j) amax = fmax(amax, fabs((double)v[32 * b + j]));
+    const int se = mx_scale_exp(amax);
+    s[b] = (uint8_t)(se + 127);
+    for (int j = 0; j < 32; ++j) q[32 * b + j] = e4m3_round(ldexp((double)v[32 * b + j], -se));
+  }
+}
+
+/* the values of the 256 element codes and of the 256 scale codes, from the definitions above
+ * (filled once, before any parallel region) */
+static double mx_elem_tab[256], mx_scale_tab[256];
+static int mx_tab_ready = 0;
+static void mx_tables(void) {
+  if (mx_tab_ready) return;
+  for (int c = 0; c < 256; ++c) {
+    mx_elem_tab[c] = e4m3_value((uint8_t)c);
+    mx_scale_tab[c] = ldexp(1.0, c - 127);
+  }
+  mx_tab_ready = 1;
+}
+
+/* value of element k of row r of a quantized matrix (mx_tables() called first) */
+static double mx_value(const uint8_t* q, const uint8_t* s, int K, long r, int k) {
+  return mx_elem_tab[q[(size_t)r * K + k]] * mx_scale_tab[s[(size_t)r * mx_ks(K) + k / 32]];
+}
+
+/* Quantize src [rows, K] (fp32 values) into q [rows, K] and s [rows, KS]. */
+ORACLE_EXPORT int oracle_quantize_mxfp8(const float* src, long rows, int K, uint8_t* q, uint8_t* s) {
+  if (rows < 0 || K < 32 || K % 32 != 0 || (rows > 0 && (!src || !q || !s))) return -1;
+  const int KS = mx_ks(K);
+#pragma omp parallel for schedule(static)
+  for (long r = 0; r < rows; ++r) mx_quantize_row(src + (size_t)r * K, K, q + (size_t)r * K, s + (size_t)r * KS);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------------------
+ * Layer forward with MX-FP8 operands.  x (q, s) [N, H]; W_gate, W_up (q, s) [E*I, H]
+ * (expert e's row i is row e*I + i); W_down (q, s) [E*H, I].  For every pair (t, e, w):
+ *   g_i = sum_h W_gate[e,i,h] x[t,h],  u_i = sum_h W_up[e,i,h] x[t,h]   (dequantized values)
+ *   a_i = silu(g_i) u_i, rounded to fp32, then quantized as one row of I values (MX-FP8)
+ *   y_h = sum_i W_down[e,h,i] a~_i   (a~: the dequantized quantized a)
+ *   out[t] += w y
+ * The quantization of a is a decision taken in fp32 (the precision the layer's kernels hold
+ * a in).  Optional per-pair outputs (NULL to skip): gu [P, 2I] = [g | u] in double, and the
+ * quantized a: aq [P, I] codes and as [P, KS(I)] scale codes.  H and I multiples of 32.
+ * ---------------------------------------------------------------------------------- */
+ORACLE_EXPORT int oracle_layer_fwd_mxfp8(const uint8_t* xq, const uint8_t* xs, const uint8_t* gq, const uint8_t* gs,
+                                         const uint8_t* uq, const uint8_t* us, const uint8_t* dq, const uint8_t* dsc,
+                                         int N, int H, int I, int E, int P, const int32_t* pair_t,
+                                         const int32_t* pair_e, const float* pair_w, double* out, double* gu,
+                                         uint8_t* aq, uint8_t* as) {
+  if (N < 0 || H < 32 || I < 32 || H % 32 || I % 32 || E < 1 || P < 0 || !out) return -1;
+  if (N > 0 && (!xq || !xs)) return -1;
+  if (!gq || !gs || !uq || !us || !dq || !dsc) return -1;
+  if (P > 0 && (!pair_t || !pair_e || !pair_w)) return -1;
+  if (check_pairs(N, E, P, pair_t, pair_e)) return -1;
+  memset(out, 0, sizeof(double) * (size_t)N * H);
+  mx_tables();
+  int32_t *tptr, *tlist;
+  if (group_pairs(P, pair_t, N, &tptr, &tlist)) return -2;
+  const int KSI = mx_ks(I);
+  int fail = 0;
+#pragma omp parallel
+  {
+    real* xv = (real*)malloc(sizeof(real) * (size_t)H);
+    real* g = (real*)malloc(sizeof(real) * (size_t)I);
+    real* u = (real*)malloc(sizeof(real) * (size_t)I);
+    float* a32 = (float*)malloc(sizeof(float) * (size_t)I);
+    uint8_t* aqr = (uint8_t*)malloc((size_t)I);
+    uint8_t* asr = (uint8_t*)malloc((size_t)KSI);
+    if (!xv || !g || !u || !a32 || !aqr || !asr) {
+#pragma omp atomic write
+      fail = 1;
+    } else {
+#pragma omp for schedule(dynamic, 4)
+      for (int t = 0; t < N; ++t) {
+        if (tptr[t] == tptr[t + 1]) continue;
+        for (int h = 0; h < H; ++h) xv[h] = (real)mx_value(xq, xs, H, t, h);
+        for (int q = tptr[t]; q < tptr[t + 1]; ++q) {
+          const int p = tlist[q], e = pair_e[p];
+          for (int i = 0; i < I; ++i) {
+            const long row = (long)e * I + i;
+            real sg = 0, su = 0;
+            for (int h = 0; h < H; ++h) {
+              sg += (real)mx_value(gq, gs, H, row, h) * xv[h];
+              su += (real)mx_value(uq, us, H, row, h) * xv[h];
+            }
+            g[i] = sg;
+            u[i] = su;
+            a32[i] = (float)(sg * sigmoid_r(sg) * su);
+          }
+          mx_quantize_row(a32, I, aqr, asr);
+          for (int h = 0; h < H; ++h) {
+            const long row = (long)e * H + h;
+            real y = 0;
+            for (int i = 0; i < I; ++i)
+              y += (real)mx_value(dq, dsc, I, row, i) * (real)(mx_elem_tab[aqr[i]] * mx_scale_tab[asr[i / 32]]);
+            out[(size_t)t * H + h] += (double)((real)pair_w[p] * y);
+          }
+          if (gu)
+            for (int i = 0; i < I; ++i) {
+              gu[(size_t)p * 2 * I + i] = (double)g[i];
+              gu[(size_t)p * 2 * I + I + i] = (double)u[i];
+            }
+          if (aq) memcpy(aq + (size_t)p * I, aqr, (size_t)I);
+          if (as) memcpy(as + (size_t)p * KSI, asr, (size_t)KSI);
+        }
+      }
+    }
+    free(xv); free(g); free(u); free(a32); free(aqr); free(asr);
+  }
+  free(tptr); free(tlist);
+  return fail ? -2 : 0;
+}
+

@@ -74,7 +74,12 @@ def _lib(real: str = "f64"):
                                       ctypes.c_int, _i32p, _i32p, _f32p, _f32p, _f32p, ctypes.c_int,
                                       _f64p, _f64p, _f64p, _f64p]
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
-    for fn in ("oracle_set_threads", "oracle_route_topk", "oracle_permute", "oracle_token_round", "oracle_layer_fwd",
+    _u8p = ctypes.POINTER(ctypes.c_uint8)
+    lib.oracle_quantize_mxfp8.argtypes = [_f32p, ctypes.c_long, ctypes.c_int, _u8p, _u8p]
+    lib.oracle_layer_fwd_mxfp8.argtypes = [_u8p, _u8p, _u8p, _u8p, _u8p, _u8p, _u8p, _u8p, ctypes.c_int,
+                                           ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p, _i32p,
+                                           _f32p, _f64p, _f64p, _u8p, _u8p]
+    for fn in ("oracle_quantize_mxfp8", "oracle_layer_fwd_mxfp8", "oracle_set_threads", "oracle_route_topk", "oracle_permute", "oracle_token_round", "oracle_layer_fwd",
                "oracle_layer_bwd", "oracle_router_logits", "oracle_router_bwd", "oracle_capacity_plan",
                "oracle_real_bytes",
                "oracle_threads"):
@@ -281,3 +286,49 @@ def router_bwd(logits, bias, idx, pair_t, pair_e, pair_ds, x=None, wr=None,
                                         *[_p(res[n], _f64p) for n in ("dz", "dwr", "dx", "dbias")]),
            "oracle_router_bwd")
     return {n: v for n, v in res.items() if v is not None}
+
+
+_u8p = ctypes.POINTER(ctypes.c_uint8)
+
+
+def mx_scale_cols(K: int) -> int:
+    """Scale bytes per row of an MX-FP8 matrix with K columns: 4 * ceil(K / 128)."""
+    return 4 * ((K + 127) // 128)
+
+
+def quantize_mxfp8(src):
+    """MX-FP8 quantization of src [..., K] (values as float32, K a multiple of 32) along its
+    last dimension: returns (codes uint8 [..., K], scale codes uint8 [..., 4 ceil(K/128)])."""
+    src = _f32(src)
+    K = src.shape[-1]
+    rows = int(np.prod(src.shape[:-1])) if src.ndim > 1 else 1
+    q = np.empty(src.shape, np.uint8)
+    s = np.empty(src.shape[:-1] + (mx_scale_cols(K),), np.uint8)
+    _check(_lib().oracle_quantize_mxfp8(_p(src, _f32p), rows, K, _p(q, _u8p), _p(s, _u8p)), "oracle_quantize_mxfp8")
+    return q, s
+
+
+def layer_fwd_mxfp8(x, wg, wu, wd, pair_t, pair_e, pair_w, want_stages=False, real="f64"):
+    """Layer forward on MX-FP8 operands: x, wg, wu, wd are (codes, scale codes) pairs as from
+    quantize_mxfp8 of x [N,H], W_gate / W_up [E,I,H] and W_down [E,H,I].  Returns out [N,H]
+    (float64) and, with want_stages, a dict with gu [P,2I] (float64), aq [P,I] and as [P,KS(I)]
+    (the quantized activation of every pair)."""
+    (xq, xs), (gq, gs), (uq, us), (dq, ds) = x, wg, wu, wd
+    N, H = xq.shape
+    E, I, _ = gq.shape
+    pair_t, pair_e, pair_w = _i32(pair_t), _i32(pair_e), _f32(pair_w)
+    P = len(pair_t)
+    c = lambda a: np.ascontiguousarray(a, np.uint8)  # noqa: E731
+    xq, xs, gq, gs, uq, us, dq, ds = map(c, (xq, xs, gq, gs, uq, us, dq, ds))
+    out = np.empty((N, H), np.float64)
+    st = None
+    if want_stages:
+        st = {"gu": np.empty((P, 2 * I), np.float64), "aq": np.empty((P, I), np.uint8),
+              "as": np.empty((P, mx_scale_cols(I)), np.uint8)}
+    _check(_lib(real).oracle_layer_fwd_mxfp8(
+        _p(xq, _u8p), _p(xs, _u8p), _p(gq, _u8p), _p(gs, _u8p), _p(uq, _u8p), _p(us, _u8p), _p(dq, _u8p),
+        _p(ds, _u8p), N, H, I, E, P, _p(pair_t, _i32p), _p(pair_e, _i32p), _p(pair_w, _f32p), _p(out, _f64p),
+        None if st is None else _p(st["gu"], _f64p), None if st is None else _p(st["aq"], _u8p),
+        None if st is None else _p(st["as"], _u8p)), "oracle_layer_fwd_mxfp8")
+    return (out, st) if want_stages else out
+

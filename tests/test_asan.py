@@ -1,7 +1,7 @@
 """Host-code sanitizer runs, on the CPU (no GPU is touched):
 
 * the C oracle built with gcc -fsanitize=address,undefined, running the oracle's pins
-  (tests/test_oracle.py) on that build;
+  (tests/test_oracle.py, tests/test_oracle_fp8.py) on that build;
 * libmoe.so with AddressSanitizer on its host pass only (argument validation, workspace and
   plan sizing, launch sequencing up to the first HIP call), running the C-ABI checks
   (tests/test_abi.py) on that build.
@@ -18,16 +18,17 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 pytestmark = pytest.mark.slow
 
 
-def _child(env_extra, test_file, extra_args=()):
+def _child(env_extra, test_files, extra_args=()):
     env = dict(os.environ)
     env.update(env_extra)
     env["ASAN_OPTIONS"] = "detect_leaks=0:halt_on_error=1:abort_on_error=0:exitcode=86"
     env["UBSAN_OPTIONS"] = "halt_on_error=1:print_stacktrace=1:exitcode=87"
+    test_files = [test_files] if isinstance(test_files, str) else list(test_files)
     cmd = [sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider", "-m", "not gpu and not slow",
-           os.path.join(ROOT, "tests", test_file), *extra_args]
+           *[os.path.join(ROOT, "tests", f) for f in test_files], *extra_args]
     r = subprocess.run(cmd, cwd=ROOT, env=env, capture_output=True, text=True, timeout=900)
     tail = (r.stdout + r.stderr)[-4000:]
-    assert r.returncode == 0, f"sanitized run of {test_file} failed (rc {r.returncode}):\n{tail}"
+    assert r.returncode == 0, f"sanitized run of {test_files} failed (rc {r.returncode}):\n{tail}"
     assert "ERROR: AddressSanitizer" not in r.stderr and "runtime error:" not in r.stderr, tail
     return r
 
@@ -47,7 +48,7 @@ def test_oracle_pins_under_asan_ubsan(tmp_path):
                         "-fno-sanitize-recover=undefined", "-fopenmp", "-fPIC", "-shared",
                         f"-DORACLE_REAL={ctype}", "-fvisibility=hidden", src, "-o", str(out), "-lm"], check=True)
     preload = _gcc_runtime("libasan.so") + ":" + _gcc_runtime("libubsan.so")
-    r = _child({"ORACLE_LIB_DIR": str(tmp_path), "LD_PRELOAD": preload}, "test_oracle.py")
+    r = _child({"ORACLE_LIB_DIR": str(tmp_path), "LD_PRELOAD": preload}, ["test_oracle.py", "test_oracle_fp8.py"])
     assert " passed" in r.stdout
 
 
