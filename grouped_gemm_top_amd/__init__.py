@@ -12,7 +12,7 @@ import os
 
 __all__ = [
     "MoEError", "lib", "lib_path", "load_library", "Plan", "route_topk", "permute", "permute_noalloc",
-    "route_token_rounding",
+    "route_token_rounding", "quantize_mxfp8", "grouped_gemm_fwd_mxfp8", "mx_scale_cols", "OP_GEMM_FWD_MXFP8",
     "route_capacity", "grouped_gemm_fwd", "unpermute_combine", "layer_bwd", "router_logits", "router_bwd",
     "workspace_bytes", "plan_rows_cap", "MOE_OK", "MOE_EINVAL", "MOE_EUNSUPPORTED", "MOE_EWORKSPACE",
     "MOE_EHIP", "OP_PERMUTE", "OP_ROUTE_TR", "OP_GEMM_FWD", "OP_LAYER_BWD", "OP_ROUTER_BWD",
@@ -25,19 +25,21 @@ MOE_F32, MOE_BF16 = 0, 1
 PLAN_TOPK, PLAN_TR, PLAN_CAP = 0, 1, 2
 CAP_POSITION, CAP_PROBS = 0, 1
 OP_PERMUTE, OP_ROUTE_TR, OP_GEMM_FWD, OP_LAYER_BWD, OP_ROUTER_BWD, OP_ROUTER_LOGITS = 0, 1, 2, 3, 4, 5
+OP_GEMM_FWD_MXFP8 = 6
 
 EXPORTED_SYMBOLS = (
     "moe_plan_rows_cap", "moe_workspace_bytes", "moe_last_error", "moe_route_topk", "moe_permute",
     "moe_permute_noalloc",
     "moe_route_token_rounding", "moe_route_capacity", "moe_grouped_gemm_fwd", "moe_unpermute_combine",
     "moe_layer_bwd",
-    "moe_router_logits", "moe_router_bwd", "moe_set_kernel_events",
+    "moe_router_logits", "moe_router_bwd", "moe_set_kernel_events", "moe_quantize_mxfp8",
+    "moe_grouped_gemm_fwd_mxfp8",
 )
 
 # kernel ids of the measurement hook (moe_kernel_id in include/moe.h)
 KERNEL_IDS = {"gateup": 0, "down": 1, "dh": 2, "dx": 3, "dwd": 4, "dw1": 5, "combine": 6, "dx_combine": 7,
               "route": 8, "permute": 9, "route_tr_plan": 10, "dswiglu": 11, "router_logits": 12,
-              "router_dz": 13, "router_dx": 14, "router_dw": 15}
+              "router_dz": 13, "router_dx": 14, "router_dw": 15, "gateup_fp8": 16, "down_fp8": 17, "quant": 18}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -100,11 +102,13 @@ def load_library(path: str):
     L.moe_router_logits.argtypes = [ctypes.c_int, vp, vp, vp, i32, i32, i32, vp, vp, sz, vp]
     L.moe_router_bwd.argtypes = [ctypes.c_int, vp, vp, vp, pp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_set_kernel_events.argtypes = [i32, vp, vp]
+    L.moe_quantize_mxfp8.argtypes = [ctypes.c_int, vp, ctypes.c_int64, i32, vp, vp, vp]
+    L.moe_grouped_gemm_fwd_mxfp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, pp, vp, vp, vp, sz, vp]
     for fn in ("moe_route_topk", "moe_permute", "moe_permute_noalloc", "moe_route_token_rounding",
                "moe_route_capacity",
                "moe_grouped_gemm_fwd",
                "moe_unpermute_combine", "moe_layer_bwd", "moe_router_logits", "moe_router_bwd",
-               "moe_set_kernel_events"):
+               "moe_set_kernel_events", "moe_quantize_mxfp8", "moe_grouped_gemm_fwd_mxfp8"):
         getattr(L, fn).restype = ctypes.c_int
     return L
 
@@ -283,6 +287,43 @@ def grouped_gemm_fwd(x, w_gate, w_up, w_down, plan: Plan, hcache=None, y=None, w
     ws = _ws(nb, x.device, ws)
     _check(lib().moe_grouped_gemm_fwd(dt, _ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down), H, I, plan.c,
                                       _ptr(hcache), _ptr(y), _ptr(ws), nb, _stream(stream)))
+    return hcache, y
+
+
+def mx_scale_cols(K: int) -> int:
+    """Scale codes per row of an MX-FP8 matrix with K columns: 4 * ceil(K / 128)."""
+    return 4 * ((K + 127) // 128)
+
+
+def quantize_mxfp8(src, q=None, scales=None, stream=None):
+    """MX-FP8 quantization of src [..., K] (bf16 or fp32, K a multiple of 32) along its last
+    dimension -> (codes uint8 [..., K], scale codes uint8 [..., 4 ceil(K/128)])."""
+    import torch
+    K = src.shape[-1]
+    rows = src.numel() // K if K else 0
+    q = q if q is not None else torch.empty(src.shape, dtype=torch.uint8, device=src.device)
+    scales = scales if scales is not None else torch.empty(src.shape[:-1] + (mx_scale_cols(K),), dtype=torch.uint8,
+                                                           device=src.device)
+    _check(lib().moe_quantize_mxfp8(_dtype_code(src), _ptr(src), rows, K, _ptr(q), _ptr(scales), _stream(stream)))
+    return q, scales
+
+
+def grouped_gemm_fwd_mxfp8(x, w_gate, w_up, w_down, plan: Plan, hcache=None, y=None, ws=None, stream=None):
+    """Forward on MX-FP8 operands; x, w_gate, w_up, w_down are (codes, scale codes) pairs from
+    quantize_mxfp8 of x [N,H], W_gate / W_up [E,I,H] and W_down [E,H,I].  -> (hcache [M_cap, 2I],
+    y [M_cap, H]), both bf16."""
+    import torch
+    (xq, xs), (gq, gs), (uq, us), (dq, dsc) = x, w_gate, w_up, w_down
+    N, H = xq.shape
+    E, I, _ = gq.shape
+    mc = max(plan.M_cap, 1)
+    hcache = hcache if hcache is not None else torch.empty((mc, 2 * I), dtype=torch.bfloat16, device=xq.device)
+    y = y if y is not None else torch.empty((mc, H), dtype=torch.bfloat16, device=xq.device)
+    nb = workspace_bytes(OP_GEMM_FWD_MXFP8, MOE_BF16, plan.N, plan.E, plan.k, H, I, plan.M_cap)
+    ws = _ws(nb, xq.device, ws)
+    _check(lib().moe_grouped_gemm_fwd_mxfp8(_ptr(xq), _ptr(xs), _ptr(gq), _ptr(gs), _ptr(uq), _ptr(us), _ptr(dq),
+                                            _ptr(dsc), H, I, plan.c, _ptr(hcache), _ptr(y), _ptr(ws), nb,
+                                            _stream(stream)))
     return hcache, y
 
 

@@ -160,6 +160,9 @@ size_t moe_workspace_bytes(moe_op op, moe_dtype dt, int32_t N, int32_t E, int32_
     case MOE_OP_ROUTER_LOGITS:
       if (check_dtype(dt) != MOE_OK || H < 1) return 0;
       return moe::router_logits_ws_bytes(N, H, E);
+    case MOE_OP_GEMM_FWD_MXFP8:
+      if (H < 32 || I < 32 || H % 32 || I % 32 || M_cap < 0) return 0;
+      return moe::gemm_fwd_mxfp8_ws_bytes(M_cap, I);
   }
   return 0;
 }
@@ -295,6 +298,48 @@ moe_status moe_grouped_gemm_fwd(moe_dtype dt, const void* x, const void* w_gate,
   return hip_status(moe::launch_gemm_fwd(dt, x, w_gate, w_up, w_down, H, I, *plan, hcache, y, ws,
                                          (hipStream_t)stream),
                     "moe_grouped_gemm_fwd");
+}
+
+moe_status moe_quantize_mxfp8(moe_dtype dt, const void* src, int64_t rows, int32_t K, uint8_t* q, uint8_t* scales,
+                              void* stream) {
+  g_err[0] = 0;
+  moe_status st;
+  if ((st = check_dtype(dt)) != MOE_OK) return st;
+  REQUIRE(rows >= 0, MOE_EINVAL, "rows must be >= 0 (got %lld)", (long long)rows);
+  REQUIRE(K >= 32 && K % 32 == 0, MOE_EUNSUPPORTED, "K must be a positive multiple of 32 (got %d)", K);
+  REQUIRE(rows == 0 || (src && q && scales), MOE_EINVAL, "NULL src/q/scales");
+  REQUIRE(aligned16(src) && aligned16(q), MOE_EUNSUPPORTED, "src and q must be 16-byte aligned");
+  REQUIRE(rows <= ((int64_t)1 << 40) / K, MOE_EINVAL, "rows too large");
+  moe::kernel_event(MOE_K_QUANT, 0, (hipStream_t)stream);
+  hipError_t e = moe::launch_quant_mxfp8(dt, src, rows, K, q, scales, (hipStream_t)stream);
+  moe::kernel_event(MOE_K_QUANT, 1, (hipStream_t)stream);
+  return hip_status(e, "moe_quantize_mxfp8");
+}
+
+moe_status moe_grouped_gemm_fwd_mxfp8(const uint8_t* x_q, const uint8_t* x_s, const uint8_t* wg_q,
+                                      const uint8_t* wg_s, const uint8_t* wu_q, const uint8_t* wu_s,
+                                      const uint8_t* wd_q, const uint8_t* wd_s, int32_t H, int32_t I,
+                                      const moe_plan* plan, void* hcache, void* y, void* ws, size_t ws_bytes,
+                                      void* stream) {
+  g_err[0] = 0;
+  moe_status st;
+  REQUIRE(H >= 32 && I >= 32, MOE_EINVAL, "H and I must be >= 32 (got H=%d, I=%d)", H, I);
+  REQUIRE(H % 32 == 0 && I % 32 == 0, MOE_EUNSUPPORTED, "H and I must be multiples of 32 (got H=%d, I=%d)", H, I);
+  if ((st = check_plan(plan)) != MOE_OK) return st;
+  REQUIRE(wg_q && wg_s && wu_q && wu_s && wd_q && wd_s, MOE_EINVAL, "NULL weight argument");
+  REQUIRE(plan->M_cap == 0 || (x_q && x_s && hcache && y), MOE_EINVAL, "NULL tensor argument");
+  REQUIRE(aligned16(x_q) && aligned16(wg_q) && aligned16(wu_q) && aligned16(wd_q) && aligned16(hcache) &&
+              aligned16(y) && aligned16(ws) && ((uintptr_t)x_s & 3u) == 0 && ((uintptr_t)wg_s & 3u) == 0 &&
+              ((uintptr_t)wu_s & 3u) == 0 && ((uintptr_t)wd_s & 3u) == 0,
+          MOE_EUNSUPPORTED, "codes, outputs and workspace must be 16-byte aligned, scale codes 4-byte aligned");
+  // the bf16 outputs bound the sizes as in the bf16 forward; the codes are half as large
+  if ((st = check_desc_sizes(MOE_BF16, plan->N, H, I, plan->M_cap)) != MOE_OK) return st;
+  const size_t need = moe::gemm_fwd_mxfp8_ws_bytes((int)mcap_of(plan), I);
+  REQUIRE(ws_bytes >= need, MOE_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  REQUIRE(ws != nullptr, MOE_EINVAL, "NULL workspace");
+  return hip_status(moe::launch_gemm_fwd_mxfp8(x_q, x_s, wg_q, wg_s, wu_q, wu_s, wd_q, wd_s, H, I, *plan, hcache, y,
+                                               ws, (hipStream_t)stream),
+                    "moe_grouped_gemm_fwd_mxfp8");
 }
 
 moe_status moe_unpermute_combine(moe_dtype dt, const void* y, int32_t H, const moe_plan* plan, const float* row_w,

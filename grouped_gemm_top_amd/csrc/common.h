@@ -49,6 +49,27 @@ __device__ __forceinline__ void load4(const bf16_t* p, float& a, float& b, float
 
 __device__ __forceinline__ float sigmoidf_(float g) { return 1.0f / (1.0f + expf(-g)); }
 
+// MX-FP8 block scale: the exponent s of the smallest power of two with amax <= 448 2^s (448 is
+// e4m3's largest value, so no value of the block clips), limited to [-127, 127].  With amax =
+// 1.m 2^(E-127), E its exponent field, and 448 = 1.75 2^8: s = E - 135, plus one when 1.m >
+// 1.75 (m > 0x600000); zero and fp32 subnormals give -127.
+__device__ __forceinline__ int mx_scale_exp(float amax) {
+  const uint32_t b = __float_as_uint(amax);
+  const int ef = (int)((b >> 23) & 0xFF);
+  if (ef == 0) return -127;
+  const int s = ef - 135 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  return s < -127 ? -127 : (s > 127 ? 127 : s);
+}
+
+// four values scaled by 2^-s (exact) and rounded to e4m3 codes (v_cvt_pk_fp8_f32: nearest,
+// ties to even), byte j = value j
+__device__ __forceinline__ uint32_t mx_pack4(float a, float b, float c, float d, int s) {
+  const int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(a, -s), __builtin_amdgcn_ldexpf(b, -s), 0,
+                                                false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(c, -s), __builtin_amdgcn_ldexpf(d, -s), w,
+                                                    true);
+}
+
 // Device facts the launch shapes need (cached per device by the host side).
 struct DevInfo {
   int cus;   // compute units
@@ -81,6 +102,12 @@ hipError_t launch_token_round(const int32_t* idx, const float* probs, const floa
 hipError_t launch_combine(moe_dtype dt, const void* y, int H, const moe_plan& p, const float* row_w,
                           void* out, hipStream_t s);
 size_t gemm_fwd_ws_bytes(moe_dtype dt, int M_cap, int I);
+hipError_t launch_quant_mxfp8(moe_dtype dt, const void* src, long long rows, int K, uint8_t* q, uint8_t* scales,
+                              hipStream_t s);
+size_t gemm_fwd_mxfp8_ws_bytes(int M_cap, int I);
+hipError_t launch_gemm_fwd_mxfp8(const void* xq, const void* xs, const void* wgq, const void* wgs, const void* wuq,
+                                 const void* wus, const void* wdq, const void* wds, int H, int I, const moe_plan& p,
+                                 void* hcache, void* y, void* ws, hipStream_t s);
 hipError_t launch_gemm_fwd(moe_dtype dt, const void* x, const void* wg, const void* wu, const void* wd, int H,
                            int I, const moe_plan& p, void* hcache, void* y, void* ws, hipStream_t s);
 size_t router_bwd_ws_bytes(int N, int H, int E);

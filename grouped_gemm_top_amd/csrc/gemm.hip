@@ -992,6 +992,30 @@ hipError_t launch_gemm_fwd(moe_dtype dt, const void* x, const void* wg, const vo
   return gemm_fwd_t<float>(x, wg, wu, wd, H, I, p, hcache, y, ws, s);
 }
 
+// MX-FP8 forward: the workspace holds A's codes [M_cap, I] and its scale codes [M_cap, KS(I)].
+size_t gemm_fwd_mxfp8_ws_bytes(int M_cap, int I) {
+  const size_t ksi = 4 * (size_t)((I + 127) / 128);
+  return align256((size_t)M_cap * I) + align256((size_t)M_cap * ksi) + 256;
+}
+
+hipError_t launch_gemm_fwd_mxfp8(const void* xq, const void* xs, const void* wgq, const void* wgs, const void* wuq,
+                                 const void* wus, const void* wdq, const void* wds, int H, int I, const moe_plan& p,
+                                 void* hcache, void* y, void* ws, hipStream_t s) {
+  gg::Args a{};
+  a.x = xq; a.xs = xs; a.wg = wgq; a.wgs = wgs; a.wu = wuq; a.wus = wus; a.wd = wdq; a.wds = wds;
+  a.counts = p.counts; a.offsets = p.offsets; a.row_token = p.row_token; a.row_w = p.row_w;
+  a.E = p.E; a.H = H; a.I = I; a.N = p.N; a.M_cap = p.M_cap;
+  char* w = (char*)ws;
+  void* aq = w;
+  void* as = w + align256((size_t)p.M_cap * I);
+  a.out0 = hcache; a.out1 = aq; a.out2 = as;
+  const long long mt = (long long)(p.M_cap + 255) / 256 + p.E;
+  hipError_t err = run_gemm_bf16<gg::GATEUP8>(a, mt * ((I + 127) / 128), s);
+  if (err != hipSuccess) return err;
+  a.act = aq; a.acts = as; a.out0 = y; a.out1 = nullptr; a.out2 = nullptr;
+  return run_gemm_bf16<gg::DOWN8>(a, mt * ((H + 255) / 256), s);
+}
+
 size_t layer_bwd_ws_bytes(moe_dtype dt, int N, int M_cap, int H, int I) {
   (void)N;
   const size_t es = dt == MOE_BF16 ? 2 : 4;

@@ -64,6 +64,8 @@ using gg::DH;
 using gg::DX;
 using gg::DWD;
 using gg::DW1;
+using gg::GATEUP8;
+using gg::DOWN8;
 
 constexpr int NT = 512;        // threads per workgroup
 constexpr int BM = 256, BN = 256, BK = 32;  // varlen-K tiles; k = 32 per stage
@@ -76,6 +78,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 
 // A_KC / B_KC: operand is K-contiguous in memory; GA / GB: operand rows are gathered through
@@ -83,13 +86,16 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // memory instructions one epilogue issues (used for the vmcnt immediates); MI: row blocks of 16
 // per wavefront, so an M-tile has 64 MI rows (varlen-M: 320, which makes a group of up to 320
 // rows a single M-tile; varlen-K: 256).
+// F8: MX-FP8 operands (e4m3 codes with a scale per 32 values along K, v_mfma_scale_f32_16x16x128_f8f6f4).
 template <int K> struct KT;
-template <> struct KT<GATEUP> { static constexpr bool A_KC = true, B_KC = true, VK = false, GA = true, GB = false; static constexpr int ST = 32, MI = 5; };
-template <> struct KT<DOWN> { static constexpr bool A_KC = true, B_KC = true, VK = false, GA = false, GB = false; static constexpr int ST = 16, MI = 5; };
-template <> struct KT<DH> { static constexpr bool A_KC = true, B_KC = false, VK = false, GA = true, GB = false; static constexpr int ST = 40, MI = 5; };
-template <> struct KT<DX> { static constexpr bool A_KC = true, B_KC = false, VK = false, GA = false, GB = false; static constexpr int ST = 16, MI = 5; };
-template <> struct KT<DWD> { static constexpr bool A_KC = false, B_KC = false, VK = true, GA = true, GB = false; static constexpr int ST = 16, MI = 4; };
-template <> struct KT<DW1> { static constexpr bool A_KC = false, B_KC = false, VK = true, GA = false, GB = true; static constexpr int ST = 16, MI = 4; };
+template <> struct KT<GATEUP> { static constexpr bool A_KC = true, B_KC = true, VK = false, GA = true, GB = false, F8 = false; static constexpr int ST = 32, MI = 5; };
+template <> struct KT<DOWN> { static constexpr bool A_KC = true, B_KC = true, VK = false, GA = false, GB = false, F8 = false; static constexpr int ST = 16, MI = 5; };
+template <> struct KT<DH> { static constexpr bool A_KC = true, B_KC = false, VK = false, GA = true, GB = false, F8 = false; static constexpr int ST = 40, MI = 5; };
+template <> struct KT<DX> { static constexpr bool A_KC = true, B_KC = false, VK = false, GA = false, GB = false, F8 = false; static constexpr int ST = 16, MI = 5; };
+template <> struct KT<DWD> { static constexpr bool A_KC = false, B_KC = false, VK = true, GA = true, GB = false, F8 = false; static constexpr int ST = 16, MI = 4; };
+template <> struct KT<DW1> { static constexpr bool A_KC = false, B_KC = false, VK = true, GA = false, GB = true, F8 = false; static constexpr int ST = 16, MI = 4; };
+template <> struct KT<GATEUP8> { static constexpr bool A_KC = true, B_KC = true, VK = false, GA = true, GB = false, F8 = true; static constexpr int ST = 32, MI = 5; };
+template <> struct KT<DOWN8> { static constexpr bool A_KC = true, B_KC = true, VK = false, GA = false, GB = false, F8 = true; static constexpr int ST = 16, MI = 5; };
 
 // Per-kind tile geometry: BMK rows per M-tile; a stage covers BKS values of k and holds OPA
 // bytes of A then OPB bytes of B; NST stages form the LDS ring.
@@ -98,11 +104,19 @@ template <> struct KT<DW1> { static constexpr bool A_KC = false, B_KC = false, V
 //            of 72 KB.  K-strided B: 64 k-rows of 512 bytes.
 //  varlen-K: k = 32 per stage, both operands K-strided (32 k-rows of 512 bytes); four stages.
 //            NA: A load instructions per stage (16 rows of 64 bytes each).
+//  MX-FP8 (F8): k = 128 e4m3 codes per stage, so a row of a stage is again one 128-byte line and
+//            the operand areas match the bf16 ones byte for byte; after them each stage holds
+//            the block scales of its rows, one 32-bit word (four blocks of 32) per row: SCA
+//            bytes for A (40 rows per wavefront) and SCB for B (32 rows per wavefront).
 template <int KIND> struct Geo {
-  static constexpr bool VK = KT<KIND>::VK;
+  static constexpr bool VK = KT<KIND>::VK, F8 = KT<KIND>::F8;
+  static constexpr int ES = F8 ? 1 : 2;  // bytes per operand element
   static constexpr int MI = KT<KIND>::MI, BMK = 64 * MI;
-  static constexpr int BKS = VK ? BK : 64, NST = VK ? NSTG : 2;
-  static constexpr int OPA = BMK * 2 * BKS, OPB = BN * 2 * BKS, STGK = OPA + OPB, NA = BMK / 16;
+  static constexpr int BKS = VK ? BK : (F8 ? 128 : 64), NST = VK ? NSTG : 2;
+  static constexpr int OPA = BMK * ES * BKS, OPB = BN * ES * BKS, NA = BMK / 16;
+  static constexpr int SCA = F8 ? 8 * 40 * 4 : 0, SCB = F8 ? 8 * 32 * 4 : 0;
+  static constexpr int STGK = OPA + OPB + SCA + SCB;
+  static constexpr int TOKSLOTS = VK ? NSTG : 2;  // token slots per wavefront
 };
 
 // LDS loads.  They are written as inline assembly on purpose: the compiler then does not
@@ -141,6 +155,11 @@ __device__ __forceinline__ void dma16(const i32x4& r, uint32_t m0, uint32_t voff
 }
 __device__ __forceinline__ void dma4(const i32x4& r, uint32_t m0, uint32_t voff) {
   asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(sgpr4(r)), "{m0}"(m0)
+               : "memory");
+}
+// the same with a wavefront-uniform byte offset soff (r already in SGPRs)
+__device__ __forceinline__ void dma4s(const i32x4& r, uint32_t m0, uint32_t voff, uint32_t soff) {
+  asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(r), "s"(soff), "{m0}"(m0)
                : "memory");
 }
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -216,8 +235,8 @@ struct Sched {
       c.mt = local - c.nt * mtiles;
       c.mlen = min(BMK, cnt - c.mt * BMK);
       switch (KIND) {
-        case GATEUP: case DH: c.K = a.H; break;
-        case DOWN: c.K = a.I; break;
+        case GATEUP: case GATEUP8: case DH: c.K = a.H; break;
+        case DOWN: case DOWN8: c.K = a.I; break;
         default: c.K = 2 * a.I; break;  // DX
       }
     } else {
@@ -267,6 +286,8 @@ struct Loader {
   using G = Geo<KIND>;
   i32x4 rA, rB, rB2;          // descriptors; rB2: the up-projection half (GATEUP rows, DX k-rows)
   uint32_t vA[5], vB[4];      // this lane's byte offsets at k = 0 (OOB when masked)
+  i32x4 rSA, rSB, rSB2;       // MX-FP8: descriptors of the A and B scale codes (rSB2: up rows)
+  uint32_t vSA, vSB;          // MX-FP8: this lane's scale-row byte offsets (OOB when masked)
   uint32_t colA[4], colB[4];  // K-strided: column byte offsets (OOB when masked)
   int kc_c;                   // k-chunk this lane loads (K-contiguous)
   int mn_k[4], mn_c[4];       // k-row and column chunk this lane loads (K-strided)
@@ -299,6 +320,8 @@ struct Loader {
   // per-tile state; tok = this wavefront's token slot of the tile's first step
   __device__ __forceinline__ void setup(const Args& a, const Tile& c, const int* tok, int w, int L, int nMg) {
     const int H = a.H, I = a.I;
+    constexpr uint32_t ES = (uint32_t)G::ES;
+    constexpr bool GU = KIND == GATEUP || KIND == GATEUP8, DN = KIND == DOWN || KIND == DOWN8;
     if constexpr (!T::VK) {
       uint32_t rowA[5], rowB[4];  // K-contiguous: row byte offsets (OOB when masked)
       const long long rb = (long long)c.roff + (long long)c.mt * G::BMK;  // first row of the M-tile
@@ -306,35 +329,35 @@ struct Loader {
       for (int q = 0; q < 5; ++q) {
         const int r = 8 * (w + 8 * q) + (L >> 3);  // < 320
         const bool ok = c.valid && r < c.mlen;
-        if constexpr (KIND == GATEUP || KIND == DH) {
+        if constexpr (GU || KIND == DH) {
           const int t = tok[8 * q + (L >> 3)];
-          rowA[q] = ok ? (uint32_t)t * (uint32_t)H * 2u : OOB;
-        } else if constexpr (KIND == DOWN) {
-          rowA[q] = ok ? (uint32_t)r * (uint32_t)I * 2u : OOB;
+          rowA[q] = ok ? (uint32_t)t * (uint32_t)H * ES : OOB;
+        } else if constexpr (DN) {
+          rowA[q] = ok ? (uint32_t)r * (uint32_t)I * ES : OOB;
         } else {  // DX: rows of dH = [dG | dU]
           rowA[q] = ok ? (uint32_t)r * (uint32_t)(2 * I) * 2u : OOB;
         }
       }
-      if constexpr (KIND == GATEUP || KIND == DH) rA = dmadesc(KIND == GATEUP ? a.x : a.dout, (long long)a.N * H * 2);
-      if constexpr (KIND == DOWN) rA = dmadesc_off(a.act, rb * I * 2, (long long)c.mlen * I * 2);
+      if constexpr (GU || KIND == DH) rA = dmadesc(KIND == DH ? a.dout : a.x, (long long)a.N * H * ES);
+      if constexpr (DN) rA = dmadesc_off(a.act, rb * I * ES, (long long)c.mlen * I * ES);
       if constexpr (KIND == DX) rA = dmadesc_off(a.dh, rb * 2 * I * 2, (long long)c.mlen * 2 * I * 2);
-      if constexpr (KIND == GATEUP) {
+      if constexpr (GU) {
         // tile row n = 8w + 64q + (L >> 3): rows 64..127 of each 128-row half are up-projection
         // rows (q odd), for i = 128 nt + 64 (q >> 1) + (n & 63)
-        const long long es = (long long)c.e * I * H * 2;
-        rB = dmadesc_off(a.wg, es, (long long)I * H * 2);
-        rB2 = dmadesc_off(a.wu, es, (long long)I * H * 2);
+        const long long es = (long long)c.e * I * H * ES;
+        rB = dmadesc_off(a.wg, es, (long long)I * H * ES);
+        rB2 = dmadesc_off(a.wu, es, (long long)I * H * ES);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int i = c.nt * 128 + (q >> 1) * 64 + 8 * w + (L >> 3);
-          rowB[q] = c.valid ? (uint32_t)i * (uint32_t)H * 2u : OOB;  // i >= I lies past the range
+          rowB[q] = c.valid ? (uint32_t)i * (uint32_t)H * ES : OOB;  // i >= I lies past the range
         }
-      } else if constexpr (KIND == DOWN) {
-        rB = dmadesc_off(a.wd, (long long)c.e * H * I * 2, (long long)H * I * 2);
+      } else if constexpr (DN) {
+        rB = dmadesc_off(a.wd, (long long)c.e * H * I * ES, (long long)H * I * ES);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int n = c.nt * BN + 8 * (w + 8 * q) + (L >> 3);
-          rowB[q] = (c.valid && n < H) ? (uint32_t)n * (uint32_t)I * 2u : OOB;
+          rowB[q] = (c.valid && n < H) ? (uint32_t)n * (uint32_t)I * ES : OOB;
         }
       } else if constexpr (KIND == DH) {
         rB = dmadesc_off(a.wd, (long long)c.e * H * I * 2, (long long)H * I * 2);
@@ -361,9 +384,35 @@ struct Loader {
 #pragma unroll
         for (int q = 0; q < 4; ++q) vB[q] = rowB[q] + 16u * (uint32_t)kc_c;
       }
+      if constexpr (G::F8) {
+        // Scale words: lane l < 40 loads the word of A row 8(w + 8(l >> 3)) + (l & 7) (the rows
+        // whose codes this wavefront loads; tok[l] is that row's token), lane l < 32 the word
+        // of B row 8(w + 8(l >> 3)) + (l & 7); rows of a matrix hold 4 ceil(K / 128) bytes.
+        const int KSH = 4 * ((H + 127) / 128), KSI = 4 * ((I + 127) / 128);
+        const int r = 8 * (w + 8 * (L >> 3)) + (L & 7);
+        const bool oka = c.valid && L < 40 && r < c.mlen;
+        if constexpr (KIND == GATEUP8) {
+          rSA = dmadesc(a.xs, (long long)a.N * KSH);
+          vSA = oka ? (uint32_t)tok[L] * (uint32_t)KSH : OOB;
+          const long long eo = (long long)c.e * I * KSH;
+          rSB = dmadesc_off(a.wgs, eo, (long long)I * KSH);
+          rSB2 = dmadesc_off(a.wus, eo, (long long)I * KSH);
+          const int i = c.nt * 128 + ((L >> 4) & 1) * 64 + 8 * w + (L & 7);  // q = L >> 3: gate (even), up (odd)
+          vSB = (c.valid && L < 32 && i < I) ? (uint32_t)i * (uint32_t)KSH : OOB;
+          rSB2 = sgpr4(rSB2);
+        } else {  // DOWN8: A is the tile's rows of the quantized activation, B is W_down[e]
+          rSA = dmadesc_off(a.acts, rb * KSI, (long long)c.mlen * KSI);
+          vSA = oka ? (uint32_t)r * (uint32_t)KSI : OOB;
+          rSB = dmadesc_off(a.wds, (long long)c.e * H * KSI, (long long)H * KSI);
+          const int n = c.nt * BN + r;
+          vSB = (c.valid && L < 32 && n < H) ? (uint32_t)n * (uint32_t)KSI : OOB;
+        }
+        rSA = sgpr4(rSA);
+        rSB = sgpr4(rSB);
+      }
       rA = sgpr4(rA);
       rB = sgpr4(rB);
-      if constexpr (KIND == GATEUP || KIND == DX) rB2 = sgpr4(rB2);
+      if constexpr (GU || KIND == DX) rB2 = sgpr4(rB2);
       return;
     }
     if constexpr (KIND == DWD) {
@@ -407,8 +456,24 @@ struct Loader {
     const int H = a.H, I = a.I;
     // the descriptors in SGPRs once per step (the inline assembly takes them as scalar operands)
     const i32x4 rA = sgpr4(this->rA), rB = sgpr4(this->rB);
-    const i32x4 rB2 = (KIND == GATEUP || KIND == DX) ? sgpr4(this->rB2) : rB;
+    const i32x4 rB2 = (KIND == GATEUP || KIND == GATEUP8 || KIND == DX) ? sgpr4(this->rB2) : rB;
     const int k0 = c.kt * G::BKS;
+    constexpr uint32_t ES = (uint32_t)G::ES;
+    if constexpr (G::F8) {
+      // the step's scale words (word kt of each row: the four blocks of this k-step), lanes
+      // outside the wavefront's rows inactive so they write no LDS
+      const uint32_t msc = mS + (uint32_t)(G::OPA + G::OPB);
+      const uint32_t so4 = (uint32_t)ufl(4 * c.kt);
+      const i32x4 rSA_ = sgpr4(rSA), rSB_ = sgpr4(rSB);
+      if (L < 40) dma4s(rSA_, msc + (uint32_t)(160 * w), vSA, so4);
+      if constexpr (KIND == GATEUP8) {
+        const i32x4 rSB2_ = sgpr4(rSB2);
+        if (L < 32 && !(L & 8)) dma4s(rSB_, msc + (uint32_t)(G::SCA + 128 * w), vSB, so4);
+        if (L < 32 && (L & 8)) dma4s(rSB2_, msc + (uint32_t)(G::SCA + 128 * w), vSB, so4);
+      } else {
+        if (L < 32) dma4s(rSB_, msc + (uint32_t)(G::SCA + 128 * w), vSB, so4);
+      }
+    }
     if constexpr (!T::VK) {
       const uint32_t mB = mS + (uint32_t)G::OPA;
       // the uniform advance is only used where it is non-negative and keeps every lane inside
@@ -416,14 +481,14 @@ struct Loader {
       bool fast = k0 + G::BKS <= c.K;
       if constexpr (KIND == DX) fast = fast && (k0 + G::BKS <= I || k0 >= I);
       if (fast) {
-        const uint32_t so = (uint32_t)k0 * 2u;
+        const uint32_t so = (uint32_t)k0 * ES;
 #pragma unroll
         for (int q = 0; q < 5; ++q) dma16(rA, mS + (uint32_t)(w + 8 * q) * 1024u, vA[q], so);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const uint32_t m = mB + (uint32_t)(w + 8 * q) * 1024u;
-          if constexpr (KIND == GATEUP) dma16((q & 1) ? rB2 : rB, m, vB[q], so);
-          if constexpr (KIND == DOWN) dma16(rB, m, vB[q], so);
+          if constexpr (KIND == GATEUP || KIND == GATEUP8) dma16((q & 1) ? rB2 : rB, m, vB[q], so);
+          if constexpr (KIND == DOWN || KIND == DOWN8) dma16(rB, m, vB[q], so);
           if constexpr (KIND == DH) dma16(rB, m, vB[q], (uint32_t)k0 * (uint32_t)I * 2u);
           if constexpr (KIND == DX) {
             const bool up = k0 >= I;  // the whole stage lies in one half
@@ -432,16 +497,18 @@ struct Loader {
         }
         return;
       }
-      // K tail (or a dX stage across k = I): full per-lane offsets, k >= K masked
-      const bool kv = k0 + 8 * kc_c < c.K;
+      // K tail (or a dX stage across k = I): full per-lane offsets, k >= K masked (a 16-byte
+      // chunk holds 16 / ES values and K is a multiple of them, so a chunk is all in or all out)
+      const bool kv = k0 + (16 / (int)ES) * kc_c < c.K;
 #pragma unroll
       for (int q = 0; q < 5; ++q)
-        dma16(rA, mS + (uint32_t)(w + 8 * q) * 1024u, kv ? vA[q] + (uint32_t)k0 * 2u : OOB, 0u);
+        dma16(rA, mS + (uint32_t)(w + 8 * q) * 1024u, kv ? vA[q] + (uint32_t)k0 * ES : OOB, 0u);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const uint32_t m = mB + (uint32_t)(w + 8 * q) * 1024u;
-        if constexpr (KIND == GATEUP) dma16((q & 1) ? rB2 : rB, m, kv ? vB[q] + (uint32_t)k0 * 2u : OOB, 0u);
-        if constexpr (KIND == DOWN) dma16(rB, m, kv ? vB[q] + (uint32_t)k0 * 2u : OOB, 0u);
+        if constexpr (KIND == GATEUP || KIND == GATEUP8)
+          dma16((q & 1) ? rB2 : rB, m, kv ? vB[q] + (uint32_t)k0 * ES : OOB, 0u);
+        if constexpr (KIND == DOWN || KIND == DOWN8) dma16(rB, m, kv ? vB[q] + (uint32_t)k0 * ES : OOB, 0u);
         if constexpr (KIND == DH) {
           const uint32_t k = (uint32_t)(k0 + mn_k[q]);
           dma16(rB, m, colB[q] + k * (uint32_t)I * 2u, 0u);  // k >= H lies past the range
@@ -565,9 +632,10 @@ __device__ __forceinline__ void epilogue(const Args& a, const Tile& c, f32x4 (&a
   const int H = a.H, I = a.I;
   constexpr int MI = KT<KIND>::MI;
   const long long rb = (long long)c.roff + (long long)c.mt * Geo<KIND>::BMK;
-  if constexpr (KIND == GATEUP) {
+  if constexpr (KIND == GATEUP || KIND == GATEUP8) {
     const rsrc_t rh = gg::mkr_off(a.out0, rb * 2 * I * 2, (long long)c.mlen * 2 * I * 2);
-    const rsrc_t ra = gg::mkr_off(a.out1, rb * I * 2, (long long)c.mlen * I * 2);
+    const rsrc_t ra = KIND == GATEUP ? gg::mkr_off(a.out1, rb * I * 2, (long long)c.mlen * I * 2)
+                                     : gg::mkr_off(a.out1, rb * I, (long long)c.mlen * I);
     const int i0 = c.nt * 128 + wn * 64;  // first i of this wavefront's 64 gate and 64 up columns
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
@@ -580,6 +648,44 @@ __device__ __forceinline__ void epilogue(const Args& a, const Tile& c, f32x4 (&a
         const int q = L & 15, ii = i0 + (q & 7) * 8;
         const uint32_t off = m * (uint32_t)(2 * I) * 2u + (uint32_t)((q >= 8 ? I : 0) + ii) * 2u;
         st16(rh, ii < I ? off : OOB, v);
+      }
+      if constexpr (KIND == GATEUP8) {
+        // A = silu(G) * U quantized to MX-FP8 for the down GEMM: the wavefront's 64 columns are
+        // two blocks of 32 (column blocks j = 0, 1 and 2, 3); a row's block lies in the four
+        // lanes L & 15 + 16 g (eight values each), whose maximum gives the block's scale.
+        // Columns >= I hold zeros (their weight rows loaded as zeros), so their blocks get
+        // scale code 0, which also fills the scale row's padding entries.
+        f32x4 av[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) av[j][v] = acc[i][j][v] * sigm(acc[i][j][v]) * acc[i][j + 4][v];
+        int se[2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          float mx = 0.f;
+#pragma unroll
+          for (int j = 2 * b; j < 2 * b + 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) mx = fmaxf(mx, fabsf(av[j][v]));
+          mx = fmaxf(mx, __shfl_xor(mx, 16));
+          mx = fmaxf(mx, __shfl_xor(mx, 32));
+          se[b] = mx_scale_exp(mx);
+        }
+        const uint32_t m = (uint32_t)(16 * (4 * i + wm) + (L & 15));  // rows >= mlen: past the range
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t wq = mx_pack4(av[j][0], av[j][1], av[j][2], av[j][3], se[j >> 1]);
+          const int ii = i0 + 16 * j + 4 * (L >> 4);
+          __builtin_amdgcn_raw_buffer_store_b32(wq, ra, ii < I ? m * (uint32_t)I + (uint32_t)ii : OOB, 0, 0);
+        }
+        // the two scale codes of the row, by the lanes of column group 0 (i0 / 32 < KSI - 1)
+        const int KSI = 4 * ((I + 127) / 128);
+        const rsrc_t rs = gg::mkr_off(a.out2, rb * KSI, (long long)c.mlen * KSI);
+        const uint16_t sc2 = (uint16_t)((se[0] + 127) | ((se[1] + 127) << 8));
+        __builtin_amdgcn_raw_buffer_store_b16(sc2, rs, (L >> 4) == 0 ? m * (uint32_t)KSI + (uint32_t)(i0 / 32) : OOB,
+                                              0, 0);
+        continue;
       }
       // A = silu(G) * U, staged in the first 64 columns
       f32x4 ab[8];
@@ -598,7 +704,7 @@ __device__ __forceinline__ void epilogue(const Args& a, const Tile& c, f32x4 (&a
         if (q < 8) st16(ra, ii < I ? m * (uint32_t)I * 2u + (uint32_t)ii * 2u : OOB, v);
       }
     }
-  } else if constexpr (KIND == DOWN || KIND == DX) {
+  } else if constexpr (KIND == DOWN || KIND == DOWN8 || KIND == DX) {
     const rsrc_t ro = gg::mkr_off(a.out0, rb * H * 2, (long long)c.mlen * H * 2);
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
@@ -784,7 +890,7 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
   constexpr bool GATHER = T::GA || T::GB;
 
   __shared__ __attribute__((aligned(1024))) char s_ring[G::NST * G::STGK];
-  __shared__ __attribute__((aligned(256))) int s_tok[8 * NSTG * (TOKB / 4)];
+  __shared__ __attribute__((aligned(256))) int s_tok[8 * G::TOKSLOTS * (TOKB / 4)];
   __shared__ int s_sched[1025];
   __shared__ int s_wsum[9];
   __shared__ __attribute__((aligned(256))) char s_stg[T::VK ? 4 * 4096 : 16];
@@ -802,8 +908,8 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
   S.xcd = blockIdx.x & 7;
   S.slot = blockIdx.x >> 3;
   switch (KIND) {
-    case GATEUP: S.nN = (a.I + 127) / 128; break;
-    case DOWN: case DX: case DW1: S.nN = (a.H + BN - 1) / BN; break;
+    case GATEUP: case GATEUP8: S.nN = (a.I + 127) / 128; break;
+    case DOWN: case DOWN8: case DX: case DW1: S.nN = (a.H + BN - 1) / BN; break;
     default: S.nN = (a.I + BN - 1) / BN; break;  // DH, DWD
   }
   S.nMg = (a.I + BM - 1) / BM;
@@ -931,6 +1037,60 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
     }
   };
 
+  // MX-FP8 step, half h: the MFMAs of this wavefront's column blocks 4h .. 4h + 3 over the
+  // stage's k = 128 (v_mfma_scale_f32_16x16x128_f8f6f4, e4m3 x e4m3).  The instruction takes
+  // lane row (L & 15), bytes 16 (L >> 4) .. + 15 and 64 + 16 (L >> 4) .. + 15 of its 128: the two
+  // chunks the bf16 step reads for its two k-substeps, so a fragment is those two reads.  The
+  // scale of (row L & 15, block L >> 4) is byte L >> 4 of the row's scale word, which the lane
+  // shifts down to byte 0 (the byte the instruction reads).  A's words sit in the stage at
+  // 40 w + 8 q + r for row 8 (w + 8 q) + r, B's at 32 w + 8 q + r (the order of their loads).
+  auto mma_stage8 = [&](const char* sa, int nb, int h) __attribute__((always_inline)) {
+    int kco = kc_off, sho = 8 * (L >> 4), lro = L & 15;
+    asm volatile("" : "+v"(kco), "+v"(sho), "+v"(lro));
+    const char* sb = sa + G::OPA;
+    const uint32_t* sca = reinterpret_cast<const uint32_t*>(sa + G::OPA + G::OPB);
+    const uint32_t* scb = reinterpret_cast<const uint32_t*>(sa + G::OPA + G::OPB + G::SCA);
+    auto frag8 = [&](const char* op, int r0) __attribute__((always_inline)) {
+      struct P { bf16x8 lo, hi; } pr{frag_kc(op, r0, 0, kco), frag_kc(op, r0, 1, kco)};
+      return __builtin_bit_cast(i32x8, pr);
+    };
+    auto scale_a = [&](int m) __attribute__((always_inline)) {
+      return (int)(sca[40 * ((m >> 3) & 7) + 8 * (m >> 6) + (m & 7)] >> sho);
+    };
+    auto scale_b = [&](int n) __attribute__((always_inline)) {
+      return (int)(scb[32 * ((n >> 3) & 7) + 8 * (n >> 6) + (n & 7)] >> sho);
+    };
+    i32x8 fb[4];
+    int sbv[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int n0 = wn * 128 + 16 * (4 * h + jj);
+      fb[jj] = frag8(sb, n0);
+      sbv[jj] = scale_b(n0 + lro);
+    }
+    i32x8 fa = frag8(sa, 16 * wm);
+    int sav = scale_a(16 * wm + lro);
+#pragma unroll
+    for (int i = 0; i < G::MI; ++i) {
+      i32x8 fn;
+      int sn = 0;
+      if (i + 1 < G::MI) {
+        fn = frag8(sa, 16 * (4 * (i + 1) + wm));
+        sn = scale_a(16 * (4 * (i + 1) + wm) + lro);
+      }
+      if (i == 0 || nb > 64 * i) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          acc[i][4 * h + jj] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[jj], fa, acc[i][4 * h + jj], 0, 0,
+                                                                                0, sbv[jj], 0, sav);
+      }
+      if (i + 1 < G::MI) {
+        fa = fn;
+        sav = sn;
+      }
+    }
+  };
+
   // Varlen-K step: fa / fb hold this step's fragments, read during the previous step.  The
   // MFMAs go column block by column block; once a column's four MFMAs are issued its B
   // fragment is refilled with the next step's from the stage at `sn`, and after the last
@@ -955,7 +1115,7 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
   Loader<KIND> ld;
   ld.init(w, L);
   const i32x4 rtok = dmadesc(a.row_token, 4LL * (long long)a.M_cap);
-  int* my_tok = s_tok + w * NSTG * (TOKB / 4);  // this wavefront's token slots
+  int* my_tok = s_tok + w * G::TOKSLOTS * (TOKB / 4);  // this wavefront's token slots
   const uint32_t tok_m0 = lds_addr(my_tok);
   const uint32_t ring_m0 = lds_addr(s_ring);  // stage 0
 
@@ -1016,9 +1176,17 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
         // and after their first k-substep), so one issues loads while the other runs MFMAs
         const char* sa = s_ring + ((gs + kt) & 1) * G::STGK;
         if (wn == 0 && kt + 1 < nk) issue_step(Cc, kt + 1, gs + kt + 1);
-        if (nb > 0) mma_stage(sa, nb, 0);
+        if constexpr (G::F8) {
+          if (nb > 0) mma_stage8(sa, nb, 0);
+        } else {
+          if (nb > 0) mma_stage(sa, nb, 0);
+        }
         if (wn != 0 && kt + 1 < nk) issue_step(Cc, kt + 1, gs + kt + 1);
-        if (nb > 0) mma_stage(sa, nb, 1);
+        if constexpr (G::F8) {
+          if (nb > 0) mma_stage8(sa, nb, 1);
+        } else {
+          if (nb > 0) mma_stage(sa, nb, 1);
+        }
       }
       // every wavefront is done with the ring: the last step's stage stages the epilogue, the
       // other takes the next tile's first step, issued before the epilogue so that its wait
@@ -1181,5 +1349,7 @@ template hipError_t run_gemm_bf16<gg::DH>(const gg::Args&, long long, hipStream_
 template hipError_t run_gemm_bf16<gg::DX>(const gg::Args&, long long, hipStream_t);
 template hipError_t run_gemm_bf16<gg::DWD>(const gg::Args&, long long, hipStream_t);
 template hipError_t run_gemm_bf16<gg::DW1>(const gg::Args&, long long, hipStream_t);
+template hipError_t run_gemm_bf16<gg::GATEUP8>(const gg::Args&, long long, hipStream_t);
+template hipError_t run_gemm_bf16<gg::DOWN8>(const gg::Args&, long long, hipStream_t);
 
 }  // namespace moe

@@ -6,8 +6,12 @@
 namespace moe {
 namespace gg {
 
-// The six grouped GEMMs of the layer; the values equal their moe_kernel_id.
-enum Kind { GATEUP = MOE_K_GATEUP, DOWN = MOE_K_DOWN, DH = MOE_K_DH, DX = MOE_K_DX, DWD = MOE_K_DWD, DW1 = MOE_K_DW1 };
+// The six grouped GEMMs of the layer and the two MX-FP8 forward GEMMs; the values equal their
+// moe_kernel_id.
+enum Kind {
+  GATEUP = MOE_K_GATEUP, DOWN = MOE_K_DOWN, DH = MOE_K_DH, DX = MOE_K_DX, DWD = MOE_K_DWD, DW1 = MOE_K_DW1,
+  GATEUP8 = MOE_K_GATEUP_FP8, DOWN8 = MOE_K_DOWN_FP8
+};
 
 struct Args {
   const void* x;      // [N,H] activations (gathered)
@@ -21,6 +25,15 @@ struct Args {
   void* out0;         // GATEUP: hcache; DOWN: y; DH: dH; DX: dXe; DWD: dW_down; DW1: dW_gate
   void* out1;         // GATEUP: act;  DH: A';  DW1: dW_up
   float* dspart;      // DH: [M_cap, nTN] partial row-dots
+  // MX-FP8 kinds: x, wg, wu, wd, act hold e4m3 codes and these their scale codes
+  // ([rows, 4 ceil(K/128)] bytes, K the row length); GATEUP8 writes A's codes to out1 and its
+  // scale codes to out2
+  const void* xs;
+  const void* wgs;
+  const void* wus;
+  const void* wds;
+  const void* acts;
+  void* out2;
   const int32_t* counts;
   const int32_t* offsets;
   const int32_t* row_token;

@@ -77,7 +77,8 @@ typedef enum moe_op {
   MOE_OP_GEMM_FWD = 2,
   MOE_OP_LAYER_BWD = 3,
   MOE_OP_ROUTER_BWD = 4,
-  MOE_OP_ROUTER_LOGITS = 5
+  MOE_OP_ROUTER_LOGITS = 5,
+  MOE_OP_GEMM_FWD_MXFP8 = 6
 } moe_op;
 
 /*
@@ -232,6 +233,48 @@ moe_status moe_grouped_gemm_fwd(moe_dtype dt, const void* x, const void* w_gate,
                                 void* hcache, void* y, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * MX-FP8 (the fine-grained FP8 grouped GEMM of [GG] "한계": FP8 operands with a scale for each
+ * small block along the contraction dimension, here in the OCP microscaling layout that
+ * gfx950's scaled matrix instructions consume).  Element codes are e4m3 (sign, 4 exponent bits
+ * with bias 7, 3 mantissa bits, largest finite 448, no infinities); each block of 32
+ * consecutive values along K has a scale code c, scale 2^(c - 127).
+ * Layout of a quantized row-major [rows, K] matrix: codes q [rows, K] (one byte each) and
+ * scale codes [rows, KS] with KS = 4 * ceil(K / 128) (the four blocks of a 128-wide k-step form
+ * one 32-bit word): scales[r, b] scales q[r, 32b .. 32b + 31]; entries b >= K/32 are 0.
+ *
+ * moe_quantize_mxfp8: quantize src [rows, K] (dtype dt, row-major) into that layout.  Each
+ * block's scale is the smallest power of two X with max |v| <= 448 X (no value clips), the code
+ * limited to 0..254; each value is stored as v / X rounded to nearest e4m3, ties to even.
+ * Deterministic, bit for bit.  K a positive multiple of 32; src and q 16-byte aligned.  A
+ * weight tensor [E, out, in] is quantized as rows = E*out, K = in: W_gate and W_up along H,
+ * W_down along I; activations x [N, H] along H.  Callers quantize the weights once per
+ * update and reuse them over micro-batches.
+ */
+moe_status moe_quantize_mxfp8(moe_dtype dt, const void* src, int64_t rows, int32_t K, uint8_t* q, uint8_t* scales,
+                              void* stream);
+
+/*
+ * Grouped expert MLP forward on MX-FP8 operands: the bf16 forward's computation with x,
+ * W_gate, W_up (each quantized along H) and W_down (along I) given as codes and scale codes,
+ * on gfx950's scaled fp8 matrix instructions (fp32 accumulation):
+ *   [G | U] = x[t] [W_gate[e]; W_up[e]]^T  ->  hcache (bf16, as moe_grouped_gemm_fwd writes it,
+ *                                               for the bf16 backward)
+ *   A = silu(G) * U in fp32, quantized along I in the layout above into the workspace
+ *   y[r] = A W_down[e]^T  ->  y (bf16)
+ * x_q [N, H], x_s [N, KS(H)]; wg_q / wu_q [E, I, H], wg_s / wu_s [E, I, KS(H)]; wd_q [E, H, I],
+ * wd_s [E, H, KS(I)]; hcache [M_cap, 2I] and y [M_cap, H] bf16.  H and I must be multiples of
+ * 32.  Workspace: moe_workspace_bytes(MOE_OP_GEMM_FWD_MXFP8, MOE_BF16, N, E, k, H, I, M_cap);
+ * after the call it holds A's codes [M_cap, I] at byte 0 and A's scale codes [M_cap, KS(I)] at
+ * byte M_cap*I rounded up to a multiple of 256 (rows in plan order; rows >= M not written).
+ * moe_unpermute_combine then sums y as in the bf16 path.
+ */
+moe_status moe_grouped_gemm_fwd_mxfp8(const uint8_t* x_q, const uint8_t* x_s, const uint8_t* wg_q,
+                                      const uint8_t* wg_s, const uint8_t* wu_q, const uint8_t* wu_s,
+                                      const uint8_t* wd_q, const uint8_t* wd_s, int32_t H, int32_t I,
+                                      const moe_plan* plan, void* hcache, void* y, void* ws, size_t ws_bytes,
+                                      void* stream);
+
+/*
  * Weighted combine back to token order ([EP] "여러 Expert의 결과도 같은 토큰으로
  * 돌아오기"; [DEP] "3) Combine"):
  *   out[t] = sum over r in tok_rows(t) of row_w[r] * y[r]     (row_w NULL: weights 1)
@@ -330,7 +373,10 @@ typedef enum moe_kernel_id {
   MOE_K_ROUTER_DZ = 13,  /* moe_router_bwd: dz from dS */
   MOE_K_ROUTER_DX = 14,  /* moe_router_bwd: dx_out = dx_in + dz W_r^T */
   MOE_K_ROUTER_DW = 15,  /* moe_router_bwd: dW_r and dbias (sliced product + ordered reduction) */
-  MOE_K_COUNT = 16
+  MOE_K_GATEUP_FP8 = 16, /* moe_grouped_gemm_fwd_mxfp8: gate/up grouped GEMM + SwiGLU + A quantization */
+  MOE_K_DOWN_FP8 = 17,   /* moe_grouped_gemm_fwd_mxfp8: down grouped GEMM */
+  MOE_K_QUANT = 18,      /* moe_quantize_mxfp8 */
+  MOE_K_COUNT = 19
 } moe_kernel_id;
 
 moe_status moe_set_kernel_events(int32_t kernel_id, void* start_event, void* stop_event);

@@ -18,7 +18,7 @@ FAKE = 0x10000  # a non-NULL, 16-byte aligned address; never dereferenced by the
 def _declared():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", src)))
 
 
 @pytest.fixture(scope="module")
