@@ -29,6 +29,7 @@ METRIC = "MoE layer fwd+bwd ms & TFLOPS (% bf16 MFMA peak), E=128 H=2048 I=512 k
 PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 2.4 GHz x 4096 FLOP/clk (dense)
 PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+PEAK_FP8_TFLOPS = 5033.2      # dense fp8 MFMA: twice the bf16 rate
 GEMMS = ("gateup", "down", "dh", "dx", "dwd", "dw1")
 ALL_KERNELS = ("route", "permute", "route_tr_plan", "gateup", "down", "combine", "dh", "dswiglu", "dwd", "dx",
                "dx_combine", "dw1")
@@ -150,6 +151,79 @@ def padded_fractions(counts, M):
             "fixed_128row_tiles": round(float((128 * ((c + 127) // 128)).sum()) / m - 1.0, 5)}
 
 
+def fp8_forward(args, wl, x, wg, wu, wd, plan, M, e_act, kern_ms):
+    """The MX-FP8 forward on the same plan: the weights quantized once (timed on their own, a
+    cost the caller pays once per weight update), then per step x quantized and the gate/up and
+    down GEMMs on fp8 operands, each kernel timed with HIP events on its launch stream."""
+    import torch
+    import grouped_gemm_top_amd as G
+    N, H, I, E = wl.N, wl.H, wl.I, wl.E
+    qw = [G.quantize_mxfp8(t) for t in (wg, wu, wd)]
+    xq = G.quantize_mxfp8(x)
+    mc = max(plan.M_cap, 1)
+    hc8 = torch.empty((mc, 2 * I), dtype=torch.bfloat16, device="cuda")
+    y8 = torch.empty((mc, H), dtype=torch.bfloat16, device="cuda")
+    ws8 = torch.empty(G.workspace_bytes(G.OP_GEMM_FWD_MXFP8, G.MOE_BF16, N, E, wl.k, H, I, plan.M_cap),
+                      dtype=torch.uint8, device="cuda")
+    a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a_.record()
+    for t, q in zip((wg, wu, wd), qw):
+        G.quantize_mxfp8(t, q=q[0], scales=q[1])
+    b_.record()
+    torch.cuda.synchronize()
+    wq_ms = a_.elapsed_time(b_)
+
+    def step8():
+        G.quantize_mxfp8(x, q=xq[0], scales=xq[1])
+        G.grouped_gemm_fwd_mxfp8(xq, qw[0], qw[1], qw[2], plan, hcache=hc8, y=y8, ws=ws8)
+
+    for _ in range(args.warmup):
+        step8()
+    names = ("quant", "gateup_fp8", "down_fp8")
+    evs = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)] for n in names}
+    for pairs in evs.values():
+        for e0, e1 in pairs:
+            e0.record()
+            e1.record()
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        for n in names:
+            G.set_kernel_events(n, *evs[n][i])
+        step8()
+    torch.cuda.synchronize()
+    for n in names:
+        G.set_kernel_events(n, None, None)
+    us = {n: 1e3 * float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs[n]])) for n in names}
+    f_gu, f_dn = 4.0 * M * H * I, 2.0 * M * H * I
+    sc = 1.0 + 1.0 / 32  # codes plus one scale byte per 32
+    b_gu = 2.0 * e_act * I * H * sc + N * H * sc + 2.0 * M * 2 * I + M * I * sc
+    b_dn = e_act * H * I * sc + M * I * sc + 2.0 * M * H
+    gemm_us = us["gateup_fp8"] + us["down_fp8"]
+    bf16_us = 1e3 * (kern_ms["gateup"] + kern_ms["down"])
+    out = {"note": "MX-FP8 forward (e4m3, one power-of-two scale per 32 values along K) on the bf16 run's plan; "
+                   "weights quantized once, x every step",
+           "kernels_us": {n: round(v, 2) for n, v in us.items()},
+           "weights_quant_ms": round(wq_ms, 3),
+           "fwd_gemms_us": round(gemm_us, 2), "bf16_fwd_gemms_us": round(bf16_us, 2),
+           "speedup_vs_bf16_gemms": round(bf16_us / gemm_us, 3),
+           "fwd_gemm_tflops": round((f_gu + f_dn) / (gemm_us * 1e-6) / 1e12, 1),
+           "pct_fp8_peak": round(100.0 * (f_gu + f_dn) / (gemm_us * 1e-6) / 1e12 / PEAK_FP8_TFLOPS, 2)}
+    dom = "gateup_fp8" if us["gateup_fp8"] >= us["down_fp8"] else "down_fp8"
+    f, b = (f_gu, b_gu) if dom == "gateup_fp8" else (f_dn, b_dn)
+    t_s = us[dom] * 1e-6
+    if b / (PEAK_HBM_GBS * 1e9) >= f / (PEAK_FP8_TFLOPS * 1e12):
+        out["roofline"] = {"kernel": dom, "bound": "hbm", "achieved": round(b / t_s / 1e9, 1), "peak": PEAK_HBM_GBS,
+                           "unit": "GB/s", "frac": round(b / t_s / 1e9 / PEAK_HBM_GBS, 4), "traffic": None,
+                           "algorithmic_bytes": b, "us": round(us[dom], 2)}
+    else:
+        out["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": round(f / t_s / 1e12, 1),
+                           "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(f / t_s / 1e12 / PEAK_FP8_TFLOPS, 4),
+                           "traffic": None, "algorithmic_flops": f, "us": round(us[dom], 2)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -172,6 +246,9 @@ def main():
                          "FETCH_SIZE / WRITE_SIZE counters); peak: only the measured device peaks "
                          "(dense bf16 MFMA and HBM streaming probes)")
     ap.add_argument("--peaks", type=int, default=1, help="measure the device peaks after the layer (1/0)")
+    ap.add_argument("--fp8", type=int, default=1,
+                    help="also time the MX-FP8 forward (quantize x, gate/up + down on fp8 operands) beside the "
+                         "bf16 forward GEMMs (1/0; bf16 top-k workloads)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -418,6 +495,8 @@ def main():
             "logits_tflops": round(fl / (r_us["router_logits"] * 1e-6) / 1e12, 2),
             "bwd_us": round(r_us["router_dz"] + r_us["router_dx"] + r_us["router_dw"], 2),
         }
+    if args.fp8 and wl.dtype == "bf16" and not rt and args.kernel_events:
+        res["fp8"] = fp8_forward(args, wl, x, wg, wu, wd, plan, M, e_act, kern_ms)
     # The bound the whole step can reach: the larger of its FLOPs at the MFMA peak and its
     # algorithmic bytes (every tensor touched once per pass) at the HBM peak.
     lb = layer_bytes(wl, M, e_act, es)
