@@ -95,6 +95,65 @@ __global__ __launch_bounds__(256) void k_cvt_fp8(const float* __restrict__ src, 
   if (i < n2) dst[i] = (uint16_t)__builtin_amdgcn_cvt_pk_fp8_f32(src[2 * i], src[2 * i + 1], 0, false);
 }
 
+// Repeated reads of a buffer of `chunks` kilobytes, `passes` times over, as kilobyte loads of
+// one wavefront each (wavefront v of the grid takes chunks v, v + V, ... of the pass sequence).
+// mode 0: buffer_load_dwordx4 into VGPRs (eight in flight, XOR-folded into sink); mode 1:
+// buffer_load_dwordx4 ... lds into a 16 KB LDS ring per wavefront with at most 12 in flight,
+// the load form the GEMM kernels use; mode 2: the same with the lanes' 16-byte chunks in the
+// permuted order of the GEMMs' K-strided stages (each chunk still read once).  Times the two paths from L2 (a small buffer) or HBM.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+template <int MODE>
+__global__ __launch_bounds__(256) void k_reread(const char* __restrict__ src, uint32_t chunks, uint32_t passes,
+                                                uint32_t* __restrict__ sink) {
+  __shared__ __attribute__((aligned(1024))) char ring[4 * 16384];
+  const uint32_t L = threadIdx.x & 63;
+  const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t V = gridDim.x * 4, v0 = blockIdx.x * 4 + w;
+  const uint64_t total = (uint64_t)chunks * passes;
+  const uint64_t base = (uint64_t)src;
+  const i32x4 d = {(int)(uint32_t)base, (int)((uint32_t)(base >> 32) & 0xFFFFu), (int)(chunks * 1024u), 0x00020000};
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(src), (short)0,
+                                                                     (int)(chunks * 1024u), 0x00020000);
+  uint32_t x = 0;
+  if constexpr (MODE == 0) {
+    uint64_t c = v0;
+    for (; c + 7 * (uint64_t)V < total; c += 8 * (uint64_t)V) {
+      uint4 t[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t off = (uint32_t)((c + u * (uint64_t)V) % chunks) * 1024u + L * 16u;
+        t[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x ^= t[u].x ^ t[u].y ^ t[u].z ^ t[u].w;
+    }
+    for (; c < total; c += V) {
+      const uint4 t = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    r, (uint32_t)(c % chunks) * 1024u + L * 16u, 0, 0));
+      x ^= t.x ^ t.y ^ t.z ^ t.w;
+    }
+  } else {
+    const i32x4 ds = {__builtin_amdgcn_readfirstlane(d.x), __builtin_amdgcn_readfirstlane(d.y),
+                      __builtin_amdgcn_readfirstlane(d.z), __builtin_amdgcn_readfirstlane(d.w)};
+    const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(ring + w * 16384);
+    uint32_t q = 0;
+    for (uint64_t c = v0; c < total; c += V, ++q) {
+      uint32_t pos = L;
+      if constexpr (MODE == 2) {
+        // the K-strided GEMM stage order: k-row k = 2 (q & 15) + (L >> 5) of 512 bytes, lane
+        // position L & 31 holding chunk (L & 31) ^ f(k), f(k) = 2 ((k & 3) | (((k >> 3) & 1) << 2))
+        const uint32_t k = 2u * (q & 15u) + (L >> 5);
+        pos = (L & 32u) | ((L & 31u) ^ (2u * ((k & 3u) | (((k >> 3) & 1u) << 2))));
+      }
+      const uint32_t off = (uint32_t)(c % chunks) * 1024u + pos * 16u;
+      asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds\n\ts_waitcnt vmcnt(12)"
+                   ::"v"(off), "s"(ds), "{m0}"(m0 + (q & 15u) * 1024u) : "memory");
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  sink[(size_t)blockIdx.x * 256 + threadIdx.x] = x;
+}
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 }  // namespace
@@ -141,5 +200,23 @@ extern "C" int moe_probe_cvt_fp8(const float* src, int n, uint8_t* dst, void* st
   if (!src || !dst || n < 2 || n % 2 != 0 || ((uintptr_t)dst & 1u)) return 1;
   const int n2 = n / 2;
   hipLaunchKernelGGL(k_cvt_fp8, dim3((n2 + 255) / 256), dim3(256), 0, (hipStream_t)stream, src, n2, (uint16_t*)dst);
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+extern "C" int moe_probe_reread(const void* src, size_t bytes, int passes, int mode, int blocks, uint32_t* sink,
+                                void* stream) {
+  if (!src || !sink || !aligned16(src) || bytes < 1024 || bytes % 1024 != 0 || bytes > ((size_t)1 << 30) ||
+      passes < 1 || passes > 4096 || mode < 0 || mode > 2 || blocks < 1 || blocks > 65536)
+    return 1;
+  const uint32_t chunks = (uint32_t)(bytes / 1024);
+  if (mode == 0)
+    hipLaunchKernelGGL(k_reread<0>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const char*)src, chunks,
+                       (uint32_t)passes, sink);
+  else if (mode == 1)
+    hipLaunchKernelGGL(k_reread<1>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const char*)src, chunks,
+                       (uint32_t)passes, sink);
+  else
+    hipLaunchKernelGGL(k_reread<2>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const char*)src, chunks,
+                       (uint32_t)passes, sink);
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }

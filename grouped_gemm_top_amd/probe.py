@@ -10,7 +10,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 
 PROBE_SYMBOLS = ("moe_probe_mfma_bf16", "moe_probe_copy", "moe_probe_read", "moe_probe_mfma_fp8_layout",
-                 "moe_probe_cvt_fp8")
+                 "moe_probe_cvt_fp8", "moe_probe_reread")
 FLOP_PER_ITER_WAVE = 131072  # eight 16x16x32 (or four 32x32x16) bf16 MFMAs
 
 
@@ -32,6 +32,7 @@ def lib():
         L.moe_probe_read.argtypes = [vp, sz, i32, vp, vp]
         L.moe_probe_mfma_fp8_layout.argtypes = [vp, vp, vp, vp, i32, vp, vp]
         L.moe_probe_cvt_fp8.argtypes = [vp, i32, vp, vp]
+        L.moe_probe_reread.argtypes = [vp, sz, i32, i32, i32, vp, vp]
         for n in PROBE_SYMBOLS:
             getattr(L, n).restype = i32
         _LIB = L
@@ -109,6 +110,12 @@ def measure_peaks(reps: int = 5) -> dict:
     out["copy_gbs"] = round(best(lambda: copy(src, dst, sblocks)) / 1e9, 1)
     out["read_gbs"] = round(best(lambda: read(src, sblocks, isink)) / 1e9, 1)
     del src, dst
+    # kilobyte loads into LDS (the GEMMs' load form) of a 2 MiB buffer, 512 passes: each XCD
+    # reads its eighth of it, which stays in its L2
+    small = torch.ones(1 << 19, dtype=torch.float32, device="cuda")
+    rblocks = 2 * cus
+    rsink = torch.empty(rblocks * 256, dtype=torch.int32, device="cuda")
+    out["l2_lds_load_gbs"] = round(best(lambda: reread(small, 512, 1, rblocks, rsink)) / 1e9, 1)
     return out
 
 
@@ -129,3 +136,12 @@ def cvt_fp8(src, dst, stream=None):
     assert src.numel() == dst.numel() and src.numel() % 2 == 0
     _check(lib().moe_probe_cvt_fp8(ctypes.c_void_p(src.data_ptr()), src.numel(), ctypes.c_void_p(dst.data_ptr()),
                                    _stream(stream)), "moe_probe_cvt_fp8")
+
+
+def reread(src, passes: int, mode: int, blocks: int, sink, stream=None) -> int:
+    """Queue the re-read probe over src (cuda, contiguous, a multiple of 1 KiB); mode 0 loads
+    into registers, mode 1 into LDS.  Returns the bytes read."""
+    nb = src.numel() * src.element_size()
+    _check(lib().moe_probe_reread(ctypes.c_void_p(src.data_ptr()), nb, passes, mode, blocks,
+                                  ctypes.c_void_p(sink.data_ptr()), _stream(stream)), "moe_probe_reread")
+    return nb * passes

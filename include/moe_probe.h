@@ -50,6 +50,15 @@ int moe_probe_mfma_fp8_layout(const uint8_t* a, const uint8_t* b, const uint32_t
  * dst[i] = code of src[i], i < n; n even, dst 2-byte aligned. */
 int moe_probe_cvt_fp8(const float* src, int n, uint8_t* dst, void* stream);
 
+/* Re-read probe: reads the `bytes` bytes of src (a multiple of 1024, at most 1 GiB, 16-byte
+ * aligned) `passes` times over (1..4096) as kilobyte loads, one wavefront each, `blocks`
+ * workgroups of 256 threads (1..65536).  mode 0 loads into registers and writes each
+ * thread's XOR of the words it read to sink[blocks * 256]; mode 1 loads into LDS with
+ * buffer_load_dwordx4 ... lds (the form the GEMM kernels use) and writes 0 there; mode 2 is
+ * mode 1 with each kilobyte's 16-byte chunks taken in the lane order of the GEMMs' K-strided
+ * stages. */
+int moe_probe_reread(const void* src, size_t bytes, int passes, int mode, int blocks, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
