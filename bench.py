@@ -44,12 +44,12 @@ def kernel_work(name, wl, M, e_act, es):
         return 4.0 * M * H * I, es * (2.0 * e_act * I * H + N * H + 3.0 * M * I)
     if name == "down":
         return 2.0 * M * H * I, es * (1.0 * e_act * H * I + M * I + M * H)
-    if name == "dh":
-        if es == 2:  # bf16: the dA' GEMM writes fp32 dA'; the dSwiGLU kernel does the rest
-            return 2.0 * M * H * I, es * (1.0 * e_act * H * I + N * H) + 4.0 * M * I
-        return 2.0 * M * H * I, es * (1.0 * e_act * H * I + N * H + 5.0 * M * I) + 4.0 * M * ((I + 127) // 128)
-    if name == "dswiglu" and es == 2:  # reads dA' (fp32), G, U, w; writes dG, dU, A', dS
-        return 0.0, 4.0 * M * I + es * 5.0 * M * I + 8.0 * M
+    # dS partials per row of the dH kernel's dSwiGLU epilogue
+    n_part = 2 * ((I + 255) // 256) if es == 2 else (I + 127) // 128
+    if name == "dh":  # reads W_down, dOut rows, G, U, w; writes dG, dU, A' and the dS partials
+        return 2.0 * M * H * I, es * (1.0 * e_act * H * I + N * H + 5.0 * M * I) + 4.0 * M * (n_part + 1)
+    if name == "dswiglu":  # the ordered sum of the dS partials
+        return 0.0, 4.0 * M * n_part + 8.0 * M
     if name == "dx":
         return 4.0 * M * H * I, es * (2.0 * e_act * I * H + 2.0 * M * I + M * H)
     if name == "dwd":

@@ -835,84 +835,6 @@ __global__ __launch_bounds__(NTHR, 2) void k_grouped_gemm(Args a, const int32_t*
   }
 }
 
-// dSwiGLU of the bf16 path, one wavefront per expert row r (rows at or past M only clear dS in
-// row order).  From the row's fp32 dA' (the dH GEMM's output), its cached G, U and its routing
-// weight w ("SonicMoE" section "3 기여 ①": only [G | U] is cached; dS = <dA', A>):
-//   A = silu(G) U,  dS = <dA', A>,  dA = w dA',
-//   dG = dA U sg (1 + G (1 - sg)),  dU = dA silu(G),  A' = w A       (sg = sigmoid(G))
-// dS goes to (t, j) order through row_pair for top-k plans and stays in row order for token-
-// rounding plans; its sum runs in a fixed order.
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {  // round to nearest even
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
-}
-__global__ __launch_bounds__(256) void k_dswiglu_bf16(const float* __restrict__ dap, const uint16_t* __restrict__ hc,
-                                                      const float* __restrict__ row_w,
-                                                      const int32_t* __restrict__ offsets, int E,
-                                                      const int32_t* __restrict__ row_pair, int by_pair, int M_cap,
-                                                      int I, uint16_t* __restrict__ dh, uint16_t* __restrict__ aprime,
-                                                      float* __restrict__ ds) {
-  const int lane = threadIdx.x & 63;
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= M_cap) return;
-  const int M = offsets[E];
-  if (r >= M) {
-    if (!by_pair && lane == 0) ds[r] = 0.f;
-    return;
-  }
-  const float w = row_w[r];
-  const float* dr = dap + (size_t)r * I;
-  const uint16_t* gr = hc + (size_t)r * 2 * I;
-  uint16_t* dhr = dh + (size_t)r * 2 * I;
-  uint16_t* apr = aprime + (size_t)r * I;
-  float acc = 0.f;
-  for (int c = 8 * lane; c < I; c += 512) {  // 8 columns per lane (I is a multiple of 8)
-    const float4 d0 = *reinterpret_cast<const float4*>(dr + c);
-    const float4 d1 = *reinterpret_cast<const float4*>(dr + c + 4);
-    const uint4 gv = *reinterpret_cast<const uint4*>(gr + c);
-    const uint4 uv = *reinterpret_cast<const uint4*>(gr + I + c);
-    const float dv[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-    const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w}, uw[4] = {uv.x, uv.y, uv.z, uv.w};
-    uint32_t og[4], ou[4], oa[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float rg[2], ru[2], ra[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const float g = __uint_as_float(h ? (gw[q] & 0xFFFF0000u) : (gw[q] << 16));
-        const float u = __uint_as_float(h ? (uw[q] & 0xFFFF0000u) : (uw[q] << 16));
-        // sigmoid with the hardware exponential and reciprocal (about 1 ulp each)
-        const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g));
-        const float silu = g * sg;
-        const float act = silu * u;
-        const float d = dv[2 * q + h];
-        acc += d * act;
-        const float da = w * d;
-        rg[h] = da * u * sg * (1.0f + g * (1.0f - sg));
-        ru[h] = da * silu;
-        ra[h] = w * act;
-      }
-      og[q] = pk_bf16(rg[0], rg[1]);
-      ou[q] = pk_bf16(ru[0], ru[1]);
-      oa[q] = pk_bf16(ra[0], ra[1]);
-    }
-    *reinterpret_cast<uint4*>(dhr + c) = make_uint4(og[0], og[1], og[2], og[3]);
-    *reinterpret_cast<uint4*>(dhr + I + c) = make_uint4(ou[0], ou[1], ou[2], ou[3]);
-    *reinterpret_cast<uint4*>(apr + c) = make_uint4(oa[0], oa[1], oa[2], oa[3]);
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-  if (lane == 0) {
-    if (by_pair) {
-      const int p = row_pair[r];
-      if (p >= 0) ds[p] = acc;
-    } else {
-      ds[r] = acc;
-    }
-  }
-}
-
 // dS: ordered sum of the N-tile partials; scattered to (t, j) order through row_pair for
 // top-k plans, kept in row order for token-rounding plans.
 __global__ __launch_bounds__(256) void k_ds_reduce(const float* __restrict__ dspart, int nTN,
@@ -1019,9 +941,10 @@ hipError_t launch_gemm_fwd_mxfp8(const void* xq, const void* xs, const void* wgq
 size_t layer_bwd_ws_bytes(moe_dtype dt, int N, int M_cap, int H, int I) {
   (void)N;
   const size_t es = dt == MOE_BF16 ? 2 : 4;
-  const size_t nTN = (size_t)(I + gg::BN - 1) / gg::BN;
-  // fp32: the dH kernel's dS partials; bf16: the dH GEMM's fp32 dA'
-  const size_t part = dt == MOE_BF16 ? (size_t)M_cap * I * 4 : (size_t)M_cap * nTN * 4;
+  // the dH kernel's dS partials per row: fp32, one per 128-column N-tile; bf16, one per
+  // wavefront half (128 columns) of each 256-column N-tile
+  const size_t nP = dt == MOE_BF16 ? 2 * (size_t)((I + 255) / 256) : (size_t)((I + gg::BN - 1) / gg::BN);
+  const size_t part = (size_t)M_cap * nP * 4;
   return align256((size_t)M_cap * 2 * I * es) + align256((size_t)M_cap * I * es) +
          align256((size_t)M_cap * H * es) + align256(part) + 256;
 }
@@ -1032,8 +955,9 @@ static hipError_t layer_bwd_t(const void* dout, const void* x, const void* wg, c
                               void* dwu, void* dwd, float* ds, void* ws, hipStream_t s) {
   const size_t es = sizeof(T);
   constexpr bool BF = std::is_same<T, bf16_t>::value;
-  const int tn = BF ? 256 : gg::BN;  // N-tile width of the dH kernel (one dS partial per N-tile)
+  const int tn = BF ? 256 : gg::BN;  // N-tile width of the dH kernel
   const int nTN = (I + tn - 1) / tn;
+  const int nP = BF ? 2 * nTN : nTN;  // dS partials per row (bf16: one per 128-column half tile)
   char* w = (char*)ws;
   void* dh = w;
   w += align256((size_t)p.M_cap * 2 * I * es);
@@ -1041,8 +965,8 @@ static hipError_t layer_bwd_t(const void* dout, const void* x, const void* wg, c
   w += align256((size_t)p.M_cap * I * es);
   void* dxe = w;
   w += align256((size_t)p.M_cap * H * es);
-  float* dspart = (float*)w;  // fp32: dS partials; bf16: dA' [M_cap, I] in fp32
-  w += align256((size_t)p.M_cap * (BF ? I : nTN) * 4);
+  float* dspart = (float*)w;  // dS partials [M_cap, nP]
+  w += align256((size_t)p.M_cap * nP * 4);
 
   gg::Args a{};
   a.x = x; a.wg = wg; a.wu = wu; a.wd = wd; a.dout = dout; a.hcache = hcache;
@@ -1062,30 +986,16 @@ static hipError_t layer_bwd_t(const void* dout, const void* x, const void* wg, c
   using KDW1 = std::integral_constant<int, gg::DW1>;
   hipError_t err;
 
-  if constexpr (BF) {
-    // dA' = dOut[t] W_down^T (varlen-M GEMM, fp32 out), then the dSwiGLU kernel:
-    // dH = [dG | dU], A' = w A and dS
-    a.out0 = dspart; a.out1 = nullptr;
-    if ((err = launch(KDH{}, mt * nTN)) != hipSuccess) return err;
-    if (p.M_cap > 0) {
-      kernel_event(MOE_K_DSWIGLU, 0, s);
-      hipLaunchKernelGGL(gg::k_dswiglu_bf16, dim3((p.M_cap + 3) / 4), dim3(256), 0, s, dspart,
-                         (const uint16_t*)hcache, p.row_w, p.offsets, p.E, p.row_pair,
-                         p.kind == MOE_PLAN_TOPK ? 1 : 0, p.M_cap, I, (uint16_t*)dh, (uint16_t*)aprime, ds);
-      kernel_event(MOE_K_DSWIGLU, 1, s);
-      if ((err = hipGetLastError()) != hipSuccess) return err;
-    }
-  } else {
-    // dH epilogue kernel: dH = [dG | dU], A' = w A, dS partials; then their ordered sum
-    a.out0 = dh; a.out1 = aprime; a.dspart = dspart;
-    if ((err = launch(KDH{}, mt * nTN)) != hipSuccess) return err;
-    if (p.M_cap > 0) {
-      kernel_event(MOE_K_DSWIGLU, 0, s);
-      hipLaunchKernelGGL(gg::k_ds_reduce, dim3((p.M_cap + 255) / 256), dim3(256), 0, s, dspart, nTN, p.offsets,
-                         p.E, p.row_pair, p.kind == MOE_PLAN_TOPK ? 1 : 0, p.M_cap, ds);
-      kernel_event(MOE_K_DSWIGLU, 1, s);
-      if ((err = hipGetLastError()) != hipSuccess) return err;
-    }
+  // dA' = dOut[t] W_down^T (varlen-M GEMM) with the dSwiGLU epilogue: dH = [dG | dU],
+  // A' = w A and the dS partials; then their ordered sum
+  a.out0 = dh; a.out1 = aprime; a.dspart = dspart;
+  if ((err = launch(KDH{}, mt * nTN)) != hipSuccess) return err;
+  if (p.M_cap > 0) {
+    kernel_event(MOE_K_DSWIGLU, 0, s);
+    hipLaunchKernelGGL(gg::k_ds_reduce, dim3((p.M_cap + 255) / 256), dim3(256), 0, s, dspart, nP, p.offsets, p.E,
+                       p.row_pair, p.kind == MOE_PLAN_TOPK ? 1 : 0, p.M_cap, ds);
+    kernel_event(MOE_K_DSWIGLU, 1, s);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   // The two weight-gradient kernels run first and dX last.  The bf16 kernels store their dW
   // (805 MB in all at the headline shape) with the non-temporal policy, since no later kernel

@@ -645,24 +645,96 @@ __device__ __forceinline__ void epilogue(const Args& a, const Tile& c, f32x4 (&a
       }
     }
   } else if constexpr (KIND == DH) {
-    // dA' in fp32 for the dSwiGLU kernel that follows; each block goes through the staging
-    // area in two halves of 64 columns: 16 lanes store 256 contiguous bytes of one row, rows
-    // >= mlen lie past the descriptor's range
-    const rsrc_t ro = gg::mkr_off(a.out0, rb * I * 4, (long long)c.mlen * I * 4);
+    // The dSwiGLU epilogue: acc holds dA' = dOut[t] W_down^T for 16-row blocks of 128 i columns.
+    // With the cached [G | U] of the same rows and columns and the row's weight w:
+    //   A = silu(G) U,  dA = w dA',  dG = dA U s (1 + G (1 - s)),  dU = dA silu(G)  (s = sigmoid(G)),
+    //   A' = w A,  and this wavefront's part of dS = <dA', A> over its 128 columns.
+    // G and U come in as rows of 256 contiguous bytes (16 lanes per row) through the
+    // wavefront's 8 KB of staging (G in the first 4 KB, U in the second), are read back in the
+    // accumulator layout, and dG / dU replace them in place; A' follows in the G half.  dH =
+    // [dG | dU] and A' leave as rows of 256 bytes again.  dS partial q = 2 n-tile + wn of row r
+    // goes to dspart[r nP + q] (nP = 2 ceil(I / 256)), summed in order by the next kernel.
+    // Rows >= mlen and columns >= I lie past the descriptors' ranges: their loads read zeros
+    // and their stores are dropped.
+    const rsrc_t rhc = gg::mkr_off(a.hcache, rb * 2 * I * 2, (long long)c.mlen * 2 * I * 2);
+    const rsrc_t rdh = gg::mkr_off(a.out0, rb * 2 * I * 2, (long long)c.mlen * 2 * I * 2);
+    const rsrc_t rap = gg::mkr_off(a.out1, rb * I * 2, (long long)c.mlen * I * 2);
+    const rsrc_t rw = gg::mkr_off(a.row_w, rb * 4, (long long)c.mlen * 4);
+    const int nP = 2 * ((I + 255) / 256);
+    const rsrc_t rds = gg::mkr_off(a.dspart, rb * nP * 4, (long long)c.mlen * nP * 4);
     const int c0 = c.nt * BN + wn * 128;
+    char* sgu = st;         // G, then dG, then A'
+    char* suu = st + 4096;  // U, then dU
+    const int q = L & 15, g4 = L >> 4;
+    const int col = c0 + 8 * q;  // the 8 columns this lane moves in row-contiguous form
+    // (loading block i + 1's G and U during block i would keep 33 more registers live and
+    // pushes them into scratch, which made the epilogue twice as slow)
+    uint4 gv[4], uv[4];
+    float w = 0.f;
+    auto gu_load = [&](int i) __attribute__((always_inline)) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t m = (uint32_t)(16 * (4 * i + wm) + 4 * p + g4);
+        const uint32_t off = m * (uint32_t)(2 * I) * 2u + (uint32_t)col * 2u;
+        gv[p] = gg::bld16(rhc, col < I ? off : OOB);
+        uv[p] = gg::bld16(rhc, col < I ? off + (uint32_t)I * 2u : OOB);
+      }
+      w = __int_as_float(gg::bld4(rw, (uint32_t)(16 * (4 * i + wm) + q) * 4u));
+    };
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
+      gu_load(i);
+      const float wi = w;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        stage_write_f32(st, acc[i], h, L);
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const uint4 v = stage_read(st, p, L);
-          const uint32_t m = (uint32_t)(16 * (4 * i + wm) + 4 * p + (L >> 4));
-          const int col = c0 + 64 * h + 4 * (L & 15);
-          st16(ro, col < I ? m * (uint32_t)I * 4u + (uint32_t)col * 4u : OOB, v);
-        }
+      for (int p = 0; p < 4; ++p) {
+        const int r = 4 * p + g4;
+        *reinterpret_cast<uint4*>(sgu + r * 256 + ((q ^ r) << 4)) = gv[p];
+        *reinterpret_cast<uint4*>(suu + r * 256 + ((q ^ r) << 4)) = uv[p];
       }
+      float ds = 0.f;
+      u32x2 apk[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int o = q * 256 + (((2 * j + (g4 >> 1)) ^ q) << 4) + (g4 & 1) * 8;
+        const u32x2 G2 = *reinterpret_cast<const u32x2*>(sgu + o);
+        const u32x2 U2 = *reinterpret_cast<const u32x2*>(suu + o);
+        float rg[4], ru[4], ra[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const uint32_t gw = v < 2 ? G2.x : G2.y, uw = v < 2 ? U2.x : U2.y;
+          const float gg_ = __uint_as_float((v & 1) ? (gw & 0xFFFF0000u) : (gw << 16));
+          const float u = __uint_as_float((v & 1) ? (uw & 0xFFFF0000u) : (uw << 16));
+          const float sg = sigm(gg_);
+          const float silu = gg_ * sg;
+          const float act = silu * u;
+          const float d = acc[i][j][v];
+          ds += d * act;
+          const float da = wi * d;
+          rg[v] = da * u * sg * (1.0f + gg_ * (1.0f - sg));
+          ru[v] = da * silu;
+          ra[v] = wi * act;
+        }
+        *reinterpret_cast<u32x2*>(sgu + o) = u32x2{pk2(rg[0], rg[1]), pk2(rg[2], rg[3])};
+        *reinterpret_cast<u32x2*>(suu + o) = u32x2{pk2(ru[0], ru[1]), pk2(ru[2], ru[3])};
+        apk[j] = u32x2{pk2(ra[0], ra[1]), pk2(ra[2], ra[3])};
+      }
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t m = (uint32_t)(16 * (4 * i + wm) + 4 * p + g4);
+        const uint32_t off = m * (uint32_t)(2 * I) * 2u + (uint32_t)col * 2u;
+        st16(rdh, col < I ? off : OOB, stage_read(sgu, p, L));
+        st16(rdh, col < I ? off + (uint32_t)I * 2u : OOB, stage_read(suu, p, L));
+      }
+      stage_write_pk(sgu, apk, L);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t m = (uint32_t)(16 * (4 * i + wm) + 4 * p + g4);
+        st16(rap, col < I ? m * (uint32_t)I * 2u + (uint32_t)col * 2u : OOB, stage_read(sgu, p, L));
+      }
+      ds += __shfl_xor(ds, 16);
+      ds += __shfl_xor(ds, 32);
+      const uint32_t doff = ((uint32_t)(16 * (4 * i + wm) + q) * (uint32_t)nP + (uint32_t)(2 * c.nt + wn)) * 4u;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ds), rds, g4 == 0 ? doff : OOB, 0, 0);
     }
   } else if constexpr (KIND == DWD) {
     const rsrc_t ro = gg::mkr_off(a.out0, (long long)c.e * H * I * 2, (long long)H * I * 2);
@@ -1118,7 +1190,7 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
       // every wavefront is done with the ring: the last step's stage stages the epilogue, the
       // other takes the next tile's first step, issued before the epilogue so that its wait
       // does not include the epilogue's stores
-      char* st = s_ring + ((gs + nk - 1) & 1) * G::STGK + w * 4096;
+      char* st = s_ring + ((gs + nk - 1) & 1) * G::STGK + w * (KIND == DH ? 8192 : 4096);
       lds_barrier();
       gs += nk;
       {

@@ -359,7 +359,7 @@ moe_status moe_router_bwd(moe_dtype dt, const float* logits, const float* bias, 
 typedef enum moe_kernel_id {
   MOE_K_GATEUP = 0,      /* forward gate/up grouped GEMM + SwiGLU epilogue */
   MOE_K_DOWN = 1,        /* forward down grouped GEMM */
-  MOE_K_DH = 2,          /* backward dH kernel: bf16 the dA' grouped GEMM; fp32 with the dSwiGLU epilogue */
+  MOE_K_DH = 2,          /* backward dH kernel: the dA' grouped GEMM with the dSwiGLU epilogue */
   MOE_K_DX = 3,          /* backward dX grouped GEMM (expert rows) */
   MOE_K_DWD = 4,         /* backward dW_down varlen-K GEMM */
   MOE_K_DW1 = 5,         /* backward dW_gate / dW_up varlen-K GEMM */
@@ -368,7 +368,7 @@ typedef enum moe_kernel_id {
   MOE_K_ROUTE = 8,       /* top-k router kernel */
   MOE_K_PERMUTE = 9,     /* histogram + scan + scatter of moe_permute */
   MOE_K_ROUTE_TR_PLAN = 10, /* the token-rounding plan kernels after the router */
-  MOE_K_DSWIGLU = 11,    /* bf16: dSwiGLU, A' and dS from dA'; fp32: ordered sum of the dS partials */
+  MOE_K_DSWIGLU = 11,    /* ordered sum of the dH kernel's dS partials */
   MOE_K_ROUTER_LOGITS = 12, /* moe_router_logits */
   MOE_K_ROUTER_DZ = 13,  /* moe_router_bwd: dz from dS */
   MOE_K_ROUTER_DX = 14,  /* moe_router_bwd: dx_out = dx_in + dz W_r^T */
