@@ -797,7 +797,6 @@ __device__ __forceinline__ uint32_t vk_out(const Args& a, const Tile& c, int i, 
 //    `pst` (4 KB per block; stage_write placement); a storer stores its own blocks through
 //    its 4 KB slot `own`.
 //  part 2 (storers, after a second barrier): the partner loader's (w - 4) blocks from its `pst`.
-// An empty group's tile (zero = true) stores zeros for both and uses no LDS.
 template <int KIND>
 __device__ __forceinline__ void vk_epilogue1(const Args& a, const Tile& c, f32x4 (&acc)[4][8], int wm, int wn,
                                              int L_, int nMg, char* pst, char* own) {
@@ -834,21 +833,26 @@ __device__ __forceinline__ void vk_epilogue2(const Args& a, const Tile& c, int w
       st16_nt(ro, off, v);
     }
 }
+// The zeros of an expert without rows.  Its weight gradient (DWD: dW_down[e], DW1: dW_gate[e]
+// or dW_up[e]) is one contiguous region, so its tiles split the region into equal chunks of
+// whole kilobytes, tile (mt, nt) taking chunk (mt - seg nMg) nN + nt, and write them as plain
+// kilobyte rows (64 lanes x 16 bytes): the storers' wavefront wm the stores q = wm, wm + 4,
+// ....
 template <int KIND>
-__device__ __forceinline__ void vk_zero(const Args& a, const Tile& c, int wm, int L_, int nMg) {
+__device__ __forceinline__ void vk_zero(const Args& a, const Tile& c, int wm, int L_, int nN, int nMg) {
   int L = L_;
   asm volatile("" : "+v"(L));
   const uint4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int wn = 0; wn < 2; ++wn)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        rsrc_t ro;
-        const uint32_t off = vk_out<KIND>(a, c, i, p, wm, wn, nMg, L, ro);
-        st16_nt(ro, off, z);
-      }
+  const long long region = (long long)a.H * a.I * 2;
+  const int seg = KIND == DW1 && c.mt >= nMg;
+  const int ntl = (KIND == DWD ? (a.H + BM - 1) / BM : nMg) * nN;  // tiles per region
+  const long long kb = (region + 1023) / 1024;
+  const int ckb = (int)((kb + ntl - 1) / ntl);  // kilobytes per chunk
+  const int lt = (c.mt - seg * nMg) * nN + c.nt;
+  const rsrc_t ro = gg::mkr_off(seg ? a.out1 : a.out0, (long long)c.e * region, region);
+  const uint32_t base = (uint32_t)lt * (uint32_t)ckb * 1024u + (uint32_t)L * 16u;
+#pragma unroll 1
+  for (int q = wm; q < ckb; q += 4) st16_nt(ro, base + (uint32_t)q * 1024u, z);
 }
 
 // ------------------------------------------------------------------ fragments
@@ -1222,7 +1226,7 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
     Tile Cc;
     S.decode(a, Cc, 0);
     while (Cc.valid && Cc.nk == 0) {
-      if (!loader) vk_zero<KIND>(a, Cc, wm, L, S.nMg);
+      if (!loader) vk_zero<KIND>(a, Cc, wm, L, S.nN, S.nMg);
       S.decode(a, Cc, Cc.it + 1);
     }
     if (!Cc.valid) return;
@@ -1316,7 +1320,7 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
         for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
       S.decode(a, Cc, Cc.it + 1);
       while (Cc.valid && Cc.nk == 0) {
-        if (!loader) vk_zero<KIND>(a, Cc, wm, L, S.nMg);
+        if (!loader) vk_zero<KIND>(a, Cc, wm, L, S.nN, S.nMg);
         S.decode(a, Cc, Cc.it + 1);
       }
       if (!Cc.valid) break;
