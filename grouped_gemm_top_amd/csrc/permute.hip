@@ -6,7 +6,9 @@
 //         sort by expert id so each expert's rows are one contiguous slice, bincount
 //   [DEP] "Deep EP", section "2) Dispatch" (ragged layout needs offset/index metadata)
 //
-// A stable counting sort over the N*k (token, slot) pairs, never a comparison sort:
+// A stable counting sort over the N*k (token, slot) pairs, never a comparison sort, in two
+// launches while the token blocks are few (k_perm_hist, then k_perm_scan_scatter: every block
+// sums the whole histogram itself), else in three:
 //   k_perm_hist     per block of TB tokens: expert histogram in LDS -> bcnt[b][e]
 //   k_perm_scan     counts[e] = sum_b bcnt[b][e]; offsets = exclusive scan over e;
 //                   bbase[b][e] = offsets[e] + sum_{b'<b} bcnt[b'][e]
@@ -126,13 +128,13 @@ __global__ __launch_bounds__(1024) void k_perm_scan(const int32_t* __restrict__ 
   }
 }
 
-__global__ __launch_bounds__(kPT) void k_perm_scatter(const int32_t* __restrict__ idx, const float* __restrict__ w,
-                                                      int N, int E, int k, const int32_t* __restrict__ bbase,
-                                                      int32_t* __restrict__ row_token, float* __restrict__ row_w,
-                                                      int32_t* __restrict__ row_pair, int32_t* __restrict__ tok_ptr,
-                                                      int32_t* __restrict__ tok_rows) {
-  __shared__ uint32_t s_bits[1024 * 2];         // expert e: tokens 0-31 and 32-63 of the block
-  __shared__ uint32_t s_texp[kTB * (1024 / 32)];  // token tl: its experts, EW words of 32 ids
+// The scatter of block b's pairs (tokens 64 b .. 64 b + 63): bb[e] is the first row of expert
+// e that this block fills.  Called by every thread of the block.
+__device__ __forceinline__ void perm_scatter_block(const int32_t* __restrict__ idx, const float* __restrict__ w,
+                                                   int N, int E, int k, const int* bb, int32_t* __restrict__ row_token,
+                                                   float* __restrict__ row_w, int32_t* __restrict__ row_pair,
+                                                   int32_t* __restrict__ tok_ptr, int32_t* __restrict__ tok_rows,
+                                                   uint32_t* s_bits, uint32_t* s_texp) {
   const int EW = (E + 31) >> 5;
   for (int q = threadIdx.x; q < 2 * E; q += kPT) s_bits[q] = 0u;
   for (int q = threadIdx.x; q < kTB * EW; q += kPT) s_texp[q] = 0u;
@@ -150,7 +152,6 @@ __global__ __launch_bounds__(kPT) void k_perm_scatter(const int32_t* __restrict_
   }
   if (threadIdx.x < nt) tok_ptr[t0 + threadIdx.x] = (t0 + threadIdx.x) * k;
   __syncthreads();
-  const int32_t* bb = bbase + (size_t)blockIdx.x * E;
   for (int q = threadIdx.x; q < np; q += kPT) {
     const int e = ib[q];
     const int tl = q / k, j = q - tl * k;
@@ -180,6 +181,100 @@ __global__ __launch_bounds__(kPT) void k_perm_scatter(const int32_t* __restrict_
     for (int x = (e >> 5) + 1; x < EW; ++x) nrow += __popc(tx[x]);
     if (j >= nrow) tok_rows[(size_t)t * k + j] = -1;
   }
+}
+
+__global__ __launch_bounds__(kPT) void k_perm_scatter(const int32_t* __restrict__ idx, const float* __restrict__ w,
+                                                      int N, int E, int k, const int32_t* __restrict__ bbase,
+                                                      int32_t* __restrict__ row_token, float* __restrict__ row_w,
+                                                      int32_t* __restrict__ row_pair, int32_t* __restrict__ tok_ptr,
+                                                      int32_t* __restrict__ tok_rows) {
+  __shared__ uint32_t s_bits[1024 * 2];         // expert e: tokens 0-31 and 32-63 of the block
+  __shared__ uint32_t s_texp[kTB * (1024 / 32)];  // token tl: its experts, EW words of 32 ids
+  perm_scatter_block(idx, w, N, E, k, bbase + (size_t)blockIdx.x * E, row_token, row_w, row_pair, tok_ptr, tok_rows,
+                     s_bits, s_texp);
+}
+
+// The scan and the scatter in one launch, for plans with few blocks: every block sums the
+// whole histogram itself (counts[e] over all nb blocks and its own base over the blocks before
+// it, a pass over nb E integers), scans the counts over e, and scatters its pairs; block 0 also
+// writes counts, offsets and tok_ptr[N].  The sums are integer, so every block derives the same
+// offsets as k_perm_scan.
+__global__ __launch_bounds__(kPT) void k_perm_scan_scatter(const int32_t* __restrict__ idx,
+                                                           const float* __restrict__ w, int N, int E, int k,
+                                                           const int32_t* __restrict__ bcnt, int nb,
+                                                           int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ row_token, float* __restrict__ row_w,
+                                                           int32_t* __restrict__ row_pair, int32_t* __restrict__ tok_ptr,
+                                                           int32_t* __restrict__ tok_rows) {
+  __shared__ int s_tot[1024];
+  __shared__ int s_base[1024];
+  __shared__ int s_wave[5];
+  __shared__ uint32_t s_bits[1024 * 2];
+  __shared__ uint32_t s_texp[kTB * (1024 / 32)];
+  const int b = blockIdx.x;
+  // eight independent loads in flight per thread (the sums are integer, so their order is free)
+  auto colsum = [&](int e, int q0, int q1) __attribute__((always_inline)) {
+    int acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    int q = q0;
+    for (; q + 8 <= q1; q += 8) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc[u] += bcnt[(size_t)(q + u) * E + e];
+    }
+    for (; q < q1; ++q) acc[0] += bcnt[(size_t)q * E + e];
+    return ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+  };
+  for (int e = threadIdx.x; e < E; e += kPT) {
+    const int bef = colsum(e, 0, b);
+    s_tot[e] = bef + colsum(e, b, nb);
+    s_base[e] = bef;
+  }
+  __syncthreads();
+  // exclusive scan of the totals: thread x owns experts 4x .. 4x + 3 (E <= 1024)
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int v4[4], sum = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int e = 4 * threadIdx.x + u;
+    v4[u] = e < E ? s_tot[e] : 0;
+    sum += v4[u];
+  }
+  int x = sum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) s_wave[wv] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int q = 0; q < kPT / 64; ++q) {
+      const int v = s_wave[q];
+      s_wave[q] = run;
+      run += v;
+    }
+    s_wave[kPT / 64] = run;
+  }
+  __syncthreads();
+  int ex = s_wave[wv] + x - sum;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int e = 4 * threadIdx.x + u;
+    if (e < E) {
+      if (b == 0) {
+        counts[e] = v4[u];
+        offsets[e] = ex;
+      }
+      s_base[e] += ex;  // this thread alone touches entry e here
+    }
+    ex += v4[u];
+  }
+  if (b == 0 && threadIdx.x == 0) {
+    offsets[E] = s_wave[kPT / 64];
+    tok_ptr[N] = N * k;
+  }
+  __syncthreads();
+  perm_scatter_block(idx, w, N, E, k, s_base, row_token, row_w, row_pair, tok_ptr, tok_rows, s_bits, s_texp);
 }
 
 // Scratch of moe_permute_noalloc: a fixed device array, one copy per GPU for the life of the
@@ -225,15 +320,19 @@ hipError_t launch_perm_hist(const int32_t* idx, int N, int E, int k, int32_t* bc
   return hipGetLastError();
 }
 
-hipError_t launch_permute(const int32_t* idx, const float* w, int N, int E, int k, const moe_plan& p, void* ws,
-                          hipStream_t s) {
+// The histogram step is done (bcnt in the workspace, blocks of kTB tokens): the scan and the
+// scatter, in one launch while the blocks are few enough for every block to sum the whole
+// histogram (nb^2 E integers read in all), else in two.
+static hipError_t launch_perm_finish(const int32_t* idx, const float* w, int N, int E, int k, const moe_plan& p,
+                                     void* ws, hipStream_t s) {
   const int nb = (N + kTB - 1) / kTB;
   int32_t* bcnt = (int32_t*)ws;
   int32_t* bbase = (int32_t*)((char*)ws + ((((size_t)nb * E * 4) + 255) & ~(size_t)255));
   hipError_t err;
-  if (nb > 0) {
-    hipLaunchKernelGGL(k_perm_hist<kTB>, dim3(nb), dim3(kPT), 0, s, idx, N, E, k, bcnt);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (nb > 0 && (long long)nb * nb * E <= (1LL << 25)) {
+    hipLaunchKernelGGL(k_perm_scan_scatter, dim3(nb), dim3(kPT), 0, s, idx, w, N, E, k, bcnt, nb, p.counts,
+                       p.offsets, p.row_token, p.row_w, p.row_pair, p.tok_ptr, p.tok_rows);
+    return hipGetLastError();
   }
   hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, s, bcnt, nb, N, E, k, bbase, p.counts, p.offsets,
                      p.tok_ptr);
@@ -244,6 +343,17 @@ hipError_t launch_permute(const int32_t* idx, const float* w, int N, int E, int 
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   return hipSuccess;
+}
+
+hipError_t launch_permute(const int32_t* idx, const float* w, int N, int E, int k, const moe_plan& p, void* ws,
+                          hipStream_t s) {
+  const int nb = (N + kTB - 1) / kTB;
+  if (nb > 0) {
+    hipLaunchKernelGGL(k_perm_hist<kTB>, dim3(nb), dim3(kPT), 0, s, idx, N, E, k, (int32_t*)ws);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return launch_perm_finish(idx, w, N, E, k, p, ws, s);
 }
 
 }  // namespace moe

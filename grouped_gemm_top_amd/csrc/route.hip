@@ -19,15 +19,32 @@ constexpr int kPerLane = kMaxE / 64;
 // the softmax over the chosen k (the full-E denominator cancels); probs is the full softmax.
 // tok_norm (optional) is the sum of the chosen probs, the normaliser token rounding uses.
 // ---------------------------------------------------------------------------------------
+// Maximum over the wavefront, returned to every lane: xor-1 and xor-2 quad permutations, the
+// half-row and row mirrors (each lane then holds its 16-lane row's maximum), then the four row
+// maxima read out through SGPRs.  Exact: a maximum involves no rounding.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp_f<0xB1>(x));   // quad permutation [1,0,3,2]
+  x = fmaxf(x, dpp_f<0x4E>(x));   // quad permutation [2,3,0,1]
+  x = fmaxf(x, dpp_f<0x141>(x));  // row half mirror
+  x = fmaxf(x, dpp_f<0x140>(x));  // row mirror
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+// The routing of token t by one wavefront.  sz: the wavefront's LDS scratch (k floats, the
+// chosen logits).
 template <int PL>  // experts per lane: E <= 64 * PL
-__global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ logits,
-                                                    const float* __restrict__ bias, int N, int E, int k,
-                                                    int32_t* __restrict__ idx, float* __restrict__ w,
-                                                    float* __restrict__ probs, float* __restrict__ tok_norm) {
-  __shared__ float s_z[4][kMaxE];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + wave;
-  if (t >= N) return;  // whole wavefronts exit together; no block barrier below
+__device__ __forceinline__ void route_token(const float* __restrict__ logits, const float* __restrict__ bias, int t,
+                                            int E, int k, int32_t* __restrict__ idx, float* __restrict__ w,
+                                            float* __restrict__ probs, float* __restrict__ tok_norm, float* sz) {
+  const int lane = threadIdx.x & 63;
   const float* lt = logits + (size_t)t * E;
   // all loads first (clamped index, masked afterwards), so they are in flight together
   float z[PL];
@@ -42,37 +59,36 @@ __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ lo
   }
   float zmax = 0.f;
   for (int j = 0; j < k; ++j) {
-    float bz = 0.f;
+    // the largest available z: the lane's own maximum, then the wavefront's (row maxima with
+    // DPP moves, then the four rows through SGPRs); a lane with nothing left offers -inf
+    float lm = -__builtin_inff();
+#pragma unroll
+    for (int q = 0; q < PL; ++q)
+      if ((avail >> q) & 1u) lm = fmaxf(lm, z[q]);
+    const float bz = wave_max(lm);
+    // the lowest expert id holding it: the lowest q with a match, then the lowest lane (-0
+    // and +0 compare equal)
     int be = INT_MAX;
 #pragma unroll
-    for (int q = 0; q < PL; ++q) {
-      if ((avail >> q) & 1u) {
-        if (be == INT_MAX || z[q] > bz) {  // ascending q = ascending id: strict '>' keeps the lower id
-          bz = z[q];
-          be = lane + 64 * q;
-        }
-      }
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float oz = __shfl_xor(bz, off);
-      const int oe = __shfl_xor(be, off);
-      const bool take = oe != INT_MAX && (be == INT_MAX || oz > bz || (oz == bz && oe < be));
-      if (take) { bz = oz; be = oe; }
+    for (int q = PL - 1; q >= 0; --q) {
+      const uint64_t m = __ballot(((avail >> q) & 1u) && z[q] == bz);
+      if (m) be = 64 * q + __builtin_ctzll(m);
     }
     if ((be & 63) == lane) avail &= ~(1u << (be >> 6));
-    if (lane == 0) idx[(size_t)t * k + j] = be;
+    if (lane == 0) {
+      idx[(size_t)t * k + j] = be;
+      sz[j] = bz;
+    }
     if (j == 0) zmax = bz;
-    if (lane == 0) s_z[wave][j] = bz;
   }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   // renormalised weights: softmax over the chosen k
   float sk = 0.f;
-  for (int j = lane; j < k; j += 64) sk += expf(s_z[wave][j] - zmax);
+  for (int j = lane; j < k; j += 64) sk += expf(sz[j] - zmax);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) sk += __shfl_xor(sk, off);
-  for (int j = lane; j < k; j += 64) w[(size_t)t * k + j] = expf(s_z[wave][j] - zmax) / sk;
+  for (int j = lane; j < k; j += 64) w[(size_t)t * k + j] = expf(sz[j] - zmax) / sk;
   if (probs || tok_norm) {
     float ez[PL];
     float sa = 0.f;
@@ -92,11 +108,23 @@ __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ lo
       // sum of the chosen probabilities, in slot order, from the same fp32 values as probs
       if (lane == 0) {
         float s = 0.f;
-        for (int j = 0; j < k; ++j) s += expf(s_z[wave][j] - zmax) / sa;
+        for (int j = 0; j < k; ++j) s += expf(sz[j] - zmax) / sa;
         tok_norm[t] = s;
       }
     }
   }
+}
+
+template <int PL>
+__global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ logits,
+                                                    const float* __restrict__ bias, int N, int E, int k,
+                                                    int32_t* __restrict__ idx, float* __restrict__ w,
+                                                    float* __restrict__ probs, float* __restrict__ tok_norm) {
+  __shared__ float s_z[4][kMaxE];
+  const int wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= N) return;  // whole wavefronts exit together; no block barrier below
+  route_token<PL>(logits, bias, t, E, k, idx, w, probs, tok_norm, s_z[wave]);
 }
 
 hipError_t launch_route_topk(const float* logits, const float* bias, int N, int E, int k, int32_t* idx,

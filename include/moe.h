@@ -366,7 +366,7 @@ typedef enum moe_kernel_id {
   MOE_K_COMBINE = 6,     /* weighted combine (moe_unpermute_combine) */
   MOE_K_DX_COMBINE = 7,  /* unweighted combine of dX rows inside moe_layer_bwd */
   MOE_K_ROUTE = 8,       /* top-k router kernel */
-  MOE_K_PERMUTE = 9,     /* histogram + scan + scatter of moe_permute */
+  MOE_K_PERMUTE = 9,     /* moe_permute: histogram, then scan + scatter (one kernel while the blocks are few) */
   MOE_K_ROUTE_TR_PLAN = 10, /* the token-rounding plan kernels after the router */
   MOE_K_DSWIGLU = 11,    /* ordered sum of the dH kernel's dS partials */
   MOE_K_ROUTER_LOGITS = 12, /* moe_router_logits */
