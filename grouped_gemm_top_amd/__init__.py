@@ -400,7 +400,8 @@ def router_bwd(logits, topk_idx, plan: Plan, ds, x, w_r, bias=None, dx_in=None, 
         dbias = dbias if dbias is not None else torch.empty((E,), dtype=torch.float32, device=dev)
     else:
         dbias = None
-    nb = workspace_bytes(OP_ROUTER_BWD, dt, plan.N, plan.E, plan.k, H, 8, 0) if (want_dw or want_dbias) else 0
+    nb = workspace_bytes(OP_ROUTER_BWD, dt, plan.N, plan.E, plan.k, H, 8, 0) if (want_dx or want_dw or want_dbias) \
+        else 0
     ws = _ws(nb, dev, ws) if nb else None
     _check(lib().moe_router_bwd(dt, _ptr(logits), _ptr(bias), _ptr(topk_idx), plan.c, _ptr(ds), _ptr(x), _ptr(w_r),
                                 H, _ptr(dx_in), _ptr(dx_out), _ptr(dlogits), _ptr(dw_r), _ptr(dbias), _ptr(ws), nb,

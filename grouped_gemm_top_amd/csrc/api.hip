@@ -156,10 +156,10 @@ size_t moe_workspace_bytes(moe_op op, moe_dtype dt, int32_t N, int32_t E, int32_
       return moe::layer_bwd_ws_bytes(dt, N, M_cap, H, I);
     case MOE_OP_ROUTER_BWD:
       if (check_dtype(dt) != MOE_OK || H < 1) return 0;
-      return moe::router_bwd_ws_bytes(N, H, E);
+      return moe::router_bwd_ws_bytes(dt, N, H, E);
     case MOE_OP_ROUTER_LOGITS:
       if (check_dtype(dt) != MOE_OK || H < 1) return 0;
-      return moe::router_logits_ws_bytes(N, H, E);
+      return moe::router_logits_ws_bytes(dt, N, H, E);
     case MOE_OP_GEMM_FWD_MXFP8:
       if (H < 32 || I < 32 || H % 32 || I % 32 || M_cap < 0) return 0;
       return moe::gemm_fwd_mxfp8_ws_bytes(M_cap, I);
@@ -391,9 +391,10 @@ moe_status moe_router_logits(moe_dtype dt, const void* x, const float* w_r, cons
   REQUIRE(N >= 0, MOE_EINVAL, "N must be >= 0 (got %d)", N);
   REQUIRE(E >= 1 && E <= 1024, MOE_EINVAL, "E must be in [1, 1024] (got %d)", E);
   REQUIRE(H >= 1, MOE_EINVAL, "H must be >= 1 (got %d)", H);
-  REQUIRE((int64_t)N * H < ((int64_t)1 << 40) && (int64_t)N * E < ((int64_t)1 << 40), MOE_EINVAL, "N too large");
+  REQUIRE((int64_t)N * (H + 8) * 2 <= kDescBytes && (int64_t)(H + 1) * (N + 8) * 2 <= kDescBytes, MOE_EUNSUPPORTED,
+          "N*H too large for one router call (N=%d, H=%d: the operand planes exceed 2 GiB)", N, H);
   REQUIRE(N == 0 || (x && w_r && logits), MOE_EINVAL, "NULL x/w_r/logits");
-  const size_t need = moe::router_logits_ws_bytes(N, H, E);
+  const size_t need = moe::router_logits_ws_bytes(dt, N, H, E);
   REQUIRE(ws_bytes >= need, MOE_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   REQUIRE(ws != nullptr, MOE_EINVAL, "NULL workspace");
   return hip_status(moe::launch_router_logits(dt, x, w_r, bias, N, H, E, logits, ws, (hipStream_t)stream),
@@ -414,8 +415,10 @@ moe_status moe_router_bwd(moe_dtype dt, const float* logits, const float* bias, 
   REQUIRE(N == 0 || plan->M_cap == 0 || ds, MOE_EINVAL, "NULL ds");
   REQUIRE(!dx_out || (dx_in && w_r), MOE_EINVAL, "dx_out needs dx_in and w_r");
   REQUIRE(!(dw_r || dbias) || N == 0 || x, MOE_EINVAL, "dw_r / dbias need x");
-  if (dw_r || dbias) {
-    const size_t need = moe::router_bwd_ws_bytes(N, H, plan->E);
+  REQUIRE((int64_t)N * (H + 8) * 2 <= kDescBytes && (int64_t)(H + 1) * (N + 8) * 2 <= kDescBytes, MOE_EUNSUPPORTED,
+          "N*H too large for one router call (N=%d, H=%d: the operand planes exceed 2 GiB)", N, H);
+  if (dx_out || dw_r || dbias) {
+    const size_t need = moe::router_bwd_ws_bytes(dt, N, H, plan->E);
     REQUIRE(ws_bytes >= need, MOE_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
     REQUIRE(ws != nullptr, MOE_EINVAL, "NULL workspace");
   }

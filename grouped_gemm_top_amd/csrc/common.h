@@ -110,8 +110,17 @@ hipError_t launch_gemm_fwd_mxfp8(const void* xq, const void* xs, const void* wgq
                                  void* hcache, void* y, void* ws, hipStream_t s);
 hipError_t launch_gemm_fwd(moe_dtype dt, const void* x, const void* wg, const void* wu, const void* wd, int H,
                            int I, const moe_plan& p, void* hcache, void* y, void* ws, hipStream_t s);
-size_t router_bwd_ws_bytes(int N, int H, int E);
-size_t router_logits_ws_bytes(int N, int H, int E);
+size_t router_bwd_ws_bytes(moe_dtype dt, int N, int H, int E);
+size_t router_logits_ws_bytes(moe_dtype dt, int N, int H, int E);
+// the router's products on the matrix cores (router_mm.hip)
+size_t router_logits_mm_ws_bytes(moe_dtype dt, int N, int H, int E);
+size_t router_bwd_mm_ws_bytes(moe_dtype dt, int N, int H, int E);
+hipError_t launch_router_logits_mm(moe_dtype dt, const void* x, const float* wr, const float* bias, int N, int H,
+                                   int E, float* logits, void* ws, float** part, int* S, hipStream_t s);
+hipError_t launch_router_dx_mm(moe_dtype dt, const float* dlogits, const float* wr, int N, int H, int E,
+                               const void* dx_in, void* dx_out, void* ws, hipStream_t s);
+hipError_t launch_router_dw_mm(moe_dtype dt, const void* x, const float* dlogits, int N, int H, int E, void* ws,
+                               float** part, int* S, hipStream_t s);
 hipError_t launch_router_logits(moe_dtype dt, const void* x, const float* wr, const float* bias, int N, int H, int E,
                                 float* logits, void* ws, hipStream_t s);
 hipError_t launch_router_bwd(moe_dtype dt, const float* logits, const float* bias, const int32_t* idx,

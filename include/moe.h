@@ -314,8 +314,11 @@ moe_status moe_layer_bwd(moe_dtype dt, const void* dout, const void* x, const vo
  * score is linear in the hidden state:
  *   logits[t,e] = sum_h x[t,h] * w_r[h,e]  (+ bias[e] when bias is not NULL)
  * accumulated in fp32 in a fixed order (the h range is cut into slices whose partial sums are
- * added in slice order; bitwise reproducible).  x [N,H] of dtype dt; w_r fp32 [H,E]; bias
- * fp32 [E] or NULL; logits fp32 [N,E] (written).  Requires 1 <= E <= 1024, H >= 1.
+ * added in slice order; bitwise reproducible).  It runs on the bf16 matrix instructions with
+ * each fp32 operand split exactly into three bf16 parts (v = hi + mid + lo), dropping only the
+ * part products below 2^-24 of the leading one: fp32 accuracy.  x [N,H] of dtype dt; w_r fp32
+ * [H,E]; bias fp32 [E] or NULL; logits fp32 [N,E] (written).  Requires 1 <= E <= 1024,
+ * H >= 1, and (N+8)*H*2 and (H+1)*(N+8)*2 below 2 GiB (else MOE_EUNSUPPORTED).
  * Workspace: moe_workspace_bytes(MOE_OP_ROUTER_LOGITS, dt, N, E, 1, H, 0, 0).
  */
 moe_status moe_router_logits(moe_dtype dt, const void* x, const float* w_r, const float* bias, int32_t N,
@@ -338,8 +341,9 @@ moe_status moe_router_logits(moe_dtype dt, const void* x, const float* w_r, cons
  * rounding and capacity plans, row order), the layout moe_layer_bwd writes.  logits, dlogits fp32 [N,E]; bias
  * fp32 [E] or NULL; topk_idx int32 [N,k]; x, dx_in, dx_out [N,H] of dtype dt (dx_out may be
  * dx_in: in place); w_r fp32 [H,E]; dw_r fp32 [H,E]; dbias fp32 [E].  Everything is written
- * fresh, in a fixed order (bitwise reproducible).  Workspace: moe_workspace_bytes(
- * MOE_OP_ROUTER_BWD, dt, N, E, k, H, 0, 0) when dw_r or dbias is requested, else none.
+ * fresh, in a fixed order (bitwise reproducible); the two products run like moe_router_logits'
+ * (split bf16 parts, fp32 accuracy; the same size limit).  Workspace: moe_workspace_bytes(
+ * MOE_OP_ROUTER_BWD, dt, N, E, k, H, 0, 0) when dx_out, dw_r or dbias is requested, else none.
  */
 moe_status moe_router_bwd(moe_dtype dt, const float* logits, const float* bias, const int32_t* topk_idx,
                           const moe_plan* plan, const float* ds, const void* x, const float* w_r, int32_t H,

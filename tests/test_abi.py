@@ -60,9 +60,19 @@ def test_workspace_bytes(L):
         assert L.moe_workspace_bytes(op, G.MOE_BF16, 4096, 128, 0, 2048, 512, 32768) == 0  # k = 0
     assert L.moe_workspace_bytes(G.OP_GEMM_FWD, G.MOE_BF16, 64, 8, 2, 60, 32, 128) == 0     # H % 8
     assert L.moe_workspace_bytes(G.OP_LAYER_BWD, 9, 64, 8, 2, 64, 32, 128) == 0            # dtype
-    # the router backward's workspace holds the sliced dW_r / dbias partial sums
-    assert L.moe_workspace_bytes(G.OP_ROUTER_BWD, G.MOE_BF16, 4096, 128, 8, 2048, 0, 0) >= 2049 * 128 * 4
+    # the router backward's workspace holds the operand planes (three bf16 parts of dlogits
+    # and W_r, x^T with a row of ones, dlogits^T) and the sliced dW_r / dbias partial sums
+    need = (3 * 4096 * 128 + 3 * 2048 * 128 + 2049 * 4096 + 3 * 128 * 4096) * 2 + 2049 * 128 * 4
+    assert L.moe_workspace_bytes(G.OP_ROUTER_BWD, G.MOE_BF16, 4096, 128, 8, 2048, 0, 0) >= need
+    # the logits' workspace holds W_r^T's three parts (and x's for fp32 x)
+    assert L.moe_workspace_bytes(G.OP_ROUTER_LOGITS, G.MOE_BF16, 4096, 128, 1, 2048, 8, 0) >= 3 * 128 * 2048 * 2
+    assert (L.moe_workspace_bytes(G.OP_ROUTER_LOGITS, G.MOE_F32, 4096, 128, 1, 2048, 8, 0)
+            >= 3 * 128 * 2048 * 2 + 3 * 4096 * 2048 * 2)
     assert L.moe_workspace_bytes(G.OP_ROUTER_BWD, 9, 4096, 128, 8, 2048, 0, 0) == 0         # dtype
+    # no tokens: still a valid query (the sizing must not divide by the empty tile count)
+    for op in (G.OP_ROUTER_BWD, G.OP_ROUTER_LOGITS):
+        for dt in (G.MOE_BF16, G.MOE_F32):
+            assert L.moe_workspace_bytes(op, dt, 0, 128, 8, 2048, 8, 0) > 0
     # forward workspace holds the activation A [M_cap, I]
     assert L.moe_workspace_bytes(G.OP_GEMM_FWD, G.MOE_BF16, 4096, 128, 8, 2048, 512, 32768) >= 32768 * 512 * 2
 
