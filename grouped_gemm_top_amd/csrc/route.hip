@@ -188,8 +188,15 @@ __global__ __launch_bounds__(1024) void k_tr_sizes(const int32_t* __restrict__ b
   const int e = threadIdx.x;
   int r = 0;
   if (e < E) {
-    int c = 0;
-    for (int b = 0; b < nb; ++b) c += bcnt[(size_t)b * E + e];
+    // eight independent loads in flight (integer sums: the order is free)
+    int cc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    int b = 0;
+    for (; b + 8 <= nb; b += 8) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) cc[u] += bcnt[(size_t)(b + u) * E + e];
+    }
+    for (; b < nb; ++b) cc[0] += bcnt[(size_t)b * E + e];
+    const int c = ((cc[0] + cc[1]) + (cc[2] + cc[3])) + ((cc[4] + cc[5]) + (cc[6] + cc[7]));
     if (cap) {
       r = c < param ? c : param;
     } else {
@@ -246,6 +253,7 @@ __global__ __launch_bounds__(1024) void k_tr_select(const uint64_t* __restrict__
                                                     int32_t* __restrict__ row_of, int32_t* __restrict__ row_token,
                                                     float* __restrict__ row_w, int32_t* __restrict__ row_pair) {
   __shared__ int s_hist[256];
+  __shared__ int s_whist[16][256];  // per-wavefront histograms: keys crowd into a few bins
   __shared__ int s_wave[17];
   __shared__ unsigned long long s_prefix;
   __shared__ int s_remaining;
@@ -260,12 +268,23 @@ __global__ __launch_bounds__(1024) void k_tr_select(const uint64_t* __restrict__
     uint64_t mask = 0ull;
     for (int pass = 0; pass < 8; ++pass) {
       const int shift = 56 - 8 * pass;
-      if (threadIdx.x < 256) s_hist[threadIdx.x] = 0;
+      {
+        int* wh = &s_whist[0][0];
+        for (int q = threadIdx.x; q < 16 * 256; q += 1024) wh[q] = 0;
+      }
       __syncthreads();
       const uint64_t prefix = s_prefix;
+      int* myh = s_whist[threadIdx.x >> 6];
       for (int t = threadIdx.x; t < N; t += 1024) {
         const uint64_t key = ke[t];
-        if ((key & mask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], 1);
+        if ((key & mask) == prefix) atomicAdd(&myh[(key >> shift) & 255u], 1);
+      }
+      __syncthreads();
+      if (threadIdx.x < 256) {
+        int h = 0;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) h += s_whist[q][threadIdx.x];
+        s_hist[threadIdx.x] = h;
       }
       __syncthreads();
       // the bin holding the rem-th largest key: thread q takes bin 255 - q, so its exclusive
@@ -311,6 +330,18 @@ __global__ __launch_bounds__(1024) void k_tr_select(const uint64_t* __restrict__
   }
 }
 
+// the kept rows of token t among experts [e0, e1), eight loads in flight
+__device__ __forceinline__ int tr_count_rows(const int32_t* __restrict__ row_of, int N, int t, int e0, int e1) {
+  int cc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  int e = e0;
+  for (; e + 8 <= e1; e += 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) cc[u] += row_of[(size_t)(e + u) * N + t] >= 0;
+  }
+  for (; e < e1; ++e) cc[0] += row_of[(size_t)e * N + t] >= 0;
+  return ((cc[0] + cc[1]) + (cc[2] + cc[3])) + ((cc[4] + cc[5]) + (cc[6] + cc[7]));
+}
+
 // Token-major row lists from row_of [E, N].  One block per 64 tokens; thread (g, tl) covers
 // token t0 + tl and the experts of quarter g (e in [g E/4, (g+1) E/4)), so every load reads 64
 // consecutive tokens of one expert.
@@ -320,25 +351,39 @@ __global__ __launch_bounds__(256) void k_tr_tokcount(const int32_t* __restrict__
   const int tl = threadIdx.x & 63, g = threadIdx.x >> 6;
   const int t = blockIdx.x * 64 + tl;
   const int e0 = g * E / 4, e1 = (g + 1) * E / 4;
-  int c = 0;
-  if (t < N)
-    for (int e = e0; e < e1; ++e) c += row_of[(size_t)e * N + t] >= 0;
-  s_c[g][tl] = c;
+  s_c[g][tl] = t < N ? tr_count_rows(row_of, N, t, e0, e1) : 0;
   __syncthreads();
   if (g == 0 && t < N) tcount[t] = s_c[0][tl] + s_c[1][tl] + s_c[2][tl] + s_c[3][tl];
 }
 
-// exclusive scan of tcount[0..N) into tok_ptr[0..N]; one block of 1024 threads
+// exclusive scan of tcount[0..N) into tok_ptr[0..N]; one block of 1024 threads over segments of
+// 16384 tokens: the segment goes through LDS (coalesced loads and stores), thread x scans its 16
+// consecutive tokens x 16 .. x 16 + 15 there, and one block scan joins the threads
 __global__ __launch_bounds__(1024) void k_scan_tokens(const int32_t* __restrict__ tcount, int N,
                                                       int32_t* __restrict__ tok_ptr) {
+  __shared__ int s_seg[16384 + 1024];
   __shared__ int s_wave[17];
   int run = 0;
-  for (int base = 0; base < N; base += 1024) {
-    const int t = base + threadIdx.x;
-    const int v = t < N ? tcount[t] : 0;
+  for (int base = 0; base < N; base += 16384) {
+    const int n = min(16384, N - base);
+    // element q at q + q / 16, so that the 16 runs of a wavefront's lanes fall in distinct banks
+    for (int q = threadIdx.x; q < 16384; q += 1024) s_seg[q + (q >> 4)] = q < n ? tcount[base + q] : 0;
+    __syncthreads();
+    int* my = s_seg + 17 * threadIdx.x;
+    int sum = 0;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) sum += my[u];
     int total;
-    const int ex = block_excl_scan_1024(v, s_wave, &total);
-    if (t < N) tok_ptr[t] = run + ex;
+    int ex = run + block_excl_scan_1024(sum, s_wave, &total);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int v = my[u];
+      my[u] = ex;
+      ex += v;
+    }
+    __syncthreads();
+    for (int q = threadIdx.x; q < n; q += 1024) tok_ptr[base + q] = s_seg[q + (q >> 4)];
+    __syncthreads();
     run += total;
   }
   if (threadIdx.x == 0) tok_ptr[N] = run;
@@ -353,15 +398,21 @@ __global__ __launch_bounds__(256) void k_tr_tokfill(const int32_t* __restrict__ 
   const int tl = threadIdx.x & 63, g = threadIdx.x >> 6;
   const int t = blockIdx.x * 64 + tl;
   const int e0 = g * E / 4, e1 = (g + 1) * E / 4;
-  int c = 0;
-  if (t < N)
-    for (int e = e0; e < e1; ++e) c += row_of[(size_t)e * N + t] >= 0;
-  s_c[g][tl] = c;
+  s_c[g][tl] = t < N ? tr_count_rows(row_of, N, t, e0, e1) : 0;
   __syncthreads();
   if (t >= N) return;
   int p = tok_ptr[t];
   for (int q = 0; q < g; ++q) p += s_c[q][tl];
-  for (int e = e0; e < e1; ++e) {
+  int e = e0;
+  for (; e + 8 <= e1; e += 8) {
+    int r[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) r[u] = row_of[(size_t)(e + u) * N + t];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (r[u] >= 0) tok_rows[p++] = r[u];
+  }
+  for (; e < e1; ++e) {
     const int r = row_of[(size_t)e * N + t];
     if (r >= 0) tok_rows[p++] = r;
   }
