@@ -71,8 +71,9 @@ def layer_bytes(wl, M, e_act, es):
 
 def load_traffic(name, workload):
     """HBM bytes per launch of kernel `name`, from the rocprofv3 FETCH_SIZE / WRITE_SIZE passes
-    summarised in profiles/traffic_<workload>.txt.  Returned only while the kernel's source file
-    still hashes to the value recorded beside the counters; otherwise None."""
+    summarised in profiles/traffic_<workload>.txt.  Returned only while the kernel's source files
+    (comma-separated, hashed in order) still hash to the value recorded beside the counters;
+    otherwise None."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
     if not os.path.exists(path):
@@ -82,11 +83,13 @@ def load_traffic(name, workload):
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    src = os.path.join(ROOT, "grouped_gemm_top_amd", "csrc", kv.get(f"{name}.source", "gemm.hip"))
-    if not os.path.exists(src):
-        return None
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    if kv.get(f"{name}.source_sha") != sha:
+    h = hashlib.sha256()
+    for f in kv.get(f"{name}.source", "gemm.hip").split(","):
+        src = os.path.join(ROOT, "grouped_gemm_top_amd", "csrc", f.strip())
+        if not os.path.exists(src):
+            return None
+        h.update(open(src, "rb").read())
+    if kv.get(f"{name}.source_sha") != h.hexdigest()[:16]:
         return None
     try:
         return float(kv[f"{name}.hbm_bytes_per_launch"])
