@@ -1006,7 +1006,10 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
     };
     if constexpr (KIND == DH) {
       // (fewer live fragments, for the register budget of the dSwiGLU epilogue) all A
-      // fragments first, then the B fragments one column block ahead
+      // fragments first, then the B fragments one column block ahead.  Every row block is
+      // computed, also those past the tile's rows (zeros, never stored): in this order the
+      // row-block test becomes a branch around each MFMA, which costs more than the MFMAs
+      // it saves.
       bf16x8 fa[G::MI];
 #pragma unroll
       for (int i = 0; i < G::MI; ++i) fa[i] = frag_a(i);
@@ -1016,8 +1019,7 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
         bf16x8 fn;
         if (j + 1 < 8) fn = frag_b(j + 1);
 #pragma unroll
-        for (int i = 0; i < G::MI; ++i)
-          if (i == 0 || nb > 64 * i) acc[i][j] = mma(fb, fa[i], acc[i][j]);
+        for (int i = 0; i < G::MI; ++i) acc[i][j] = mma(fb, fa[i], acc[i][j]);
         if (j + 1 < 8) fb = fn;
       }
     } else {
