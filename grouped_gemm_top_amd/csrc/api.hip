@@ -235,8 +235,7 @@ moe_status moe_route_token_rounding(const float* logits, const float* bias, int3
   REQUIRE(ws_bytes >= need, MOE_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   REQUIRE(ws != nullptr, MOE_EINVAL, "NULL workspace");
   // the token normaliser sits right after the block histogram in the workspace
-  const size_t nb = ((size_t)N + 255) / 256;
-  float* tok_norm = (float*)((char*)ws + (((nb * E * 4) + 255) & ~(size_t)255));
+  float* tok_norm = moe::tr_tok_norm(ws, N, E);
   hipStream_t s = (hipStream_t)stream;
   moe::kernel_event(MOE_K_ROUTE, 0, s);
   hipError_t e = moe::launch_route_topk(logits, bias, N, E, k, topk_idx, topk_w, probs, tok_norm, s);
@@ -264,8 +263,7 @@ moe_status moe_route_capacity(const float* logits, const float* bias, int32_t N,
   const size_t need = moe::tr_ws_bytes(N, E);
   REQUIRE(ws_bytes >= need, MOE_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   REQUIRE(ws != nullptr, MOE_EINVAL, "NULL workspace");
-  const size_t nb = ((size_t)N + 255) / 256;
-  float* tok_norm = (float*)((char*)ws + (((nb * E * 4) + 255) & ~(size_t)255));
+  float* tok_norm = moe::tr_tok_norm(ws, N, E);
   hipStream_t s = (hipStream_t)stream;
   moe::kernel_event(MOE_K_ROUTE, 0, s);
   hipError_t e = moe::launch_route_topk(logits, bias, N, E, k, topk_idx, topk_w, probs, tok_norm, s);

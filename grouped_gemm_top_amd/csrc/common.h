@@ -94,6 +94,7 @@ hipError_t permute_scratch(void** out);  // device address of the no-alloc permu
 hipError_t launch_permute(const int32_t* idx, const float* w, int N, int E, int k, const moe_plan& p,
                           void* ws, hipStream_t s);
 size_t tr_ws_bytes(int N, int E);
+float* tr_tok_norm(void* ws, int N, int E);  // where the plan's workspace holds the token normalisers
 // cap = 0: token rounding with granule param; cap = 1: capacity plan with capacity param, keys with
 // (use_p = 1) or without (0) the score, row weights from topk_w
 hipError_t launch_token_round(const int32_t* idx, const float* probs, const float* tok_norm, const float* topk_w,

@@ -313,10 +313,10 @@ size_t permute_ws_bytes(int N, int E) {
   return 2 * (((nb * E * 4) + 255) & ~(size_t)255) + 256;
 }
 
-// histogram over blocks of 256 tokens (the token-rounding plan's layout: bcnt[ceil(N/256)][E])
+// histogram over blocks of 64 tokens (the token-rounding plan's layout: bcnt[ceil(N/64)][E])
 hipError_t launch_perm_hist(const int32_t* idx, int N, int E, int k, int32_t* bcnt, hipStream_t s) {
-  const int nb = (N + 255) / 256;
-  hipLaunchKernelGGL(k_perm_hist<256>, dim3(nb), dim3(kPT), 0, s, idx, N, E, k, bcnt);
+  const int nb = (N + kTB - 1) / kTB;
+  hipLaunchKernelGGL(k_perm_hist<kTB>, dim3(nb), dim3(kPT), 0, s, idx, N, E, k, bcnt);
   return hipGetLastError();
 }
 
