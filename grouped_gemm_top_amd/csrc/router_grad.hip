@@ -23,14 +23,28 @@ namespace rg {
 
 constexpr int NT = 256;
 
+// sum over z < S of part[z * n + i], added in slice order, eight loads in flight
+__device__ __forceinline__ float slice_sum(const float* __restrict__ part, int S, size_t n, size_t i) {
+  float s = 0.f;
+  int z = 0;
+  for (; z + 8 <= S; z += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = part[(size_t)(z + u) * n + i];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; z < S; ++z) s += part[(size_t)z * n + i];
+  return s;
+}
+
 // dW_r [H,E] and dbias [E] from S partial slices [S, H+1, E] (row H holds the bias sums),
 // summed in slice order.
 __global__ __launch_bounds__(NT) void k_dwr_reduce(const float* __restrict__ part, int S, int H, int E,
                                                    float* __restrict__ dwr, float* __restrict__ dbias) {
   const size_t n = (size_t)(H + 1) * E;
   for (size_t i = (size_t)blockIdx.x * NT + threadIdx.x; i < n; i += (size_t)gridDim.x * NT) {
-    float s = 0.f;
-    for (int z = 0; z < S; ++z) s += part[(size_t)z * n + i];
+    const float s = slice_sum(part, S, n, i);
     if (i < (size_t)H * E) {
       if (dwr) dwr[i] = s;
     } else if (dbias) {
@@ -44,8 +58,7 @@ __global__ __launch_bounds__(NT) void k_logits_reduce(const float* __restrict__ 
                                                       const float* __restrict__ bias, float* __restrict__ logits) {
   const size_t n = (size_t)N * E;
   for (size_t i = (size_t)blockIdx.x * NT + threadIdx.x; i < n; i += (size_t)gridDim.x * NT) {
-    float s = 0.f;
-    for (int z = 0; z < S; ++z) s += part[(size_t)z * n + i];
+    const float s = slice_sum(part, S, n, i);
     logits[i] = bias ? s + bias[i % E] : s;
   }
 }
@@ -70,10 +83,13 @@ __device__ __forceinline__ float wave_max(float v) {
 __global__ __launch_bounds__(256) void k_router_dz(const float* __restrict__ logits, const float* __restrict__ bias,
                                                     const int32_t* __restrict__ idx, moe_plan p,
                                                     const float* __restrict__ ds, float* __restrict__ dz) {
-  extern __shared__ float s_rows[];
+  extern __shared__ float s_rows[];  // four rows of E, then offsets[0 .. E]
   const int L = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wv;
   const int N = p.N, E = p.E, k = p.k;
+  int* s_off = reinterpret_cast<int*>(s_rows + 4 * E);
+  for (int q = threadIdx.x; q <= E; q += 256) s_off[q] = p.offsets[q];
+  __syncthreads();
   if (t >= N) return;
   float* row = s_rows + (size_t)wv * E;
   for (int m = L; m < E; m += 64) row[m] = 0.f;
@@ -102,7 +118,7 @@ __global__ __launch_bounds__(256) void k_router_dz(const float* __restrict__ log
     int lo = 0, hi = E;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (p.offsets[mid] <= r) lo = mid; else hi = mid;
+      if (s_off[mid] <= r) lo = mid; else hi = mid;
     }
     const float d = p.kind == MOE_PLAN_TOPK ? ds[p.row_pair[r]] : ds[r];
     const float v = d * p.row_w[r];
@@ -158,7 +174,7 @@ hipError_t launch_router_bwd(moe_dtype dt, const float* logits, const float* bia
     return hipGetLastError();
   }
   kernel_event(MOE_K_ROUTER_DZ, 0, s);
-  hipLaunchKernelGGL(rg::k_router_dz, dim3((unsigned)((N + 3) / 4)), dim3(256), (size_t)4 * E * 4, s, logits, bias,
+  hipLaunchKernelGGL(rg::k_router_dz, dim3((unsigned)((N + 3) / 4)), dim3(256), (size_t)(5 * E + 1) * 4, s, logits, bias,
                      idx, p, ds, dlogits);
   kernel_event(MOE_K_ROUTER_DZ, 1, s);
   hipError_t e = hipGetLastError();

@@ -11,7 +11,8 @@
 // A bf16 x is its own single part.  Part products whose two indices add up to more than 2
 // (at most 2^-24 of the leading term each) are left out, so an fp32 x fp32 product takes six
 // MFMA terms and a bf16 x fp32 one three; the error is then that of an fp32 dot product in
-// another summation order.
+// another summation order.  The dx product of a bf16 layer, whose result is rounded to bf16,
+// takes two parts a side and the three products of index sum <= 1.
 //
 // Operands reach the GEMM as "planes": bf16 parts [S][rows][ld], K-contiguous (row r holds
 // the K values of output row / column r), made by two small passes that split and, where the
@@ -44,7 +45,8 @@ __device__ __forceinline__ void split3(float v, bf16_t& h, bf16_t& m, bf16_t& l)
 }
 
 // Planes from a K-contiguous source: src[r * ld + k] (r < R, k < K) -> dst[s][r][k], row length
-// Kp (a multiple of 8, >= K; entries k >= K are zero).  S = 1 copies (bf16 source), S = 3 splits.
+// Kp (a multiple of 8, >= K; entries k >= K are zero).  S = 1 copies (bf16 source), S = 3 splits,
+// S = 2 keeps the first two parts (16 significant bits).
 template <typename T, int S>
 __global__ __launch_bounds__(NT) void k_plane_kc(const T* __restrict__ src, int R, int K, long long ld,
                                                  bf16_t* __restrict__ dst, long long pstride, int Kp) {
@@ -60,7 +62,11 @@ __global__ __launch_bounds__(NT) void k_plane_kc(const T* __restrict__ src, int 
     if constexpr (S == 1) {
       o[0][u] = f32_to_bf16(v);
     } else {
-      split3(v, o[0][u], o[1][u], o[2][u]);
+      bf16_t h, m, l;
+      split3(v, h, m, l);
+      o[0][u] = h;
+      o[1][u] = m;
+      if constexpr (S == 3) o[2][u] = l;
     }
   }
 #pragma unroll
@@ -69,40 +75,67 @@ __global__ __launch_bounds__(NT) void k_plane_kc(const T* __restrict__ src, int 
 }
 
 // Planes from a source laid out the other way: src[k * ld + r] (k < K, r < R) -> dst[s][r][k],
-// row length Kp (zero for k >= K), through a 32 x 32 LDS tile.  ones: one more row, r = R,
-// of ones (part 0; the other parts zero) for k < K.
+// row length Kp (zero for k >= K), through an LDS tile of 64 k x RT r (RT = 64 for bf16
+// sources, 32 for fp32 ones: 8 KB of source either way): 16-byte loads along r (where ld and
+// src allow them) and 16-byte stores along k.  ones: one more row, r = R, of ones (part 0; the
+// other parts zero) for k < K.
+template <typename T> constexpr int plane_rt() { return sizeof(T) == 2 ? 64 : 32; }
 template <typename T, int S>
 __global__ __launch_bounds__(NT) void k_plane_t(const T* __restrict__ src, int K, int R, long long ld,
                                                 bf16_t* __restrict__ dst, long long pstride, int Kp, int ones) {
-  __shared__ float tile[32][33];
-  const int k0 = blockIdx.x * 32, r0 = blockIdx.y * 32;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
+  constexpr int RT = plane_rt<T>();
+  __shared__ float tile[64][RT + 1];
+  constexpr int EPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
+  constexpr int CPR = RT / EPC;             // chunks per tile row (8)
+  constexpr int RPP = NT / CPR;             // tile rows per pass (32)
+  const int k0 = blockIdx.x * 64, r0 = blockIdx.y * RT;
+  const bool vec = (ld % EPC) == 0 && ((uintptr_t)src & 15u) == 0;
+  const int c = threadIdx.x % CPR, kr = threadIdx.x / CPR;
+  for (int p = 0; p < 64; p += RPP) {
+    const int kl = p + kr, k = k0 + kl, r = r0 + c * EPC;
+    float v[EPC];
+    if (k < K && vec && r + EPC <= R) {
+      const uint4 u = *reinterpret_cast<const uint4*>(src + (long long)k * ld + r);
+      const T* e = reinterpret_cast<const T*>(&u);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int k = k0 + ty + 8 * i, r = r0 + tx;
-    float v = 0.f;
-    if (k < K) {
-      if (r < R) v = to_f32<T>(src[(long long)k * ld + r]);
-      else if (ones && r == R) v = 1.f;
+      for (int q = 0; q < EPC; ++q) v[q] = to_f32<T>(e[q]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < EPC; ++q) {
+        float x = 0.f;
+        if (k < K) {
+          if (r + q < R) x = to_f32<T>(src[(long long)k * ld + r + q]);
+          else if (ones && r + q == R) x = 1.f;
+        }
+        v[q] = x;
+      }
     }
-    tile[ty + 8 * i][tx] = v;
+#pragma unroll
+    for (int q = 0; q < EPC; ++q) tile[kl][c * EPC + q] = v[q];
   }
   __syncthreads();
   const int Rout = R + (ones ? 1 : 0);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = r0 + ty + 8 * i, k = k0 + tx;
+  const int ck = threadIdx.x & 7, rr = threadIdx.x >> 3;
+  for (int p = 0; p < RT; p += 32) {
+    const int rl = p + rr, r = r0 + rl, k = k0 + 8 * ck;
     if (r >= Rout || k >= Kp) continue;
-    const float v = tile[tx][ty + 8 * i];
-    if constexpr (S == 1) {
-      dst[(long long)r * Kp + k] = f32_to_bf16(v);
-    } else {
-      bf16_t h, m, l;
-      split3(v, h, m, l);
-      dst[(long long)r * Kp + k] = h;
-      dst[pstride + (long long)r * Kp + k] = m;
-      dst[2 * pstride + (long long)r * Kp + k] = l;
+    bf16_t o[S][8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float v = tile[8 * ck + u][rl];
+      if constexpr (S == 1) {
+        o[0][u] = f32_to_bf16(v);
+      } else {
+        bf16_t h, m, l;
+        split3(v, h, m, l);
+        o[0][u] = h;
+        o[1][u] = m;
+        if constexpr (S == 3) o[2][u] = l;
+      }
     }
+#pragma unroll
+    for (int s2 = 0; s2 < S; ++s2)
+      *reinterpret_cast<uint4*>(dst + s2 * pstride + (long long)r * Kp + k) = *reinterpret_cast<const uint4*>(o[s2]);
   }
 }
 
@@ -110,11 +143,11 @@ enum Mode { PART = 0, LOGITS = 1, DX = 2 };
 
 // C[M,Nn] = sum over k in slice blockIdx.z of A[m][k] B[n][k], A and B given as planes
 // (SA, SB parts, leading dimensions lda, ldb, part strides pa, pb; rows past M / Nn and k past
-// K read as zero).
+// K read as zero); the part products whose indices add up to at most DMAX.
 //  PART:   out fp32 [gridDim.z][M][Nn], slice blockIdx.z
 //  LOGITS: out fp32 [M][Nn] = C + bias[n] (bias may be NULL; one slice)
 //  DX:     out T [M][Nn] = cin + C (one slice), T = bf16 (cdt 1) or fp32 (cdt 0)
-template <int SA, int SB, int MODE>
+template <int SA, int SB, int MODE, int DMAX = 2>
 __global__ __launch_bounds__(NT) void k_bmm(const bf16_t* __restrict__ A, long long pa, int lda,
                                             const bf16_t* __restrict__ B, long long pb, int ldb, int M, int Nn,
                                             int K, int kslice, const float* __restrict__ bias,
@@ -189,9 +222,9 @@ __global__ __launch_bounds__(NT) void k_bmm(const bf16_t* __restrict__ A, long l
       for (int s = 0; s < SB; ++s)
 #pragma unroll
         for (int j = 0; j < 2; ++j) fb[s][j] = frag(sB[s], 32 * wn + 16 * j, sub);
-      // smallest terms first: part index sums 2, 1, 0
+      // smallest terms first: part index sums DMAX .. 0
 #pragma unroll
-      for (int d = 2; d >= 0; --d)
+      for (int d = DMAX; d >= 0; --d)
 #pragma unroll
         for (int sa = 0; sa < SA; ++sa) {
           const int sb = d - sa;
@@ -278,27 +311,28 @@ hipError_t plane_t(const T* src, int K, int R, long long ld, bf16_t* dst, long l
                    hipStream_t s) {
   const int Rout = R + (ones ? 1 : 0);
   if (Rout == 0 || Kp == 0) return hipSuccess;
-  hipLaunchKernelGGL((rm::k_plane_t<T, S>), dim3((unsigned)((Kp + 31) / 32), (unsigned)((Rout + 31) / 32)),
+  constexpr int RT = rm::plane_rt<T>();
+  hipLaunchKernelGGL((rm::k_plane_t<T, S>), dim3((unsigned)((Kp + 63) / 64), (unsigned)((Rout + RT - 1) / RT)),
                      dim3(rm::NT), 0, s, src, K, R, ld, dst, pstride, Kp, ones);
   return hipGetLastError();
 }
-template <int SA, int SB, int MODE>
+template <int SA, int SB, int MODE, int DMAX = 2>
 hipError_t bmm(const bf16_t* A, long long pa, int lda, const bf16_t* B, long long pb, int ldb, int M, int Nn, int K,
                int S, const float* bias, const void* cin, void* cout, int cdt, hipStream_t s) {
   if (M <= 0 || Nn <= 0) return hipSuccess;
   const int kslice = ((K + S - 1) / S + rm::TK - 1) / rm::TK * rm::TK;
   const dim3 g((unsigned)((M + rm::TM - 1) / rm::TM), (unsigned)((Nn + rm::TN - 1) / rm::TN), (unsigned)S);
-  hipLaunchKernelGGL((rm::k_bmm<SA, SB, MODE>), g, dim3(rm::NT), 0, s, A, pa, lda, B, pb, ldb, M, Nn, K, kslice,
+  hipLaunchKernelGGL((rm::k_bmm<SA, SB, MODE, DMAX>), g, dim3(rm::NT), 0, s, A, pa, lda, B, pb, ldb, M, Nn, K, kslice,
                      bias, cin, cout, cdt);
   return hipGetLastError();
 }
 
-// k-slices of a reduction over K with `tiles` output tiles: about 1024 workgroups (four per
-// CU, so that the loads of some overlap the MFMAs of others), at least 128 k per slice, at
-// most 16 slices
+// k-slices of a reduction over K with `tiles` output tiles: about 512 workgroups (two per CU,
+// so that the loads of one overlap the MFMAs of the other, with fewer partial sums to add than
+// at four), at least 128 k per slice, at most 16 slices
 int slices(long long tiles, int K) {
   if (tiles <= 0) return 1;  // no rows: nothing to split
-  long long S = (1024 + tiles - 1) / tiles;
+  long long S = (512 + tiles - 1) / tiles;
   const long long smax = K / 128;
   if (S > smax) S = smax;
   if (S > 16) S = 16;
@@ -367,10 +401,18 @@ hipError_t launch_router_dx_mm(moe_dtype dt, const float* dlogits, const float* 
   p += a256((size_t)3 * N * E8 * 2);
   bf16_t* wp = reinterpret_cast<bf16_t*>(p);  // [3][H][E8]
   const long long pz = (long long)N * E8, pw = (long long)H * E8;
-  hipError_t e = plane_kc<float, 3>(dlogits, N, E, E, dzp, pz, E8, s);
+  hipError_t e;
+  if (dt == MOE_BF16) {
+    // the result is rounded to bf16: two parts a side and the products of index sum <= 1
+    // (16 significant bits each, about 2^-16 of each term) are far inside its precision
+    e = plane_kc<float, 2>(dlogits, N, E, E, dzp, pz, E8, s);
+    if (e == hipSuccess) e = plane_kc<float, 2>(wr, H, E, E, wp, pw, E8, s);
+    if (e == hipSuccess) e = bmm<2, 2, rm::DX, 1>(dzp, pz, E8, wp, pw, E8, N, H, E8, 1, nullptr, dx_in, dx_out, 1, s);
+    return e;
+  }
+  e = plane_kc<float, 3>(dlogits, N, E, E, dzp, pz, E8, s);
   if (e == hipSuccess) e = plane_kc<float, 3>(wr, H, E, E, wp, pw, E8, s);
-  if (e == hipSuccess)
-    e = bmm<3, 3, rm::DX>(dzp, pz, E8, wp, pw, E8, N, H, E8, 1, nullptr, dx_in, dx_out, dt == MOE_BF16 ? 1 : 0, s);
+  if (e == hipSuccess) e = bmm<3, 3, rm::DX>(dzp, pz, E8, wp, pw, E8, N, H, E8, 1, nullptr, dx_in, dx_out, 0, s);
   return e;
 }
 

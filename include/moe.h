@@ -342,7 +342,8 @@ moe_status moe_router_logits(moe_dtype dt, const void* x, const float* w_r, cons
  * fp32 [E] or NULL; topk_idx int32 [N,k]; x, dx_in, dx_out [N,H] of dtype dt (dx_out may be
  * dx_in: in place); w_r fp32 [H,E]; dw_r fp32 [H,E]; dbias fp32 [E].  Everything is written
  * fresh, in a fixed order (bitwise reproducible); the two products run like moe_router_logits'
- * (split bf16 parts, fp32 accuracy; the same size limit).  Workspace: moe_workspace_bytes(
+ * (split bf16 parts, fp32 accuracy; the same size limit), except that the dx share of a bf16
+ * layer, which is rounded to bf16, keeps 16 significant bits of each operand.  Workspace: moe_workspace_bytes(
  * MOE_OP_ROUTER_BWD, dt, N, E, k, H, 0, 0) when dx_out, dw_r or dbias is requested, else none.
  */
 moe_status moe_router_bwd(moe_dtype dt, const float* logits, const float* bias, const int32_t* topk_idx,
