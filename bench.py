@@ -31,7 +31,7 @@ PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 PEAK_FP8_TFLOPS = 5033.2      # dense fp8 MFMA: twice the bf16 rate
 GEMMS = ("gateup", "down", "dh", "dx", "dwd", "dw1")
-ALL_KERNELS = ("route", "permute", "route_tr_plan", "gateup", "down", "combine", "dh", "dswiglu", "dwd", "dx",
+ALL_KERNELS = ("route", "permute", "route_tr_plan", "gateup", "down", "combine", "dh", "dwd", "dx",
                "dx_combine", "dw1")
 
 
@@ -48,16 +48,16 @@ def kernel_work(name, wl, M, e_act, es):
     n_part = 2 * ((I + 255) // 256) if es == 2 else (I + 127) // 128
     if name == "dh":  # reads W_down, dOut rows, G, U, w; writes dG, dU, A' and the dS partials
         return 2.0 * M * H * I, es * (1.0 * e_act * H * I + N * H + 5.0 * M * I) + 4.0 * M * (n_part + 1)
-    if name == "dswiglu":  # the ordered sum of the dS partials
-        return 0.0, 4.0 * M * n_part + 8.0 * M
     if name == "dx":
         return 4.0 * M * H * I, es * (2.0 * e_act * I * H + 2.0 * M * I + M * H)
     if name == "dwd":
         return 2.0 * M * H * I, es * (1.0 * E * H * I + N * H + M * I)
     if name == "dw1":
         return 4.0 * M * H * I, es * (2.0 * E * I * H + N * H + 2.0 * M * I)
-    if name in ("combine", "dx_combine"):
+    if name == "combine":
         return 2.0 * M * H, es * (1.0 * M * H + N * H) + 8.0 * M
+    if name == "dx_combine":  # also the ordered sum of the dS partials
+        return 2.0 * M * H, es * (1.0 * M * H + N * H) + 8.0 * M + 4.0 * M * n_part + 8.0 * M
     return 0.0, 0.0
 
 
@@ -428,7 +428,7 @@ def main():
         res["gemm_pct_peak"] = round(100.0 * res["gemm_tflops"] / peak, 2)
         res["fwd_ms"] = round(sum(kern_ms.get(n, 0.0) for n in ("route", "permute", "route_tr_plan", "gateup",
                                                                   "down", "combine")), 4)
-        res["bwd_ms"] = round(sum(kern_ms.get(n, 0.0) for n in ("dh", "dswiglu", "dwd", "dx", "dx_combine",
+        res["bwd_ms"] = round(sum(kern_ms.get(n, 0.0) for n in ("dh", "dwd", "dx", "dx_combine",
                                                                   "dw1")), 4)
         kinfo = {}
         for n in names:

@@ -12,18 +12,50 @@
 // loads the vectors of up to RB rows before it accumulates any of them, so RB loads per lane
 // are in flight instead of one (with one load at a time the kernel is bound by memory
 // latency, not bandwidth); the sum still runs row by row in ascending order.
+//
+// The dX combine also finishes dS ([SM] "3 기여 ①": the router-score gradient of each row,
+// left by the dH GEMM's epilogue as nP partial sums per row): thread i of token t's
+// workgroup adds the partials of the token's rows i, i + 256, ... in partial order and writes
+// the pair's entry (top-k plans) or the row's (other plans, whose unused rows M .. M_cap get
+// zeros from extra workgroups of 4096 rows each).
 #include "common.h"
 
 namespace moe {
 
+struct DsSum {
+  const float* part;  // [M_cap, nP]; NULL: no dS work
+  int nP, by_pair;
+  float* ds;
+};
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_combine(const T* __restrict__ y, int H, const int32_t* __restrict__ tok_ptr,
                                                  const int32_t* __restrict__ tok_rows,
-                                                 const float* __restrict__ row_w, T* __restrict__ out) {
+                                                 const float* __restrict__ row_w, T* __restrict__ out, moe_plan p,
+                                                 DsSum d) {
   constexpr int VEC = 16 / sizeof(T);
   constexpr int RB = 8;
   const int t = blockIdx.x;
+  if (t >= p.N) {  // zero the unused rows' dS (row-ordered plans)
+    const int M = p.offsets[p.E];
+    const int lo = max(M, (t - p.N) * 4096), hi = min(p.M_cap, (t - p.N + 1) * 4096);
+    for (int r = lo + (int)threadIdx.x; r < hi; r += 256) d.ds[r] = 0.f;
+    return;
+  }
   const int q0 = tok_ptr[t], q1 = tok_ptr[t + 1];
+  for (int i = threadIdx.x; d.part && i < q1 - q0; i += 256) {
+    const int r = tok_rows[q0 + i];
+    if (r >= 0) {
+      float sum = 0.f;
+      for (int q = 0; q < d.nP; ++q) sum += d.part[(size_t)r * d.nP + q];
+      if (d.by_pair) {
+        const int pr = p.row_pair[r];
+        if (pr >= 0) d.ds[pr] = sum;
+      } else {
+        d.ds[r] = sum;
+      }
+    }
+  }
   const int nv = H / VEC;
   for (int v = threadIdx.x; v < nv; v += 256) {
     float acc[VEC];
@@ -61,14 +93,17 @@ __global__ __launch_bounds__(256) void k_combine(const T* __restrict__ y, int H,
 }
 
 hipError_t launch_combine(moe_dtype dt, const void* y, int H, const moe_plan& p, const float* row_w, void* out,
-                          hipStream_t s) {
-  if (p.N == 0) return hipSuccess;
+                          hipStream_t s, const float* dspart, int nP, float* ds) {
+  DsSum d{dspart, nP, p.kind == MOE_PLAN_TOPK ? 1 : 0, ds};
+  const long long z = (dspart && !d.by_pair) ? ((long long)p.M_cap + 4095) / 4096 : 0;
+  const long long g = (long long)p.N + z;
+  if (g == 0) return hipSuccess;
   if (dt == MOE_BF16)
-    hipLaunchKernelGGL(k_combine<bf16_t>, dim3(p.N), dim3(256), 0, s, (const bf16_t*)y, H, p.tok_ptr, p.tok_rows,
-                       row_w, (bf16_t*)out);
+    hipLaunchKernelGGL(k_combine<bf16_t>, dim3((unsigned)g), dim3(256), 0, s, (const bf16_t*)y, H, p.tok_ptr,
+                       p.tok_rows, row_w, (bf16_t*)out, p, d);
   else
-    hipLaunchKernelGGL(k_combine<float>, dim3(p.N), dim3(256), 0, s, (const float*)y, H, p.tok_ptr, p.tok_rows,
-                       row_w, (float*)out);
+    hipLaunchKernelGGL(k_combine<float>, dim3((unsigned)g), dim3(256), 0, s, (const float*)y, H, p.tok_ptr,
+                       p.tok_rows, row_w, (float*)out, p, d);
   return hipGetLastError();
 }
 

@@ -100,8 +100,8 @@ float* tr_tok_norm(void* ws, int N, int E);  // where the plan's workspace holds
 hipError_t launch_token_round(const int32_t* idx, const float* probs, const float* tok_norm, const float* topk_w,
                               int N, int E, int k, int cap, int param, int use_p, const moe_plan& p, void* ws,
                               hipStream_t s);
-hipError_t launch_combine(moe_dtype dt, const void* y, int H, const moe_plan& p, const float* row_w,
-                          void* out, hipStream_t s);
+hipError_t launch_combine(moe_dtype dt, const void* y, int H, const moe_plan& p, const float* row_w, void* out,
+                          hipStream_t s, const float* dspart = nullptr, int nP = 0, float* ds = nullptr);
 size_t gemm_fwd_ws_bytes(moe_dtype dt, int M_cap, int I);
 hipError_t launch_quant_mxfp8(moe_dtype dt, const void* src, long long rows, int K, uint8_t* q, uint8_t* scales,
                               hipStream_t s);

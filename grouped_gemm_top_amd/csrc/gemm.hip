@@ -835,28 +835,6 @@ __global__ __launch_bounds__(NTHR, 2) void k_grouped_gemm(Args a, const int32_t*
   }
 }
 
-// dS: ordered sum of the N-tile partials; scattered to (t, j) order through row_pair for
-// top-k plans, kept in row order for token-rounding plans.
-__global__ __launch_bounds__(256) void k_ds_reduce(const float* __restrict__ dspart, int nTN,
-                                                   const int32_t* __restrict__ offsets, int E,
-                                                   const int32_t* __restrict__ row_pair, int by_pair, int M_cap,
-                                                   float* __restrict__ ds) {
-  const int r = blockIdx.x * 256 + threadIdx.x;
-  if (r >= M_cap) return;
-  const int M = offsets[E];
-  if (r >= M) {
-    if (!by_pair) ds[r] = 0.f;
-    return;
-  }
-  float s = 0.f;
-  for (int q = 0; q < nTN; ++q) s += dspart[(size_t)r * nTN + q];
-  if (by_pair) {
-    const int p = row_pair[r];
-    if (p >= 0) ds[p] = s;
-  } else {
-    ds[r] = s;
-  }
-}
 
 }  // namespace gg
 
@@ -987,16 +965,9 @@ static hipError_t layer_bwd_t(const void* dout, const void* x, const void* wg, c
   hipError_t err;
 
   // dA' = dOut[t] W_down^T (varlen-M GEMM) with the dSwiGLU epilogue: dH = [dG | dU],
-  // A' = w A and the dS partials; then their ordered sum
+  // A' = w A and the dS partials (their ordered sum runs in the dX combine below)
   a.out0 = dh; a.out1 = aprime; a.dspart = dspart;
   if ((err = launch(KDH{}, mt * nTN)) != hipSuccess) return err;
-  if (p.M_cap > 0) {
-    kernel_event(MOE_K_DSWIGLU, 0, s);
-    hipLaunchKernelGGL(gg::k_ds_reduce, dim3((p.M_cap + 255) / 256), dim3(256), 0, s, dspart, nP, p.offsets, p.E,
-                       p.row_pair, p.kind == MOE_PLAN_TOPK ? 1 : 0, p.M_cap, ds);
-    kernel_event(MOE_K_DSWIGLU, 1, s);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-  }
   // The two weight-gradient kernels run first and dX last.  The bf16 kernels store their dW
   // (805 MB in all at the headline shape) with the non-temporal policy, since no later kernel
   // of the step reads it; of the orders measured with those stores this one is the fastest
@@ -1012,7 +983,7 @@ static hipError_t layer_bwd_t(const void* dout, const void* x, const void* wg, c
   a.out0 = dxe; a.out1 = nullptr;
   if ((err = launch(KDX{}, mt * ((H + tn - 1) / tn))) != hipSuccess) return err;
   kernel_event(MOE_K_DX_COMBINE, 0, s);
-  err = launch_combine(sizeof(T) == 2 ? MOE_BF16 : MOE_F32, dxe, H, p, nullptr, dx, s);
+  err = launch_combine(sizeof(T) == 2 ? MOE_BF16 : MOE_F32, dxe, H, p, nullptr, dx, s, dspart, nP, ds);
   kernel_event(MOE_K_DX_COMBINE, 1, s);
   return err;
 }

@@ -223,10 +223,54 @@ __global__ __launch_bounds__(kPT) void k_perm_scan_scatter(const int32_t* __rest
     for (; q < q1; ++q) acc[0] += bcnt[(size_t)q * E + e];
     return ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
   };
-  for (int e = threadIdx.x; e < E; e += kPT) {
-    const int bef = colsum(e, 0, b);
-    s_tot[e] = bef + colsum(e, b, nb);
-    s_base[e] = bef;
+  if (2 * E <= kPT) {
+    // G groups of E threads (G a power of two, G E <= kPT): group g sums the blocks g, g + G,
+    // ... of expert e, those before b into the base and all into the total, eight loads in
+    // flight; then the G partial sums are added
+    __shared__ int s_pb[kPT], s_pt[kPT];
+    int G = 2;
+    while (2 * G * E <= kPT) G *= 2;
+    const int g = threadIdx.x / E, e = threadIdx.x - g * E;
+    int pb = 0, pt = 0;
+    if (g < G) {
+      int ab[8] = {0, 0, 0, 0, 0, 0, 0, 0}, at[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      int q = g;
+      for (; q + 7 * G < nb; q += 8 * G) {
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = bcnt[(size_t)(q + u * G) * E + e];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          at[u] += v[u];
+          if (q + u * G < b) ab[u] += v[u];
+        }
+      }
+      for (; q < nb; q += G) {
+        const int v = bcnt[(size_t)q * E + e];
+        at[0] += v;
+        if (q < b) ab[0] += v;
+      }
+      pb = ((ab[0] + ab[1]) + (ab[2] + ab[3])) + ((ab[4] + ab[5]) + (ab[6] + ab[7]));
+      pt = ((at[0] + at[1]) + (at[2] + at[3])) + ((at[4] + at[5]) + (at[6] + at[7]));
+    }
+    s_pb[threadIdx.x] = pb;
+    s_pt[threadIdx.x] = pt;
+    __syncthreads();
+    if (threadIdx.x < E) {
+      int sb = 0, st = 0;
+      for (int q = 0; q < G; ++q) {
+        sb += s_pb[q * E + threadIdx.x];
+        st += s_pt[q * E + threadIdx.x];
+      }
+      s_base[threadIdx.x] = sb;
+      s_tot[threadIdx.x] = st;
+    }
+  } else {
+    for (int e = threadIdx.x; e < E; e += kPT) {
+      const int bef = colsum(e, 0, b);
+      s_tot[e] = bef + colsum(e, b, nb);
+      s_base[e] = bef;
+    }
   }
   __syncthreads();
   // exclusive scan of the totals: thread x owns experts 4x .. 4x + 3 (E <= 1024)

@@ -373,7 +373,7 @@ typedef enum moe_kernel_id {
   MOE_K_ROUTE = 8,       /* top-k router kernel */
   MOE_K_PERMUTE = 9,     /* moe_permute: histogram, then scan + scatter (one kernel while the blocks are few) */
   MOE_K_ROUTE_TR_PLAN = 10, /* the token-rounding plan kernels after the router */
-  MOE_K_DSWIGLU = 11,    /* ordered sum of the dH kernel's dS partials */
+  MOE_K_DSWIGLU = 11,    /* not launched on its own any more: the dX combine sums the dS partials */
   MOE_K_ROUTER_LOGITS = 12, /* moe_router_logits */
   MOE_K_ROUTER_DZ = 13,  /* moe_router_bwd: dz from dS */
   MOE_K_ROUTER_DX = 14,  /* moe_router_bwd: dx_out = dx_in + dz W_r^T */
