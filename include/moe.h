@@ -292,7 +292,9 @@ moe_status moe_unpermute_combine(moe_dtype dt, const void* y, int32_t H, const m
  *                                              without loading Y, [SM] "3 기여 ①")
  *   dA   = w dA';  dG = dA U s (1 + G (1 - s)), s = sigmoid(G);  dU = dA silu(G)
  *   A'   = w A                                (dH, dS and A' from one epilogue,
- *                                              [SM] "4.2 Epilogue 융합")
+ *                                              [SM] "4.2 Epilogue 융합"; dS leaves it as
+ *                                              per-tile partials that the dX combine adds
+ *                                              in a fixed order)
  *   dW_down[e] = sum_r dOut[t]^T A'           (varlen-K grouped GEMM, dOut gathered)
  *   dW_gate[e] = sum_r dG^T x[t],  dW_up[e] = sum_r dU^T x[t]   (varlen-K, x gathered)
  *   dx[t] = sum over rows of t of (dG W_gate[e] + dU W_up[e])  (varlen-M GEMM + combine)
