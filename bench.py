@@ -231,7 +231,8 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=30,
+                    help="untimed steps first (the clock and caches settle over the first few dozen)")
     ap.add_argument("--config", type=int, default=2, help="workload number (1-5); 2 is the headline")
     ap.add_argument("--cpu-tokens", type=int, default=4096,
                     help="tokens in the CPU-oracle baseline sample (0 disables it)")
