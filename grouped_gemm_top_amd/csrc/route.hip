@@ -37,9 +37,10 @@ __device__ __forceinline__ float wave_max(float x) {
   return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
-// The routing of token t by one wavefront.  sz: the wavefront's LDS scratch (k floats, the
-// chosen logits).
-template <int PL>  // experts per lane: E <= 64 * PL
+// The routing of token t by one wavefront.  SMALLK (k <= 64): lane j keeps round j's logit and
+// expert in registers and the wavefront writes them at the end; otherwise lane 0 writes each
+// round's expert and sz (the wavefront's LDS scratch, k floats) holds the chosen logits.
+template <int PL, bool SMALLK>  // experts per lane: E <= 64 * PL
 __device__ __forceinline__ void route_token(const float* __restrict__ logits, const float* __restrict__ bias, int t,
                                             int E, int k, int32_t* __restrict__ idx, float* __restrict__ w,
                                             float* __restrict__ probs, float* __restrict__ tok_norm, float* sz) {
@@ -57,6 +58,8 @@ __device__ __forceinline__ void route_token(const float* __restrict__ logits, co
     if (e < E) avail |= 1u << q;
   }
   float zmax = 0.f;
+  float myz = 0.f;  // SMALLK: lane j's round
+  int myid = 0;
   for (int j = 0; j < k; ++j) {
     // the largest available z: the lane's own maximum, then the wavefront's (row maxima with
     // DPP moves, then the four rows through SGPRs); a lane with nothing left offers -inf
@@ -74,20 +77,37 @@ __device__ __forceinline__ void route_token(const float* __restrict__ logits, co
       if (m) be = 64 * q + __builtin_ctzll(m);
     }
     if ((be & 63) == lane) avail &= ~(1u << (be >> 6));
-    if (lane == 0) {
+    if constexpr (SMALLK) {
+      if (lane == j) {
+        myz = bz;
+        myid = be;
+      }
+    } else if (lane == 0) {
       idx[(size_t)t * k + j] = be;
       sz[j] = bz;
     }
     if (j == 0) zmax = bz;
   }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   // renormalised weights: softmax over the chosen k
   float sk = 0.f;
-  for (int j = lane; j < k; j += 64) sk += expf(sz[j] - zmax);
+  if constexpr (SMALLK) {
+    if (lane < k) {
+      idx[(size_t)t * k + lane] = myid;
+      sk = expf(myz - zmax);
+    }
+  } else {
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    for (int j = lane; j < k; j += 64) sk += expf(sz[j] - zmax);
+  }
+  const float ek = sk;  // SMALLK: this lane's term
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) sk += __shfl_xor(sk, off);
-  for (int j = lane; j < k; j += 64) w[(size_t)t * k + j] = expf(sz[j] - zmax) / sk;
+  if constexpr (SMALLK) {
+    if (lane < k) w[(size_t)t * k + lane] = ek / sk;
+  } else {
+    for (int j = lane; j < k; j += 64) w[(size_t)t * k + j] = expf(sz[j] - zmax) / sk;
+  }
   if (probs || tok_norm) {
     float ez[PL];
     float sa = 0.f;
@@ -105,7 +125,12 @@ __device__ __forceinline__ void route_token(const float* __restrict__ logits, co
     }
     if (tok_norm) {
       // sum of the chosen probabilities, in slot order, from the same fp32 values as probs
-      if (lane == 0) {
+      if constexpr (SMALLK) {
+        const float pj = ek / sa;  // lane j: round j's probability (lanes >= k: unused)
+        float s = 0.f;
+        for (int j = 0; j < k; ++j) s += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pj), j));
+        if (lane == 0) tok_norm[t] = s;
+      } else if (lane == 0) {
         float s = 0.f;
         for (int j = 0; j < k; ++j) s += expf(sz[j] - zmax) / sa;
         tok_norm[t] = s;
@@ -114,27 +139,39 @@ __device__ __forceinline__ void route_token(const float* __restrict__ logits, co
   }
 }
 
-template <int PL>
+template <int PL, bool SMALLK>
 __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ logits,
                                                     const float* __restrict__ bias, int N, int E, int k,
                                                     int32_t* __restrict__ idx, float* __restrict__ w,
                                                     float* __restrict__ probs, float* __restrict__ tok_norm) {
-  __shared__ float s_z[4][kMaxE];
+  __shared__ float s_z[4][SMALLK ? 1 : kMaxE];
   const int wave = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wave;
   if (t >= N) return;  // whole wavefronts exit together; no block barrier below
-  route_token<PL>(logits, bias, t, E, k, idx, w, probs, tok_norm, s_z[wave]);
+  route_token<PL, SMALLK>(logits, bias, t, E, k, idx, w, probs, tok_norm, s_z[wave]);
+}
+
+template <bool SMALLK>
+static void launch_route_pl(const float* logits, const float* bias, int N, int E, int k, int32_t* idx, float* w,
+                            float* probs, float* tok_norm, hipStream_t s) {
+  const dim3 g((N + 3) / 4), b(256);
+  if (E <= 64)
+    hipLaunchKernelGGL((k_route_topk<1, SMALLK>), g, b, 0, s, logits, bias, N, E, k, idx, w, probs, tok_norm);
+  else if (E <= 128)
+    hipLaunchKernelGGL((k_route_topk<2, SMALLK>), g, b, 0, s, logits, bias, N, E, k, idx, w, probs, tok_norm);
+  else if (E <= 256)
+    hipLaunchKernelGGL((k_route_topk<4, SMALLK>), g, b, 0, s, logits, bias, N, E, k, idx, w, probs, tok_norm);
+  else if (E <= 512)
+    hipLaunchKernelGGL((k_route_topk<8, SMALLK>), g, b, 0, s, logits, bias, N, E, k, idx, w, probs, tok_norm);
+  else
+    hipLaunchKernelGGL((k_route_topk<16, SMALLK>), g, b, 0, s, logits, bias, N, E, k, idx, w, probs, tok_norm);
 }
 
 hipError_t launch_route_topk(const float* logits, const float* bias, int N, int E, int k, int32_t* idx,
                              float* w, float* probs, float* tok_norm, hipStream_t s) {
   if (N == 0) return hipSuccess;
-  const dim3 g((N + 3) / 4), b(256);
-  if (E <= 64) hipLaunchKernelGGL(k_route_topk<1>, g, b, 0, s, logits, bias, N, E, k, idx, w, probs, tok_norm);
-  else if (E <= 128) hipLaunchKernelGGL(k_route_topk<2>, g, b, 0, s, logits, bias, N, E, k, idx, w, probs, tok_norm);
-  else if (E <= 256) hipLaunchKernelGGL(k_route_topk<4>, g, b, 0, s, logits, bias, N, E, k, idx, w, probs, tok_norm);
-  else if (E <= 512) hipLaunchKernelGGL(k_route_topk<8>, g, b, 0, s, logits, bias, N, E, k, idx, w, probs, tok_norm);
-  else hipLaunchKernelGGL(k_route_topk<16>, g, b, 0, s, logits, bias, N, E, k, idx, w, probs, tok_norm);
+  if (k <= 64) launch_route_pl<true>(logits, bias, N, E, k, idx, w, probs, tok_norm, s);
+  else launch_route_pl<false>(logits, bias, N, E, k, idx, w, probs, tok_norm, s);
   return hipGetLastError();
 }
 

@@ -2,7 +2,7 @@
 indices bit for bit and weights to 1e-5 (ties included: the lowest expert id wins); the plan
 bit for bit, on shapes that take the two-launch permute (histogram, then scan and scatter in
 one kernel whose every block sums the whole histogram) and the three-launch one (histogram,
-scan, scatter), with ragged token blocks, one expert, k = E and E = 1024."""
+scan, scatter), with ragged token blocks, one expert, k = E, k > 64 and E = 1024."""
 import numpy as np
 import pytest
 
@@ -26,6 +26,7 @@ CASES = [
     (200, 16, 16, False, 2),        # k = E
     (300, 32, 32, False, 2),
     (1000, 1024, 8, True, 2),
+    (300, 128, 100, True, 2),       # k > 64: the router keeps its choices in LDS
     (16384, 256, 8, False, 2),
     (65536, 64, 4, False, 3),       # nb^2 E > 2^25
 ]
