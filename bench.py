@@ -291,7 +291,7 @@ def main():
         print(json.dumps(pk), flush=True)
         return
     G.lib()
-    wl = W.CONFIGS[args.config]
+    wl = W.WORKLOADS[args.config]
     print(f"# generating {wl.name}", file=sys.stderr, flush=True)
     T = W.generate(wl)
     dev = "cuda"

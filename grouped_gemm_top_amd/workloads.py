@@ -4,8 +4,8 @@ This module only draws random inputs; it holds none of the layer's arithmetic.  
 HIP path (through tests and the benchmark) and the CPU oracle consume exactly the arrays it
 returns, so the two sides always see identical inputs.
 
-Recipe (fixed, so every run of a configuration sees the same numbers):
-  * numpy PCG64 streams from ``SeedSequence(seed)``, seed = 1000 + configuration number (or
+Recipe (fixed, so every run of a workload sees the same numbers):
+  * numpy PCG64 streams from ``SeedSequence(seed)``, seed = 1000 + workload number (or
     an explicit seed).  The sequence is spawned into one child per draw slot, in the order
     x [N,H], W_r [H,E], bias [E], W_gate [E,I,H], W_up [E,I,H], W_down [E,H,I], dOut [N,H],
     expert permutation; each tensor is cut into chunks of 2^22 elements and chunk c is drawn
@@ -59,7 +59,7 @@ class Workload:
 # 가속" (Experiments: E=128, H=2048, moe_intermediate=512, top_k=8, N=4096), the
 # DeepSeek-V3 expert shape of the same page (E=256, H=2048, I=512), the E=128 / k=4 model of
 # "Deep EP" (GPT-OSS structure), and the high-sparsity token-rounding regime of "SonicMoE".
-CONFIGS = {
+WORKLOADS = {
     1: Workload("tiny-fp32", N=64, H=64, I=32, E=8, k=2, dtype="f32", seed=1001),
     2: Workload("microbench-E128-H2048-I512-k8-N4096", N=4096, H=2048, I=512, E=128, k=8,
                 dtype="bf16", seed=1002),

@@ -49,7 +49,7 @@ def _assert_quant_equal(gq, gs, arr):
 
 
 def test_quantize_bit_exact_headline_tensors():
-    wl = W.CONFIGS[2]
+    wl = W.WORKLOADS[2]
     T = W.generate(wl)
     g = Guards()
     for name, arr in (("x", T.x), ("wg", T.wg), ("wd", T.wd)):
@@ -196,7 +196,7 @@ def test_fwd_mxfp8_against_oracle(shape):
 def test_fwd_mxfp8_headline_sampled():
     """The headline layer (E=128, H=2048, I=512, k=8, N=4096), compared on the rows of 256
     sampled tokens (rows are independent given the weights)."""
-    T = W.generate(W.CONFIGS[2])
+    T = W.generate(W.WORKLOADS[2])
     res = _run_fp8(T)
     toks = np.sort(np.random.default_rng(2).choice(T.wl.N, 256, replace=False))
     _check_fp8(T, res, toks)

@@ -298,7 +298,7 @@ def test_capacity_headline_layer(policy):
     """The headline layer (E=128, H=2048, I=512, k=8, N=4096) with capacity factor 1
     (C = N k / E = 256), on a sample of tokens and experts."""
     import dataclasses
-    wl = dataclasses.replace(W.CONFIGS[2], name="headline-cap", routing="cap", mtile=256, cap_policy=policy)
+    wl = dataclasses.replace(W.WORKLOADS[2], name="headline-cap", routing="cap", mtile=256, cap_policy=policy)
     T = W.generate(wl)
     res = run_gpu(T)
     check_routing(T, res)
@@ -310,7 +310,7 @@ def test_capacity_headline_layer(policy):
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
 def test_config(cfg):
-    wl = W.CONFIGS[cfg]
+    wl = W.WORKLOADS[cfg]
     log(f"[config {cfg}] {wl.name}: generating inputs")
     T = W.generate(wl)
     D = upload(T)

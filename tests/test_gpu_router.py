@@ -128,7 +128,7 @@ def test_router_empty_input():
 @pytest.mark.parametrize("cfg", [2])
 def test_router_config(cfg):
     # the full-size layer the benchmark times (E=128, H=2048, I=512, k=8, N=4096), in full
-    _router_case(W.generate(W.CONFIGS[cfg]), f"config {cfg}")
+    _router_case(W.generate(W.WORKLOADS[cfg]), f"config {cfg}")
 
 
 def test_router_capacity_plan():

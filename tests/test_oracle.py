@@ -64,7 +64,7 @@ def test_topk_bias_enters_selection_and_weights():
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
 def test_topk_all_configs_vs_numpy(cfg):
-    wl = W.CONFIGS[cfg]
+    wl = W.WORKLOADS[cfg]
     T = W.generate(wl, weights=False)
     idx, w, probs = oracle.route_topk(T.logits, T.bias, wl.k, want_probs=True)
     z = T.logits if T.bias is None else T.logits + T.bias
@@ -160,7 +160,7 @@ def _check_plan_invariants(idx, w, pl, E):
 
 @pytest.mark.parametrize("cfg", [1, 2, 4])
 def test_plan_invariants(cfg):
-    wl = W.CONFIGS[cfg]
+    wl = W.WORKLOADS[cfg]
     T = W.generate(wl, weights=False)
     idx, w, _ = oracle.route_topk(T.logits, T.bias, wl.k)
     pl = oracle.permute(idx, w, wl.E)
@@ -168,7 +168,7 @@ def test_plan_invariants(cfg):
 
 
 def test_permute_unpermute_identity():
-    wl = W.CONFIGS[1]
+    wl = W.WORKLOADS[1]
     T = W.generate(wl)
     idx, w, _ = oracle.route_topk(T.logits, T.bias, wl.k)
     pl = oracle.permute(idx, w, wl.E)
@@ -282,7 +282,7 @@ def _autograd_ref(x, wg, wu, wd, dout, pt, pe, pw):
 
 
 def test_bwd_matches_autograd_config1_shape():
-    wl = W.CONFIGS[1]
+    wl = W.WORKLOADS[1]
     T = W.generate(wl)
     idx, w, _ = oracle.route_topk(T.logits, T.bias, wl.k)
     pt, pe, pw = oracle.pairs_from_topk(idx, w)
@@ -432,7 +432,7 @@ def test_token_round_identity_when_counts_are_multiples():
 
 
 def test_token_round_config5_counts():
-    wl = W.CONFIGS[5]
+    wl = W.WORKLOADS[5]
     T = W.generate(wl, weights=False)
     idx, w, probs = oracle.route_topk(T.logits, T.bias, wl.k, want_probs=True)
     pl = oracle.token_round(probs, idx, wl.mtile)

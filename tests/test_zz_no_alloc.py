@@ -54,7 +54,7 @@ def _routing(wl):
 
 
 def test_noalloc_matches_workspace_permute():
-    big = W.CONFIGS[2]                      # N = 4096, E = 128, k = 8
+    big = W.WORKLOADS[2]                      # N = 4096, E = 128, k = 8
     small = W.custom("noalloc-small", N=300, H=8, I=8, E=12, k=4, bias="normal", bias_std=0.7, seed=31)
     bi, bw = _routing(big)
     si, sw = _routing(small)
