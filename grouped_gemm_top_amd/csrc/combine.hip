@@ -11,7 +11,8 @@
 // order (deterministic, no atomics).  Pure HBM streaming: each y row is read once.  A thread
 // loads the vectors of up to RB rows before it accumulates any of them, so RB loads per lane
 // are in flight instead of one (with one load at a time the kernel is bound by memory
-// latency, not bandwidth); the sum still runs row by row in ascending order.
+// latency, not bandwidth), two such vectors at once on rows of 512 vectors or a multiple
+// (NV below); the sum still runs row by row in ascending order.
 //
 // The dX combine also finishes dS ([SM] "3 기여 ①": the router-score gradient of each row,
 // left by the dH GEMM's epilogue as nP partial sums per row): thread i of token t's
@@ -28,7 +29,12 @@ struct DsSum {
   float* ds;
 };
 
-template <typename T>
+// NV: vectors per thread at a time (v0 + 256 h, h < NV), NV * RB loads in flight; NV = 2 for
+// rows of 512 vectors or a multiple (H = 4096 in bf16), whose rows then come from HBM.  Other
+// widths keep NV = 1 (with a partial second vector the workgroup's threads would carry unequal
+// work, which measured slower), in a kernel of their own so that their register count, and
+// with it the number of workgroups a CU holds, stays that of one vector.
+template <typename T, int NV>
 __global__ __launch_bounds__(256) void k_combine(const T* __restrict__ y, int H, const int32_t* __restrict__ tok_ptr,
                                                  const int32_t* __restrict__ tok_rows,
                                                  const float* __restrict__ row_w, T* __restrict__ out, moe_plan p,
@@ -57,12 +63,14 @@ __global__ __launch_bounds__(256) void k_combine(const T* __restrict__ y, int H,
     }
   }
   const int nv = H / VEC;
-  for (int v = threadIdx.x; v < nv; v += 256) {
-    float acc[VEC];
+  for (int v0 = threadIdx.x; v0 < nv; v0 += 256 * NV) {
+    float acc[NV][VEC];
 #pragma unroll
-    for (int c = 0; c < VEC; ++c) acc[c] = 0.f;
+    for (int h = 0; h < NV; ++h)
+#pragma unroll
+      for (int c = 0; c < VEC; ++c) acc[h][c] = 0.f;
     for (int qb = q0; qb < q1; qb += RB) {
-      uint4 raw[RB];
+      uint4 raw[NV][RB];
       float wr[RB];
       uint32_t live = 0u;  // bit u: slot qb + u is one of the token's rows
 #pragma unroll
@@ -73,22 +81,30 @@ __global__ __launch_bounds__(256) void k_combine(const T* __restrict__ y, int H,
         const int rr = r < 0 ? 0 : r;
         if (qb + u < q1 && r >= 0) live |= 1u << u;
         wr[u] = row_w ? row_w[rr] : 1.0f;
-        raw[u] = *reinterpret_cast<const uint4*>(y + (size_t)rr * H + (size_t)v * VEC);
+#pragma unroll
+        for (int h = 0; h < NV; ++h)
+          raw[h][u] = *reinterpret_cast<const uint4*>(y + (size_t)rr * H + (size_t)(v0 + 256 * h) * VEC);
       }
 #pragma unroll
       for (int u = 0; u < RB; ++u) {
         if (live & (1u << u)) {  // uniform across the workgroup
-          const T* vals = reinterpret_cast<const T*>(&raw[u]);
 #pragma unroll
-          for (int c = 0; c < VEC; ++c) acc[c] += wr[u] * to_f32<T>(vals[c]);
+          for (int h = 0; h < NV; ++h) {
+            const T* vals = reinterpret_cast<const T*>(&raw[h][u]);
+#pragma unroll
+            for (int c = 0; c < VEC; ++c) acc[h][c] += wr[u] * to_f32<T>(vals[c]);
+          }
         }
       }
     }
-    uint4 o;
-    T* ov = reinterpret_cast<T*>(&o);
 #pragma unroll
-    for (int c = 0; c < VEC; ++c) ov[c] = from_f32<T>(acc[c]);
-    *reinterpret_cast<uint4*>(out + (size_t)t * H + (size_t)v * VEC) = o;
+    for (int h = 0; h < NV; ++h) {
+      uint4 o;
+      T* ov = reinterpret_cast<T*>(&o);
+#pragma unroll
+      for (int c = 0; c < VEC; ++c) ov[c] = from_f32<T>(acc[h][c]);
+      *reinterpret_cast<uint4*>(out + (size_t)t * H + (size_t)(v0 + 256 * h) * VEC) = o;
+    }
   }
 }
 
@@ -98,12 +114,16 @@ hipError_t launch_combine(moe_dtype dt, const void* y, int H, const moe_plan& p,
   const long long z = (dspart && !d.by_pair) ? ((long long)p.M_cap + 4095) / 4096 : 0;
   const long long g = (long long)p.N + z;
   if (g == 0) return hipSuccess;
-  if (dt == MOE_BF16)
-    hipLaunchKernelGGL(k_combine<bf16_t>, dim3((unsigned)g), dim3(256), 0, s, (const bf16_t*)y, H, p.tok_ptr,
-                       p.tok_rows, row_w, (bf16_t*)out, p, d);
-  else
-    hipLaunchKernelGGL(k_combine<float>, dim3((unsigned)g), dim3(256), 0, s, (const float*)y, H, p.tok_ptr,
-                       p.tok_rows, row_w, (float*)out, p, d);
+  const bool two = (H / (dt == MOE_BF16 ? 8 : 4)) % 512 == 0;
+  if (dt == MOE_BF16) {
+    auto* k = two ? k_combine<bf16_t, 2> : k_combine<bf16_t, 1>;
+    hipLaunchKernelGGL(k, dim3((unsigned)g), dim3(256), 0, s, (const bf16_t*)y, H, p.tok_ptr, p.tok_rows, row_w,
+                       (bf16_t*)out, p, d);
+  } else {
+    auto* k = two ? k_combine<float, 2> : k_combine<float, 1>;
+    hipLaunchKernelGGL(k, dim3((unsigned)g), dim3(256), 0, s, (const float*)y, H, p.tok_ptr, p.tok_rows, row_w,
+                       (float*)out, p, d);
+  }
   return hipGetLastError();
 }
 
