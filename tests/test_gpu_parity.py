@@ -48,6 +48,19 @@ def test_ragged_tiles(dtype):
     assert not bad, bad
 
 
+@pytest.mark.parametrize("dtype,H", [("f32", 2048), ("bf16", 4096)])
+def test_wide_rows_combine(dtype, H):
+    """Rows of 512 16-byte vectors (fp32 H = 2048, bf16 H = 4096): the combines' two-vector
+    kernel instance, forward and dX, with ragged row counts; compared in full."""
+    wl = W.custom(f"wide-{dtype}", N=96, H=H, I=64, E=6, k=2, dtype=dtype, bias="normal", bias_std=0.5, seed=31)
+    T = W.generate(wl)
+    res = run_gpu(T)
+    check_routing(T, res)
+    errs, bad = check_layer(T, res)
+    log(f"[wide rows {dtype} H={H}] {errs}")
+    assert not bad, bad
+
+
 def test_ragged_k_tails_bf16():
     """bf16 with H and I not multiples of 64 (H = 200, I = 72): the K tails of every kernel
     (the last k-step of gate/up and dH over H, of down over I, of dX over 2I) and ragged N
