@@ -49,19 +49,27 @@ __global__ __launch_bounds__(256) void k_combine(const T* __restrict__ y, int H,
     return;
   }
   const int q0 = tok_ptr[t], q1 = tok_ptr[t + 1];
-  for (int i = threadIdx.x; d.part && i < q1 - q0; i += 256) {
-    const int r = tok_rows[q0 + i];
-    if (r >= 0) {
-      float sum = 0.f;
-      for (int q = 0; q < d.nP; ++q) sum += d.part[(size_t)r * d.nP + q];
-      if (d.by_pair) {
-        const int pr = p.row_pair[r];
-        if (pr >= 0) d.ds[pr] = sum;
-      } else {
-        d.ds[r] = sum;
-      }
+  // dS of the token's first 256 rows: thread i loads row i's first DSP partials (and its pair)
+  // before the row sums below and adds them after, so that their latency overlaps that work;
+  // the sum runs in partial order either way
+  constexpr int DSP = 4;
+  int dr = -1, dpair = -1;
+  float dp[DSP];
+  if (d.part && (int)threadIdx.x < q1 - q0) {
+    dr = tok_rows[q0 + threadIdx.x];
+    if (dr >= 0) {
+#pragma unroll
+      for (int q = 0; q < DSP; ++q) dp[q] = q < d.nP ? d.part[(size_t)dr * d.nP + q] : 0.f;
+      if (d.by_pair) dpair = p.row_pair[dr];
     }
   }
+  auto ds_out = [&](int r, int pair, float sum) __attribute__((always_inline)) {
+    if (d.by_pair) {
+      if (pair >= 0) d.ds[pair] = sum;
+    } else {
+      d.ds[r] = sum;
+    }
+  };
   const int nv = H / VEC;
   for (int v0 = threadIdx.x; v0 < nv; v0 += 256 * NV) {
     float acc[NV][VEC];
@@ -104,6 +112,23 @@ __global__ __launch_bounds__(256) void k_combine(const T* __restrict__ y, int H,
 #pragma unroll
       for (int c = 0; c < VEC; ++c) ov[c] = from_f32<T>(acc[h][c]);
       *reinterpret_cast<uint4*>(out + (size_t)t * H + (size_t)(v0 + 256 * h) * VEC) = o;
+    }
+  }
+  if (dr >= 0) {
+    float sum = 0.f;
+#pragma unroll
+    for (int q = 0; q < DSP; ++q)
+      if (q < d.nP) sum += dp[q];
+    for (int q = DSP; q < d.nP; ++q) sum += d.part[(size_t)dr * d.nP + q];
+    ds_out(dr, dpair, sum);
+  }
+  // rows past the first 256 of a token (plans that give a token more rows than that)
+  for (int i = threadIdx.x + 256; d.part && i < q1 - q0; i += 256) {
+    const int r = tok_rows[q0 + i];
+    if (r >= 0) {
+      float sum = 0.f;
+      for (int q = 0; q < d.nP; ++q) sum += d.part[(size_t)r * d.nP + q];
+      ds_out(r, d.by_pair ? p.row_pair[r] : -1, sum);
     }
   }
 }
