@@ -130,11 +130,12 @@ __global__ __launch_bounds__(1024) void k_perm_scan(const int32_t* __restrict__ 
 
 // The scatter of block b's pairs (tokens 64 b .. 64 b + 63): bb[e] is the first row of expert
 // e that this block fills.  Called by every thread of the block.
-__device__ __forceinline__ void perm_scatter_block(const int32_t* __restrict__ idx, const float* __restrict__ w,
-                                                   int N, int E, int k, const int* bb, int32_t* __restrict__ row_token,
-                                                   float* __restrict__ row_w, int32_t* __restrict__ row_pair,
-                                                   int32_t* __restrict__ tok_ptr, int32_t* __restrict__ tok_rows,
-                                                   uint32_t* s_bits, uint32_t* s_texp) {
+// The block's two LDS bitmaps: s_bits[2e ..] = which of the block's 64 tokens chose expert e,
+// s_texp[tl EW ..] = which experts token tl chose.  Needs only the router's ids, so a caller
+// can run it before its scan (the loads of the ids then overlap the scan's); the bitmaps are
+// complete after the caller's next __syncthreads.
+__device__ __forceinline__ void perm_block_bits(const int32_t* __restrict__ idx, int N, int E, int k,
+                                                int32_t* __restrict__ tok_ptr, uint32_t* s_bits, uint32_t* s_texp) {
   const int EW = (E + 31) >> 5;
   for (int q = threadIdx.x; q < 2 * E; q += kPT) s_bits[q] = 0u;
   for (int q = threadIdx.x; q < kTB * EW; q += kPT) s_texp[q] = 0u;
@@ -151,7 +152,20 @@ __device__ __forceinline__ void perm_scatter_block(const int32_t* __restrict__ i
     }
   }
   if (threadIdx.x < nt) tok_ptr[t0 + threadIdx.x] = (t0 + threadIdx.x) * k;
-  __syncthreads();
+}
+
+// The block's rows, from the bitmaps of perm_block_bits (complete: the caller synchronised
+// after it) and the experts' row bases bb.
+__device__ __forceinline__ void perm_block_rows(const int32_t* __restrict__ idx, const float* __restrict__ w,
+                                                int N, int E, int k, const int* bb, int32_t* __restrict__ row_token,
+                                                float* __restrict__ row_w, int32_t* __restrict__ row_pair,
+                                                int32_t* __restrict__ tok_rows, const uint32_t* s_bits,
+                                                const uint32_t* s_texp) {
+  const int EW = (E + 31) >> 5;
+  const int t0 = blockIdx.x * kTB;
+  const int nt = min(kTB, N - t0);
+  const int np = nt * k;
+  const int32_t* ib = idx + (size_t)t0 * k;
   for (int q = threadIdx.x; q < np; q += kPT) {
     const int e = ib[q];
     const int tl = q / k, j = q - tl * k;
@@ -183,6 +197,16 @@ __device__ __forceinline__ void perm_scatter_block(const int32_t* __restrict__ i
   }
 }
 
+__device__ __forceinline__ void perm_scatter_block(const int32_t* __restrict__ idx, const float* __restrict__ w,
+                                                   int N, int E, int k, const int* bb, int32_t* __restrict__ row_token,
+                                                   float* __restrict__ row_w, int32_t* __restrict__ row_pair,
+                                                   int32_t* __restrict__ tok_ptr, int32_t* __restrict__ tok_rows,
+                                                   uint32_t* s_bits, uint32_t* s_texp) {
+  perm_block_bits(idx, N, E, k, tok_ptr, s_bits, s_texp);
+  __syncthreads();
+  perm_block_rows(idx, w, N, E, k, bb, row_token, row_w, row_pair, tok_rows, s_bits, s_texp);
+}
+
 __global__ __launch_bounds__(kPT) void k_perm_scatter(const int32_t* __restrict__ idx, const float* __restrict__ w,
                                                       int N, int E, int k, const int32_t* __restrict__ bbase,
                                                       int32_t* __restrict__ row_token, float* __restrict__ row_w,
@@ -212,6 +236,9 @@ __global__ __launch_bounds__(kPT) void k_perm_scan_scatter(const int32_t* __rest
   __shared__ uint32_t s_bits[1024 * 2];
   __shared__ uint32_t s_texp[kTB * (1024 / 32)];
   const int b = blockIdx.x;
+  // the block's bitmaps first: their id loads overlap the histogram sums below (the sums'
+  // __syncthreads completes them)
+  perm_block_bits(idx, N, E, k, tok_ptr, s_bits, s_texp);
   // eight independent loads in flight per thread (the sums are integer, so their order is free)
   auto colsum = [&](int e, int q0, int q1) __attribute__((always_inline)) {
     int acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -318,7 +345,7 @@ __global__ __launch_bounds__(kPT) void k_perm_scan_scatter(const int32_t* __rest
     tok_ptr[N] = N * k;
   }
   __syncthreads();
-  perm_scatter_block(idx, w, N, E, k, s_base, row_token, row_w, row_pair, tok_ptr, tok_rows, s_bits, s_texp);
+  perm_block_rows(idx, w, N, E, k, s_base, row_token, row_w, row_pair, tok_rows, s_bits, s_texp);
 }
 
 // Scratch of moe_permute_noalloc: a fixed device array, one copy per GPU for the life of the
