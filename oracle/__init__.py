@@ -9,6 +9,8 @@ from .oracle import (  # noqa: F401
     layer_bwd,
     layer_fwd,
     layer_fwd_mxfp8,
+    dx_weights_mxfp8,
+    dx_mxfp8,
     lib_path,
     mx_scale_cols,
     pairs_from_plan,

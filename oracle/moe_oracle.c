@@ -428,12 +428,12 @@ ORACLE_EXPORT int oracle_layer_fwd(const float* x, const float* wg, const float*
  *   dx[t]     += W_gate[e]^T dg + W_up[e]^T du
  * Experts without pairs get dW = 0.  dx excludes the router path.  Any output pointer may
  * be NULL to skip that part.  dx [N,H], dW_gate/dW_up [E,I,H], dW_down [E,H,I], dS [P],
- * all double.
+ * all double; dh [P, 2I] = [dg | du] of every pair, double.
  * ---------------------------------------------------------------------------------- */
 ORACLE_EXPORT int oracle_layer_bwd(const float* dout, const float* x, const float* wg, const float* wu,
                                    const float* wd, int N, int H, int I, int E, int P, const int32_t* pair_t,
                                    const int32_t* pair_e, const float* pair_w, double* dx, double* dwg,
-                                   double* dwu, double* dwd, double* ds) {
+                                   double* dwu, double* dwd, double* ds, double* dh) {
   if (N < 0 || H < 1 || I < 1 || E < 1 || P < 0 || !dout || !x || !wg || !wu || !wd) return -1;
   if (P > 0 && (!pair_t || !pair_e || !pair_w)) return -1;
   if (check_pairs(N, E, P, pair_t, pair_e)) return -1;
@@ -483,6 +483,12 @@ ORACLE_EXPORT int oracle_layer_bwd(const float* dout, const float* x, const floa
     free(g); free(u); free(y); free(dy); free(da);
   }
   if (fail) { free(A); free(DG); free(DU); return -2; }
+  if (dh)
+    for (size_t p = 0; p < (size_t)P; ++p)
+      for (int i = 0; i < I; ++i) {
+        dh[p * 2 * I + i] = (double)DG[p * I + i];
+        dh[p * 2 * I + I + i] = (double)DU[p * I + i];
+      }
 
   /* phase 2, per token: dx */
   if (dx) {
@@ -863,3 +869,58 @@ ORACLE_EXPORT int oracle_layer_fwd_mxfp8(const uint8_t* xq, const uint8_t* xs, c
   return fail ? -2 : 0;
 }
 
+
+/* ------------------------------------------------------------------------------------
+ * The backward's dX product on MX-FP8 operands (the FP8 grouped GEMM of [GG] "한계" applied
+ * to dX = dH W).  For every pair p (token t, expert e):
+ *   dh~ = the pair's row dh[p] = [dg | du] (2I fp32 values) quantized as one MX-FP8 row
+ *   dx[t, h] += sum_k dh~[k] wt~[e, h, k]
+ * where wt (q, s) [E*H, 2I] holds, as row e*H + h, expert e's [W_gate^T | W_up^T] row h
+ * (W_gate[e][i][h] for k = i < I, then W_up[e][k - I][h]) quantized along its 2I values, and ~
+ * marks dequantized values.  The quantization of dh is a decision taken on the fp32 values the
+ * caller passes.  Optional dhq [P, 2I] / dhs [P, KS(2I)] (NULL to skip): the quantized rows.
+ * dx [N, H] double.  H and I multiples of 32.
+ * ---------------------------------------------------------------------------------- */
+ORACLE_EXPORT int oracle_dx_mxfp8(const float* dh, const uint8_t* wq, const uint8_t* ws, int N, int H, int I, int E,
+                                  int P, const int32_t* pair_t, const int32_t* pair_e, double* dx, uint8_t* dhq,
+                                  uint8_t* dhs) {
+  if (N < 0 || H < 32 || I < 32 || H % 32 || I % 32 || E < 1 || P < 0 || !dx || !wq || !ws) return -1;
+  if (P > 0 && (!dh || !pair_t || !pair_e)) return -1;
+  if (check_pairs(N, E, P, pair_t, pair_e)) return -1;
+  memset(dx, 0, sizeof(double) * (size_t)N * H);
+  mx_tables();
+  int32_t *tptr, *tlist;
+  if (group_pairs(P, pair_t, N, &tptr, &tlist)) return -2;
+  const int K = 2 * I, KS = mx_ks(K);
+  int fail = 0;
+#pragma omp parallel
+  {
+    uint8_t* q = (uint8_t*)malloc((size_t)K);
+    uint8_t* sc = (uint8_t*)malloc((size_t)KS);
+    real* v = (real*)malloc(sizeof(real) * (size_t)K);
+    if (!q || !sc || !v) {
+#pragma omp atomic write
+      fail = 1;
+    } else {
+#pragma omp for schedule(dynamic, 4)
+      for (int t = 0; t < N; ++t) {
+        for (int c = tptr[t]; c < tptr[t + 1]; ++c) {
+          const int p = tlist[c], e = pair_e[p];
+          mx_quantize_row(dh + (size_t)p * K, K, q, sc);
+          for (int k = 0; k < K; ++k) v[k] = (real)(mx_elem_tab[q[k]] * mx_scale_tab[sc[k / 32]]);
+          for (int h = 0; h < H; ++h) {
+            const long row = (long)e * H + h;
+            real acc = 0;
+            for (int k = 0; k < K; ++k) acc += (real)mx_value(wq, ws, K, row, k) * v[k];
+            dx[(size_t)t * H + h] += (double)acc;
+          }
+          if (dhq) memcpy(dhq + (size_t)p * K, q, (size_t)K);
+          if (dhs) memcpy(dhs + (size_t)p * KS, sc, (size_t)KS);
+        }
+      }
+    }
+    free(q); free(sc); free(v);
+  }
+  free(tptr); free(tlist);
+  return fail ? -2 : 0;
+}

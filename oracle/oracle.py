@@ -64,7 +64,7 @@ def _lib(real: str = "f64"):
                                      _f64p]
     lib.oracle_layer_bwd.argtypes = [_f32p, _f32p, _f32p, _f32p, _f32p, ctypes.c_int,
                                      ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                     _i32p, _i32p, _f32p, _f64p, _f64p, _f64p, _f64p, _f64p]
+                                     _i32p, _i32p, _f32p, _f64p, _f64p, _f64p, _f64p, _f64p, _f64p]
     lib.oracle_capacity_plan.argtypes = [_f32p, _i32p, _f32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                          ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p, _i32p, _i32p, _f32p,
                                          _i32p, _i32p, _i32p]
@@ -79,7 +79,9 @@ def _lib(real: str = "f64"):
     lib.oracle_layer_fwd_mxfp8.argtypes = [_u8p, _u8p, _u8p, _u8p, _u8p, _u8p, _u8p, _u8p, ctypes.c_int,
                                            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p, _i32p,
                                            _f32p, _f64p, _f64p, _u8p, _u8p]
-    for fn in ("oracle_quantize_mxfp8", "oracle_layer_fwd_mxfp8", "oracle_set_threads", "oracle_route_topk", "oracle_permute", "oracle_token_round", "oracle_layer_fwd",
+    lib.oracle_dx_mxfp8.argtypes = [_f32p, _u8p, _u8p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_int, _i32p, _i32p, _f64p, _u8p, _u8p]
+    for fn in ("oracle_quantize_mxfp8", "oracle_layer_fwd_mxfp8", "oracle_dx_mxfp8", "oracle_set_threads", "oracle_route_topk", "oracle_permute", "oracle_token_round", "oracle_layer_fwd",
                "oracle_layer_bwd", "oracle_router_logits", "oracle_router_bwd", "oracle_capacity_plan",
                "oracle_real_bytes",
                "oracle_threads"):
@@ -228,7 +230,7 @@ def layer_fwd(x, wg, wu, wd, pair_t, pair_e, pair_w, real="f64"):
 def layer_bwd(dout, x, wg, wu, wd, pair_t, pair_e, pair_w, want=("dx", "dwg", "dwu", "dwd", "ds"),
               real="f64"):
     """Returns a dict with the requested float64 gradients: dx [N,H], dwg/dwu [E,I,H],
-    dwd [E,H,I], ds [P] (per pair)."""
+    dwd [E,H,I], ds [P] (per pair), dh [P,2I] (each pair's [dg | du], only when asked for)."""
     dout, x, wg, wu, wd = _f32(dout), _f32(x), _f32(wg), _f32(wu), _f32(wd)
     N, H = x.shape
     E, I, _ = wg.shape
@@ -240,10 +242,11 @@ def layer_bwd(dout, x, wg, wu, wd, pair_t, pair_e, pair_w, want=("dx", "dwg", "d
     res["dwu"] = np.empty((E, I, H), np.float64) if "dwu" in want else None
     res["dwd"] = np.empty((E, H, I), np.float64) if "dwd" in want else None
     res["ds"] = np.empty((P,), np.float64) if "ds" in want else None
+    res["dh"] = np.empty((P, 2 * I), np.float64) if "dh" in want else None
     _check(_lib(real).oracle_layer_bwd(_p(dout, _f32p), _p(x, _f32p), _p(wg, _f32p), _p(wu, _f32p),
                                        _p(wd, _f32p), N, H, I, E, P, _p(pair_t, _i32p),
                                        _p(pair_e, _i32p), _p(pair_w, _f32p),
-                                       *[_p(res[n], _f64p) for n in ("dx", "dwg", "dwu", "dwd", "ds")]),
+                                       *[_p(res[n], _f64p) for n in ("dx", "dwg", "dwu", "dwd", "ds", "dh")]),
            "oracle_layer_bwd")
     return {n: v for n, v in res.items() if v is not None}
 
@@ -332,3 +335,31 @@ def layer_fwd_mxfp8(x, wg, wu, wd, pair_t, pair_e, pair_w, want_stages=False, re
         None if st is None else _p(st["as"], _u8p)), "oracle_layer_fwd_mxfp8")
     return (out, st) if want_stages else out
 
+
+
+def dx_weights_mxfp8(wg, wu):
+    """The dX product's weight operand: for each expert e, [W_gate[e]^T | W_up[e]^T] ([H, 2I]:
+    row h holds W_gate[e][i][h] for i < I, then W_up[e][i][h]) quantized along its rows ->
+    (codes uint8 [E, H, 2I], scale codes uint8 [E, H, 4 ceil(2I/128)])."""
+    wt = np.concatenate([np.swapaxes(_f32(wg), 1, 2), np.swapaxes(_f32(wu), 1, 2)], axis=2)
+    return quantize_mxfp8(np.ascontiguousarray(wt))
+
+
+def dx_mxfp8(dh, wt, pair_t, pair_e, N, want_codes=False, real="f64"):
+    """dx [N,H] (float64) of the dX product on MX-FP8 operands: each pair's dh row [2I] (fp32
+    values) quantized, times its expert's quantized [W_gate^T | W_up^T] rows (wt = (codes,
+    scale codes) from dx_weights_mxfp8), summed per token.  With want_codes also the
+    quantized dh rows (codes [P, 2I], scale codes [P, KS(2I)])."""
+    wq, ws = (np.ascontiguousarray(a, np.uint8) for a in wt)
+    E, H, K = wq.shape
+    I = K // 2
+    dh = _f32(dh)
+    pair_t, pair_e = _i32(pair_t), _i32(pair_e)
+    P = len(pair_t)
+    dx = np.empty((N, H), np.float64)
+    q = np.empty((P, K), np.uint8) if want_codes else None
+    s = np.empty((P, mx_scale_cols(K)), np.uint8) if want_codes else None
+    _check(_lib(real).oracle_dx_mxfp8(_p(dh, _f32p), _p(wq, _u8p), _p(ws, _u8p), N, H, I, E, P, _p(pair_t, _i32p),
+                                      _p(pair_e, _i32p), _p(dx, _f64p), None if q is None else _p(q, _u8p),
+                                      None if s is None else _p(s, _u8p)), "oracle_dx_mxfp8")
+    return (dx, q, s) if want_codes else dx

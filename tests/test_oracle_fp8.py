@@ -180,3 +180,80 @@ def test_quantize_shapes_and_ragged_k(K):
     # each value within half an e4m3 step (relative 2^-4, or 2^-10 X below the normal range)
     X = np.repeat(2.0 ** (s[:, : K // 32].astype(np.float64) - 127), 32, axis=1)
     assert np.all(np.abs(d - v) <= np.maximum(np.abs(v) * 2.0 ** -4, 2.0 ** -10 * X) * (1 + 1e-12))
+
+
+def _small_bwd(seed=6, N=40, H=64, I=96, E=4, k=2):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((N, H)).astype(np.float32)
+    wg = (0.05 * rng.standard_normal((E, I, H))).astype(np.float32)
+    wu = (0.05 * rng.standard_normal((E, I, H))).astype(np.float32)
+    wd = (0.05 * rng.standard_normal((E, H, I))).astype(np.float32)
+    dout = rng.standard_normal((N, H)).astype(np.float32)
+    lg = rng.standard_normal((N, E)).astype(np.float32)
+    idx, w, _ = oracle.route_topk(lg, None, k)
+    pt, pe, pw = oracle.pairs_from_topk(idx, w)
+    return x, wg, wu, wd, dout, (pt, pe, pw), (N, H, I, E)
+
+
+def test_layer_bwd_dh_output_reproduces_dx():
+    """The backward's per-pair [dg | du] output, pushed through the weights by numpy
+    (dx[t] = sum over t's pairs of W_gate[e]^T dg + W_up[e]^T du), gives the backward's own dx."""
+    x, wg, wu, wd, dout, (pt, pe, pw), (N, H, I, E) = _small_bwd()
+    r = oracle.layer_bwd(dout, x, wg, wu, wd, pt, pe, pw, want=("dx", "dh"))
+    dh = r["dh"]
+    w64 = np.concatenate([wg.astype(np.float64), wu.astype(np.float64)], axis=1)  # [E, 2I, H]
+    contrib = np.einsum("pkh,pk->ph", w64[pe], dh)
+    ref = np.zeros((N, H))
+    np.add.at(ref, pt, contrib)
+    np.testing.assert_allclose(r["dx"], ref, rtol=1e-10, atol=1e-12)
+
+
+def test_dx_weights_layout_and_codes():
+    """The dX product's weight operand: row h of expert e is W_gate[e][:, h] then W_up[e][:, h],
+    each 32-block quantized by the pinned row quantization (torch's e4m3 rounding of v / X,
+    X from the literal scale rule)."""
+    x, wg, wu, wd, dout, _, (N, H, I, E) = _small_bwd()
+    q, s = oracle.dx_weights_mxfp8(wg, wu)
+    assert q.shape == (E, H, 2 * I) and s.shape == (E, H, oracle.mx_scale_cols(2 * I))
+    for e, h in ((0, 0), (1, 17), (E - 1, H - 1)):
+        row = np.concatenate([wg[e, :, h], wu[e, :, h]]).astype(np.float64)
+        for b in range(2 * I // 32):
+            blk = row[32 * b:32 * b + 32]
+            c = literal_scale_code(float(np.abs(blk).max()))
+            assert s[e, h, b] == c
+            np.testing.assert_array_equal(q[e, h, 32 * b:32 * b + 32], torch_e4m3_codes(blk / 2.0 ** (c - 127)))
+
+
+def test_dx_mxfp8_against_numpy():
+    """The dX product on MX-FP8 operands against a numpy product of torch-decoded operands:
+    each pair's dh row quantized by the literal rule, times its expert's decoded weight rows,
+    summed per token."""
+    x, wg, wu, wd, dout, (pt, pe, pw), (N, H, I, E) = _small_bwd()
+    dh = oracle.layer_bwd(dout, x, wg, wu, wd, pt, pe, pw, want=("dh",))["dh"].astype(np.float32)
+    wt = oracle.dx_weights_mxfp8(wg, wu)
+    dx, dq, dsc = oracle.dx_mxfp8(dh, wt, pt, pe, N, want_codes=True)
+    for p in range(0, len(pt), 5):
+        for b in range(2 * I // 32):
+            blk = dh[p, 32 * b:32 * b + 32].astype(np.float64)
+            c = literal_scale_code(float(np.abs(blk).max()))
+            assert dsc[p, b] == c
+            np.testing.assert_array_equal(dq[p, 32 * b:32 * b + 32], torch_e4m3_codes(blk / 2.0 ** (c - 127)))
+    wdec = torch_decode(*wt)  # [E, H, 2I]
+    contrib = np.einsum("phk,pk->ph", wdec[pe], torch_decode(dq, dsc))
+    ref = np.zeros((N, H))
+    np.add.at(ref, pt, contrib)
+    np.testing.assert_allclose(dx, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_dx_mxfp8_within_quantization_bound():
+    """Against the unquantized fp64 dx: the error stays within what quantizing both operands
+    allows (each e4m3 value within 2^-4 relative, so a product within about 2^-3 of its
+    magnitude): |dx_q - dx| <= 0.13 sum |dh| |W| per element."""
+    x, wg, wu, wd, dout, (pt, pe, pw), (N, H, I, E) = _small_bwd()
+    r = oracle.layer_bwd(dout, x, wg, wu, wd, pt, pe, pw, want=("dx", "dh"))
+    dxq = oracle.dx_mxfp8(r["dh"].astype(np.float32), oracle.dx_weights_mxfp8(wg, wu), pt, pe, N)
+    w64 = np.abs(np.concatenate([wg.astype(np.float64), wu.astype(np.float64)], axis=1))
+    bound = np.zeros((N, H))
+    np.add.at(bound, pt, np.einsum("pkh,pk->ph", w64[pe], np.abs(r["dh"])))
+    assert np.all(np.abs(dxq - r["dx"]) <= 0.13 * bound + 1e-12)
+    assert np.abs(dxq - r["dx"]).max() > 0  # the quantization is not the identity here
