@@ -13,6 +13,7 @@ import os
 __all__ = [
     "MoEError", "lib", "lib_path", "load_library", "Plan", "route_topk", "permute", "permute_noalloc",
     "route_token_rounding", "quantize_mxfp8", "grouped_gemm_fwd_mxfp8", "mx_scale_cols", "OP_GEMM_FWD_MXFP8",
+    "quantize_dx_weights_mxfp8", "layer_bwd_mxfp8", "OP_LAYER_BWD_MXFP8",
     "route_capacity", "grouped_gemm_fwd", "unpermute_combine", "layer_bwd", "router_logits", "router_bwd",
     "workspace_bytes", "plan_rows_cap", "MOE_OK", "MOE_EINVAL", "MOE_EUNSUPPORTED", "MOE_EWORKSPACE",
     "MOE_EHIP", "OP_PERMUTE", "OP_ROUTE_TR", "OP_GEMM_FWD", "OP_LAYER_BWD", "OP_ROUTER_BWD",
@@ -26,6 +27,7 @@ PLAN_TOPK, PLAN_TR, PLAN_CAP = 0, 1, 2
 CAP_POSITION, CAP_PROBS = 0, 1
 OP_PERMUTE, OP_ROUTE_TR, OP_GEMM_FWD, OP_LAYER_BWD, OP_ROUTER_BWD, OP_ROUTER_LOGITS = 0, 1, 2, 3, 4, 5
 OP_GEMM_FWD_MXFP8 = 6
+OP_LAYER_BWD_MXFP8 = 7
 
 EXPORTED_SYMBOLS = (
     "moe_plan_rows_cap", "moe_workspace_bytes", "moe_last_error", "moe_route_topk", "moe_permute",
@@ -33,13 +35,14 @@ EXPORTED_SYMBOLS = (
     "moe_route_token_rounding", "moe_route_capacity", "moe_grouped_gemm_fwd", "moe_unpermute_combine",
     "moe_layer_bwd",
     "moe_router_logits", "moe_router_bwd", "moe_set_kernel_events", "moe_quantize_mxfp8",
-    "moe_grouped_gemm_fwd_mxfp8",
+    "moe_grouped_gemm_fwd_mxfp8", "moe_quantize_dx_weights_mxfp8", "moe_layer_bwd_mxfp8",
 )
 
 # kernel ids of the measurement hook (moe_kernel_id in include/moe.h)
 KERNEL_IDS = {"gateup": 0, "down": 1, "dh": 2, "dx": 3, "dwd": 4, "dw1": 5, "combine": 6, "dx_combine": 7,
               "route": 8, "permute": 9, "route_tr_plan": 10, "dswiglu": 11, "router_logits": 12,
-              "router_dz": 13, "router_dx": 14, "router_dw": 15, "gateup_fp8": 16, "down_fp8": 17, "quant": 18}
+              "router_dz": 13, "router_dx": 14, "router_dw": 15, "gateup_fp8": 16, "down_fp8": 17, "quant": 18,
+              "dx_fp8": 19}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -104,11 +107,15 @@ def load_library(path: str):
     L.moe_set_kernel_events.argtypes = [i32, vp, vp]
     L.moe_quantize_mxfp8.argtypes = [ctypes.c_int, vp, ctypes.c_int64, i32, vp, vp, vp]
     L.moe_grouped_gemm_fwd_mxfp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, pp, vp, vp, vp, sz, vp]
+    L.moe_quantize_dx_weights_mxfp8.argtypes = [ctypes.c_int, vp, vp, i32, i32, i32, vp, vp, vp]
+    L.moe_layer_bwd_mxfp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, pp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                      vp]
     for fn in ("moe_route_topk", "moe_permute", "moe_permute_noalloc", "moe_route_token_rounding",
                "moe_route_capacity",
                "moe_grouped_gemm_fwd",
                "moe_unpermute_combine", "moe_layer_bwd", "moe_router_logits", "moe_router_bwd",
-               "moe_set_kernel_events", "moe_quantize_mxfp8", "moe_grouped_gemm_fwd_mxfp8"):
+               "moe_set_kernel_events", "moe_quantize_mxfp8", "moe_grouped_gemm_fwd_mxfp8",
+               "moe_quantize_dx_weights_mxfp8", "moe_layer_bwd_mxfp8"):
         getattr(L, fn).restype = ctypes.c_int
     return L
 
@@ -360,6 +367,43 @@ def layer_bwd(dout, x, w_gate, w_up, w_down, plan: Plan, hcache, dx=None, dw_gat
     _check(lib().moe_layer_bwd(dt, _ptr(dout), _ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down), H, I, plan.c,
                                _ptr(hcache), _ptr(dx), _ptr(dw_gate), _ptr(dw_up), _ptr(dw_down), _ptr(ds),
                                _ptr(ws), nb, _stream(stream)))
+    return dict(dx=dx, dw_gate=dw_gate, dw_up=dw_up, dw_down=dw_down, ds=ds)
+
+
+def quantize_dx_weights_mxfp8(w_gate, w_up, q=None, scales=None, stream=None):
+    """The dX product's MX-FP8 weight operand: each expert's [W_gate^T | W_up^T] ([H, 2I])
+    quantized along 2I -> (codes uint8 [E, H, 2I], scale codes uint8 [E, H, 4 ceil(2I/128)])."""
+    import torch
+    E, I, H = w_gate.shape
+    q = q if q is not None else torch.empty((E, H, 2 * I), dtype=torch.uint8, device=w_gate.device)
+    scales = scales if scales is not None else torch.empty((E, H, mx_scale_cols(2 * I)), dtype=torch.uint8,
+                                                           device=w_gate.device)
+    _check(lib().moe_quantize_dx_weights_mxfp8(_dtype_code(w_gate), _ptr(w_gate), _ptr(w_up), E, H, I, _ptr(q),
+                                               _ptr(scales), _stream(stream)))
+    return q, scales
+
+
+def layer_bwd_mxfp8(dout, x, w_gate, w_up, w_down, wt, plan: Plan, hcache, dx=None, dw_gate=None, dw_up=None,
+                    dw_down=None, ds=None, ws=None, stream=None):
+    """layer_bwd for bf16 layers with the dX product on MX-FP8 operands; wt = (codes, scale
+    codes) from quantize_dx_weights_mxfp8.  -> dict(dx, dw_gate, dw_up, dw_down, ds)."""
+    import torch
+    N, H = x.shape
+    E, I, _ = w_gate.shape
+    wq, wsc = wt
+    dev = x.device
+    dx = dx if dx is not None else torch.empty_like(x)
+    dw_gate = dw_gate if dw_gate is not None else torch.empty_like(w_gate)
+    dw_up = dw_up if dw_up is not None else torch.empty_like(w_up)
+    dw_down = dw_down if dw_down is not None else torch.empty_like(w_down)
+    if ds is None:
+        shape = (N, plan.k) if plan.kind == PLAN_TOPK else (max(plan.M_cap, 1),)
+        ds = torch.empty(shape, dtype=torch.float32, device=dev)
+    nb = workspace_bytes(OP_LAYER_BWD_MXFP8, MOE_BF16, plan.N, plan.E, plan.k, H, I, plan.M_cap)
+    ws = _ws(nb, dev, ws)
+    _check(lib().moe_layer_bwd_mxfp8(_ptr(dout), _ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(wq),
+                                     _ptr(wsc), H, I, plan.c, _ptr(hcache), _ptr(dx), _ptr(dw_gate), _ptr(dw_up),
+                                     _ptr(dw_down), _ptr(ds), _ptr(ws), nb, _stream(stream)))
     return dict(dx=dx, dw_gate=dw_gate, dw_up=dw_up, dw_down=dw_down, ds=ds)
 
 

@@ -163,6 +163,9 @@ size_t moe_workspace_bytes(moe_op op, moe_dtype dt, int32_t N, int32_t E, int32_
     case MOE_OP_GEMM_FWD_MXFP8:
       if (H < 32 || I < 32 || H % 32 || I % 32 || M_cap < 0) return 0;
       return moe::gemm_fwd_mxfp8_ws_bytes(M_cap, I);
+    case MOE_OP_LAYER_BWD_MXFP8:
+      if (H < 32 || I < 32 || H % 32 || I % 32 || M_cap < 0) return 0;
+      return moe::layer_bwd_mxfp8_ws_bytes(N, M_cap, H, I);
   }
   return 0;
 }
@@ -379,6 +382,52 @@ moe_status moe_layer_bwd(moe_dtype dt, const void* dout, const void* x, const vo
   return hip_status(moe::launch_layer_bwd(dt, dout, x, w_gate, w_up, w_down, H, I, *plan, hcache, dx, dw_gate,
                                           dw_up, dw_down, ds, ws, (hipStream_t)stream),
                     "moe_layer_bwd");
+}
+
+moe_status moe_quantize_dx_weights_mxfp8(moe_dtype dt, const void* w_gate, const void* w_up, int32_t E, int32_t H,
+                                         int32_t I, uint8_t* wt_q, uint8_t* wt_s, void* stream) {
+  g_err[0] = 0;
+  moe_status st;
+  if ((st = check_dtype(dt)) != MOE_OK) return st;
+  REQUIRE(E >= 1 && E <= 1024, MOE_EINVAL, "E must be in [1, 1024] (got %d)", E);
+  REQUIRE(H >= 32 && I >= 32, MOE_EINVAL, "H and I must be >= 32 (got H=%d, I=%d)", H, I);
+  REQUIRE(H % 32 == 0 && I % 32 == 0, MOE_EUNSUPPORTED, "H and I must be multiples of 32 (got H=%d, I=%d)", H, I);
+  REQUIRE(w_gate && w_up && wt_q && wt_s, MOE_EINVAL, "NULL argument");
+  REQUIRE(aligned16(wt_q), MOE_EUNSUPPORTED, "wt_q must be 16-byte aligned");
+  REQUIRE((int64_t)H * 2 * I <= kDescBytes, MOE_EUNSUPPORTED, "one expert's [H=%d, 2I=%d] codes must be < 2 GiB", H,
+          2 * I);
+  moe::kernel_event(MOE_K_QUANT, 0, (hipStream_t)stream);
+  hipError_t e = moe::launch_quant_dx_weights(dt, w_gate, w_up, E, H, I, wt_q, wt_s, (hipStream_t)stream);
+  moe::kernel_event(MOE_K_QUANT, 1, (hipStream_t)stream);
+  return hip_status(e, "moe_quantize_dx_weights_mxfp8");
+}
+
+moe_status moe_layer_bwd_mxfp8(const void* dout, const void* x, const void* w_gate, const void* w_up,
+                               const void* w_down, const uint8_t* wt_q, const uint8_t* wt_s, int32_t H, int32_t I,
+                               const moe_plan* plan, const void* hcache, void* dx, void* dw_gate, void* dw_up,
+                               void* dw_down, float* ds, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  moe_status st;
+  REQUIRE(H >= 32 && I >= 32, MOE_EINVAL, "H and I must be >= 32 (got H=%d, I=%d)", H, I);
+  REQUIRE(H % 32 == 0 && I % 32 == 0, MOE_EUNSUPPORTED, "H and I must be multiples of 32 (got H=%d, I=%d)", H, I);
+  if ((st = check_plan(plan)) != MOE_OK) return st;
+  REQUIRE(w_gate && w_up && w_down && dw_gate && dw_up && dw_down && wt_q && wt_s, MOE_EINVAL,
+          "NULL weight/gradient argument");
+  REQUIRE(plan->N == 0 || (dout && x && dx), MOE_EINVAL, "NULL activation argument");
+  REQUIRE(plan->M_cap == 0 || (hcache && ds), MOE_EINVAL, "NULL hcache/ds argument");
+  REQUIRE(aligned16(dout) && aligned16(x) && aligned16(w_gate) && aligned16(w_up) && aligned16(w_down) &&
+              aligned16(hcache) && aligned16(dx) && aligned16(dw_gate) && aligned16(dw_up) && aligned16(dw_down) &&
+              aligned16(ws) && aligned16(wt_q) && ((uintptr_t)wt_s & 3u) == 0,
+          MOE_EUNSUPPORTED, "tensors and workspace must be 16-byte aligned, wt_s 4-byte aligned");
+  if ((st = check_desc_sizes(MOE_BF16, plan->N, H, I, plan->M_cap)) != MOE_OK) return st;
+  REQUIRE((int64_t)H * 2 * I <= kDescBytes, MOE_EUNSUPPORTED, "one expert's [H=%d, 2I=%d] codes must be < 2 GiB", H,
+          2 * I);
+  const size_t need = moe::layer_bwd_mxfp8_ws_bytes(plan->N, (int)mcap_of(plan), H, I);
+  REQUIRE(ws_bytes >= need, MOE_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  REQUIRE(ws != nullptr, MOE_EINVAL, "NULL workspace");
+  return hip_status(moe::launch_layer_bwd_mxfp8(dout, x, w_gate, w_up, w_down, wt_q, wt_s, H, I, *plan, hcache, dx,
+                                                dw_gate, dw_up, dw_down, ds, ws, (hipStream_t)stream),
+                    "moe_layer_bwd_mxfp8");
 }
 
 moe_status moe_router_logits(moe_dtype dt, const void* x, const float* w_r, const float* bias, int32_t N,

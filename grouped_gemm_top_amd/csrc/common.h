@@ -132,4 +132,12 @@ size_t layer_bwd_ws_bytes(moe_dtype dt, int N, int M_cap, int H, int I);
 hipError_t launch_layer_bwd(moe_dtype dt, const void* dout, const void* x, const void* wg, const void* wu,
                             const void* wd, int H, int I, const moe_plan& p, const void* hcache, void* dx,
                             void* dwg, void* dwu, void* dwd, float* ds, void* ws, hipStream_t s);
+// the backward with its dX product on MX-FP8 operands (bf16 layers)
+hipError_t launch_quant_dx_weights(moe_dtype dt, const void* wg, const void* wu, int E, int H, int I, uint8_t* q,
+                                   uint8_t* scales, hipStream_t s);
+size_t layer_bwd_mxfp8_ws_bytes(int N, int M_cap, int H, int I);
+hipError_t launch_layer_bwd_mxfp8(const void* dout, const void* x, const void* wg, const void* wu, const void* wd,
+                                  const void* wtq, const void* wts, int H, int I, const moe_plan& p,
+                                  const void* hcache, void* dx, void* dwg, void* dwu, void* dwd, float* ds, void* ws,
+                                  hipStream_t s);
 }  // namespace moe

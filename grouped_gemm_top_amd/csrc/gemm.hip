@@ -927,10 +927,19 @@ size_t layer_bwd_ws_bytes(moe_dtype dt, int N, int M_cap, int H, int I) {
          align256((size_t)M_cap * H * es) + align256(part) + 256;
 }
 
+// MX-FP8 dX product: moe_layer_bwd's workspace, then the scale codes of the quantized dH
+// [M_cap, KS(2I)] (its codes [M_cap, 2I] reuse the A' region, free once dW_down has run).
+size_t layer_bwd_mxfp8_ws_bytes(int N, int M_cap, int H, int I) {
+  return layer_bwd_ws_bytes(MOE_BF16, N, M_cap, H, I) + align256((size_t)M_cap * 4 * ((2 * I + 127) / 128));
+}
+
+// wtq / wts: the quantized [W_gate^T | W_up^T] of every expert for a dX product on MX-FP8
+// operands (bf16 layers only), or NULL for the bf16 product.
 template <typename T>
 static hipError_t layer_bwd_t(const void* dout, const void* x, const void* wg, const void* wu, const void* wd,
                               int H, int I, const moe_plan& p, const void* hcache, void* dx, void* dwg,
-                              void* dwu, void* dwd, float* ds, void* ws, hipStream_t s) {
+                              void* dwu, void* dwd, float* ds, void* ws, hipStream_t s, const void* wtq = nullptr,
+                              const void* wts = nullptr) {
   const size_t es = sizeof(T);
   constexpr bool BF = std::is_same<T, bf16_t>::value;
   const int tn = BF ? 256 : gg::BN;  // N-tile width of the dH kernel
@@ -981,11 +990,34 @@ static hipError_t layer_bwd_t(const void* dout, const void* x, const void* wg, c
   if ((err = launch(KDW1{}, (long long)p.E * mtw * ((H + tn - 1) / tn))) != hipSuccess) return err;
   // dXe = dH [W_gate; W_up]   (varlen-M), then the unweighted combine to token order
   a.out0 = dxe; a.out1 = nullptr;
-  if ((err = launch(KDX{}, mt * ((H + tn - 1) / tn))) != hipSuccess) return err;
+  if (BF && wtq != nullptr) {
+    // on MX-FP8 operands: dH quantized along its 2I values (codes into the A' region, scale
+    // codes after the workspace's other parts), then the product out[m][h] = sum_k dH~[m][k]
+    // W~^T[e][h][k] as DOWN8's GEMM with K = 2I
+    uint8_t* dhq = static_cast<uint8_t*>(aprime);
+    uint8_t* dhs = reinterpret_cast<uint8_t*>(w);
+    kernel_event(MOE_K_QUANT, 0, s);
+    err = launch_quant_mxfp8(MOE_BF16, dh, p.M_cap, 2 * I, dhq, dhs, s);
+    kernel_event(MOE_K_QUANT, 1, s);
+    if (err != hipSuccess) return err;
+    gg::Args a8 = a;
+    a8.act = dhq; a8.acts = dhs; a8.wd = wtq; a8.wds = wts; a8.out0 = dxe; a8.out1 = nullptr;
+    a8.I = 2 * I;
+    if ((err = run_gemm_bf16<gg::DX8>(a8, mt * ((H + tn - 1) / tn), s)) != hipSuccess) return err;
+  } else if ((err = launch(KDX{}, mt * ((H + tn - 1) / tn))) != hipSuccess) {
+    return err;
+  }
   kernel_event(MOE_K_DX_COMBINE, 0, s);
   err = launch_combine(sizeof(T) == 2 ? MOE_BF16 : MOE_F32, dxe, H, p, nullptr, dx, s, dspart, nP, ds);
   kernel_event(MOE_K_DX_COMBINE, 1, s);
   return err;
+}
+
+hipError_t launch_layer_bwd_mxfp8(const void* dout, const void* x, const void* wg, const void* wu, const void* wd,
+                                  const void* wtq, const void* wts, int H, int I, const moe_plan& p,
+                                  const void* hcache, void* dx, void* dwg, void* dwu, void* dwd, float* ds, void* ws,
+                                  hipStream_t s) {
+  return layer_bwd_t<bf16_t>(dout, x, wg, wu, wd, H, I, p, hcache, dx, dwg, dwu, dwd, ds, ws, s, wtq, wts);
 }
 
 hipError_t launch_layer_bwd(moe_dtype dt, const void* dout, const void* x, const void* wg, const void* wu,

@@ -68,6 +68,7 @@ using gg::DWD;
 using gg::DW1;
 using gg::GATEUP8;
 using gg::DOWN8;
+using gg::DX8;
 
 constexpr int NT = 512;        // threads per workgroup
 constexpr int BM = 256, BN = 256, BK = 32;  // varlen-K tiles; k = 32 per stage
@@ -90,6 +91,9 @@ template <> struct KT<DWD> { static constexpr bool A_KC = false, B_KC = false, V
 template <> struct KT<DW1> { static constexpr bool A_KC = false, B_KC = false, VK = true, GA = false, GB = true, F8 = false; static constexpr int ST = 16, MI = 4; };
 template <> struct KT<GATEUP8> { static constexpr bool A_KC = true, B_KC = true, VK = false, GA = true, GB = false, F8 = true; static constexpr int ST = 32, MI = 5; };
 template <> struct KT<DOWN8> { static constexpr bool A_KC = true, B_KC = true, VK = false, GA = false, GB = false, F8 = true; static constexpr int ST = 16, MI = 5; };
+// DX8 is DOWN8's product out[m][h] = sum_k A[m][k] B[h][k] with A = the rows' quantized dH
+// ([M, 2I]), B = expert e's quantized [W_gate^T | W_up^T] ([H, 2I]): launched with Args.I = 2I.
+template <> struct KT<DX8> : KT<DOWN8> {};
 
 // Per-kind tile geometry: BMK rows per M-tile; a stage covers BKS values of k and holds OPA
 // bytes of A then OPB bytes of B; NST stages form the LDS ring.
@@ -164,7 +168,7 @@ struct Sched {
       c.mlen = min(BMK, cnt - c.mt * BMK);
       switch (KIND) {
         case GATEUP: case GATEUP8: case DH: c.K = a.H; break;
-        case DOWN: case DOWN8: c.K = a.I; break;
+        case DOWN: case DOWN8: case DX8: c.K = a.I; break;
         default: c.K = 2 * a.I; break;  // DX
       }
     } else {
@@ -248,7 +252,7 @@ struct Loader {
   __device__ __forceinline__ void setup(const Args& a, const Tile& c, const int* tok, int w, int L, int nMg) {
     const int H = a.H, I = a.I;
     constexpr uint32_t ES = (uint32_t)G::ES;
-    constexpr bool GU = KIND == GATEUP || KIND == GATEUP8, DN = KIND == DOWN || KIND == DOWN8;
+    constexpr bool GU = KIND == GATEUP || KIND == GATEUP8, DN = KIND == DOWN || KIND == DOWN8 || KIND == DX8;
     if constexpr (!T::VK) {
       uint32_t rowA[5], rowB[4];  // K-contiguous: row byte offsets (OOB when masked)
       const long long rb = (long long)c.roff + (long long)c.mt * G::BMK;  // first row of the M-tile
@@ -327,7 +331,7 @@ struct Loader {
           const int i = c.nt * 128 + ((L >> 4) & 1) * 64 + 8 * w + (L & 7);  // q = L >> 3: gate (even), up (odd)
           vSB = (c.valid && L < 32 && i < I) ? (uint32_t)i * (uint32_t)KSH : OOB;
           rSB2 = sgpr4(rSB2);
-        } else {  // DOWN8: A is the tile's rows of the quantized activation, B is W_down[e]
+        } else {  // DOWN8 / DX8: A is the tile's rows of the quantized activation (dH), B is W_down[e] (W^T[e])
           rSA = dmadesc_off(a.acts, rb * KSI, (long long)c.mlen * KSI);
           vSA = oka ? (uint32_t)r * (uint32_t)KSI : OOB;
           rSB = dmadesc_off(a.wds, (long long)c.e * H * KSI, (long long)H * KSI);
@@ -415,7 +419,7 @@ struct Loader {
         for (int q = 0; q < 4; ++q) {
           const uint32_t m = mB + (uint32_t)(w + 8 * q) * 1024u;
           if constexpr (KIND == GATEUP || KIND == GATEUP8) dma16((q & 1) ? rB2 : rB, m, vB[q], so);
-          if constexpr (KIND == DOWN || KIND == DOWN8) dma16(rB, m, vB[q], so);
+          if constexpr (KIND == DOWN || KIND == DOWN8 || KIND == DX8) dma16(rB, m, vB[q], so);
           if constexpr (KIND == DH) dma16(rB, m, vB[q], (uint32_t)k0 * (uint32_t)I * 2u);
           if constexpr (KIND == DX) {
             const bool up = k0 >= I;  // the whole stage lies in one half
@@ -435,7 +439,7 @@ struct Loader {
         const uint32_t m = mB + (uint32_t)(w + 8 * q) * 1024u;
         if constexpr (KIND == GATEUP || KIND == GATEUP8)
           dma16((q & 1) ? rB2 : rB, m, kv ? vB[q] + (uint32_t)k0 * ES : OOB, 0u);
-        if constexpr (KIND == DOWN || KIND == DOWN8) dma16(rB, m, kv ? vB[q] + (uint32_t)k0 * ES : OOB, 0u);
+        if constexpr (KIND == DOWN || KIND == DOWN8 || KIND == DX8) dma16(rB, m, kv ? vB[q] + (uint32_t)k0 * ES : OOB, 0u);
         if constexpr (KIND == DH) {
           const uint32_t k = (uint32_t)(k0 + mn_k[q]);
           dma16(rB, m, colB[q] + k * (uint32_t)I * 2u, 0u);  // k >= H lies past the range
@@ -631,7 +635,7 @@ __device__ __forceinline__ void epilogue(const Args& a, const Tile& c, f32x4 (&a
         if (q < 8) st16(ra, ii < I ? m * (uint32_t)I * 2u + (uint32_t)ii * 2u : OOB, v);
       }
     }
-  } else if constexpr (KIND == DOWN || KIND == DOWN8 || KIND == DX) {
+  } else if constexpr (KIND == DOWN || KIND == DOWN8 || KIND == DX || KIND == DX8) {
     const rsrc_t ro = gg::mkr_off(a.out0, rb * H * 2, (long long)c.mlen * H * 2);
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
@@ -912,7 +916,7 @@ __global__ __launch_bounds__(NT, 1) void k_gg_bf16(Args a, const int32_t* __rest
   S.slot = blockIdx.x >> 3;
   switch (KIND) {
     case GATEUP: case GATEUP8: S.nN = (a.I + 127) / 128; break;
-    case DOWN: case DOWN8: case DX: case DW1: S.nN = (a.H + BN - 1) / BN; break;
+    case DOWN: case DOWN8: case DX: case DX8: case DW1: S.nN = (a.H + BN - 1) / BN; break;
     default: S.nN = (a.I + BN - 1) / BN; break;  // DH, DWD
   }
   S.nMg = (a.I + BM - 1) / BM;
@@ -1356,5 +1360,6 @@ template hipError_t run_gemm_bf16<gg::DWD>(const gg::Args&, long long, hipStream
 template hipError_t run_gemm_bf16<gg::DW1>(const gg::Args&, long long, hipStream_t);
 template hipError_t run_gemm_bf16<gg::GATEUP8>(const gg::Args&, long long, hipStream_t);
 template hipError_t run_gemm_bf16<gg::DOWN8>(const gg::Args&, long long, hipStream_t);
+template hipError_t run_gemm_bf16<gg::DX8>(const gg::Args&, long long, hipStream_t);
 
 }  // namespace moe

@@ -10,7 +10,8 @@ namespace gg {
 // moe_kernel_id.
 enum Kind {
   GATEUP = MOE_K_GATEUP, DOWN = MOE_K_DOWN, DH = MOE_K_DH, DX = MOE_K_DX, DWD = MOE_K_DWD, DW1 = MOE_K_DW1,
-  GATEUP8 = MOE_K_GATEUP_FP8, DOWN8 = MOE_K_DOWN_FP8
+  GATEUP8 = MOE_K_GATEUP_FP8, DOWN8 = MOE_K_DOWN_FP8,
+  DX8 = MOE_K_DX_FP8  // the dX product on MX-FP8 operands: DOWN8's GEMM with K = 2I
 };
 
 struct Args {

@@ -78,7 +78,8 @@ typedef enum moe_op {
   MOE_OP_LAYER_BWD = 3,
   MOE_OP_ROUTER_BWD = 4,
   MOE_OP_ROUTER_LOGITS = 5,
-  MOE_OP_GEMM_FWD_MXFP8 = 6
+  MOE_OP_GEMM_FWD_MXFP8 = 6,
+  MOE_OP_LAYER_BWD_MXFP8 = 7
 } moe_op;
 
 /*
@@ -275,6 +276,32 @@ moe_status moe_grouped_gemm_fwd_mxfp8(const uint8_t* x_q, const uint8_t* x_s, co
                                       void* stream);
 
 /*
+ * The backward's dX product on MX-FP8 operands: the FP8 grouped GEMM of [GG] "한계" applied to
+ * dXe = dH [W_gate; W_up] of moe_layer_bwd, in the MX-FP8 layout of moe_quantize_mxfp8.
+ *
+ * moe_quantize_dx_weights_mxfp8: its weight operand.  For each expert e the matrix
+ * [W_gate[e]^T | W_up[e]^T] ([H, 2I]: row h holds W_gate[e][i][h] for i < I, then
+ * W_up[e][i][h]) quantized along its rows, 2I values in blocks of 32 (I a multiple of 32, so
+ * no block mixes gate and up): codes wt_q [E, H, 2I], scale codes wt_s [E, H, 4 ceil(2I/128)].
+ * Quantized once per weight update; bit for bit what moe_quantize_mxfp8 gives for that matrix.
+ *   w_gate, w_up [E, I, H] (dtype dt); H, I multiples of 32; H * 2I bytes below 2 GiB.
+ *
+ * moe_layer_bwd_mxfp8: moe_layer_bwd for bf16 layers with its dX product on MX-FP8 operands:
+ * each row's dH = [dG | dU] (stored in bf16, as in moe_layer_bwd) is quantized along its 2I
+ * values, and dXe is taken from those codes and wt_q / wt_s, then combined per token in
+ * ascending row order as before.  dW_gate, dW_up, dW_down and dS come from the same kernels
+ * as in moe_layer_bwd, bit for bit; dx differs by the quantization of both operands.
+ * H, I multiples of 32.  Workspace: moe_workspace_bytes(MOE_OP_LAYER_BWD_MXFP8, MOE_BF16, ...)
+ * (moe_layer_bwd's plus the dH scale codes).
+ */
+moe_status moe_quantize_dx_weights_mxfp8(moe_dtype dt, const void* w_gate, const void* w_up, int32_t E, int32_t H,
+                                         int32_t I, uint8_t* wt_q, uint8_t* wt_s, void* stream);
+moe_status moe_layer_bwd_mxfp8(const void* dout, const void* x, const void* w_gate, const void* w_up,
+                               const void* w_down, const uint8_t* wt_q, const uint8_t* wt_s, int32_t H, int32_t I,
+                               const moe_plan* plan, const void* hcache, void* dx, void* dw_gate, void* dw_up,
+                               void* dw_down, float* ds, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Weighted combine back to token order ([EP] "여러 Expert의 결과도 같은 토큰으로
  * 돌아오기"; [DEP] "3) Combine"):
  *   out[t] = sum over r in tok_rows(t) of row_w[r] * y[r]     (row_w NULL: weights 1)
@@ -382,8 +409,10 @@ typedef enum moe_kernel_id {
   MOE_K_ROUTER_DW = 15,  /* moe_router_bwd: dW_r and dbias (sliced product + ordered reduction) */
   MOE_K_GATEUP_FP8 = 16, /* moe_grouped_gemm_fwd_mxfp8: gate/up grouped GEMM + SwiGLU + A quantization */
   MOE_K_DOWN_FP8 = 17,   /* moe_grouped_gemm_fwd_mxfp8: down grouped GEMM */
-  MOE_K_QUANT = 18,      /* moe_quantize_mxfp8 */
-  MOE_K_COUNT = 19
+  MOE_K_QUANT = 18,      /* moe_quantize_mxfp8, moe_quantize_dx_weights_mxfp8, and moe_layer_bwd_mxfp8's
+                            quantization of dH */
+  MOE_K_DX_FP8 = 19,     /* moe_layer_bwd_mxfp8: the dX grouped GEMM on MX-FP8 operands */
+  MOE_K_COUNT = 20
 } moe_kernel_id;
 
 moe_status moe_set_kernel_events(int32_t kernel_id, void* start_event, void* stop_event);
