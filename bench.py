@@ -227,6 +227,73 @@ def fp8_forward(args, wl, x, wg, wu, wd, plan, M, e_act, kern_ms):
     return out
 
 
+def fp8_backward_dx(args, wl, x, wg, wu, wd, dout, plan, hcache, M, e_act, kern_ms):
+    """The backward with its dX product on MX-FP8 operands (moe_layer_bwd_mxfp8) on the bf16
+    run's plan and forward: each expert's [W_gate^T | W_up^T] quantized once (timed on its own,
+    a cost paid once per weight update), then per step the whole backward, with the quantization
+    of dH and the fp8 dX GEMM timed by HIP events beside the bf16 run's dX GEMM."""
+    import torch
+    import grouped_gemm_top_amd as G
+    N, H, I, E = wl.N, wl.H, wl.I, wl.E
+    wt = G.quantize_dx_weights_mxfp8(wg, wu)
+    a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a_.record()
+    G.quantize_dx_weights_mxfp8(wg, wu, q=wt[0], scales=wt[1])
+    b_.record()
+    torch.cuda.synchronize()
+    wq_ms = a_.elapsed_time(b_)
+    o = dict(dx=torch.empty_like(x), dw_gate=torch.empty_like(wg), dw_up=torch.empty_like(wu),
+             dw_down=torch.empty_like(wd), ds=torch.empty((N, wl.k), dtype=torch.float32, device="cuda"))
+    ws8 = torch.empty(G.workspace_bytes(G.OP_LAYER_BWD_MXFP8, G.MOE_BF16, N, E, wl.k, H, I, plan.M_cap),
+                      dtype=torch.uint8, device="cuda")
+
+    def stepb():
+        G.layer_bwd_mxfp8(dout, x, wg, wu, wd, wt, plan, hcache, ws=ws8, **o)
+
+    for _ in range(args.warmup):
+        stepb()
+    names = ("quant", "dx_fp8")
+    evs = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)] for n in names}
+    for pairs in evs.values():
+        for e0, e1 in pairs:
+            e0.record()
+            e1.record()
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        for n in names:
+            G.set_kernel_events(n, *evs[n][i])
+        stepb()
+    torch.cuda.synchronize()
+    for n in names:
+        G.set_kernel_events(n, None, None)
+    us = {n: 1e3 * float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs[n]])) for n in names}
+    sc = 1.0 + 1.0 / 32  # codes plus one scale byte per 32
+    f = 4.0 * M * H * I
+    b = M * 2 * I * sc + 2.0 * e_act * I * H * sc + 2.0 * M * H  # dH codes, weight codes, dXe (bf16)
+    bf16_us = 1e3 * kern_ms["dx"]
+    t_s = us["dx_fp8"] * 1e-6
+    out = {"note": "backward with the dX product on MX-FP8 operands (moe_layer_bwd_mxfp8) on the bf16 run's plan; "
+                   "[W_gate^T | W_up^T] quantized once, dH every step; dW and dS as in the bf16 backward",
+           "kernels_us": {"quant_dh": round(us["quant"], 2), "dx_fp8": round(us["dx_fp8"], 2)},
+           "weights_quant_ms": round(wq_ms, 3),
+           "bf16_dx_us": round(bf16_us, 2),
+           "speedup_vs_bf16_dx": round(bf16_us / (us["quant"] + us["dx_fp8"]), 3),
+           "gemm_speedup_vs_bf16_dx": round(bf16_us / us["dx_fp8"], 3),
+           "dx_fp8_tflops": round(f / t_s / 1e12, 1)}
+    if b / (PEAK_HBM_GBS * 1e9) >= f / (PEAK_FP8_TFLOPS * 1e12):
+        out["roofline"] = {"kernel": "dx_fp8", "bound": "hbm", "achieved": round(b / t_s / 1e9, 1),
+                           "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(b / t_s / 1e9 / PEAK_HBM_GBS, 4),
+                           "traffic": None, "algorithmic_bytes": b, "us": round(us["dx_fp8"], 2)}
+    else:
+        out["roofline"] = {"kernel": "dx_fp8", "bound": "mfma", "achieved": round(f / t_s / 1e12, 1),
+                           "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                           "frac": round(f / t_s / 1e12 / PEAK_FP8_TFLOPS, 4), "traffic": None,
+                           "algorithmic_flops": f, "us": round(us["dx_fp8"], 2)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -252,7 +319,8 @@ def main():
     ap.add_argument("--peaks", type=int, default=1, help="measure the device peaks after the layer (1/0)")
     ap.add_argument("--fp8", type=int, default=1,
                     help="also time the MX-FP8 forward (quantize x, gate/up + down on fp8 operands) beside the "
-                         "bf16 forward GEMMs (1/0; bf16 top-k workloads)")
+                         "bf16 forward GEMMs, and the backward's dX product on fp8 operands beside the bf16 one "
+                         "(1/0; bf16 top-k workloads)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -501,6 +569,9 @@ def main():
         }
     if args.fp8 and wl.dtype == "bf16" and not rt and args.kernel_events:
         res["fp8"] = fp8_forward(args, wl, x, wg, wu, wd, plan, M, e_act, kern_ms)
+        if wl.H % 32 == 0 and wl.I % 32 == 0:
+            res["fp8"]["backward_dx"] = fp8_backward_dx(args, wl, x, wg, wu, wd, dout, plan, hcache, M, e_act,
+                                                        kern_ms)
     # The bound the whole step can reach: the larger of its FLOPs at the MFMA peak and its
     # algorithmic bytes (every tensor touched once per pass) at the HBM peak.
     lb = layer_bytes(wl, M, e_act, es)
