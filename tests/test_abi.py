@@ -232,3 +232,28 @@ def test_probe_library_exports_and_validation():
     assert P.moe_probe_copy(f, f, 0, 8, None) == 0              # empty: nothing to queue
     assert P.moe_probe_read(f, 32, 8, None, None) == 1
     assert P.moe_probe_read(f, 32, 70000, f, None) == 1         # too many blocks
+
+
+def test_mxfp8_dx_errors(L):
+    """moe_quantize_dx_weights_mxfp8 and moe_layer_bwd_mxfp8 refuse bad arguments before
+    anything is queued (H and I multiples of 32, weight codes given and aligned, workspace)."""
+    f = ctypes.c_void_p(FAKE)
+    qd = L.moe_quantize_dx_weights_mxfp8
+    assert qd(G.MOE_BF16, f, f, 8, 64, 48, f, f, None) == G.MOE_EUNSUPPORTED   # I % 32
+    assert qd(G.MOE_BF16, f, f, 8, 80, 32, f, f, None) == G.MOE_EUNSUPPORTED   # H % 32
+    assert qd(G.MOE_BF16, f, f, 0, 64, 32, f, f, None) == G.MOE_EINVAL         # E
+    assert qd(G.MOE_BF16, f, None, 8, 64, 32, f, f, None) == G.MOE_EINVAL      # NULL w_up
+    assert qd(G.MOE_BF16, f, f, 8, 64, 32, ctypes.c_void_p(FAKE + 4), f, None) == G.MOE_EUNSUPPORTED
+    assert qd(7, f, f, 8, 64, 32, f, f, None) == G.MOE_EUNSUPPORTED            # dtype
+    p = _plan()
+    need = L.moe_workspace_bytes(G.OP_LAYER_BWD_MXFP8, G.MOE_BF16, 64, 8, 2, 64, 32, p.M_cap)
+    assert need > L.moe_workspace_bytes(G.OP_LAYER_BWD, G.MOE_BF16, 64, 8, 2, 64, 32, p.M_cap)
+    assert L.moe_workspace_bytes(G.OP_LAYER_BWD_MXFP8, G.MOE_BF16, 64, 8, 2, 64, 40, p.M_cap) == 0
+
+    def call(ws=need, H=64, I=32, wq=f, wsc=f):
+        return L.moe_layer_bwd_mxfp8(f, f, f, f, f, wq, wsc, H, I, ctypes.byref(p), f, f, f, f, f, f, f, ws, None)
+    assert call(ws=need - 1) == G.MOE_EWORKSPACE
+    assert call(I=40) == G.MOE_EUNSUPPORTED
+    assert call(H=72) == G.MOE_EUNSUPPORTED
+    assert call(wq=None) == G.MOE_EINVAL
+    assert call(wsc=ctypes.c_void_p(FAKE + 2)) == G.MOE_EUNSUPPORTED          # scale codes 4-byte aligned
