@@ -216,10 +216,17 @@ def _run_bwd8(T):
     g = D["guards"]
     f32, i32, u8, bf = torch.float32, torch.int32, torch.uint8, torch.bfloat16
     idx, w = g.alloc("idx", (N, k), i32), g.alloc("w", (N, k), f32)
-    G.route_topk(D["logits"], k, bias=D["bias"], idx=idx, w=w)
-    plan = G.Plan(N, E, k, alloc=lambda name, n, dtype: g.alloc("plan." + name, (n,), dtype))
-    G.permute(idx, w, E, plan=plan, ws=g.alloc("ws_perm", (G.workspace_bytes(G.OP_PERMUTE, G.MOE_BF16, N, E, k),),
-                                                u8))
+    probs = g.alloc("probs", (N, E), f32)
+    alloc = lambda name, n, dtype: g.alloc("plan." + name, (n,), dtype)  # noqa: E731
+    if wl.routing == "tr":
+        plan = G.Plan(N, E, k, kind=G.PLAN_TR, mtile=wl.mtile, alloc=alloc)
+        G.route_token_rounding(D["logits"], k, wl.mtile, bias=D["bias"], plan=plan, idx=idx, w=w, probs=probs,
+                               ws=g.alloc("ws_tr", (G.workspace_bytes(G.OP_ROUTE_TR, G.MOE_BF16, N, E, k),), u8))
+    else:
+        G.route_topk(D["logits"], k, bias=D["bias"], idx=idx, w=w, probs=probs)
+        plan = G.Plan(N, E, k, alloc=alloc)
+        G.permute(idx, w, E, plan=plan,
+                  ws=g.alloc("ws_perm", (G.workspace_bytes(G.OP_PERMUTE, G.MOE_BF16, N, E, k),), u8))
     mc = plan.M_cap
     hc, y = g.alloc("hcache", (mc, 2 * I), bf), g.alloc("y", (mc, H), bf)
     G.grouped_gemm_fwd(D["x"], D["wg"], D["wu"], D["wd"], plan, hcache=hc, y=y,
@@ -231,7 +238,7 @@ def _run_bwd8(T):
     for tag in ("bf16", "fp8"):
         o = dict(dx=g.alloc(f"dx_{tag}", (N, H), bf), dw_gate=g.alloc(f"dwg_{tag}", (E, I, H), bf),
                  dw_up=g.alloc(f"dwu_{tag}", (E, I, H), bf), dw_down=g.alloc(f"dwd_{tag}", (E, H, I), bf),
-                 ds=g.alloc(f"ds_{tag}", (N, k), f32))
+                 ds=g.alloc(f"ds_{tag}", (N, k) if wl.routing != "tr" else (mc,), f32))
         if tag == "bf16":
             nb = G.workspace_bytes(G.OP_LAYER_BWD, G.MOE_BF16, N, E, k, H, I, mc)
             ws = g.alloc("ws_bwd", (nb,), u8)
@@ -250,6 +257,7 @@ def _run_bwd8(T):
     o_sc = o_ap + a256(mc * I * 2) + a256(mc * H * 2) + a256(mc * 2 * ((I + 255) // 256) * 4)
     ks = G.mx_scale_cols(2 * I)
     res = dict(plan=plan.host(), outs=outs, wtq=wt[0].cpu().numpy(), wts=wt[1].cpu().numpy(),
+               idx=idx.cpu().numpy(), probs=probs.cpu().numpy(),
                dh_bits=wsh[: m * 2 * I * 2].view(np.uint16).reshape(m, 2 * I),
                dhq=wsh[o_ap: o_ap + m * 2 * I].reshape(m, 2 * I), dhs=wsh[o_sc: o_sc + m * ks].reshape(m, ks))
     return res
@@ -258,7 +266,12 @@ def _run_bwd8(T):
 def _check_bwd8(T, res, toks=None):
     wl = T.wl
     N, E = wl.N, wl.E
-    op = oracle_plan(T)
+    if wl.routing == "tr":
+        # the token-rounding plan, bit-exact given the GPU's own probabilities and indices; the
+        # oracle side then runs on it
+        op = oracle.token_round(res["probs"], res["idx"], wl.mtile)
+    else:
+        op = oracle_plan(T)
     for n in ("counts", "offsets", "row_token", "row_pair"):
         np.testing.assert_array_equal(res["plan"][n], op[n], err_msg=n)
     # the weight operand: bit-exact
@@ -316,6 +329,17 @@ def test_bwd_dx_mxfp8_against_oracle(shape):
     res = _run_bwd8(T)
     res2 = _run_bwd8(T)
     assert np.array_equal(res["outs"]["fp8"]["dx"], res2["outs"]["fp8"]["dx"])
+    _check_bwd8(T, res)
+
+
+def test_bwd_dx_mxfp8_token_rounding():
+    """A token-rounding plan (row capacity above the rows used, dS in row order): dW and dS
+    bitwise as in the bf16 backward, dH's codes bit-exact, dx within 1e-2 on the GPU's codes."""
+    wl = W.custom("bwd8-tr", N=320, H=256, I=128, E=8, k=2, dtype="bf16", bias="normal", bias_std=0.4,
+                  routing="tr", mtile=32, seed=47)
+    T = W.generate(wl)
+    res = _run_bwd8(T)
+    assert int(res["plan"]["offsets"][-1]) > 0
     _check_bwd8(T, res)
 
 
